@@ -1,0 +1,143 @@
+"""fp64 CPU oracle of the gated delta-rule recurrence (ctypes front end).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The HIP
+library never imports it, and it imports nothing from the HIP library.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, IEEE double, token by
+token).  This module only builds/loads it and marshals numpy float64 arrays.
+Every function copies its state argument and returns the updated copy, so
+callers' arrays are never modified.
+
+Functions (each cites the page it follows in ``gdn_oracle.c``):
+  gdn_step      one decode step, state [B,Hv,Dv,Dk]     (metaltile gated_delta.rs)
+  gdn_prefill   varlen prefill over a pool, per token  (pymllm gdn_chunkwise API)
+  comba_step    one Comba step, state [B,H,K,V]         (KBench comba_decode_step)
+  gates         g (log-space) and beta from a, b        (regolith gdn.metal header)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gdn_oracle.c`` into ``liboracle.so`` with gcc (IEEE double)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_gdn_step.restype = ctypes.c_int
+        lib.oracle_gdn_step.argtypes = [_dp] * 7 + [ctypes.c_int] * 5
+        lib.oracle_gdn_prefill.restype = ctypes.c_int
+        lib.oracle_gdn_prefill.argtypes = (
+            [_dp] * 6 + [ctypes.c_int64, _i64p, _i64p, ctypes.c_int, ctypes.c_int64]
+            + [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_int, ctypes.c_double, _dp])
+        lib.oracle_comba_step.restype = ctypes.c_int
+        lib.oracle_comba_step.argtypes = [_dp] * 7 + [ctypes.c_double, _dp] + [ctypes.c_int] * 4
+        lib.oracle_gates.restype = None
+        lib.oracle_gates.argtypes = [_dp] * 6 + [ctypes.c_int64, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def gdn_step(state, q, k, v, g, beta):
+    """One decode step.  state [B,Hv,Dv,Dk], q,k [B,Hk,Dk], v [B,Hv,Dv],
+    g (log-space) and beta [B,Hv].  Returns (state_new, y) in float64."""
+    lib = _load()
+    S = _f64(state).copy()
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, Hv, Dv, Dk = S.shape
+    Hk = q.shape[1]
+    assert q.shape == (B, Hk, Dk) and k.shape == (B, Hk, Dk)
+    assert v.shape == (B, Hv, Dv) and g.shape == (B, Hv) and beta.shape == (B, Hv)
+    y = np.zeros((B, Hv, Dv), dtype=np.float64)
+    rc = lib.oracle_gdn_step(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(y), B, Hk, Hv, Dk, Dv)
+    if rc != 0:
+        raise ValueError("oracle_gdn_step: invalid shape")
+    return S, y
+
+
+def gdn_prefill(q, k, v, g, beta, pool, cache_indices, cu_seqlens, scale=None,
+                l2norm=True, eps=1e-6):
+    """Token-by-token varlen prefill.  q,k [T,Hk,Dk], v [T,Hv,Dv], g/beta [T,Hv],
+    pool [P,Hv,Dv,Dk].  Returns (pool_new, y) in float64; scale None -> Dk^-1/2."""
+    lib = _load()
+    P = _f64(pool).copy()
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    ci = np.ascontiguousarray(np.asarray(cache_indices, dtype=np.int64))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N_s = ci.shape[0]
+    assert cu.shape == (N_s + 1,)
+    if scale is None:
+        scale = Dk ** -0.5
+    y = np.zeros((T, Hv, Dv), dtype=np.float64)
+    rc = lib.oracle_gdn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(P), P.shape[0],
+        ci.ctypes.data_as(_i64p), cu.ctypes.data_as(_i64p), N_s, T, Hk, Hv, Dk, Dv,
+        float(scale), 1 if l2norm else 0, float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_gdn_prefill: invalid shape or index")
+    return P, y
+
+
+def comba_step(state, q, k, v, p, beta, g, scale=None):
+    """One Comba step.  state [B,H,K,V]; q,k,p [B,H,K]; v [B,H,V]; beta,g [B,H].
+    Returns (state_new, o) in float64; scale None -> K^-1/2."""
+    lib = _load()
+    S = _f64(state).copy()
+    q, k, v, p, beta, g = map(_f64, (q, k, v, p, beta, g))
+    B, H, K, V = S.shape
+    if scale is None:
+        scale = K ** -0.5
+    o = np.zeros((B, H, V), dtype=np.float64)
+    rc = lib.oracle_comba_step(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(beta),
+                               _ptr(g), float(scale), _ptr(o), B, H, K, V)
+    if rc != 0:
+        raise ValueError("oracle_comba_step: invalid shape")
+    return S, o
+
+
+def gates(a, b, A_log, dt_bias):
+    """g = -exp(A_log) softplus(a + dt_bias) (log-space) and beta = sigmoid(b);
+    a, b [T,Hv], A_log and dt_bias [Hv].  Returns (g, beta) in float64."""
+    lib = _load()
+    a, b, A_log, dt_bias = map(_f64, (a, b, A_log, dt_bias))
+    T, Hv = a.shape
+    g = np.zeros((T, Hv), dtype=np.float64)
+    beta = np.zeros((T, Hv), dtype=np.float64)
+    lib.oracle_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta), T, Hv)
+    return g, beta

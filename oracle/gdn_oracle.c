@@ -1,0 +1,231 @@
+/*
+ * Plain sequential fp64 CPU oracle of the gated delta-rule recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library: every value here is computed
+ * from its definition, token by token, in double precision, with no chunking,
+ * blocking or fusion.  Callers convert every stored bf16/fp32 input exactly to
+ * double before the call and compare against the double results.
+ *
+ * Sources (the four pages this project is built from):
+ *  - metaltile-std `gated_delta.rs` (docs.rs), module doc, "Recurrence per step"
+ *    and "Layouts": decay, key read, delta, rank-1 write, readout; state
+ *    [B,Hv,Dv,Dk] with Dk fastest; q,k [B,Hk,Dk]; head sharing hk = hv/(Hv/Hk).
+ *  - KBench `comba_decode_step` spec, spec_md and contract_md: the Comba step
+ *    with a separate read key p and a query scale; state [B,H,K,V], V fastest.
+ *  - pymllm `gdn_chunkwise` docs, `gdn_extend_chunkwise` parameters: packed
+ *    variable-length prefill over a state pool picked by cache_indices and
+ *    delimited by cu_seqlens, q/k not pre-normalised, raw gate inputs a, b
+ *    with A_log and dt_bias.
+ *  - regolith `gdn.metal` header comment: gate = exp(-exp(A_log) softplus(a +
+ *    dt_bias)), beta = sigmoid(b), q/k L2 norm with eps 1e-6, q scaled by
+ *    Dk^-1/2.
+ *
+ * Build: gcc -O2 -fPIC -shared -o liboracle.so gdn_oracle.c -lm
+ * (no -ffast-math, no FMA contraction flags: IEEE double throughout).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/*
+ * One gated delta-rule step on one value head, in the order the metaltile
+ * page's "Recurrence per step" gives it.  S is that head's state, stored
+ * value-major: S[j*Dk + i] with j the value index (Dv) and i the key index
+ * (Dk).  `gate_log` is the log-space decay; the gate is exp(gate_log).
+ *   1. decay:      S <- exp(g) S
+ *   2. key read:   kv[j] = sum_i S[j,i] k[i]
+ *   3. delta:      d[j]  = beta (v[j] - kv[j])
+ *   4. write:      S[j,i] <- S[j,i] + d[j] k[i]
+ *   5. readout:    y[j]  = sum_i S[j,i] q[i]   (updated state, no scale)
+ * kv and d are scratch arrays of length Dv.
+ */
+static void gdn_head_step(double* S, const double* q, const double* k,
+                          const double* v, double gate_log, double beta,
+                          double* y, int Dk, int Dv, double* kv, double* d) {
+  const double alpha = exp(gate_log);
+  for (int j = 0; j < Dv; ++j)
+    for (int i = 0; i < Dk; ++i) S[(size_t)j * Dk + i] *= alpha;
+  for (int j = 0; j < Dv; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < Dk; ++i) acc += S[(size_t)j * Dk + i] * k[i];
+    kv[j] = acc;
+  }
+  for (int j = 0; j < Dv; ++j) d[j] = beta * (v[j] - kv[j]);
+  for (int j = 0; j < Dv; ++j)
+    for (int i = 0; i < Dk; ++i) S[(size_t)j * Dk + i] += d[j] * k[i];
+  for (int j = 0; j < Dv; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < Dk; ++i) acc += S[(size_t)j * Dk + i] * q[i];
+    y[j] = acc;
+  }
+}
+
+/*
+ * Decode step for a dense batch (metaltile page, `mt_gated_delta_step`
+ * layouts): state [B,Hv,Dv,Dk] updated in place, q,k [B,Hk,Dk],
+ * v,y [B,Hv,Dv], g (log-space), beta [B,Hv].  Value head hv reads key head
+ * hk = hv / (Hv/Hk) (contiguous groups, the page's DISPATCH INVARIANTS).
+ * Returns 0, or -1 on an invalid shape.
+ */
+int oracle_gdn_step(double* state, const double* q, const double* k,
+                    const double* v, const double* g, const double* beta,
+                    double* y, int B, int Hk, int Hv, int Dk, int Dv) {
+  if (B < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return -1;
+  double* kv = (double*)malloc(sizeof(double) * (size_t)Dv * 2);
+  if (!kv) return -1;
+  double* d = kv + Dv;
+  const int group = Hv / Hk;
+  for (int b = 0; b < B; ++b) {
+    for (int hv = 0; hv < Hv; ++hv) {
+      const int hk = hv / group;
+      const size_t n = (size_t)b * Hv + hv;
+      const size_t qk = ((size_t)b * Hk + hk) * Dk;
+      gdn_head_step(state + n * Dv * Dk, q + qk, k + qk, v + n * Dv, g[n],
+                    beta[n], y + n * Dv, Dk, Dv, kv, d);
+    }
+  }
+  free(kv);
+  return 0;
+}
+
+/*
+ * x / sqrt(sum x^2 + eps), the L2 normalisation the regolith kernel applies
+ * to q and k (its header comment; eps = 1e-6 there).  An all-zero row maps
+ * to zero.
+ */
+static void l2_normalise(const double* x, double* out, int n, double eps) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
+  const double r = 1.0 / sqrt(ss + eps);
+  for (int i = 0; i < n; ++i) out[i] = x[i] * r;
+}
+
+/*
+ * Variable-length prefill over a state pool (pymllm `gdn_extend_chunkwise`
+ * contract), computed token by token with no chunking:
+ *   for each sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1) and each
+ *   value head hv, the state pool[cache_indices[s], hv] is advanced by one
+ *   gated delta-rule step per token and written back in place.
+ * q,k [T,Hk,Dk]; v,y [T,Hv,Dv]; g (log-space), beta [T,Hv];
+ * pool [pool_size,Hv,Dv,Dk]; cache_indices [N_s]; cu_seqlens [N_s+1].
+ * If l2norm != 0 the step uses k/sqrt(|k|^2+eps) and
+ * scale*q/sqrt(|q|^2+eps); otherwise k and scale*q.
+ * Slots not named in cache_indices are never touched.
+ * Returns 0, or -1 on an invalid shape or index.
+ */
+int oracle_gdn_prefill(const double* q, const double* k, const double* v,
+                       const double* g, const double* beta, double* pool,
+                       int64_t pool_size, const int64_t* cache_indices,
+                       const int64_t* cu_seqlens, int N_s, int64_t T_tot,
+                       int Hk, int Hv, int Dk, int Dv, double scale, int l2norm,
+                       double eps, double* y) {
+  if (N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return -1;
+  if (N_s > 0 && (cu_seqlens[0] != 0 || cu_seqlens[N_s] != T_tot)) return -1;
+  for (int s = 0; s < N_s; ++s) {
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    if (cache_indices[s] < 0 || cache_indices[s] >= pool_size) return -1;
+  }
+  double* work = (double*)malloc(sizeof(double) * ((size_t)Dv * 2 + (size_t)Dk * 2));
+  if (!work) return -1;
+  double* kv = work;
+  double* d = kv + Dv;
+  double* kn = d + Dv;
+  double* qn = kn + Dk;
+  const int group = Hv / Hk;
+  for (int s = 0; s < N_s; ++s) {
+    const int64_t slot = cache_indices[s];
+    for (int hv = 0; hv < Hv; ++hv) {
+      const int hk = hv / group;
+      double* S = pool + ((size_t)slot * Hv + hv) * (size_t)Dv * Dk;
+      for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+        const double* kt = k + ((size_t)t * Hk + hk) * Dk;
+        const double* qt = q + ((size_t)t * Hk + hk) * Dk;
+        if (l2norm) {
+          l2_normalise(kt, kn, Dk, eps);
+          l2_normalise(qt, qn, Dk, eps);
+        } else {
+          memcpy(kn, kt, sizeof(double) * Dk);
+          memcpy(qn, qt, sizeof(double) * Dk);
+        }
+        for (int i = 0; i < Dk; ++i) qn[i] *= scale;
+        const size_t th = (size_t)t * Hv + hv;
+        gdn_head_step(S, qn, kn, v + th * Dv, g[th], beta[th], y + th * Dv, Dk,
+                      Dv, kv, d);
+      }
+    }
+  }
+  free(work);
+  return 0;
+}
+
+/*
+ * One Comba step for a dense batch (KBench `comba_decode_step` spec_md,
+ * elementwise form), state [B,H,K,V] with V fastest, updated in place:
+ *   S[i,j] <- exp(g) S[i,j]
+ *   u[j]    = beta (v[j] - sum_i p[i] S[i,j])     (read with p)
+ *   S[i,j] <- S[i,j] + k[i] u[j]                   (write with k)
+ *   o[j]    = sum_i (scale q[i]) S[i,j]            (updated state)
+ * q,k,p [B,H,K]; v,o [B,H,V]; beta, g [B,H].
+ * Returns 0, or -1 on an invalid shape.
+ */
+int oracle_comba_step(double* state, const double* q, const double* k,
+                      const double* v, const double* p, const double* beta,
+                      const double* g, double scale, double* o, int B, int H,
+                      int K, int V) {
+  if (B < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
+  double* u = (double*)malloc(sizeof(double) * (size_t)V);
+  if (!u) return -1;
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const size_t n = (size_t)b * H + h;
+      double* S = state + n * (size_t)K * V;
+      const double* qn = q + n * K;
+      const double* kn = k + n * K;
+      const double* pn = p + n * K;
+      const double* vn = v + n * V;
+      const double alpha = exp(g[n]);
+      for (int i = 0; i < K; ++i)
+        for (int j = 0; j < V; ++j) S[(size_t)i * V + j] *= alpha;
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += pn[i] * S[(size_t)i * V + j];
+        u[j] = beta[n] * (vn[j] - acc);
+      }
+      for (int i = 0; i < K; ++i)
+        for (int j = 0; j < V; ++j) S[(size_t)i * V + j] += kn[i] * u[j];
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += (scale * qn[i]) * S[(size_t)i * V + j];
+        o[n * V + j] = acc;
+      }
+    }
+  }
+  free(u);
+  return 0;
+}
+
+/*
+ * Gate prologue for prefill (pymllm `gdn_extend_chunkwise` parameters a, b,
+ * A_log, dt_bias; formula from the regolith header comment), in exact fp64:
+ *   g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (log-space)
+ *   beta[t,h] = 1 / (1 + exp(-b[t,h]))
+ * softplus(x) = log(1 + e^x), evaluated as max(x,0) + log1p(exp(-|x|)),
+ * which is the same function without overflow (no threshold).
+ */
+void oracle_gates(const double* a, const double* b, const double* A_log,
+                  const double* dt_bias, double* g, double* beta, int64_t T,
+                  int Hv) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int h = 0; h < Hv; ++h) {
+      const size_t n = (size_t)t * Hv + h;
+      const double x = a[n] + dt_bias[h];
+      const double sp = (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+      g[n] = -exp(A_log[h]) * sp;
+      beta[n] = 1.0 / (1.0 + exp(-b[n]));
+    }
+  }
+}

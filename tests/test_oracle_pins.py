@@ -1,0 +1,413 @@
+"""Pins of the fp64 CPU oracle against closed forms, invariants, brute force
+and the values the pages print.  CPU only.
+
+Every test here checks the oracle against something other than itself:
+  * closed forms of the gated delta rule (unit key with beta = 1 and no decay
+    maps k to v; beta = 0 is pure decay; one token from a zero state gives
+    y = beta (q.k) v);
+  * the Comba error magnitudes the KBench spec prints for four wrong kernels;
+  * special cases of the gate and L2-norm formulas;
+  * brute force of the chunked WY algebra against the token recurrence.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import wy_chunkwise as wy
+from gated_deltanet_linear_gdn_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_state(rng, *shape, scale=0.5):
+    return scale * rng.standard_normal(shape)
+
+
+def _unit(rng, *shape):
+    z = rng.standard_normal(shape)
+    return z / np.linalg.norm(z, axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------- decode
+
+
+@pytest.mark.parametrize("Dk,Dv", [(32, 32), (64, 48), (128, 128)])
+def test_unit_key_beta_one_no_decay_maps_k_to_v(Dk, Dv):
+    rng = np.random.default_rng(1)
+    B, Hk, Hv = 2, 1, 2
+    S = _rand_state(rng, B, Hv, Dv, Dk)
+    q = rng.standard_normal((B, Hk, Dk))
+    k = _unit(rng, B, Hk, Dk)
+    v = rng.standard_normal((B, Hv, Dv))
+    g = np.zeros((B, Hv))
+    beta = np.ones((B, Hv))
+    S1, _ = oracle.gdn_step(S, q, k, v, g, beta)
+    for b in range(B):
+        for h in range(Hv):
+            # stored [Dv, Dk]: S1 @ k == v
+            np.testing.assert_allclose(S1[b, h] @ k[b, 0], v[b, h], rtol=0, atol=1e-12)
+            # a direction orthogonal to k reads the same before and after
+            u = rng.standard_normal(Dk)
+            u -= (u @ k[b, 0]) * k[b, 0]
+            np.testing.assert_allclose(S1[b, h] @ u, S[b, h] @ u, rtol=0, atol=1e-12)
+
+
+def test_beta_zero_is_pure_decay():
+    rng = np.random.default_rng(2)
+    B, Hk, Hv, Dk, Dv = 3, 2, 4, 32, 16
+    S = _rand_state(rng, B, Hv, Dv, Dk)
+    q = rng.standard_normal((B, Hk, Dk))
+    k = _unit(rng, B, Hk, Dk)
+    v = rng.standard_normal((B, Hv, Dv))
+    g = -rng.random((B, Hv))
+    S1, y = oracle.gdn_step(S, q, k, v, g, np.zeros((B, Hv)))
+    a = np.exp(g)[:, :, None, None]
+    np.testing.assert_allclose(S1, a * S, rtol=1e-15, atol=0)
+    hk = np.arange(Hv) // (Hv // Hk)
+    y_ref = np.einsum("bhji,bhi->bhj", a * S, q[:, hk])
+    np.testing.assert_allclose(y, y_ref, rtol=1e-13, atol=1e-13)
+
+
+def test_zero_state_single_token():
+    rng = np.random.default_rng(3)
+    B, Hk, Hv, Dk, Dv = 2, 2, 6, 64, 32
+    q = rng.standard_normal((B, Hk, Dk))
+    k = rng.standard_normal((B, Hk, Dk))   # any k: from zero the gate cannot matter
+    v = rng.standard_normal((B, Hv, Dv))
+    g = -rng.random((B, Hv))
+    beta = rng.random((B, Hv))
+    S1, y = oracle.gdn_step(np.zeros((B, Hv, Dv, Dk)), q, k, v, g, beta)
+    hk = np.arange(Hv) // (Hv // Hk)
+    qk = np.einsum("bhi,bhi->bh", q[:, hk], k[:, hk])
+    np.testing.assert_allclose(y, beta[..., None] * qk[..., None] * v, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S1, beta[..., None, None] * v[..., :, None] * k[:, hk][..., None, :],
+                               rtol=1e-15, atol=0)
+
+
+def test_matrix_form_of_the_step():
+    """S' = a (I - b k k^T) S + b k v^T in key-major form (stored as its transpose)."""
+    rng = np.random.default_rng(4)
+    B, Hk, Hv, Dk, Dv = 2, 1, 3, 32, 24
+    S = _rand_state(rng, B, Hv, Dv, Dk)
+    q = rng.standard_normal((B, Hk, Dk))
+    k = _unit(rng, B, Hk, Dk)
+    v = rng.standard_normal((B, Hv, Dv))
+    g = -rng.random((B, Hv))
+    beta = rng.random((B, Hv))
+    S1, y = oracle.gdn_step(S, q, k, v, g, beta)
+    for b in range(B):
+        for h in range(Hv):
+            kk = k[b, 0]
+            Sm = S[b, h].T                      # Dk x Dv, math orientation
+            Sn = np.exp(g[b, h]) * (np.eye(Dk) - beta[b, h] * np.outer(kk, kk)) @ Sm \
+                + beta[b, h] * np.outer(kk, v[b, h])
+            np.testing.assert_allclose(S1[b, h], Sn.T, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(y[b, h], Sn.T @ q[b, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_head_sharing_is_contiguous_groups():
+    """Hv/Hk value heads in a row share one key head (hk = hv // (Hv/Hk))."""
+    rng = np.random.default_rng(5)
+    B, Hk, Hv, Dk, Dv = 2, 2, 6, 32, 32
+    S = _rand_state(rng, B, Hv, Dv, Dk)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act="f32")
+    S1, y1 = oracle.gdn_step(S, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
+    rep = Hv // Hk
+    qx = np.repeat(tok["q"], rep, axis=1)
+    kx = np.repeat(tok["k"], rep, axis=1)
+    S2, y2 = oracle.gdn_step(S, qx, kx, tok["v"], tok["g"], tok["beta"])
+    assert np.array_equal(S1, S2) and np.array_equal(y1, y2)
+    # the modulo mapping (hk = hv % Hk) is a different computation
+    S3, _ = oracle.gdn_step(S, np.tile(tok["q"], (1, rep, 1)), np.tile(tok["k"], (1, rep, 1)),
+                            tok["v"], tok["g"], tok["beta"])
+    assert np.max(np.abs(S3 - S1)) > 1e-3
+
+
+def test_oracle_rejects_bad_head_ratio():
+    with pytest.raises(ValueError):
+        oracle.gdn_step(np.zeros((1, 3, 4, 4)), np.zeros((1, 2, 4)), np.zeros((1, 2, 4)),
+                        np.zeros((1, 3, 4)), np.zeros((1, 3)), np.zeros((1, 3)))
+
+
+# ----------------------------------------------------------------- comba
+
+
+def test_comba_zero_state_closed_form():
+    rng = np.random.default_rng(6)
+    B, H, K, V = 2, 3, 64, 32
+    q = rng.standard_normal((B, H, K))
+    k = _unit(rng, B, H, K)
+    p = _unit(rng, B, H, K)
+    v = rng.standard_normal((B, H, V))
+    beta = rng.random((B, H))
+    g = -rng.random((B, H))
+    S1, o = oracle.comba_step(np.zeros((B, H, K, V)), q, k, v, p, beta, g)
+    sc = K ** -0.5
+    qk = np.einsum("bhi,bhi->bh", q, k)
+    np.testing.assert_allclose(o, (beta * sc * qk)[..., None] * v, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S1, beta[..., None, None] * k[..., :, None] * v[..., None, :],
+                               rtol=1e-15, atol=0)
+
+
+def test_comba_with_p_equal_k_is_the_gated_delta_rule():
+    """Reading with p = k makes Comba the GDN step on the transposed state with
+    q pre-scaled (two independently written oracle functions agree)."""
+    rng = np.random.default_rng(7)
+    B, H, K, V = 2, 4, 32, 48
+    S = _rand_state(rng, B, H, K, V)
+    q = rng.standard_normal((B, H, K))
+    k = _unit(rng, B, H, K)
+    v = rng.standard_normal((B, H, V))
+    beta = rng.random((B, H))
+    g = -rng.random((B, H))
+    sc = 0.37
+    Sc, oc = oracle.comba_step(S, q, k, v, k, beta, g, scale=sc)
+    Sg, yg = oracle.gdn_step(np.swapaxes(S, -1, -2), sc * q, k, v, g, beta)
+    np.testing.assert_allclose(Sc, np.swapaxes(Sg, -1, -2), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oc, yg, rtol=1e-12, atol=1e-13)
+
+
+def _relF(x, ref):
+    return float(np.linalg.norm((x - ref).ravel()) / np.linalg.norm(ref.ravel()))
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, val = line.split()
+                vals[key] = float(val)
+    return vals
+
+
+def test_comba_wrong_kernels_land_where_the_spec_says():
+    """Plant each mistake the KBench spec describes into the oracle's inputs or
+    outputs and check the error lands near the printed magnitude (the worse
+    of state_new and o, relative Frobenius)."""
+    gold = _read_golden("comba_mutant_errors.txt")
+    rng = np.random.default_rng(0)
+    B, H, K, V = 32, 8, 128, 128
+    S = np.zeros((B, H, K, V))
+    for _ in range(synth.WARMUP_STEPS):
+        t = synth.comba_token(rng, B, H, K, V)
+        S, _ = oracle.comba_step(S, t["q"], t["k"], t["v"], t["p"], t["beta"], t["g"])
+    S = S.astype(np.float32)                     # the state is handed over in fp32
+    t = synth.comba_token(rng, B, H, K, V)
+    args = (t["q"], t["k"], t["v"], t["p"], t["beta"], t["g"])
+    Sr, orf = oracle.comba_step(S, *args)
+
+    def worst(Sx, ox):
+        return max(_relF(Sx, Sr), _relF(ox, orf))
+
+    errs = {
+        "bf16_state": worst(synth.round_bf16(Sr.astype(np.float32)), orf),
+        "no_forget_gate": worst(*oracle.comba_step(S, t["q"], t["k"], t["v"], t["p"], t["beta"],
+                                                   np.zeros_like(t["g"]))),
+        "read_with_k": worst(*oracle.comba_step(S, t["q"], t["k"], t["v"], t["k"], t["beta"], t["g"])),
+        "no_correction": worst(*oracle.comba_step(S, t["q"], t["k"], t["v"], np.zeros_like(t["p"]),
+                                                  t["beta"], t["g"])),
+    }
+    band = {"bf16_state": 0.25, "no_forget_gate": 0.1, "read_with_k": 0.1, "no_correction": 0.1}
+    for name, e in errs.items():
+        assert abs(e / gold[name] - 1.0) < band[name], (name, e, gold[name])
+    # a correct fp32 evaluation of the same step sits at the spec's ~1e-7
+    S32, o32 = _comba_fp32_numpy(S, *args, scale=K ** -0.5)
+    assert worst(S32, o32) < 10 * gold["correct_fp32"]
+
+
+def _comba_fp32_numpy(S, q, k, v, p, beta, g, scale):
+    """The Comba step in float32 numpy matrix form (spec_md), for calibration."""
+    f = np.float32
+    S = S.astype(f) * np.exp(g.astype(f))[..., None, None]
+    u = (v.astype(f) - np.einsum("bhij,bhi->bhj", S, p.astype(f))) * beta.astype(f)[..., None]
+    S = S + k.astype(f)[..., :, None] * u[..., None, :]
+    o = np.einsum("bhij,bhi->bhj", S, (q.astype(f) * f(scale)))
+    return S, o
+
+
+# ----------------------------------------------------------------- gates
+
+
+def test_gate_special_values():
+    Hv = 4
+    A_log = np.array([0.0, 0.5, 1.0, 2.7])
+    dt = np.array([0.3, -0.2, 1.0, 0.0])
+    a = np.tile(-dt, (3, 1))                      # a + dt_bias = 0 -> softplus = ln 2
+    b = np.zeros((3, Hv))
+    g, beta = oracle.gates(a, b, A_log, dt)
+    np.testing.assert_allclose(g, np.tile(-np.exp(A_log) * np.log(2.0), (3, 1)), rtol=1e-15)
+    np.testing.assert_allclose(beta, 0.5, rtol=0, atol=0)
+    # A_log = 0: g = -softplus(x); large x: softplus(x) -> x; very negative: -> e^x
+    x = np.array([[30.0, -30.0, 2.0, -1.0]])
+    g, beta = oracle.gates(x, x, np.zeros(Hv), np.zeros(Hv))
+    np.testing.assert_allclose(g[0, 0], -30.0, rtol=1e-13)
+    np.testing.assert_allclose(g[0, 1], -np.exp(-30.0), rtol=1e-12)
+    np.testing.assert_allclose(g[0, 2], -np.log1p(np.exp(2.0)), rtol=1e-15)
+    np.testing.assert_allclose(beta[0], 1.0 / (1.0 + np.exp(-x[0])), rtol=1e-15)
+    # symmetric pair: sigmoid(x) + sigmoid(-x) = 1, softplus(x) - softplus(-x) = x
+    g1, b1 = oracle.gates(np.array([[1.7]]), np.array([[1.7]]), np.zeros(1), np.zeros(1))
+    g2, b2 = oracle.gates(np.array([[-1.7]]), np.array([[-1.7]]), np.zeros(1), np.zeros(1))
+    np.testing.assert_allclose(b1 + b2, 1.0, rtol=1e-15)
+    np.testing.assert_allclose(-g1 + g2, 1.7, rtol=1e-14)
+
+
+# ----------------------------------------------------------------- prefill
+
+
+def _prefill_case(rng, lengths, Hk=2, Hv=4, Dk=16, Dv=8, pool=5):
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool, act="f32")
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    P0 = _rand_state(rng, pool, Hv, Dv, Dk)
+    return inp, g, beta, P0
+
+
+def test_l2norm_special_rows():
+    """A unit key becomes k (1 + 1e-6)^-1/2; a zero row stays zero (no NaN)."""
+    rng = np.random.default_rng(8)
+    Dk, Dv = 16, 8
+    k = _unit(rng, 1, 1, Dk)
+    q = _unit(rng, 1, 1, Dk)
+    v = rng.standard_normal((1, 1, Dv))
+    P, y = oracle.gdn_prefill(q, k, v, np.zeros((1, 1)), np.ones((1, 1)), np.zeros((1, 1, Dv, Dk)),
+                              [0], [0, 1], scale=1.0)
+    c = (1 + 1e-6) ** -0.5
+    np.testing.assert_allclose(P[0, 0], np.outer(v[0, 0], c * k[0, 0]), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(y[0, 0], c * c * (q[0, 0] @ k[0, 0]) * v[0, 0], rtol=1e-13, atol=1e-15)
+    P, y = oracle.gdn_prefill(np.zeros((1, 1, Dk)), np.zeros((1, 1, Dk)), v, np.zeros((1, 1)),
+                              np.ones((1, 1)), np.zeros((1, 1, Dv, Dk)), [0], [0, 1])
+    assert np.all(P == 0) and np.all(y == 0)
+
+
+def test_prefill_is_the_decode_loop():
+    """Prefill equals repeated decode steps on normalised, pre-scaled q/k."""
+    rng = np.random.default_rng(9)
+    lengths = [5, 0, 3]
+    inp, g, beta, P0 = _prefill_case(rng, lengths)
+    for name in ("q", "k", "v"):
+        inp[name] = inp[name].astype(np.float64)
+    P, y = oracle.gdn_prefill(inp["q"], inp["k"], inp["v"], g, beta, P0, inp["cache_indices"],
+                              inp["cu_seqlens"])
+    Dk = inp["q"].shape[-1]
+    nrm = lambda x: x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-6)
+    cu, ci = inp["cu_seqlens"], inp["cache_indices"]
+    for s in range(len(lengths)):
+        S = P0[ci[s]][None]
+        for t in range(cu[s], cu[s + 1]):
+            S, ys = oracle.gdn_step(S, (Dk ** -0.5) * nrm(inp["q"][t])[None], nrm(inp["k"][t])[None],
+                                    inp["v"][t][None], g[t][None], beta[t][None])
+            np.testing.assert_allclose(y[t], ys[0], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(P[ci[s]], S[0], rtol=1e-13, atol=1e-14)
+
+
+def test_prefill_decay_only():
+    """beta = 0: S_T = exp(sum g) S_0 and y_t = exp(G_t) S_0 q^_t."""
+    rng = np.random.default_rng(10)
+    inp, g, beta, P0 = _prefill_case(rng, [7])
+    P, y = oracle.gdn_prefill(inp["q"], inp["k"], inp["v"], g, np.zeros_like(beta), P0,
+                              inp["cache_indices"], inp["cu_seqlens"])
+    slot = inp["cache_indices"][0]
+    G = np.cumsum(g, axis=0)                          # [T, Hv]
+    np.testing.assert_allclose(P[slot], np.exp(G[-1])[:, None, None] * P0[slot], rtol=1e-13)
+    Dk = inp["q"].shape[-1]
+    q64 = inp["q"].astype(np.float64)
+    qn = q64 / np.sqrt(np.sum(q64 ** 2, -1, keepdims=True) + 1e-6) * Dk ** -0.5
+    hk = np.arange(4) // 2
+    for t in range(7):
+        ref = np.exp(G[t])[:, None] * np.einsum("hji,hi->hj", P0[slot], qn[t, hk])
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_orthonormal_keys_closed_form():
+    """beta = 1, no decay, orthonormal keys, no L2 norm:
+    S_T (key-major) = (I - sum k k^T) S_0 + sum k v^T."""
+    rng = np.random.default_rng(11)
+    Dk, Dv, T = 16, 8, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    k = Qm[:, :T].T[:, None, :]                      # [T,1,Dk] orthonormal rows
+    q = rng.standard_normal((T, 1, Dk))
+    v = rng.standard_normal((T, 1, Dv))
+    S0 = _rand_state(rng, 1, 1, Dv, Dk)
+    P, _ = oracle.gdn_prefill(q, k, v, np.zeros((T, 1)), np.ones((T, 1)), S0, [0], [0, T],
+                              scale=1.0, l2norm=False)
+    Kt = k[:, 0, :]
+    ref = S0[0, 0].T
+    ref = (np.eye(Dk) - Kt.T @ Kt) @ ref + Kt.T @ v[:, 0, :]
+    np.testing.assert_allclose(P[0, 0], ref.T, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_index_handling():
+    """Unreferenced slots are bitwise untouched; zero-length sequences are no-ops;
+    the order of sequences in the packed batch does not change any result."""
+    rng = np.random.default_rng(12)
+    lengths = [4, 0, 6]
+    inp, g, beta, P0 = _prefill_case(rng, lengths, pool=6)
+    ci, cu = inp["cache_indices"], inp["cu_seqlens"]
+    P, y = oracle.gdn_prefill(inp["q"], inp["k"], inp["v"], g, beta, P0, ci, cu)
+    untouched = [s for s in range(6) if s not in (ci[0], ci[2])]
+    for s in untouched:
+        assert np.array_equal(P[s], P0[s])
+    # reverse the packed order of the three sequences
+    order = [2, 1, 0]
+    segs = [np.arange(cu[s], cu[s + 1]) for s in order]
+    perm = np.concatenate(segs)
+    cu2 = synth.cu_from_lengths([lengths[s] for s in order])
+    P2, y2 = oracle.gdn_prefill(inp["q"][perm], inp["k"][perm], inp["v"][perm], g[perm], beta[perm],
+                                P0, ci[order], cu2)
+    assert np.array_equal(P2, P)
+    assert np.array_equal(y2, y[perm])
+
+
+def test_prefill_rejects_bad_indices():
+    z = np.zeros
+    with pytest.raises(ValueError):
+        oracle.gdn_prefill(z((2, 1, 4)), z((2, 1, 4)), z((2, 1, 4)), z((2, 1)), z((2, 1)),
+                           z((2, 1, 4, 4)), [2], [0, 2])
+    with pytest.raises(ValueError):
+        oracle.gdn_prefill(z((2, 1, 4)), z((2, 1, 4)), z((2, 1, 4)), z((2, 1)), z((2, 1)),
+                           z((2, 1, 4, 4)), [0], [0, 3])
+
+
+# ------------------------------------------------- chunked algebra, brute force
+
+
+def _one_head_case(rng, T, Dk=8, Dv=5):
+    Q = rng.standard_normal((T, Dk))
+    K = _unit(rng, T, Dk)
+    V = rng.standard_normal((T, Dv))
+    g = np.log(rng.uniform(0.5, 1.0, size=T))
+    beta = rng.uniform(0.1, 1.0, size=T)
+    S0 = _rand_state(rng, Dv, Dk)
+    return S0, Q, K, V, g, beta
+
+
+def _token_head(S0, Q, K, V, g, beta):
+    T, Dk = Q.shape
+    P, y = oracle.gdn_prefill(Q[:, None], K[:, None], V[:, None], g[:, None], beta[:, None],
+                              S0[None, None], [0], [0, T], scale=1.0, l2norm=False)
+    return y[:, 0], P[0, 0]
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("form", ["ratio", "page"])
+def test_chunked_forms_match_the_token_recurrence(chunk, form):
+    rng = np.random.default_rng(100 + chunk)
+    S0, Q, K, V, g, beta = _one_head_case(rng, T=19)   # 19: a ragged last chunk
+    y_ref, S_ref = _token_head(S0, Q, K, V, g, beta)
+    O, S = wy.chunked_head(S0, Q, K, V, g, beta, chunk, form=form)
+    np.testing.assert_allclose(O, y_ref, rtol=0, atol=1e-12 * np.abs(y_ref).max())
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=1e-12 * np.abs(S_ref).max())
+
+
+def test_printed_w_recursion_fails_from_three_tokens():
+    """Taken literally, the page's w line only agrees for chunks of <= 2 tokens."""
+    rng = np.random.default_rng(200)
+    S0, Q, K, V, g, beta = _one_head_case(rng, T=6)
+    y_ref, S_ref = _token_head(S0, Q, K, V, g, beta)
+    O2, S2 = wy.chunked_head(S0, Q, K, V, g, beta, 2, form="page", printed_w=True)
+    assert np.max(np.abs(S2 - S_ref)) < 1e-12
+    O6, S6 = wy.chunked_head(S0, Q, K, V, g, beta, 6, form="page", printed_w=True)
+    assert np.max(np.abs(S6 - S_ref)) > 1e-3
