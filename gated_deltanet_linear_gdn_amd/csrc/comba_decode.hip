@@ -1,0 +1,164 @@
+// comba_decode_step: one Comba token (gated delta rule with a decoupled read
+// key) for a dense batch.
+//
+// Math (KBench `comba_decode_step` spec, spec_md): for each (b, h) slice
+// S [K, V] (V contiguous), gate a = exp(g):
+//   u_j = beta (v_j - sum_i p_i a S[i,j]),  S'[i,j] = a S[i,j] + k_i u_j,
+//   o_j = sum_i (scale q_i) S'[i,j].
+//
+// Design (gfx950, HBM-bound): the reductions run down K, across rows, so a
+// workgroup (256 threads) holds the whole K x V slice in registers: a row of
+// V floats is V/4 lanes x float4, the 256/(V/4) row groups each own K/RG
+// consecutive rows.  One pass computes, per lane, partial column sums of
+// p_i S[i,:] and (scale q_i) S[i,:] over its rows (and the scalar
+// sum_i scale q_i k_i); the row groups combine them through LDS behind one
+// barrier.  Then u = beta (v - a Sp), o = a Sq + (scale q . k) u (the exact
+// identity for the readout from the updated state), and every lane writes
+// its rows a S + k_i u once.  The state crosses HBM exactly twice.
+
+#include "gdn_device.h"
+#include "gdn_host.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int K, int V, typename T>
+__global__ __launch_bounds__(kThreads) void comba_decode_kernel(
+    const float* state, float* state_new, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ p, const T* __restrict__ beta,
+    const float* __restrict__ g, T* __restrict__ o, float scale) {
+  constexpr int LPR = V / 4;             // lanes per row
+  constexpr int RG = kThreads / LPR;     // row groups
+  constexpr int RPT = K / RG;            // rows per thread (consecutive)
+  static_assert(K % RG == 0 && RPT >= 1, "shape");
+
+  __shared__ f32x4 red_p[RG][LPR];
+  __shared__ f32x4 red_q[RG][LPR];
+  __shared__ float red_kq[RG];
+
+  const int slice = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c4 = tid % LPR;
+  const int rg = tid / LPR;
+  const int r0 = rg * RPT;
+
+  const size_t soff = static_cast<size_t>(slice) * K * V + static_cast<size_t>(r0) * V + c4 * 4;
+  f32x4 s[RPT];
+#pragma unroll
+  for (int n = 0; n < RPT; ++n) s[n] = load_stream(state + soff + static_cast<size_t>(n) * V);
+
+  const size_t koff = static_cast<size_t>(slice) * K + r0;
+  float pr[RPT], qr[RPT], kr[RPT];
+#pragma unroll
+  for (int n = 0; n < RPT; ++n) {
+    pr[n] = Act<T>::load(p + koff + n);
+    qr[n] = scale * Act<T>::load(q + koff + n);
+    kr[n] = Act<T>::load(k + koff + n);
+  }
+  const f32x4 vv = Act<T>::load4(v + static_cast<size_t>(slice) * V + c4 * 4);
+  const float gate = expf(g[slice]);
+  const float bt = Act<T>::load(beta + slice);
+
+  f32x4 sp = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int n = 0; n < RPT; ++n) {
+    sp += pr[n] * s[n];
+    sq += qr[n] * s[n];
+    kq += qr[n] * kr[n];
+  }
+  red_p[rg][c4] = sp;
+  red_q[rg][c4] = sq;
+  if (c4 == 0) red_kq[rg] = kq;
+  __syncthreads();
+  sp = red_p[0][c4];
+  sq = red_q[0][c4];
+  kq = red_kq[0];
+#pragma unroll
+  for (int r = 1; r < RG; ++r) {
+    sp += red_p[r][c4];
+    sq += red_q[r][c4];
+    kq += red_kq[r];
+  }
+
+  const f32x4 u = bt * (vv - gate * sp);
+  if (rg == 0) Act<T>::store4(o + static_cast<size_t>(slice) * V + c4 * 4, gate * sq + kq * u);
+#pragma unroll
+  for (int n = 0; n < RPT; ++n)
+    store_stream(state_new + soff + static_cast<size_t>(n) * V, gate * s[n] + kr[n] * u);
+}
+
+template <int K, int V, typename T>
+int launch_kv(const float* state, float* state_new, const void* q, const void* k,
+              const void* v, const void* p, const void* beta, const float* g, void* o,
+              long slices, float scale, hipStream_t stream) {
+  if (slices > 0x7fffffffL) return GDN_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((comba_decode_kernel<K, V, T>), dim3(static_cast<unsigned>(slices)),
+                     dim3(kThreads), 0, stream, state, state_new, static_cast<const T*>(q),
+                     static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<const T*>(p), static_cast<const T*>(beta), g,
+                     static_cast<T*>(o), scale);
+  return launch_status();
+}
+
+template <int K, typename T>
+int launch_k(const float* state, float* state_new, const void* q, const void* k,
+             const void* v, const void* p, const void* beta, const float* g, void* o,
+             long slices, int V, float scale, hipStream_t stream) {
+  switch (V) {
+    case 32: return launch_kv<K, 32, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+    case 64: return launch_kv<K, 64, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+    case 128: return launch_kv<K, 128, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+    case 256:
+      if constexpr (K <= 128)
+        return launch_kv<K, 256, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+      break;
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+template <typename T>
+int launch(const float* state, float* state_new, const void* q, const void* k, const void* v,
+           const void* p, const void* beta, const float* g, void* o, long slices, int K, int V,
+           float scale, hipStream_t stream) {
+  switch (K) {
+    case 32: return launch_k<32, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 64: return launch_k<64, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 128: return launch_k<128, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 256: return launch_k<256, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" int comba_decode_step(const float* state, float* state_new, const void* q,
+                                 const void* k, const void* v, const void* p,
+                                 const void* beta, const float* g, void* o, int B, int H,
+                                 int K, int V, float scale, gdn_dtype act,
+                                 hipStream_t stream) {
+  using namespace gdn;
+  if (B < 0 || H < 0 || K <= 0 || V <= 0) return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (!pow2_head(K) || !pow2_head(V) || (K == 256 && V == 256)) return GDN_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return GDN_OK;
+  if (!state || !state_new || !q || !k || !v || !p || !beta || !g || !o) return GDN_ERR_NULL;
+  if (!aligned16(state) || !aligned16(state_new) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(p) || !aligned16(v) || !aligned16(o))
+    return GDN_ERR_ALIGN;
+  const size_t state_bytes = static_cast<size_t>(B) * H * K * V * sizeof(float);
+  if (state_new != state && overlaps(state, state_bytes, state_new, state_bytes))
+    return GDN_ERR_ALIAS;
+  const size_t o_bytes = static_cast<size_t>(B) * H * V * act_bytes(act);
+  if (overlaps(o, o_bytes, state_new, state_bytes) || overlaps(o, o_bytes, state, state_bytes))
+    return GDN_ERR_ALIAS;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+  const long slices = static_cast<long>(B) * H;
+  if (act == GDN_BF16)
+    return launch<bf16>(state, state_new, q, k, v, p, beta, g, o, slices, K, V, scale, stream);
+  return launch<float>(state, state_new, q, k, v, p, beta, g, o, slices, K, V, scale, stream);
+}

@@ -1,0 +1,156 @@
+// gdn_decode_step: one gated delta-rule token for a dense decode batch.
+//
+// Math (metaltile-std `gated_delta.rs`, module doc "Recurrence per step"):
+// for each (b, hv) slice S [Dv, Dk] (Dk contiguous), gate a = exp(g):
+//   kv_j = sum_i (a S[j,i]) k_i,  d_j = beta (v_j - kv_j),
+//   S'[j,i] = a S[j,i] + d_j k_i,  y_j = sum_i S'[j,i] q_i.
+//
+// Design (gfx950, HBM-bound):
+// * Every value row j of a slice is independent: it needs only its own 512 B
+//   of state (Dk = 128), the shared k and q, and v_j.  A row is spread over
+//   Dk/4 lanes, one float4 per lane, so each load/store instruction of a
+//   wave moves whole rows with 16-byte accesses (global_load_dwordx4).
+// * A workgroup (256 threads, 4 waves) owns ROWS = (256 / (Dk/4)) * NV rows
+//   of one slice; each lane keeps its NV float4s in registers from the load
+//   to the store, so the state crosses HBM exactly twice (read once, written
+//   once), with NV independent 16-byte loads in flight per lane.
+// * Both row reductions (S.k and S.q, before the update) run together as
+//   lane-group sums; the readout then uses the exact identity
+//   y_j = a (S_j . q) + d_j (k . q), so no second pass over the updated row
+//   is needed.  k . q is one extra group sum per workgroup.
+// * State traffic uses non-temporal loads and stores: each byte is touched
+//   once per step and should not evict the activations from L2.
+// * In-place (state_out == state_in) is safe: each element is read and then
+//   written by the same lane.
+
+#include "gdn_device.h"
+#include "gdn_host.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DK, int NV, typename T>
+__global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
+    const float* state_in, float* state_out, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
+    const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
+    int parts_per_slice) {
+  constexpr int LPR = DK / 4;            // lanes per row
+  constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
+  constexpr int ROWS = RPS * NV;         // rows per workgroup
+
+  const int slice = blockIdx.x / parts_per_slice;  // n = b * Hv + hv
+  const int part = blockIdx.x - slice * parts_per_slice;
+  const int b = slice / Hv;
+  const int hv = slice - b * Hv;
+  const int hk = hv / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int c4 = tid % LPR;                        // float4 column within the row
+  const int row0 = part * ROWS + tid / LPR;
+
+  const size_t qk_off = (static_cast<size_t>(b) * Hk + hk) * DK + c4 * 4;
+  const size_t slice_off = static_cast<size_t>(slice) * Dv * DK;
+  const float* sin = state_in + slice_off + c4 * 4;
+  float* sout = state_out + slice_off + c4 * 4;
+
+  // State rows first: they are the long-latency, bandwidth-bound loads.
+  f32x4 s[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int row = row0 + n * RPS;
+    if (row < Dv) s[n] = load_stream(sin + static_cast<size_t>(row) * DK);
+  }
+  const f32x4 kk = Act<T>::load4(k + qk_off);
+  const f32x4 qq = Act<T>::load4(q + qk_off);
+  const float gate = expf(g[slice]);
+  const float bt = Act<T>::load(beta + slice);
+  float vv[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int row = row0 + n * RPS;
+    vv[n] = row < Dv ? Act<T>::load(v + static_cast<size_t>(slice) * Dv + row) : 0.0f;
+  }
+  const float kq = group_sum<LPR>(dot4(kk, qq));
+
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int row = row0 + n * RPS;
+    if (row < Dv) {
+      const float sk = group_sum<LPR>(dot4(s[n], kk));
+      const float sq = group_sum<LPR>(dot4(s[n], qq));
+      const float d = bt * (vv[n] - gate * sk);
+      const f32x4 sn = gate * s[n] + d * kk;
+      store_stream(sout + static_cast<size_t>(row) * DK, sn);
+      if (c4 == 0) Act<T>::store(y + static_cast<size_t>(slice) * Dv + row, gate * sq + d * kq);
+    }
+  }
+}
+
+template <int DK, typename T>
+int launch_dk(const float* state_in, float* state_out, const void* q, const void* k,
+              const void* v, const float* g, const void* beta, void* y, int B, int Hk,
+              int Hv, int Dv, hipStream_t stream) {
+  constexpr int RPS = kThreads / (DK / 4);
+  // Register slots per lane: enough rows in flight without starving occupancy.
+  const int need = (Dv + RPS - 1) / RPS;
+  const long slices = static_cast<long>(B) * Hv;
+  auto go = [&](auto nv_tag) -> int {
+    constexpr int NV = decltype(nv_tag)::value;
+    const int parts = (Dv + RPS * NV - 1) / (RPS * NV);
+    const long blocks = slices * parts;
+    if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, T>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, state_in, state_out,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), g, static_cast<const T*>(beta),
+                       static_cast<T*>(y), Hk, Hv, Dv, parts);
+    return launch_status();
+  };
+  if (need <= 1) return go(std::integral_constant<int, 1>{});
+  if (need <= 2) return go(std::integral_constant<int, 2>{});
+  if (need <= 4) return go(std::integral_constant<int, 4>{});
+  if (need <= 8) return go(std::integral_constant<int, 8>{});
+  return go(std::integral_constant<int, 16>{});
+}
+
+template <typename T>
+int launch(const float* state_in, float* state_out, const void* q, const void* k,
+           const void* v, const float* g, const void* beta, void* y, int B, int Hk, int Hv,
+           int Dk, int Dv, hipStream_t stream) {
+  switch (Dk) {
+    case 32: return launch_dk<32, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 64: return launch_dk<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 128: return launch_dk<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 256: return launch_dk<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" int gdn_decode_step(const float* state_in, float* state_out, const void* q,
+                               const void* k, const void* v, const float* g,
+                               const void* beta, void* y, int B, int Hk, int Hv, int Dk,
+                               int Dv, gdn_dtype act, hipStream_t stream) {
+  using namespace gdn;
+  if (B < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (!pow2_head(Dk) || Dv % 32 != 0 || Dv > 256) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  if (!state_in || !state_out || !q || !k || !v || !g || !beta || !y) return GDN_ERR_NULL;
+  if (!aligned16(state_in) || !aligned16(state_out) || !aligned16(q) || !aligned16(k))
+    return GDN_ERR_ALIGN;
+  const size_t state_bytes = static_cast<size_t>(B) * Hv * Dv * Dk * sizeof(float);
+  if (state_out != state_in && overlaps(state_in, state_bytes, state_out, state_bytes))
+    return GDN_ERR_ALIAS;
+  const size_t y_bytes = static_cast<size_t>(B) * Hv * Dv * act_bytes(act);
+  if (overlaps(y, y_bytes, state_out, state_bytes) || overlaps(y, y_bytes, state_in, state_bytes))
+    return GDN_ERR_ALIAS;
+  if (act == GDN_BF16)
+    return launch<bf16>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, stream);
+  return launch<float>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, stream);
+}

@@ -1,0 +1,31 @@
+// Host-side helpers for the libgdn C ABI: argument checks and launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool is_act(gdn_dtype act) { return act == GDN_F32 || act == GDN_BF16; }
+
+inline size_t act_bytes(gdn_dtype act) { return act == GDN_BF16 ? 2 : 4; }
+
+// True when [a, a+na) and [b, b+nb) share a byte.
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+inline bool pow2_head(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+// Status of the launch just enqueued.
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace gdn

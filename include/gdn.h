@@ -1,0 +1,124 @@
+/*
+ * gdn.h - C ABI of libgdn: the gated delta-rule (Gated DeltaNet) recurrence
+ * on AMD Instinct MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a device pointer (memory the caller allocated
+ *   on the current HIP device).  The library never allocates or frees memory,
+ *   keeps no pointer after returning and never synchronises: all work is
+ *   enqueued on `stream` (0 = the null stream) and finishes asynchronously.
+ * - The recurrent state is always float32 and every state computation is
+ *   done in float32.  Activations (q, k, v, p, beta, y, o, a, b) have the
+ *   dtype `act`: GDN_F32 (float32) or GDN_BF16 (bfloat16 bits, values are
+ *   rounded to nearest-even when written).  The log-space gate g is always
+ *   float32; the gate applied to the state is exp(g).
+ * - All tensors are dense, row-major, with the last dimension contiguous.
+ * - Return value: GDN_OK (0) or a negative GDN_ERR_* code.  Argument checks
+ *   (null pointers, shapes, dtype, alignment, aliasing, workspace size) are
+ *   made on the host before any HIP call, so an invalid call touches no
+ *   device state.  GDN_ERR_LAUNCH reports a failed kernel launch; faults
+ *   inside a kernel surface at the caller's next synchronisation.
+ * - Calls on one stream run in order; calls that write the same memory from
+ *   different streams race, as with any HIP kernel.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  GDN_ERR_SHAPE = -2,       /* a size is negative or inconsistent             */
+  GDN_ERR_DTYPE = -3,       /* `act` is not a gdn_dtype                        */
+  GDN_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned where required */
+  GDN_ERR_UNSUPPORTED = -5, /* a head size or chunk size this build lacks      */
+  GDN_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required      */
+  GDN_ERR_LAUNCH = -7,      /* the kernel launch failed                        */
+  GDN_ERR_DEVICE = -8,      /* no usable HIP device                            */
+  GDN_ERR_ALIAS = -9        /* two buffers overlap in a way that is not allowed */
+};
+
+/*
+ * gdn_decode_step - one single-token gated delta-rule step for a dense decode
+ * batch.  Source: metaltile-std `gated_delta.rs` (docs.rs), module doc
+ * sections "Recurrence per step" and "Layouts", and the DISPATCH INVARIANTS
+ * of `mt_gated_delta_step`.  For every sequence b and value head hv, with
+ * key head hk = hv / (Hv / Hk) (consecutive value heads share a key head) and
+ * S the [Dv, Dk] state slice of (b, hv):
+ *     S    <- exp(g) * S
+ *     kv_j  = sum_i S[j, i] k[i]
+ *     d_j   = beta * (v_j - kv_j)
+ *     S[j, i] <- S[j, i] + d_j k[i]
+ *     y_j   = sum_i S[j, i] q[i]        (no query scale: pre-scale q)
+ *
+ * state_in  [B, Hv, Dv, Dk] float32, read only.
+ * state_out [B, Hv, Dv, Dk] float32, written.  May equal state_in exactly
+ *           (in-place update); any other overlap is GDN_ERR_ALIAS.
+ * q, k      [B, Hk, Dk] act.     v, y [B, Hv, Dv] act.
+ * g         [B, Hv] float32 (log-space gate).   beta [B, Hv] act.
+ * Requirements: Hk >= 1, Hv % Hk == 0, Dk in {32, 64, 128, 256},
+ * Dv a multiple of 32 in [32, 256], B >= 0 (B == 0 is a no-op);
+ * state_in, state_out, q and k 16-byte aligned.
+ */
+int gdn_decode_step(const float* state_in, float* state_out, const void* q,
+                    const void* k, const void* v, const float* g,
+                    const void* beta, void* y, int B, int Hk, int Hv, int Dk,
+                    int Dv, gdn_dtype act, hipStream_t stream);
+
+/*
+ * comba_decode_step - one Comba step (gated delta rule with a decoupled read
+ * key) for a dense batch.  Source: KBench `comba_decode_step` spec, sections
+ * spec_md and contract_md.  For every (b, h), S the [K, V] state slice:
+ *     S    <- exp(g) * S
+ *     u_j   = beta * (v_j - sum_i p[i] S[i, j])       (read with p)
+ *     S[i, j] <- S[i, j] + k[i] u_j                    (write with k)
+ *     o_j   = sum_i (scale q[i]) S[i, j]               (updated state)
+ *
+ * state     [B, H, K, V] float32, read only.
+ * state_new [B, H, K, V] float32, written; may equal `state` exactly.
+ * q, k, p   [B, H, K] act.   v, o [B, H, V] act.   beta [B, H] act.
+ * g         [B, H] float32 (log-decay, <= 0 in practice).
+ * scale     query scale; a value <= 0 selects K^-1/2.
+ * Requirements: K and V in {32, 64, 128, 256}, not both 256; B, H >= 0;
+ * state, state_new, q, k, p, v and o 16-byte aligned.
+ */
+int comba_decode_step(const float* state, float* state_new, const void* q,
+                      const void* k, const void* v, const void* p,
+                      const void* beta, const float* g, void* o, int B, int H,
+                      int K, int V, float scale, gdn_dtype act,
+                      hipStream_t stream);
+
+/*
+ * gdn_prefill_gates - per-token gates of a prefill batch from raw inputs.
+ * Source: pymllm `gdn_chunkwise` docs, `gdn_extend_chunkwise` parameters
+ * (a, b, A_log, dt_bias), with the formulas of the regolith `gdn.metal`
+ * header comment:
+ *     g[t, h]    = -exp(A_log[h]) * softplus(a[t, h] + dt_bias[h])
+ *     beta[t, h] = sigmoid(b[t, h])
+ * a, b [T_tot, Hv] act; A_log, dt_bias [Hv] float32;
+ * g, beta [T_tot, Hv] float32, written (g is the log-space gate).
+ * Requirements: T_tot >= 0, Hv >= 1.
+ */
+int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
+                      const float* dt_bias, float* g, float* beta,
+                      int64_t T_tot, int Hv, gdn_dtype act, hipStream_t stream);
+
+/* Human-readable name of a gdn_status value (static string, never NULL). */
+const char* gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

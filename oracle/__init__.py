@@ -7,7 +7,8 @@ library never imports it, and it imports nothing from the HIP library.
 The arithmetic lives in ``gdn_oracle.c`` (plain C, IEEE double, token by
 token).  This module only builds/loads it and marshals numpy float64 arrays.
 Every function copies its state argument and returns the updated copy, so
-callers' arrays are never modified.
+callers' arrays are never modified, unless ``inplace=True`` is passed with a
+C-contiguous float64 state (large tests use that to avoid copies).
 
 Functions (each cites the page it follows in ``gdn_oracle.c``):
   gdn_step      one decode step, state [B,Hv,Dv,Dk]     (metaltile gated_delta.rs)
@@ -71,11 +72,20 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(_dp)
 
 
-def gdn_step(state, q, k, v, g, beta):
+def _state(state, inplace):
+    if inplace:
+        if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+                and state.flags.c_contiguous and state.flags.writeable):
+            raise ValueError("inplace=True needs a writeable C-contiguous float64 state")
+        return state
+    return _f64(state).copy()
+
+
+def gdn_step(state, q, k, v, g, beta, inplace=False):
     """One decode step.  state [B,Hv,Dv,Dk], q,k [B,Hk,Dk], v [B,Hv,Dv],
     g (log-space) and beta [B,Hv].  Returns (state_new, y) in float64."""
     lib = _load()
-    S = _f64(state).copy()
+    S = _state(state, inplace)
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     B, Hv, Dv, Dk = S.shape
     Hk = q.shape[1]
@@ -114,11 +124,11 @@ def gdn_prefill(q, k, v, g, beta, pool, cache_indices, cu_seqlens, scale=None,
     return P, y
 
 
-def comba_step(state, q, k, v, p, beta, g, scale=None):
+def comba_step(state, q, k, v, p, beta, g, scale=None, inplace=False):
     """One Comba step.  state [B,H,K,V]; q,k,p [B,H,K]; v [B,H,V]; beta,g [B,H].
     Returns (state_new, o) in float64; scale None -> K^-1/2."""
     lib = _load()
-    S = _f64(state).copy()
+    S = _state(state, inplace)
     q, k, v, p, beta, g = map(_f64, (q, k, v, p, beta, g))
     B, H, K, V = S.shape
     if scale is None:

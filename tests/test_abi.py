@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdn.h declares, and rejects invalid arguments with the documented
+status before any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WORKSPACE, LAUNCH, DEVICE, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_deltanet_linear_gdn_amd import load_library
+    return load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    from gated_deltanet_linear_gdn_amd import gdn_status_string
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WORKSPACE, LAUNCH, DEVICE, ALIAS):
+        assert gdn_status_string(code).startswith("GDN_")
+    assert gdn_status_string(-1000) == "GDN_ERR_UNKNOWN"
+
+
+# Fake device addresses: never dereferenced because every call below fails a
+# host-side check first.
+A = 0x100000
+BIG = 1 << 40
+
+
+def _p(x):
+    return ctypes.c_void_p(x)
+
+
+def decode(lib, state_in=A, state_out=A + BIG, q=A + 2 * BIG, k=A + 3 * BIG, v=A + 4 * BIG,
+           g=A + 5 * BIG, beta=A + 6 * BIG, y=A + 7 * BIG, B=2, Hk=2, Hv=4, Dk=128, Dv=128, act=1):
+    return lib.gdn_decode_step(_p(state_in), _p(state_out), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                               _p(y), B, Hk, Hv, Dk, Dv, act, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, B=-1) == SHAPE
+    assert decode(lib, Hk=3, Hv=4) == SHAPE
+    assert decode(lib, Hk=0) == SHAPE
+    assert decode(lib, act=7) == DTYPE
+    assert decode(lib, Dk=96) == UNSUP
+    assert decode(lib, Dv=48) == UNSUP
+    assert decode(lib, Dv=288) == UNSUP
+    assert decode(lib, q=0) == NULL
+    assert decode(lib, state_out=0) == NULL
+    assert decode(lib, state_in=A + 4) == ALIGN
+    assert decode(lib, k=A + 3 * BIG + 8) == ALIGN
+    # partial overlap of the two states, and y inside the state
+    assert decode(lib, state_out=A + 4096) == ALIAS
+    assert decode(lib, y=A + 64) == ALIAS
+    # B == 0 is a no-op that touches nothing, even with null pointers
+    assert decode(lib, B=0, q=0, k=0) == OK
+
+
+def comba(lib, state=A, state_new=A + BIG, q=A + 2 * BIG, k=A + 3 * BIG, v=A + 4 * BIG,
+          p=A + 5 * BIG, beta=A + 6 * BIG, g=A + 7 * BIG, o=A + 8 * BIG, B=2, H=2, K=128, V=128,
+          scale=0.0, act=1):
+    return lib.comba_decode_step(_p(state), _p(state_new), _p(q), _p(k), _p(v), _p(p), _p(beta),
+                                 _p(g), _p(o), B, H, K, V, ctypes.c_float(scale), act, None)
+
+
+def test_comba_validation(lib):
+    assert comba(lib, B=-1) == SHAPE
+    assert comba(lib, K=0) == SHAPE
+    assert comba(lib, act=2) == DTYPE
+    assert comba(lib, K=96) == UNSUP
+    assert comba(lib, K=256, V=256) == UNSUP
+    assert comba(lib, p=0) == NULL
+    assert comba(lib, o=A + 8 * BIG + 2) == ALIGN
+    assert comba(lib, state_new=A + 16) == ALIAS
+    assert comba(lib, H=0, q=0) == OK
+
+
+def test_gates_validation(lib):
+    f = lib.gdn_prefill_gates
+    args = [_p(A), _p(A + BIG), _p(A + 2 * BIG), _p(A + 3 * BIG), _p(A + 4 * BIG), _p(A + 5 * BIG)]
+    assert f(*args, ctypes.c_int64(-1), 4, 1, None) == SHAPE
+    assert f(*args, ctypes.c_int64(8), 0, 1, None) == SHAPE
+    assert f(*args, ctypes.c_int64(8), 4, 5, None) == DTYPE
+    bad = list(args)
+    bad[0] = _p(0)
+    assert f(*bad, ctypes.c_int64(8), 4, 1, None) == NULL
+    alias = list(args)
+    alias[5] = _p(A + 4 * BIG + 4)
+    assert f(*alias, ctypes.c_int64(8), 4, 1, None) == ALIAS
+    assert f(*bad, ctypes.c_int64(0), 4, 1, None) == OK

@@ -1,0 +1,165 @@
+"""GPU parity of gdn_decode_step against the fp64 oracle (through the C ABI).
+
+Tolerances: state max relative error <= 1e-5; y <= 1e-5 when fp32, and when
+bf16 relative Frobenius <= 2e-2 (y is rounded to bf16 once, ~2e-3 at most).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_deltanet_linear_gdn_amd as gdn
+from gated_deltanet_linear_gdn_amd import synth
+from tests.helpers import maxrel, relF, to_dev, to_np, oracle_decode_batched
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dev_token(tok, act):
+    d = DT[act]
+    return dict(q=to_dev(tok["q"], d, DEV), k=to_dev(tok["k"], d, DEV), v=to_dev(tok["v"], d, DEV),
+                beta=to_dev(tok["beta"], d, DEV), g=to_dev(tok["g"], torch.float32, DEV))
+
+
+def _step(S_dev, t, out=None):
+    return gdn.gdn_decode_step(S_dev, out, t["q"], t["k"], t["v"], t["g"], t["beta"])
+
+
+def _check_y(y_gpu, y_ref, act):
+    if act == "f32":
+        assert maxrel(y_gpu, y_ref) <= 1e-5
+    else:
+        assert relF(y_gpu, y_ref) <= 2e-2
+        assert maxrel(y_gpu, y_ref) <= 1e-2
+
+
+def test_tiny_fp32_from_zero_then_steps():
+    """Tiny fp32 workload: B=2, Hk=2, Hv=4, Dk=Dv=32, zero state, then 4 more steps."""
+    c = synth.TINY
+    rng = np.random.default_rng(0)
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    S_ref = np.zeros((B, Hv, Dv, Dk))
+    S_dev = torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=DEV)
+    for step in range(5):
+        tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act="f32")
+        S_dev, y = _step(S_dev, _dev_token(tok, "f32"))
+        S_ref, y_ref = oracle.gdn_step(S_ref, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
+        assert maxrel(to_np(S_dev), S_ref) <= 1e-5, step
+        assert maxrel(to_np(y), y_ref) <= 1e-5, step
+
+
+SHAPES = [
+    # B, Hk, Hv, Dk, Dv
+    (3, 1, 3, 32, 32),
+    (2, 2, 6, 64, 96),
+    (3, 2, 4, 128, 128),
+    (1, 1, 2, 128, 160),   # Dv not a multiple of the rows a workgroup covers
+    (2, 3, 3, 256, 64),
+    (1, 1, 1, 256, 256),
+    (5, 4, 8, 128, 32),
+]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("B,Hk,Hv,Dk,Dv", SHAPES)
+def test_parity_shapes(B, Hk, Hv, Dk, Dv, act):
+    rng = np.random.default_rng(B * 1000 + Dk + Dv)
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act=act)
+    S_dev, y = _step(to_dev(S0, torch.float32, DEV), _dev_token(tok, act))
+    S_ref, y_ref = oracle.gdn_step(S0, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
+    assert maxrel(to_np(S_dev), S_ref) <= 1e-5
+    _check_y(to_np(y), y_ref, act)
+
+
+def test_in_place_equals_out_of_place_and_is_deterministic():
+    rng = np.random.default_rng(11)
+    B, Hk, Hv, Dk, Dv = 4, 2, 8, 128, 128
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    t = _dev_token(synth.decode_token(rng, B, Hk, Hv, Dk, Dv), "bf16")
+    S_a, y_a = _step(to_dev(S0, torch.float32, DEV), t)
+    S_b, y_b = _step(to_dev(S0, torch.float32, DEV), t)
+    S_c = to_dev(S0, torch.float32, DEV)
+    S_c2, y_c = _step(S_c, t, out=S_c)
+    assert S_c2.data_ptr() == S_c.data_ptr()
+    assert torch.equal(S_a, S_b) and torch.equal(y_a, y_b)
+    assert torch.equal(S_a, S_c) and torch.equal(y_a, y_c)
+
+
+def test_head_sharing_matches_expanded_keys_bitwise():
+    """Contiguous key-head sharing: repeating q/k to Hv heads gives identical bits."""
+    rng = np.random.default_rng(12)
+    B, Hk, Hv, Dk, Dv = 2, 2, 6, 128, 64
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+    t = _dev_token(tok, "bf16")
+    S1, y1 = _step(to_dev(S0, torch.float32, DEV), t)
+    t2 = dict(t)
+    t2["q"] = t["q"].repeat_interleave(Hv // Hk, dim=1).contiguous()
+    t2["k"] = t["k"].repeat_interleave(Hv // Hk, dim=1).contiguous()
+    S2, y2 = _step(to_dev(S0, torch.float32, DEV), t2)
+    assert torch.equal(S1, S2) and torch.equal(y1, y2)
+
+
+def test_beta_zero_is_pure_decay_on_gpu():
+    rng = np.random.default_rng(13)
+    B, Hk, Hv, Dk, Dv = 2, 1, 2, 128, 128
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act="f32")
+    tok["beta"] = np.zeros_like(tok["beta"])
+    S_dev, _ = _step(to_dev(S0, torch.float32, DEV), _dev_token(tok, "f32"))
+    ref = np.exp(tok["g"].astype(np.float64))[:, :, None, None] * S0
+    assert maxrel(to_np(S_dev), ref) <= 1e-6
+
+
+def _warm_state(rng, B, Hk, Hv, Dk, Dv, steps=synth.WARMUP_STEPS):
+    """State after `steps` oracle decode steps from zero (bf16 activations),
+    handed over as float32."""
+    S = np.zeros((B, Hv, Dv, Dk))
+    for _ in range(steps):
+        S, _ = oracle_decode_batched(S, synth.decode_token(rng, B, Hk, Hv, Dk, Dv))
+    return S.astype(np.float32)
+
+
+def test_decode_batch_b64_full_tensor():
+    """Qwen-style decode batch: B=64, Hk=16, Hv=48, Dk=Dv=128, warmed 16 steps;
+    three GPU steps checked on the full state and output."""
+    c = synth.DECODE_B64
+    rng = np.random.default_rng(0)
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    S = _warm_state(rng, B, Hk, Hv, Dk, Dv)
+    S_dev = to_dev(S, torch.float32, DEV)
+    S_ref = S.astype(np.float64)
+    for _ in range(3):
+        tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+        S_dev, y = _step(S_dev, _dev_token(tok, "bf16"))
+        S_ref, y_ref = oracle_decode_batched(S_ref, tok)
+        assert maxrel(to_np(S_dev), S_ref) <= 1e-5
+        _check_y(to_np(y), y_ref, "bf16")
+
+
+def test_decode_batch_b256_sampled():
+    """Large decode batch B=256 (0.8 GB state) in the benchmark's launch
+    configuration (functional ping-pong); the oracle follows 8 sampled
+    sequences through 4 steps.  The warmed state is 16 oracle-warmed
+    sequences tiled over the batch."""
+    c = synth.DECODE_B256
+    rng = np.random.default_rng(0)
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    W = _warm_state(rng, 16, Hk, Hv, Dk, Dv)
+    S = np.tile(W, (B // 16, 1, 1, 1))
+    bufs = [to_dev(S, torch.float32, DEV), torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=DEV)]
+    sample = np.array([0, 1, 37, 100, 128, 201, 254, 255])
+    S_ref = S[sample].astype(np.float64)
+    for step in range(4):
+        tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+        t = _dev_token(tok, "bf16")
+        _, y = gdn.gdn_decode_step(bufs[step % 2], bufs[(step + 1) % 2], t["q"], t["k"], t["v"],
+                                   t["g"], t["beta"])
+        sub = {n: a[sample] for n, a in tok.items()}
+        S_ref, y_ref = oracle_decode_batched(S_ref, sub)
+        got = bufs[(step + 1) % 2][torch.from_numpy(sample).to(DEV)]
+        assert maxrel(to_np(got), S_ref) <= 1e-5, step
+        _check_y(to_np(y)[sample], y_ref, "bf16")
