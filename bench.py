@@ -119,6 +119,79 @@ def bench_comba(steps, warmup, device):
     return dict(sec=sec, bytes=canonical, shape=dict(B=B, H=H, K=K, V=V))
 
 
+def prefill_flops_per_token(Hv, Dk, Dv, C):
+    """Canonical FLOPs of the chunkwise prefill per token: per value head,
+    the six C-wide contractions (K K^T, Q K^T, T K, T V, P V_new at 2C Dk or
+    2C Dv each) and the three state contractions (W S_0, Q S_0, K^T V_new at
+    2 Dk Dv each), counted as full products."""
+    return Hv * (6 * Dk * Dv + C * (6 * Dk + 4 * Dv))
+
+
+def bench_prefill(steps, warmup, device):
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.PREFILL_VARLEN
+    Hk, Hv, Dk, Dv, P, C = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"], c["chunk"]
+    rng = np.random.default_rng(0)
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    T = int(inp["cu_seqlens"][-1])
+    bf = torch.bfloat16
+    q, k, v = (_dev(inp[n], bf, device) for n in ("q", "k", "v"))
+    a, b = _dev(inp["a"], bf, device), _dev(inp["b"], bf, device)
+    A_log = _dev(inp["A_log"], torch.float32, device)
+    dt_bias = _dev(inp["dt_bias"], torch.float32, device)
+    ci = _dev(inp["cache_indices"], torch.int64, device)
+    cu = _dev(inp["cu_seqlens"], torch.int64, device)
+    # pool slots warmed like decode states: 16 decode steps from zero
+    pool = torch.zeros((P, Hv, Dv, Dk), dtype=torch.float32, device=device)
+    for _ in range(synth.WARMUP_STEPS):
+        t = synth.decode_token(rng, P, Hk, Hv, Dk, Dv)
+        td = {n: _dev(x, torch.float32 if n == "g" else bf, device) for n, x in t.items()}
+        gdn.gdn_decode_step(pool, pool, td["q"], td["k"], td["v"], td["g"], td["beta"])
+    g = torch.empty((T, Hv), dtype=torch.float32, device=device)
+    beta = torch.empty_like(g)
+    y = torch.empty((T, Hv, Dv), dtype=bf, device=device)
+    ws = torch.empty(gdn.gdn_chunk_prefill_workspace(T, len(lengths), Hk, Hv, Dk, Dv, C),
+                     dtype=torch.uint8, device=device)
+
+    def step(i):
+        gdn.gdn_prefill_gates(a, b, A_log, dt_bias, g, beta)
+        gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y, workspace=ws)
+
+    sec = _timed(step, steps, warmup)
+    flops = prefill_flops_per_token(Hv, Dk, Dv, C) * T
+    return dict(sec=sec, tokens=T, flops=flops, lengths=[int(x) for x in lengths],
+                shape=dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, chunk=C, pool=P))
+
+
+def bench_comba_hbm(steps, warmup, device, B=896, H=16, K=128, V=128):
+    """Comba at one of the KBench measure shapes (0.94 GB state per copy,
+    well beyond the 256 MB MALL)."""
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    rng = np.random.default_rng(1)
+    toks = []
+    for _ in range(4):
+        t = synth.comba_token(rng, B, H, K, V)
+        toks.append({n: _dev(a, torch.float32 if n == "g" else torch.bfloat16, device)
+                     for n, a in t.items()})
+    bufs = [torch.zeros((B, H, K, V), dtype=torch.float32, device=device),
+            torch.empty((B, H, K, V), dtype=torch.float32, device=device)]
+    o = torch.empty((B, H, V), dtype=torch.bfloat16, device=device)
+
+    def step(i):
+        t = toks[i % 4]
+        gdn.comba_decode_step(bufs[i % 2], bufs[(i + 1) % 2], t["q"], t["k"], t["v"], t["p"],
+                              t["beta"], t["g"], o)
+
+    sec = _timed(step, steps, warmup)
+    canonical = 2 * B * H * K * V * 4 + B * H * (6 * K + 4 * V + 6)
+    return canonical / sec / 1e9, sec
+
+
 def bench_copy(device, nbytes=2 << 30, reps=20):
     import torch
     n = nbytes // 4
@@ -187,6 +260,8 @@ def main():
     device = torch.device("cuda:0")
     dec = bench_decode(args.steps, args.warmup, device)
     com = bench_comba(args.steps, args.warmup, device)
+    com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
+    pre = bench_prefill(max(5, args.steps // 20), 3, device)
     copy_gbps = bench_copy(device)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
@@ -214,7 +289,17 @@ def main():
         "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
                   "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
                   "us_per_step": round(com["sec"] * 1e6, 2),
-                  "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+                  "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4),
+                  "measure_shape_B896_H16": {"GBps": round(com_hbm, 2),
+                                             "us_per_step": round(com_hbm_sec * 1e6, 2),
+                                             "frac_of_hbm_peak": round(com_hbm / HBM_PEAK_GBPS, 4)}},
+        "prefill": {"workload": "gdn_prefill_gates + gdn_chunk_prefill, 8 sequences of U[512,4096] "
+                                "tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64, pool 16",
+                    "tokens": pre["tokens"], "lengths": pre["lengths"],
+                    "us_per_call": round(pre["sec"] * 1e6, 2),
+                    "tokens_per_s": round(pre["tokens"] / pre["sec"], 1),
+                    "canonical_TFLOPs": round(pre["flops"] / pre["sec"] / 1e12, 2),
+                    "mfma_frac_of_bf16_peak": round(pre["flops"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

@@ -22,6 +22,7 @@ import torch
 __all__ = [
     "GdnError", "library_path", "load_library",
     "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
+    "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,13 @@ def load_library():
     lib.comba_decode_step.argtypes = [_vp] * 9 + [_i] * 4 + [_f, _i, _vp]
     lib.gdn_prefill_gates.restype = _i
     lib.gdn_prefill_gates.argtypes = [_vp] * 6 + [_i64, _i, _i, _vp]
+    lib.gdn_chunk_prefill_workspace.restype = ctypes.c_size_t
+    lib.gdn_chunk_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i]
+    lib.gdn_chunk_prefill.restype = _i
+    lib.gdn_chunk_prefill.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
+                                      + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
+    lib.gdn_validate_varlen.restype = _i
+    lib.gdn_validate_varlen.argtypes = [_vp, _vp, _i, _i64, _i64, _vp]
     _lib = lib
     return lib
 
@@ -189,3 +197,60 @@ def gdn_prefill_gates(a, b, A_log, dt_bias, g=None, beta=None):
     _call("gdn_prefill_gates", _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
           T, Hv, _act_of(a), _stream())
     return g, beta
+
+
+GDN_QK_L2NORM = 1
+
+
+def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64) -> int:
+    """Bytes of workspace ``gdn_chunk_prefill`` needs (0 for invalid sizes)."""
+    return int(load_library().gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk))
+
+
+def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, chunk=64,
+                      scale=None, l2norm=True, y=None, workspace=None):
+    """Varlen chunkwise prefill, ``state_pool`` updated in place (see
+    ``gdn_chunk_prefill`` in include/gdn.h).
+
+    q,k [T,Hk,Dk] raw; v [T,Hv,Dv]; g, beta [T,Hv] f32 (log gate, beta);
+    state_pool [P,Hv,Dv,Dk] f32; cache_indices [N_s] int64; cu_seqlens
+    [N_s+1] int64 (device tensors, contract not checked here: see
+    ``gdn_validate_varlen``); y [T,Hv,Dv] or None; workspace: a uint8 device
+    tensor of at least ``gdn_chunk_prefill_workspace`` bytes, or None.
+    Returns y."""
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    P = state_pool.shape[0]
+    N_s = cache_indices.shape[0]
+    dev = q.device
+    act = q.dtype
+    if y is None:
+        y = torch.empty((T, Hv, Dv), dtype=act, device=dev)
+    _check("q", q, (T, Hk, Dk), act, dev)
+    _check("k", k, (T, Hk, Dk), act, dev)
+    _check("v", v, (T, Hv, Dv), act, dev)
+    _check("g", g, (T, Hv), torch.float32, dev)
+    _check("beta", beta, (T, Hv), torch.float32, dev)
+    _check("state_pool", state_pool, (P, Hv, Dv, Dk), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    _check("y", y, (T, Hv, Dv), act, dev)
+    need = gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    _call("gdn_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+          _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
+          GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q), _ptr(workspace),
+          workspace.numel(), _stream())
+    return y
+
+
+def gdn_validate_varlen(cu_seqlens, cache_indices, T_tot, pool_size) -> int:
+    """Check the prefill contract of device ``cu_seqlens``/``cache_indices``
+    (synchronises the current stream).  Returns 0 or a negative status."""
+    N_s = cache_indices.shape[0]
+    return int(load_library().gdn_validate_varlen(_ptr(cu_seqlens), _ptr(cache_indices), N_s,
+                                                  int(T_tot), int(pool_size), _stream()))

@@ -1,0 +1,809 @@
+// gdn_chunk_prefill: variable-length chunkwise (WY) prefill over a state pool.
+//
+// Source: pymllm `gdn_chunkwise` docs, "Algorithm (per chunk of C tokens with
+// initial state S_0)", steps 1-3, and the `gdn_extend_chunkwise` parameters.
+// The chunk algebra is used in its division-free form (every exponent <= 0
+// for log-gates g <= 0).  Per chunk of a sequence, with k^, q^ the
+// L2-normalised keys/queries (q^ also scaled), G_t the inclusive in-chunk sum
+// of the log-gates, gamma_t = exp(G_t), and the state S = S^T of the stored
+// [Dv, Dk] slice (Dk x Dv):
+//   A_ij  = beta_i exp(G_i - G_j) k^_i . k^_j   (j < i),   T = (I + A)^-1
+//   R     = diag(beta) V - diag(beta gamma) K^ S
+//   Delta = T R                                  (the WY "new values")
+//   O     = diag(gamma) Q^ S + P Delta,  P_ij = exp(G_i - G_j) q^_i . k^_j (j <= i)
+//   S    <- gamma_C S + (diag(exp(G_C - G)) K^)^T Delta
+// which is the page's w/u~ construction, S_0 W, triu(K^T Q) and state update
+// rescaled by the cumulative decay (no 1/gamma anywhere).
+//
+// Kernels (gfx950, wave64, v_mfma_f32_16x16x32_bf16 for every contraction):
+//  1. gdn_chunk_map_kernel: scan over cu_seqlens -> first chunk of each
+//     sequence (device side, no host sync).
+//  2. gdn_wy_kernel, one wave per (chunk, value head), all chunks of all
+//     sequences in parallel: q/k row norms, G, the Gram K K^T and Q K^T on
+//     MFMA, A and P, and T by column-parallel forward substitution in fp32.
+//     Writes T and P as bf16 hi/lo pairs and G, 1/|k|, scale/|q| to the
+//     workspace.  Nothing here depends on the state.
+//  3. gdn_prefill_kernel, one workgroup per (sequence, value head, 16*NW
+//     value columns): each wave owns 16 value columns and keeps its Dk x 16
+//     slice of S in MFMA accumulators across the sequential chunk loop.  Per
+//     chunk it stages K^T in LDS (the only operand needed transposed), then
+//     runs X = K S, Y = Q S, Delta = T R, O = Y' + P Delta and the state
+//     update as chained MFMAs: every product's right operand is the
+//     previous product's accumulator converted to bf16, with the contraction
+//     index permuted identically on both sides so no data moves between
+//     lanes.  Raw bf16 q/k/v enter the MFMAs exactly; the per-row norm and
+//     decay factors are applied to fp32 accumulators.  Operands that carry
+//     the state (S, R, Delta, T) are split into bf16 hi + lo halves so the
+//     state keeps fp32-grade accuracy; with fp32 activations every product
+//     uses hi/lo on both sides.
+
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_host.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8v __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ f32x4 mma(bf16x8v a, bf16x8v b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pk(float a, float b) {
+  bf16x2v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float hi_part(float x) { return (float)(__bf16)x; }
+
+// Eight fp32 values -> bf16 hi (and lo = bf16(x - hi)) operand vectors.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8v& hi, bf16x8v& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = x[2 * p], b = x[2 * p + 1];
+    h[p] = pk(a, b);
+    l[p] = pk(a - hi_part(a), b - hi_part(b));
+  }
+  hi = __builtin_bit_cast(bf16x8v, h);
+  lo = __builtin_bit_cast(bf16x8v, l);
+}
+
+// Operand over the contraction index from two stacked 16x16 accumulator tiles
+// (rows base..base+15 in t0, base+16..base+31 in t1): element e < 4 is row
+// base + kg*4 + e, element e >= 4 is row base + 16 + kg*4 + (e-4).
+__device__ __forceinline__ void acc_operand(f32x4 t0, f32x4 t1, bf16x8v& hi, bf16x8v& lo) {
+  const float x[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+  split8(x, hi, lo);
+}
+__device__ __forceinline__ bf16x8v acc_operand_hi(f32x4 t0, f32x4 t1) {
+  u32x4 h = {pk(t0.x, t0.y), pk(t0.z, t0.w), pk(t1.x, t1.y), pk(t1.z, t1.w)};
+  return __builtin_bit_cast(bf16x8v, h);
+}
+
+__device__ __forceinline__ bf16x8v zero8() { return __builtin_bit_cast(bf16x8v, u32x4{0, 0, 0, 0}); }
+
+// Memory fragments along a row.  "pi" order matches acc_operand: elements
+// 0..3 = row[k0 + kg*4 + 0..3], 4..7 = row[k0 + 16 + kg*4 + 0..3].  "std"
+// order: elements 0..7 = row[k0 + kg*8 + 0..7].
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16> {
+  static __device__ __forceinline__ void pi(const bf16* row, int k0, int kg, bf16x8v& hi, bf16x8v& lo) {
+    const uint2 a = *reinterpret_cast<const uint2*>(row + k0 + kg * 4);
+    const uint2 b = *reinterpret_cast<const uint2*>(row + k0 + 16 + kg * 4);
+    hi = __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, b.x, b.y});
+    lo = zero8();
+  }
+  static __device__ __forceinline__ void stdo(const bf16* row, int k0, int kg, bf16x8v& hi, bf16x8v& lo) {
+    const uint4 a = *reinterpret_cast<const uint4*>(row + k0 + kg * 8);
+    hi = __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, a.z, a.w});
+    lo = zero8();
+  }
+  static __device__ __forceinline__ float sumsq(const bf16* row, int n) {
+    float s = 0.f;
+    for (int d = 0; d < n; d += 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(row + d);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x = __uint_as_float(w[p] << 16), y = __uint_as_float(w[p] & 0xffff0000u);
+        s += x * x + y * y;
+      }
+    }
+    return s;
+  }
+  static __device__ __forceinline__ void load8_raw(const bf16* p, uint32_t (&out)[4]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  }
+};
+
+template <> struct Frag<float> {
+  static __device__ __forceinline__ void pi(const float* row, int k0, int kg, bf16x8v& hi, bf16x8v& lo) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k0 + kg * 4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + k0 + 16 + kg * 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    split8(x, hi, lo);
+  }
+  static __device__ __forceinline__ void stdo(const float* row, int k0, int kg, bf16x8v& hi, bf16x8v& lo) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + k0 + kg * 8);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + k0 + kg * 8 + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    split8(x, hi, lo);
+  }
+  static __device__ __forceinline__ float sumsq(const float* row, int n) {
+    float s = 0.f;
+    for (int d = 0; d < n; d += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(row + d);
+      s += (a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w);
+    }
+    return s;
+  }
+};
+
+// Raw A-operand fragments in "pi" order, kept as loaded so that every global
+// load of a chunk can be issued before the first use; converted (and split
+// into hi/lo for fp32 activations) when consumed.
+template <typename T> struct Raw;
+template <> struct Raw<bf16> {
+  uint2 a, b;
+  static __device__ __forceinline__ Raw load(const bf16* row, int k0, int kg) {
+    return Raw{*reinterpret_cast<const uint2*>(row + k0 + kg * 4),
+               *reinterpret_cast<const uint2*>(row + k0 + 16 + kg * 4)};
+  }
+  __device__ __forceinline__ void operand(bf16x8v& hi, bf16x8v& lo) const {
+    hi = __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, b.x, b.y});
+    lo = zero8();
+  }
+};
+template <> struct Raw<float> {
+  f32x4 a, b;
+  static __device__ __forceinline__ Raw load(const float* row, int k0, int kg) {
+    return Raw{*reinterpret_cast<const f32x4*>(row + k0 + kg * 4),
+               *reinterpret_cast<const f32x4*>(row + k0 + 16 + kg * 4)};
+  }
+  __device__ __forceinline__ void operand(bf16x8v& hi, bf16x8v& lo) const {
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    split8(x, hi, lo);
+  }
+};
+
+// ----------------------------------------------------------------------------
+// 1. chunk map: scs[s] = sum_{s' < s} ceil(L_s' / C), scs[N_s] = total.
+
+__device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_tot, int64_t& b0,
+                                           int64_t& len) {
+  int64_t a = cu[s], b = cu[s + 1];
+  a = a < 0 ? 0 : (a > T_tot ? T_tot : a);
+  b = b < a ? a : (b > T_tot ? T_tot : b);
+  b0 = a;
+  len = b - a;
+}
+
+__global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
+                                                             int N_s, int64_t T_tot, int C,
+                                                             int* __restrict__ scs) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (N_s + 1023) / 1024;
+  const int s0 = tid * per;
+  int local = 0;
+  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+    int64_t b0, len;
+    seq_bounds(cu, s, T_tot, b0, len);
+    local += static_cast<int>((len + C - 1) / C);
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;  // exclusive prefix of this thread's range
+  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+    scs[s] = run;
+    int64_t b0, len;
+    seq_bounds(cu, s, T_tot, b0, len);
+    run += static_cast<int>((len + C - 1) / C);
+  }
+  if (tid == 1023) scs[N_s] = part[1023];
+}
+
+// ----------------------------------------------------------------------------
+// 2. WY pre-pass: one wave per (chunk, value head).
+
+template <typename T, int DK, int CT>
+__global__ __launch_bounds__(64) void gdn_wy_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
+    int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm,
+    bf16* __restrict__ Th, bf16* __restrict__ Tl, bf16* __restrict__ Ph, bf16* __restrict__ Pl,
+    float* __restrict__ vec) {
+  constexpr bool PRECISE = std::is_same<T, float>::value;
+  constexpr int MT = CT / 16, KB = DK / 32;
+  __shared__ float sG[CT], srk[CT], srq[CT], sb[CT];
+  __shared__ __attribute__((aligned(16))) float Am[CT][CT + 4];
+
+  const int c = blockIdx.x / Hv;
+  const int hv = blockIdx.x - c * Hv;
+  if (c >= scs[N_s]) return;
+  int lo = 0, hi = N_s;  // largest s with scs[s] <= c
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (scs[mid] <= c) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  int64_t b0, len;
+  seq_bounds(cu, s, T_tot, b0, len);
+  const int64_t j0 = static_cast<int64_t>(c - scs[s]) * C;
+  const int64_t t0 = b0 + j0;
+  const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
+  const int hk = hv / (Hv / Hk);
+  const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
+  const size_t mat = static_cast<size_t>(c) * Hv + hv;
+
+  // All K and Q fragments of the chunk, issued at once: lane (l16, kg) holds
+  // row I*16 + l16, elements kb*32 + kg*8 .. +7, for every row block I and
+  // k-block kb.  They serve as both MFMA operands of every Gram tile and give
+  // the row norms.  Rows past the last token read it again and get zero
+  // factors below.
+  bf16x8v kh[MT][KB], kl[MT][KB], qh[MT][KB], ql[MT][KB];
+  float ssk[MT], ssq[MT];
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+    const size_t roff = (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      Frag<T>::stdo(k + roff, kb * 32, kg, kh[I][kb], kl[I][kb]);
+      Frag<T>::stdo(q + roff, kb * 32, kg, qh[I][kb], ql[I][kb]);
+    }
+  }
+  float gl = 0.f, bt = 0.f;
+  if (lane < CT) {
+    const size_t th = static_cast<size_t>(t0 + min(lane, n - 1)) * Hv + hv;
+    gl = g[th];
+    bt = beta[th];
+  }
+  // row sums of squares: per-lane partials over its 8 elements of each k-block,
+  // then across the four lanes kg = 0..3 of the row
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 wk = __builtin_bit_cast(u32x4, kh[I][kb]), wq = __builtin_bit_cast(u32x4, qh[I][kb]);
+      const u32x4 vk = __builtin_bit_cast(u32x4, kl[I][kb]), vq = __builtin_bit_cast(u32x4, ql[I][kb]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // x = hi + lo exactly reconstructs fp32 inputs; lo is zero for bf16 inputs
+        const float x0 = __uint_as_float(wk[p] << 16) + __uint_as_float(vk[p] << 16);
+        const float x1 = __uint_as_float(wk[p] & 0xffff0000u) + __uint_as_float(vk[p] & 0xffff0000u);
+        const float y0 = __uint_as_float(wq[p] << 16) + __uint_as_float(vq[p] << 16);
+        const float y1 = __uint_as_float(wq[p] & 0xffff0000u) + __uint_as_float(vq[p] & 0xffff0000u);
+        a += x0 * x0 + x1 * x1;
+        b += y0 * y0 + y1 * y1;
+      }
+    }
+    a += __shfl_xor(a, 16);
+    a += __shfl_xor(a, 32);
+    b += __shfl_xor(b, 16);
+    b += __shfl_xor(b, 32);
+    ssk[I] = a;
+    ssq[I] = b;
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int I = 0; I < MT; ++I) {
+      const int t = I * 16 + l16;
+      const bool ok = t < n;
+      srk[t] = ok ? (l2norm ? 1.0f / sqrtf(ssk[I] + kNormEps) : 1.0f) : 0.f;
+      srq[t] = ok ? scale * (l2norm ? 1.0f / sqrtf(ssq[I] + kNormEps) : 1.0f) : 0.f;
+    }
+  }
+  // inclusive prefix sum of the log-gates over the chunk (wave scan)
+  float G = lane < n ? gl : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float up = __shfl_up(G, off);
+    if (lane >= off) G += up;
+  }
+  if (lane < CT) {
+    sG[lane] = G;
+    sb[lane] = lane < n ? bt : 0.f;
+  }
+  __syncthreads();
+  if (lane < CT) {
+    float* vp = vec + mat * 3 * CT;
+    vp[lane] = G;
+    vp[CT + lane] = srk[lane];
+    vp[2 * CT + lane] = srq[lane];
+  }
+
+  // Gram K K^T and Q K^T tiles (I, J), J <= I; A and P from them.
+  bf16* ph = Ph + mat * CT * CT;
+  bf16* pl = Pl + mat * CT * CT;
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+#pragma unroll
+    for (int J = 0; J < MT; ++J) {
+      if (J > I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ii = I * 16 + kg * 4 + r, jj = J * 16 + l16;
+          ph[ii * CT + jj] = 0;
+          if constexpr (PRECISE) pl[ii * CT + jj] = 0;
+        }
+        continue;
+      }
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        gk = mma(kh[I][kb], kh[J][kb], gk);
+        gq = mma(qh[I][kb], kh[J][kb], gq);
+        if constexpr (PRECISE) {
+          gk = mma(kh[I][kb], kl[J][kb], gk);
+          gk = mma(kl[I][kb], kh[J][kb], gk);
+          gq = mma(qh[I][kb], kl[J][kb], gq);
+          gq = mma(ql[I][kb], kh[J][kb], gq);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = I * 16 + kg * 4 + r, jj = J * 16 + l16;
+        const float dec = (jj <= ii) ? __expf(sG[ii] - sG[jj]) : 0.f;
+        Am[ii][jj] = (jj < ii) ? sb[ii] * dec * srk[ii] * srk[jj] * gk[r] : 0.f;
+        const float pv = (jj <= ii) ? dec * srq[ii] * srk[jj] * gq[r] : 0.f;
+        const __bf16 h = (__bf16)pv;
+        ph[ii * CT + jj] = __builtin_bit_cast(bf16, h);
+        if constexpr (PRECISE) pl[ii * CT + jj] = __builtin_bit_cast(bf16, (__bf16)(pv - (float)h));
+      }
+    }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1, unit lower triangular; lane c computes column c by
+  // forward substitution, four partial sums per row.
+  if (lane < CT) {
+    float tr[CT];
+#pragma unroll
+    for (int i = 0; i < CT; ++i) {
+      float a0 = (i == lane) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int j = 0; j + 3 < i; j += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&Am[i][j]);
+        a0 -= a.x * tr[j];
+        a1 -= a.y * tr[j + 1];
+        a2 -= a.z * tr[j + 2];
+        a3 -= a.w * tr[j + 3];
+      }
+#pragma unroll
+      for (int j = i & ~3; j < i; ++j) a0 -= Am[i][j] * tr[j];
+      tr[i] = (a0 + a1) + (a2 + a3);
+    }
+    bf16* th = Th + mat * CT * CT;
+    bf16* tl = Tl + mat * CT * CT;
+#pragma unroll
+    for (int i = 0; i < CT; ++i) {
+      const __bf16 h = (__bf16)tr[i];
+      th[i * CT + lane] = __builtin_bit_cast(bf16, h);
+      tl[i * CT + lane] = __builtin_bit_cast(bf16, (__bf16)(tr[i] - (float)h));
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 3. Sequential chunk loop per (sequence, value head, value block).
+
+template <typename T, int DK, int CT, int NW>
+__global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ beta, float* __restrict__ pool, int64_t pool_size,
+    const int64_t* __restrict__ cache_indices, const int64_t* __restrict__ cu,
+    const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk, int Hv, int Dv, int C, int maxc,
+    const bf16* __restrict__ Th, const bf16* __restrict__ Tl, const bf16* __restrict__ Ph,
+    const bf16* __restrict__ Pl, const float* __restrict__ vec, T* __restrict__ y) {
+  constexpr bool PRECISE = std::is_same<T, float>::value;
+  constexpr int BV = 16 * NW, NT = 64 * NW;
+  constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
+  constexpr int KTP = CT + 8;  // K^T row pitch in elements
+  __shared__ __attribute__((aligned(16))) T KT[DK][KTP];
+  __shared__ float fB[CT], fK[CT], fQ[CT], fD[CT];
+  __shared__ float sGC;
+
+  const int nvb = Dv / BV;
+  const int s = blockIdx.x / (Hv * nvb);
+  const int rem = blockIdx.x - s * (Hv * nvb);
+  const int hv = rem / nvb;
+  const int vb = rem - hv * nvb;
+  const int64_t slot = cache_indices[s];
+  if (slot < 0 || slot >= pool_size) return;
+  int64_t b0, len;
+  seq_bounds(cu, s, T_tot, b0, len);
+  if (len <= 0) return;
+  const int cbase = scs[s];
+  // chunks past the workspace bound only exist for cu_seqlens outside the
+  // contract; they are skipped rather than read out of bounds
+  const int nch_all = static_cast<int>((len + C - 1) / C);
+  const int nch = cbase + nch_all > maxc ? (maxc > cbase ? maxc - cbase : 0) : nch_all;
+  const int hk = hv / (Hv / Hk);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int dv = vb * BV + w * 16 + l16;
+
+  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(dv) * DK;
+  f32x4 S[DT];
+#pragma unroll
+  for (int m = 0; m < DT; ++m) S[m] = *reinterpret_cast<const f32x4*>(Sp + m * 16 + kg * 4);
+
+  for (int ci = 0; ci < nch; ++ci) {
+    const int c = cbase + ci;
+    const int64_t t0 = b0 + static_cast<int64_t>(ci) * C;
+    const int n = static_cast<int>(len - static_cast<int64_t>(ci) * C < C ? len - static_cast<int64_t>(ci) * C : C);
+    const size_t mat = static_cast<size_t>(c) * Hv + hv;
+
+    // ---- every global load of the chunk, issued before any of them is used.
+    // Rows past the chunk's last token read that token again (a branch
+    // around each load would serialise the loads) and are zeroed or get zero
+    // factors, so they contribute nothing.
+    // K^T staging: CT * DK/8 items of 8 elements, NSTG per thread (the last
+    // round may be partial for small tiles: surplus threads load an item
+    // again and skip its LDS write)
+    constexpr int NITEMS = CT * (DK / 8);
+    constexpr int NSTG = (NITEMS + NT - 1) / NT;
+    T kst[NSTG][8];
+#pragma unroll
+    for (int it = 0; it < NSTG; ++it) {
+      const int idx = min(tid + it * NT, NITEMS - 1), t = idx % CT, d8 = idx / CT;
+      const T* src = k + (static_cast<size_t>(t0 + min(t, n - 1)) * Hk + hk) * DK + d8 * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kst[it][e] = src[e];
+    }
+    Raw<T> kf[MT][KB], qf[MT][KB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const size_t roff = (static_cast<size_t>(t0 + min(mt * 16 + l16, n - 1)) * Hk + hk) * DK;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        kf[mt][kb] = Raw<T>::load(k + roff, kb * 32, kg);
+        qf[mt][kb] = Raw<T>::load(q + roff, kb * 32, kg);
+      }
+    }
+    float vv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vv[mt][r] = Act<T>::load(
+            v + (static_cast<size_t>(t0 + min(mt * 16 + kg * 4 + r, n - 1)) * Hv + hv) * Dv + dv);
+    // T (hi, lo) and P rows for the lower-triangular (mt, cb) blocks
+    Raw<bf16> thf[MT][CKB], tlf[MT][CKB], phf[MT][CKB], plf[MT][CKB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const size_t roff = mat * CT * CT + static_cast<size_t>(mt * 16 + l16) * CT;
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        thf[mt][cb] = Raw<bf16>::load(Th + roff, cb * 32, kg);
+        tlf[mt][cb] = Raw<bf16>::load(Tl + roff, cb * 32, kg);
+        phf[mt][cb] = Raw<bf16>::load(Ph + roff, cb * 32, kg);
+        if constexpr (PRECISE) plf[mt][cb] = Raw<bf16>::load(Pl + roff, cb * 32, kg);
+      }
+    }
+    float fvG = 0.f, fvK = 0.f, fvQ = 0.f, fvGC = 0.f, fvB = 0.f;
+    if (tid < CT) {
+      const float* vp = vec + mat * 3 * CT;
+      fvG = vp[tid];
+      fvK = vp[CT + tid];
+      fvQ = vp[2 * CT + tid];
+      fvGC = vp[CT - 1];  // G is flat past the last valid token
+      fvB = beta[static_cast<size_t>(t0 + min(tid, n - 1)) * Hv + hv];
+    }
+
+    __syncthreads();  // the previous chunk no longer reads K^T or the factors
+#pragma unroll
+    for (int it = 0; it < NSTG; ++it) {
+      const int idx = tid + it * NT, t = idx % CT, d8 = idx / CT;
+      if (NITEMS % NT == 0 || idx < NITEMS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) KT[d8 * 8 + e][t] = t < n ? kst[it][e] : T(0);
+      }
+    }
+    if (tid < CT) {
+      const float bt = tid < n ? fvB : 0.f;
+      const float gam = __expf(fvG);
+      fB[tid] = bt;
+      fK[tid] = bt * gam * fvK;
+      fQ[tid] = gam * fvQ;
+      fD[tid] = __expf(fvGC - fvG) * fvK;
+      if (tid == 0) sGC = __expf(fvGC);
+    }
+    __syncthreads();
+
+    // state operand over dk (hi/lo)
+    bf16x8v Sh[KB], Sl[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc_operand(S[2 * kb], S[2 * kb + 1], Sh[kb], Sl[kb]);
+
+    // X = K S (state-grade), Y = Q S (output-grade)
+    f32x4 X[MT], Y[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        bf16x8v akh, akl, aqh, aql;
+        kf[mt][kb].operand(akh, akl);
+        qf[mt][kb].operand(aqh, aql);
+        X[mt] = mma(akh, Sh[kb], X[mt]);
+        X[mt] = mma(akh, Sl[kb], X[mt]);
+        Y[mt] = mma(aqh, Sh[kb], Y[mt]);
+        if constexpr (PRECISE) {
+          X[mt] = mma(akl, Sh[kb], X[mt]);
+          Y[mt] = mma(aqh, Sl[kb], Y[mt]);
+          Y[mt] = mma(aql, Sh[kb], Y[mt]);
+        }
+      }
+    }
+
+    // R = diag(beta) V - diag(beta gamma / |k|) X   (fB = fK = 0 past the last token)
+    f32x4 R[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = mt * 16 + kg * 4 + r;
+        R[mt][r] = fB[t] * vv[mt][r] - fK[t] * X[mt][r];
+      }
+    bf16x8v Rh[CKB], Rl[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) acc_operand(R[2 * cb], R[2 * cb + 1], Rh[cb], Rl[cb]);
+
+    // Delta = T R (T lower triangular: skip blocks above the diagonal)
+    f32x4 D[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        bf16x8v th, tl, unused;
+        thf[mt][cb].operand(th, unused);
+        tlf[mt][cb].operand(tl, unused);
+        D[mt] = mma(th, Rh[cb], D[mt]);
+        D[mt] = mma(th, Rl[cb], D[mt]);
+        D[mt] = mma(tl, Rh[cb], D[mt]);
+      }
+    }
+
+    // O = diag(gamma scale / |q|) Y + P Delta -> y
+    bf16x8v Dh[CKB], Dl[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) acc_operand(D[2 * cb], D[2 * cb + 1], Dh[cb], Dl[cb]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 O;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[r] = fQ[mt * 16 + kg * 4 + r] * Y[mt][r];
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        bf16x8v ph, pl, unused;
+        phf[mt][cb].operand(ph, unused);
+        O = mma(ph, Dh[cb], O);
+        if constexpr (PRECISE) {
+          plf[mt][cb].operand(pl, unused);
+          O = mma(ph, Dl[cb], O);
+          O = mma(pl, Dh[cb], O);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = mt * 16 + kg * 4 + r;
+        if (t < n) Act<T>::store(y + (static_cast<size_t>(t0 + t) * Hv + hv) * Dv + dv, O[r]);
+      }
+    }
+
+    // S <- gamma_C S + K^T diag(exp(G_C - G) / |k|) Delta
+    f32x4 Dp[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Dp[mt][r] = fD[mt * 16 + kg * 4 + r] * D[mt][r];
+    bf16x8v Eh[CKB], El[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) acc_operand(Dp[2 * cb], Dp[2 * cb + 1], Eh[cb], El[cb]);
+    const float gC = sGC;
+#pragma unroll
+    for (int m = 0; m < DT; ++m) {
+      S[m] *= gC;
+      const T* ktrow = &KT[m * 16 + l16][0];
+#pragma unroll
+      for (int cb = 0; cb < CKB; ++cb) {
+        bf16x8v ah, al;
+        Frag<T>::pi(ktrow, cb * 32, kg, ah, al);
+        S[m] = mma(ah, Eh[cb], S[m]);
+        S[m] = mma(ah, El[cb], S[m]);
+        if constexpr (PRECISE) S[m] = mma(al, Eh[cb], S[m]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
+}
+
+// ----------------------------------------------------------------------------
+// host side
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
+
+struct Layout {
+  size_t scs, th, tl, ph, pl, vec, total;
+};
+
+inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk) {
+  const int CT = chunk_tile(chunk);
+  const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
+  const size_t mats = maxc * static_cast<size_t>(Hv);
+  Layout L;
+  size_t off = 0;
+  L.scs = off; off += up(sizeof(int) * (static_cast<size_t>(N_s) + 1));
+  L.th = off; off += up(mats * CT * CT * sizeof(bf16));
+  L.tl = off; off += up(mats * CT * CT * sizeof(bf16));
+  L.ph = off; off += up(mats * CT * CT * sizeof(bf16));
+  L.pl = off; off += up(mats * CT * CT * sizeof(bf16));
+  L.vec = off; off += up(mats * 3 * CT * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+template <typename T, int DK, int CT, int NW>
+int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
+               float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
+               int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
+               char* ws, const Layout& L, hipStream_t stream) {
+  int* scs = reinterpret_cast<int*>(ws + L.scs);
+  bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
+  bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
+  bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
+  bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
+  float* vec = reinterpret_cast<float*>(ws + L.vec);
+  const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
+  const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
+  const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW));
+  if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
+  hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
+                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, vec);
+  hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+                     dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
+                     Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, vec, static_cast<T*>(y));
+  return launch_status();
+}
+
+template <typename T, int DK, int CT>
+int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float* g,
+                const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
+                const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
+                int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
+  if (Dv % 64 == 0)
+    return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
+                                    chunk, scale, l2norm, y, ws, L, stream);
+  return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
+                                  chunk, scale, l2norm, y, ws, L, stream);
+}
+
+template <typename T, int DK>
+int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, const float* g,
+                const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
+                const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
+                int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
+  if (CT == 32)
+    return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
+                                  chunk, scale, l2norm, y, ws, L, stream);
+  return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
+                                chunk, scale, l2norm, y, ws, L, stream);
+}
+
+template <typename T>
+int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, float* pool, int64_t pool_size,
+                const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
+                int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
+                hipStream_t stream) {
+  switch (Dk) {
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk == 32 || chunk == 64; }
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int Dv,
+                                              int chunk) {
+  (void)Hk; (void)Dk; (void)Dv;
+  if (T_tot < 0 || N_s < 0 || Hv <= 0 || !gdn::valid_chunk(chunk)) return 0;
+  return gdn::layout(T_tot, N_s, Hv, chunk).total;
+}
+
+extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, float* state_pool, int64_t pool_size,
+                                 const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
+                                 int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk,
+                                 float scale, unsigned flags, void* y, gdn_dtype act,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdn;
+  if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
+      Hv % Hk != 0)
+    return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (!(Dk == 32 || Dk == 64 || Dk == 128) || Dv % 32 != 0 || Dv > 256 || !valid_chunk(chunk) ||
+      (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
+    return GDN_ERR_UNSUPPORTED;
+  if (N_s == 0) return GDN_OK;
+  if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
+  if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(state_pool) || !aligned16(workspace))
+    return GDN_ERR_ALIGN;
+  const Layout L = layout(T_tot, N_s, Hv, chunk);
+  if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  const size_t pool_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
+  const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
+  if (overlaps(y, y_bytes, state_pool, pool_bytes) || overlaps(workspace, L.total, state_pool, pool_bytes) ||
+      overlaps(workspace, L.total, y, y_bytes))
+    return GDN_ERR_ALIAS;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(Dk));
+  const int l2 = (flags & GDN_QK_L2NORM) ? 1 : 0;
+  const int CT = chunk_tile(chunk);
+  char* ws = static_cast<char*>(workspace);
+  if (act == GDN_BF16)
+    return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, stream);
+  return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, stream);
+}
+
+extern "C" int gdn_validate_varlen(const int64_t* cu_seqlens, const int64_t* cache_indices, int N_s,
+                                   int64_t T_tot, int64_t pool_size, hipStream_t stream) {
+  using namespace gdn;
+  if (N_s < 0 || T_tot < 0 || pool_size < 0) return GDN_ERR_SHAPE;
+  if (N_s == 0) return T_tot == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!cu_seqlens || !cache_indices) return GDN_ERR_NULL;
+  const size_t n = static_cast<size_t>(N_s);
+  int64_t* h = static_cast<int64_t*>(malloc(sizeof(int64_t) * (2 * n + 1)));
+  if (!h) return GDN_ERR_DEVICE;
+  int rc = GDN_OK;
+  if (hipMemcpyAsync(h, cu_seqlens, sizeof(int64_t) * (n + 1), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(h + n + 1, cache_indices, sizeof(int64_t) * n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    rc = GDN_ERR_DEVICE;
+  } else {
+    const int64_t* cu = h;
+    const int64_t* ci = h + n + 1;
+    if (cu[0] != 0 || cu[n] != T_tot) rc = GDN_ERR_SHAPE;
+    for (size_t s = 0; rc == GDN_OK && s < n; ++s)
+      if (cu[s + 1] < cu[s] || ci[s] < 0 || ci[s] >= pool_size) rc = GDN_ERR_SHAPE;
+    for (size_t a = 0; rc == GDN_OK && a < n; ++a)
+      for (size_t b = a + 1; b < n; ++b)
+        if (ci[a] == ci[b]) { rc = GDN_ERR_SHAPE; break; }
+  }
+  free(h);
+  return rc;
+}

@@ -114,6 +114,75 @@ int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
                       const float* dt_bias, float* g, float* beta,
                       int64_t T_tot, int Hv, gdn_dtype act, hipStream_t stream);
 
+/* gdn_chunk_prefill flag: L2-normalise q and k per token inside the kernel
+ * (x / sqrt(sum x^2 + 1e-6)), as the pymllm page's q is "not pre-normalised"
+ * and the regolith kernel normalises both. */
+#define GDN_QK_L2NORM 1u
+
+/*
+ * gdn_chunk_prefill_workspace - bytes of device workspace gdn_chunk_prefill
+ * needs for these sizes (0 for invalid arguments).  It depends only on T_tot,
+ * N_s, Hv and chunk; the other sizes are accepted for a stable signature.
+ */
+size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
+                                   int Dk, int Dv, int chunk);
+
+/*
+ * gdn_chunk_prefill - variable-length chunkwise (WY) prefill that advances a
+ * pool of recurrent states in place.  Source: pymllm `gdn_chunkwise` docs,
+ * module doc "Algorithm (per chunk of C tokens with initial state S_0)" steps
+ * 1-3, and the `gdn_extend_chunkwise` parameter list.  Sequence s owns the
+ * packed tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and the state slot
+ * state_pool[cache_indices[s]]; for every value head hv (key head
+ * hk = hv / (Hv/Hk)) the result equals running, token by token,
+ *     k^ = k / sqrt(|k|^2 + 1e-6),  q^ = scale * q / sqrt(|q|^2 + 1e-6)
+ *     (no normalisation without GDN_QK_L2NORM, q^ = scale * q)
+ *     S <- exp(g) S;  d = beta (v - S k^);  S <- S + d k^T;  y = S q^
+ * from the slot's current contents, then writing the final S back to the
+ * slot.  The work is arranged in chunks of `chunk` tokens (the last one of a
+ * sequence may be shorter); results depend on `chunk` only through rounding.
+ *
+ * q, k          [T_tot, Hk, Dk] act (raw; not normalised).
+ * v             [T_tot, Hv, Dv] act.
+ * g, beta       [T_tot, Hv] float32: log-space gate (<= 0 expected; the
+ *               chunk form is exact for any g but may overflow for g > 0)
+ *               and beta, e.g. from gdn_prefill_gates.
+ * state_pool    [pool_size, Hv, Dv, Dk] float32, read and written in place.
+ * cache_indices [N_s] int64, cu_seqlens [N_s + 1] int64: device arrays,
+ *               not checked by this call.  Contract: cu_seqlens[0] == 0,
+ *               non-decreasing, cu_seqlens[N_s] == T_tot; cache_indices
+ *               distinct and in [0, pool_size).  Zero-length sequences leave
+ *               their slot untouched; slots not named are never accessed.
+ *               Entries outside the contract are skipped or clamped (no
+ *               out-of-bounds access) but give unspecified results;
+ *               gdn_validate_varlen checks the contract.
+ * y             [T_tot, Hv, Dv] act, written.
+ * chunk         8, 16, 32 or 64 tokens.     scale: <= 0 selects Dk^-1/2.
+ * flags         0 or GDN_QK_L2NORM.
+ * workspace     device memory of at least gdn_chunk_prefill_workspace()
+ *               bytes, 16-byte aligned; its contents are scratch.
+ * Requirements: Dk in {32, 64, 128}; Dv a multiple of 32, <= 256;
+ * Hv % Hk == 0; q, k, state_pool 16-byte aligned.  N_s == 0 is a no-op.
+ * On an in-kernel failure the referenced slots are unspecified (the update
+ * is in place): callers that need to retry keep a copy of those slots.
+ */
+int gdn_chunk_prefill(const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, float* state_pool,
+                      int64_t pool_size, const int64_t* cache_indices,
+                      const int64_t* cu_seqlens, int N_s, int64_t T_tot,
+                      int Hk, int Hv, int Dk, int Dv, int chunk, float scale,
+                      unsigned flags, void* y, gdn_dtype act, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_validate_varlen - debug/test helper: copies cu_seqlens and
+ * cache_indices to the host (synchronising `stream`) and checks the
+ * gdn_chunk_prefill contract above.  GDN_OK, or GDN_ERR_SHAPE if violated.
+ */
+int gdn_validate_varlen(const int64_t* cu_seqlens,
+                        const int64_t* cache_indices, int N_s, int64_t T_tot,
+                        int64_t pool_size, hipStream_t stream);
+
 /* Human-readable name of a gdn_status value (static string, never NULL). */
 const char* gdn_status_string(int status);
 

@@ -110,3 +110,49 @@ def test_gates_validation(lib):
     alias[5] = _p(A + 4 * BIG + 4)
     assert f(*alias, ctypes.c_int64(8), 4, 1, None) == ALIAS
     assert f(*bad, ctypes.c_int64(0), 4, 1, None) == OK
+
+
+def prefill(lib, q=A, k=A + BIG, v=A + 2 * BIG, g=A + 3 * BIG, beta=A + 4 * BIG, pool=A + 5 * BIG,
+            P=4, ci=A + 6 * BIG, cu=A + 7 * BIG, N_s=2, T=100, Hk=2, Hv=4, Dk=128, Dv=128, chunk=64,
+            flags=1, y=A + 8 * BIG, act=1, ws=A + 9 * BIG, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk)
+    return lib.gdn_chunk_prefill(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(pool), P, _p(ci), _p(cu),
+                                 N_s, T, Hk, Hv, Dk, Dv, chunk, ctypes.c_float(0.0), flags, _p(y), act,
+                                 _p(ws), ws_bytes, None)
+
+
+def test_prefill_workspace_size(lib):
+    f = lib.gdn_chunk_prefill_workspace
+    assert f(100, 2, 2, 4, 128, 128, 64) > 0
+    assert f(100, 2, 2, 4, 128, 128, 48) == 0          # unsupported chunk
+    assert f(-1, 2, 2, 4, 128, 128, 64) == 0
+    # grows with tokens, sequences and heads
+    assert f(1000, 2, 2, 4, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
+    assert f(100, 20, 2, 4, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
+    assert f(100, 2, 2, 8, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, N_s=-1) == SHAPE
+    assert prefill(lib, Hk=3) == SHAPE
+    assert prefill(lib, act=9) == DTYPE
+    assert prefill(lib, Dk=256) == UNSUP
+    assert prefill(lib, Dv=40) == UNSUP
+    assert prefill(lib, chunk=128) == UNSUP
+    assert prefill(lib, flags=2) == UNSUP
+    assert prefill(lib, ws=0) == NULL
+    assert prefill(lib, cu=0) == NULL
+    assert prefill(lib, q=0) == NULL
+    assert prefill(lib, pool=A + 5 * BIG + 8) == ALIGN
+    assert prefill(lib, ws_bytes=1024) == WORKSPACE
+    assert prefill(lib, y=A + 5 * BIG + 64) == ALIAS      # y inside the pool
+    assert prefill(lib, N_s=0, q=0, cu=0) == OK           # nothing to do
+
+
+def test_validate_varlen_rejects_before_any_copy(lib):
+    f = lib.gdn_validate_varlen
+    assert f(_p(A), _p(A + BIG), -1, 10, 4, None) == SHAPE
+    assert f(_p(0), _p(A + BIG), 2, 10, 4, None) == NULL
+    assert f(_p(A), _p(A + BIG), 0, 0, 4, None) == OK
+    assert f(_p(A), _p(A + BIG), 0, 5, 4, None) == SHAPE

@@ -1,0 +1,234 @@
+"""GPU parity of gdn_prefill_gates + gdn_chunk_prefill against the fp64
+token-by-token oracle, and bit-exact handling of cu_seqlens/cache_indices.
+
+Tolerances: pool state max relative error <= 1e-3; y relative Frobenius
+<= 2e-2 when bf16, max relative <= 1e-3 when fp32; index handling bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_deltanet_linear_gdn_amd as gdn
+from gated_deltanet_linear_gdn_amd import synth
+from tests.helpers import maxrel, relF, to_dev, to_np, oracle_decode_batched
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=synth.WARMUP_STEPS):
+    """Pool slots warmed by `steps` oracle decode steps (decode-batch
+    distributions), handed over as float32."""
+    S = np.zeros((P, Hv, Dv, Dk))
+    for _ in range(steps):
+        S, _ = oracle_decode_batched(S, synth.decode_token(rng, P, Hk, Hv, Dk, Dv))
+    return S.astype(np.float32)
+
+
+def _run_gpu(inp, pool0, chunk, act, l2norm=True, scale=None):
+    d = DT[act]
+    a, b = to_dev(inp["a"], d, DEV), to_dev(inp["b"], d, DEV)
+    g, beta = gdn.gdn_prefill_gates(a, b, to_dev(inp["A_log"], torch.float32, DEV),
+                                    to_dev(inp["dt_bias"], torch.float32, DEV))
+    pool = to_dev(pool0, torch.float32, DEV)
+    T, Hv, Dv = inp["v"].shape
+    y = torch.full((T, Hv, Dv), float("nan"), dtype=d, device=DEV)
+    ci = to_dev(inp["cache_indices"], torch.int64, DEV)
+    cu = to_dev(inp["cu_seqlens"], torch.int64, DEV)
+    assert gdn.gdn_validate_varlen(cu, ci, T, pool0.shape[0]) == 0
+    gdn.gdn_chunk_prefill(to_dev(inp["q"], d, DEV), to_dev(inp["k"], d, DEV), to_dev(inp["v"], d, DEV),
+                          g, beta, pool, ci, cu, chunk=chunk, scale=scale, l2norm=l2norm, y=y)
+    torch.cuda.synchronize()
+    return pool, y
+
+
+def _run_oracle(inp, pool0, l2norm=True, scale=None):
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    return oracle.gdn_prefill(inp["q"], inp["k"], inp["v"], g, beta, pool0, inp["cache_indices"],
+                              inp["cu_seqlens"], scale=scale, l2norm=l2norm)
+
+
+def _check(pool_gpu, y_gpu, P_ref, y_ref, pool0, inp, act):
+    P = to_np(pool_gpu)
+    assert maxrel(P, P_ref) <= 1e-3
+    yv = to_np(y_gpu)
+    assert not np.isnan(yv).any()
+    if act == "f32":
+        assert maxrel(yv, y_ref) <= 1e-3
+    else:
+        assert relF(yv, y_ref) <= 2e-2
+    used = set(int(s) for s in inp["cache_indices"])
+    lens = np.diff(inp["cu_seqlens"])
+    for s, slot in enumerate(inp["cache_indices"]):
+        if lens[s] == 0:
+            used.discard(int(slot))
+    for slot in range(pool0.shape[0]):
+        if slot not in used:
+            assert np.array_equal(to_np(pool_gpu[slot]).astype(np.float32), pool0[slot]), slot
+
+
+def test_tiny_fp32_decode_then_prefill():
+    """Tiny fp32 workload: one decode step from zero at B=2, Hk=2, Hv=4,
+    Dk=Dv=32, then one 16-token sequence (chunk 8) into the pool made of the
+    two decoded states, writing slot 1; slot 0 must come out bit-identical."""
+    c = synth.TINY
+    rng = np.random.default_rng(0)
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act="f32")
+    S_ref, y_ref = oracle.gdn_step(np.zeros((B, Hv, Dv, Dk)), tok["q"], tok["k"], tok["v"], tok["g"],
+                                   tok["beta"])
+    t = {n: to_dev(a, torch.float32, DEV) for n, a in tok.items()}
+    S_gpu, y_gpu = gdn.gdn_decode_step(torch.zeros((B, Hv, Dv, Dk), device=DEV), None, t["q"], t["k"],
+                                       t["v"], t["g"], t["beta"])
+    assert maxrel(to_np(S_gpu), S_ref) <= 1e-5 and maxrel(to_np(y_gpu), y_ref) <= 1e-5
+    pool0 = S_ref.astype(np.float32)
+    inp = synth.prefill_inputs(rng, [c["prefill_len"]], Hk, Hv, Dk, Dv, pool_size=B, act="f32")
+    inp["cache_indices"] = np.array([1], dtype=np.int64)
+    pool, y = _run_gpu(inp, pool0, c["chunk"], "f32")
+    P_ref, yr = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, yr, pool0, inp, "f32")
+    assert np.array_equal(to_np(pool[0]).astype(np.float32), pool0[0])
+
+
+CASES = [
+    # lengths, Hk, Hv, Dk, Dv, chunk, act
+    ([1, 7, 64, 65, 130, 0, 200], 2, 4, 128, 128, 64, "bf16"),
+    ([33, 64, 95, 1], 1, 3, 64, 96, 32, "bf16"),
+    ([50, 17, 0, 31], 2, 2, 32, 64, 16, "bf16"),
+    ([40, 9], 1, 2, 128, 32, 8, "bf16"),
+    ([70, 3, 128], 2, 4, 128, 64, 64, "f32"),
+    ([45, 16], 1, 1, 64, 32, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("lengths,Hk,Hv,Dk,Dv,chunk,act", CASES)
+def test_prefill_parity(lengths, Hk, Hv, Dk, Dv, chunk, act):
+    rng = np.random.default_rng(sum(lengths) + Dk + Dv + chunk)
+    P = len(lengths) + 3
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=4)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P, act=act)
+    pool, y = _run_gpu(inp, pool0, chunk, act)
+    P_ref, y_ref = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, y_ref, pool0, inp, act)
+
+
+def test_prefill_without_l2norm_and_explicit_scale():
+    rng = np.random.default_rng(21)
+    Hk, Hv, Dk, Dv = 1, 2, 64, 64
+    pool0 = _warm_pool(rng, 3, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, [37, 70], Hk, Hv, Dk, Dv, pool_size=3)
+    # unit-norm keys so that the un-normalised recurrence stays bounded
+    k = inp["k"].astype(np.float64)
+    inp["k"] = synth.round_bf16((k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32))
+    pool, y = _run_gpu(inp, pool0, 64, "bf16", l2norm=False, scale=0.3)
+    P_ref, y_ref = _run_oracle(inp, pool0, l2norm=False, scale=0.3)
+    _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
+
+
+def _gpu_prefill_seq(inp, pool_dev, chunk, sel, act="bf16"):
+    """Run a subset of sequences `sel` (in that order) packed together."""
+    d = DT[act]
+    cu = inp["cu_seqlens"]
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in sel]).astype(np.int64)
+    lens = [int(cu[s + 1] - cu[s]) for s in sel]
+    g, beta = gdn.gdn_prefill_gates(to_dev(inp["a"][idx], d, DEV), to_dev(inp["b"][idx], d, DEV),
+                                    to_dev(inp["A_log"], torch.float32, DEV),
+                                    to_dev(inp["dt_bias"], torch.float32, DEV))
+    y = gdn.gdn_chunk_prefill(to_dev(inp["q"][idx], d, DEV), to_dev(inp["k"][idx], d, DEV),
+                              to_dev(inp["v"][idx], d, DEV), g, beta, pool_dev,
+                              to_dev(inp["cache_indices"][list(sel)], torch.int64, DEV),
+                              to_dev(synth.cu_from_lengths(lens), torch.int64, DEV), chunk=chunk)
+    return y, idx
+
+
+def test_packing_order_and_repeat_are_bitwise_invariant():
+    rng = np.random.default_rng(22)
+    Hk, Hv, Dk, Dv = 2, 4, 128, 128
+    lengths = [100, 0, 64, 3, 150]
+    pool0 = _warm_pool(rng, 7, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=7)
+    pa = to_dev(pool0, torch.float32, DEV)
+    ya, ia = _gpu_prefill_seq(inp, pa, 64, [0, 1, 2, 3, 4])
+    pb = to_dev(pool0, torch.float32, DEV)
+    yb, ib = _gpu_prefill_seq(inp, pb, 64, [4, 3, 2, 1, 0])
+    pc = to_dev(pool0, torch.float32, DEV)
+    yc, ic = _gpu_prefill_seq(inp, pc, 64, [0, 1, 2, 3, 4])
+    assert torch.equal(pa, pb) and torch.equal(pa, pc)
+    assert torch.equal(ya, yc)
+    # same tokens, different packed positions: compare per token
+    pos_b = {int(t): i for i, t in enumerate(ib)}
+    perm = torch.tensor([pos_b[int(t)] for t in ia], device=DEV)
+    assert torch.equal(ya, yb[perm])
+
+
+def test_chunk_aligned_resume_is_bitwise_equal():
+    rng = np.random.default_rng(23)
+    Hk, Hv, Dk, Dv = 2, 2, 128, 64
+    pool0 = _warm_pool(rng, 2, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, [192], Hk, Hv, Dk, Dv, pool_size=2)
+    whole = to_dev(pool0, torch.float32, DEV)
+    y_all, _ = _gpu_prefill_seq(inp, whole, 64, [0])
+    split = synth.prefill_inputs(np.random.default_rng(0), [128, 64], Hk, Hv, Dk, Dv, pool_size=2)
+    for n in ("q", "k", "v", "a", "b"):
+        split[n] = inp[n]
+    split["A_log"], split["dt_bias"] = inp["A_log"], inp["dt_bias"]
+    slot = inp["cache_indices"][0]
+    split["cache_indices"] = np.array([slot, slot], dtype=np.int64)
+    part = to_dev(pool0, torch.float32, DEV)
+    y1, _ = _gpu_prefill_seq(split, part, 64, [0])
+    y2, _ = _gpu_prefill_seq(split, part, 64, [1])
+    assert torch.equal(whole, part)
+    assert torch.equal(y_all, torch.cat([y1, y2]))
+
+
+def test_decode_loop_matches_prefill():
+    """T decode steps on normalised, pre-scaled q/k equal a T-token prefill."""
+    rng = np.random.default_rng(24)
+    Hk, Hv, Dk, Dv, T = 2, 4, 128, 128, 40
+    pool0 = _warm_pool(rng, 1, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, [T], Hk, Hv, Dk, Dv, pool_size=1, act="f32")
+    pool, y = _run_gpu(inp, pool0, 16, "f32")
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    nrm = lambda x: x / np.sqrt(np.sum(x.astype(np.float64) ** 2, -1, keepdims=True) + 1e-6)
+    S = to_dev(pool0, torch.float32, DEV)
+    for t in range(T):
+        q = to_dev((nrm(inp["q"][t]) * Dk ** -0.5)[None].astype(np.float32), torch.float32, DEV)
+        k = to_dev(nrm(inp["k"][t])[None].astype(np.float32), torch.float32, DEV)
+        S, yd = gdn.gdn_decode_step(S, S, q, k, to_dev(inp["v"][t][None], torch.float32, DEV),
+                                    to_dev(g[t][None].astype(np.float32), torch.float32, DEV),
+                                    to_dev(beta[t][None].astype(np.float32), torch.float32, DEV))
+        assert maxrel(to_np(yd[0]), to_np(y[t])) <= 1e-3, t
+    assert maxrel(to_np(S), to_np(pool)) <= 1e-4
+
+
+def test_varlen_prefill_workload_sampled():
+    """Varlen prefill workload: 8 sequences of U[512, 4096] tokens, Hk=16,
+    Hv=48, Dk=Dv=128, bf16, chunk 64, pool of 16 warmed slots, random
+    cache_indices.  The whole batch runs on the GPU; the oracle checks 3
+    sequences on 6 value heads (key heads 0 and 15)."""
+    c = synth.PREFILL_VARLEN
+    rng = np.random.default_rng(0)
+    Hk, Hv, Dk, Dv, P = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"]
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    pool, y = _run_gpu(inp, pool0, c["chunk"], "bf16")
+    yv = to_np(y)
+    assert not np.isnan(yv).any()
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    cu = inp["cu_seqlens"]
+    for s in (0, int(np.argmax(lengths)), 7):
+        idx = np.arange(cu[s], cu[s + 1])
+        slot = int(inp["cache_indices"][s])
+        for hk in (0, 15):
+            hs = np.arange(hk * 3, hk * 3 + 3)
+            P_ref, y_ref = oracle.gdn_prefill(
+                inp["q"][idx][:, [hk]], inp["k"][idx][:, [hk]], inp["v"][idx][:, hs],
+                g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0], [0, len(idx)])
+            assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, (s, hk)
+            assert relF(yv[idx][:, hs], y_ref) <= 2e-2, (s, hk)
+    untouched = sorted(set(range(P)) - set(int(x) for x in inp["cache_indices"]))
+    for slot in untouched:
+        assert np.array_equal(to_np(pool[slot]).astype(np.float32), pool0[slot])
