@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
     const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm,
     bf16* __restrict__ Th, bf16* __restrict__ Tl, bf16* __restrict__ Ph, bf16* __restrict__ Pl,
-    float* __restrict__ vec) {
+    float* __restrict__ fac, bf16* __restrict__ KTw) {
   constexpr bool PRECISE = std::is_same<T, float>::value;
   constexpr int MT = CT / 16, KB = DK / 32;
   __shared__ float sG[CT], srk[CT], srq[CT], sb[CT];
@@ -321,11 +321,39 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
     sb[lane] = lane < n ? bt : 0.f;
   }
   __syncthreads();
+  // Per-token factors of the chunk loop (zero past the last token):
+  //   beta, beta gamma / |k|, gamma scale / |q|, exp(G_C - G) / |k|,
+  // and gamma_C = exp(G_C); G is flat past the last token, so G_C = G[CT-1].
   if (lane < CT) {
-    float* vp = vec + mat * 3 * CT;
-    vp[lane] = G;
-    vp[CT + lane] = srk[lane];
-    vp[2 * CT + lane] = srq[lane];
+    float* fp = fac + mat * (4 * CT + 4);
+    const float GC = sG[CT - 1];
+    const float gam = __expf(G);
+    fp[lane] = sb[lane];
+    fp[CT + lane] = sb[lane] * gam * srk[lane];
+    fp[2 * CT + lane] = gam * srq[lane];
+    fp[3 * CT + lane] = __expf(GC - G) * srk[lane];
+    if (lane == 0) fp[4 * CT] = __expf(GC);
+  }
+  // K^T of the chunk for the bf16 chunk loop, written once per key head by
+  // the first value head of its group: KT[dk][t] (zero past the last token).
+  if constexpr (!PRECISE) {
+    if (hv % (Hv / Hk) == 0) {
+      bf16* kt = KTw + (static_cast<size_t>(c) * Hk + hk) * DK * CT;
+#pragma unroll
+      for (int I = 0; I < MT; ++I) {
+        const int t = I * 16 + l16;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 wk = __builtin_bit_cast(u32x4, kh[I][kb]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t word = wk[e >> 1];
+            const bf16 val = static_cast<bf16>((e & 1) ? (word >> 16) : (word & 0xffffu));
+            kt[(kb * 32 + kg * 8 + e) * CT + t] = t < n ? val : bf16(0);
+          }
+        }
+      }
+    }
   }
 
   // Gram K K^T and Q K^T tiles (I, J), J <= I; A and P from them.
@@ -410,7 +438,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
     const int64_t* __restrict__ cache_indices, const int64_t* __restrict__ cu,
     const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk, int Hv, int Dv, int C, int maxc,
     const bf16* __restrict__ Th, const bf16* __restrict__ Tl, const bf16* __restrict__ Ph,
-    const bf16* __restrict__ Pl, const float* __restrict__ vec, T* __restrict__ y) {
+    const bf16* __restrict__ Pl, const float* __restrict__ fac, T* __restrict__ y) {
   constexpr bool PRECISE = std::is_same<T, float>::value;
   constexpr int BV = 16 * NW, NT = 64 * NW;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
@@ -496,14 +524,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
         if constexpr (PRECISE) plf[mt][cb] = Raw<bf16>::load(Pl + roff, cb * 32, kg);
       }
     }
-    float fvG = 0.f, fvK = 0.f, fvQ = 0.f, fvGC = 0.f, fvB = 0.f;
+    float fvB = 0.f, fvK = 0.f, fvQ = 0.f, fvD = 0.f, fvC = 0.f;
     if (tid < CT) {
-      const float* vp = vec + mat * 3 * CT;
-      fvG = vp[tid];
-      fvK = vp[CT + tid];
-      fvQ = vp[2 * CT + tid];
-      fvGC = vp[CT - 1];  // G is flat past the last valid token
-      fvB = beta[static_cast<size_t>(t0 + min(tid, n - 1)) * Hv + hv];
+      const float* fp = fac + mat * (4 * CT + 4);
+      fvB = fp[tid];
+      fvK = fp[CT + tid];
+      fvQ = fp[2 * CT + tid];
+      fvD = fp[3 * CT + tid];
+      fvC = fp[4 * CT];
     }
 
     __syncthreads();  // the previous chunk no longer reads K^T or the factors
@@ -516,13 +544,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
       }
     }
     if (tid < CT) {
-      const float bt = tid < n ? fvB : 0.f;
-      const float gam = __expf(fvG);
-      fB[tid] = bt;
-      fK[tid] = bt * gam * fvK;
-      fQ[tid] = gam * fvQ;
-      fD[tid] = __expf(fvGC - fvG) * fvK;
-      if (tid == 0) sGC = __expf(fvGC);
+      fB[tid] = fvB;
+      fK[tid] = fvK;
+      fQ[tid] = fvQ;
+      fD[tid] = fvD;
+      if (tid == 0) sGC = fvC;
     }
     __syncthreads();
 
@@ -639,6 +665,297 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// 3b. The bf16 chunk loop with LDS-staged, double-buffered chunk operands.
+//
+// One workgroup per (sequence, value head, BV = 16 * NW value columns), a wave
+// per 16 columns.  What a chunk needs besides the state - K, Q, K^T, the V
+// block, T hi/lo and the per-token factors - is copied once per workgroup from
+// global memory straight into LDS (global_load_lds: no registers,
+// asynchronous) into the buffer the current chunk does not use; one wait and
+// barrier per chunk hands the two buffers over.  P is read from L2 into
+// registers at the start of the chunk that uses it.  Tile rows are padded by
+// 16 bytes, which makes every 8-byte fragment read of a 32-lane half-wave
+// bank-conflict free and leaves only a per-lane base plus an immediate offset
+// in each LDS read.
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* gbl_vptr;
+
+// A ROWS x COLS bf16 tile stored with a 16-byte pad after every row.
+template <int ROWS, int COLS>
+struct PadTile {
+  static constexpr int PITCH = COLS + 8;          // elements
+  static constexpr int SPR = COLS / 8;            // 16-byte source items per row
+  static constexpr int SLOTS = ROWS * (SPR + 1);  // 16-byte LDS slots, pads included
+  static constexpr int NBLK = (SLOTS + 63) / 64;  // 1 KiB copy blocks
+  static constexpr int ELEMS = NBLK * 512;        // storage, whole blocks
+};
+
+template <int DK, int CT, int BV>
+struct __attribute__((aligned(16))) ChunkBuf {
+  bf16 K[PadTile<CT, DK>::ELEMS];
+  bf16 Q[PadTile<CT, DK>::ELEMS];
+  bf16 KT[PadTile<DK, CT>::ELEMS];
+  bf16 Th[PadTile<CT, CT>::ELEMS];
+  bf16 Tl[PadTile<CT, CT>::ELEMS];
+  bf16 V[CT * BV];          // read two bytes at a time: no padding
+  // beta, beta gamma/|k|, gamma scale/|q|, exp(G_C-G)/|k|, gamma_C; rounded
+  // up to whole 64-float copy blocks so the last block stays inside.
+  float fac[(4 * CT + 4 + 63) / 64 * 64];
+};
+
+// Wave-wide asynchronous copy: lane i's `BYTES` (4 or 16) from `src` land at
+// `lds_block + i * BYTES`; completion is counted by vmcnt.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void* src, void* lds_block) {
+  static_assert(BYTES == 4 || BYTES == 16, "copy size");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_block, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_block, 4, 0, 0);
+}
+
+// Copy a padded tile: row r of the source starts at row_ptr(r); pad slots
+// (and slots past the last row) fetch a valid dummy item.  Wave w copies
+// blocks w, w + NW, ...; w is wave-uniform so every branch here is too.
+template <int ROWS, int COLS, int NW, typename RowPtr>
+__device__ __forceinline__ void stage_padded(bf16* dst, int w, int lane, RowPtr row_ptr) {
+  using P = PadTile<ROWS, COLS>;
+#pragma unroll
+  for (int j = 0; j < (P::NBLK + NW - 1) / NW; ++j) {
+    const int b = j * NW + w;
+    if (P::NBLK % NW == 0 || b < P::NBLK) {
+      const int slot = b * 64 + lane;
+      const int row = slot / (P::SPR + 1), item = slot % (P::SPR + 1);
+      const bool real = row < ROWS && item < P::SPR;
+      copy_to_lds<16>(row_ptr(real ? row : 0) + (real ? item : 0) * 8, dst + b * 512);
+    }
+  }
+}
+
+// Unpadded ROWS x COLS tile.
+template <int ROWS, int COLS, int NW, typename RowPtr>
+__device__ __forceinline__ void stage_plain(bf16* dst, int w, int lane, RowPtr row_ptr) {
+  constexpr int SPR = COLS / 8, NBLK = ROWS * SPR / 64;
+  static_assert(ROWS * SPR % 64 == 0, "whole blocks");
+#pragma unroll
+  for (int j = 0; j < (NBLK + NW - 1) / NW; ++j) {
+    const int b = j * NW + w;
+    if (NBLK % NW == 0 || b < NBLK) {
+      const int slot = b * 64 + lane;
+      copy_to_lds<16>(row_ptr(slot / SPR) + (slot % SPR) * 8, dst + b * 512);
+    }
+  }
+}
+
+// "pi"-order operand from row `row` of a padded tile (see acc_operand).
+template <int COLS>
+__device__ __forceinline__ bf16x8v lds_pi(const bf16* tile, int row, int k0, int kg) {
+  constexpr int PITCH = COLS + 8;
+  const bf16* p = tile + row * PITCH + k0 + kg * 4;
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+  return __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, b.x, b.y});
+}
+
+template <int DK, int CT, int NW>
+__global__ __launch_bounds__(64 * NW) void gdn_prefill_lds_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
+    const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
+    int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
+    const bf16* __restrict__ Ph, const float* __restrict__ fac, const bf16* __restrict__ KTw,
+    bf16* __restrict__ y) {
+  constexpr int BV = 16 * NW;
+  constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
+  constexpr int FSTR = 4 * CT + 4;
+  using Buf = ChunkBuf<DK, CT, BV>;
+  // Two distinct buffers (not an indexed pair): the compiler can then see
+  // that reads of one do not alias the asynchronous copies into the other
+  // and does not wait for the copies before every read.
+  __shared__ Buf buf0, buf1;
+
+  const int nvb = Dv / BV;
+  const int s = blockIdx.x / (Hv * nvb);
+  const int rem = blockIdx.x - s * (Hv * nvb);
+  const int hv = rem / nvb;
+  const int vb = rem - hv * nvb;
+  const int64_t slot = cache_indices[s];
+  if (slot < 0 || slot >= pool_size) return;
+  int64_t b0, len;
+  seq_bounds(cu, s, T_tot, b0, len);
+  if (len <= 0) return;
+  const int cbase = scs[s];
+  const int nch_all = static_cast<int>((len + C - 1) / C);
+  const int nch = cbase + nch_all > maxc ? (maxc > cbase ? maxc - cbase : 0) : nch_all;
+  const int hk = hv / (Hv / Hk);
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dvl = w * 16 + l16;  // value column within the block
+  const int dv = vb * BV + dvl;
+
+  auto chunk_rows = [&](int ci) {
+    const int64_t done = static_cast<int64_t>(ci) * C;
+    return static_cast<int>(len - done < C ? len - done : C);
+  };
+  // Start copying chunk ci into N.  Rows past the chunk's last token copy
+  // that token again; their factors are zero, so they add nothing.
+  auto fetch = [&](int ci, Buf& N) {
+    const int64_t t0 = b0 + static_cast<int64_t>(ci) * C;
+    const int last = chunk_rows(ci) - 1;
+    const size_t mat = static_cast<size_t>(cbase + ci) * Hv + hv;
+    const bf16* kb0 = k + (static_cast<size_t>(t0) * Hk + hk) * DK;
+    const bf16* qb0 = q + (static_cast<size_t>(t0) * Hk + hk) * DK;
+    const bf16* vb0 = v + (static_cast<size_t>(t0) * Hv + hv) * Dv + vb * BV;
+    const bf16* kt0 = KTw + (static_cast<size_t>(cbase + ci) * Hk + hk) * DK * CT;
+    const bf16* th0 = Th + mat * CT * CT;
+    const bf16* tl0 = Tl + mat * CT * CT;
+    stage_padded<CT, DK, NW>(N.K, w, lane, [&](int r) { return kb0 + min(r, last) * (Hk * DK); });
+    stage_padded<CT, DK, NW>(N.Q, w, lane, [&](int r) { return qb0 + min(r, last) * (Hk * DK); });
+    stage_padded<DK, CT, NW>(N.KT, w, lane, [&](int r) { return kt0 + r * CT; });
+    stage_padded<CT, CT, NW>(N.Th, w, lane, [&](int r) { return th0 + r * CT; });
+    stage_padded<CT, CT, NW>(N.Tl, w, lane, [&](int r) { return tl0 + r * CT; });
+    stage_plain<CT, BV, NW>(N.V, w, lane, [&](int r) { return vb0 + min(r, last) * (Hv * Dv); });
+    if (w == NW - 1) {
+      const float* fp = fac + mat * FSTR;
+#pragma unroll
+      for (int j = 0; j < (FSTR + 63) / 64; ++j)
+        copy_to_lds<4>(fp + min(j * 64 + lane, FSTR - 1), N.fac + j * 64);
+    }
+  };
+
+  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(dv) * DK;
+  f32x4 S[DT];
+#pragma unroll
+  for (int m = 0; m < DT; ++m) S[m] = *reinterpret_cast<const f32x4*>(Sp + m * 16 + kg * 4);
+
+  // One chunk: start copying chunk ci+1 into N, compute chunk ci from B,
+  // then wait for the copies and hand the buffers over.
+  auto step = [&](int ci, const Buf& B, Buf& N) {
+    const int n = chunk_rows(ci);
+    const int64_t t0 = b0 + static_cast<int64_t>(ci) * C;
+    const size_t mat = static_cast<size_t>(cbase + ci) * Hv + hv;
+    if (ci + 1 < nch) fetch(ci + 1, N);
+    // P rows for the lower-triangular (mt, cb) blocks, straight from L2
+    Raw<bf16> pf[MT][CKB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb)
+        pf[mt][cb] = Raw<bf16>::load(Ph + mat * CT * CT + (mt * 16 + l16) * CT, cb * 32, kg);
+
+    // state operand over dk (hi/lo)
+    bf16x8v Sh[KB], Sl[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc_operand(S[2 * kb], S[2 * kb + 1], Sh[kb], Sl[kb]);
+
+    // X = K S (state-grade)
+    f32x4 X[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8v ak = lds_pi<DK>(B.K, mt * 16 + l16, kb * 32, kg);
+        X[mt] = mma(ak, Sh[kb], X[mt]);
+        X[mt] = mma(ak, Sl[kb], X[mt]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // R = diag(beta) V - diag(beta gamma / |k|) X   (rows t = mt*16 + kg*4 + r)
+    f32x4 R[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 fb = *reinterpret_cast<const f32x4*>(B.fac + mt * 16 + kg * 4);
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(B.fac + CT + mt * 16 + kg * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float vv = bf16_to_f32(B.V[(mt * 16 + kg * 4 + r) * BV + dvl]);
+        R[mt][r] = fb[r] * vv - fk[r] * X[mt][r];
+      }
+    }
+    bf16x8v Rh[CKB], Rl[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) acc_operand(R[2 * cb], R[2 * cb + 1], Rh[cb], Rl[cb]);
+
+    // Delta = T R (T lower triangular: skip blocks above the diagonal)
+    f32x4 D[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        const bf16x8v th = lds_pi<CT>(B.Th, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v tl = lds_pi<CT>(B.Tl, mt * 16 + l16, cb * 32, kg);
+        D[mt] = mma(th, Rh[cb], D[mt]);
+        D[mt] = mma(th, Rl[cb], D[mt]);
+        D[mt] = mma(tl, Rh[cb], D[mt]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // O = diag(gamma scale / |q|) Q S + P Delta -> y   (output-grade: S hi only)
+    bf16x8v Dh[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<DK>(B.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
+      const f32x4 fq = *reinterpret_cast<const f32x4*>(B.fac + 2 * CT + mt * 16 + kg * 4);
+      f32x4 O = fq * Y;
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        bf16x8v ph, unused;
+        pf[mt][cb].operand(ph, unused);
+        O = mma(ph, Dh[cb], O);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = mt * 16 + kg * 4 + r;
+        if (t < n)
+          y[(static_cast<size_t>(t0 + t) * Hv + hv) * Dv + dv] = __builtin_bit_cast(bf16, (__bf16)O[r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // S <- gamma_C S + K^T diag(exp(G_C - G) / |k|) Delta
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(B.fac + 3 * CT + mt * 16 + kg * 4);
+    bf16x8v Eh[CKB], El[CKB];
+#pragma unroll
+    for (int cb = 0; cb < CKB; ++cb) acc_operand(D[2 * cb], D[2 * cb + 1], Eh[cb], El[cb]);
+    const float gC = B.fac[4 * CT];
+#pragma unroll
+    for (int m = 0; m < DT; ++m) {
+      S[m] *= gC;
+#pragma unroll
+      for (int cb = 0; cb < CKB; ++cb) {
+        const bf16x8v a = lds_pi<CT>(B.KT, m * 16 + l16, cb * 32, kg);
+        S[m] = mma(a, Eh[cb], S[m]);
+        S[m] = mma(a, El[cb], S[m]);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next chunk landed
+    __syncthreads();                // ... and everyone's; the current buffer is free
+  };
+
+  if (nch > 0) fetch(0, buf0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int ci = 0; ci < nch; ci += 2) {
+    step(ci, buf0, buf1);
+    if (ci + 1 < nch) step(ci + 1, buf1, buf0);
+  }
+
+#pragma unroll
+  for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
+}
+
+// ----------------------------------------------------------------------------
 // host side
 
 constexpr size_t kAlign = 256;
@@ -647,10 +964,10 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
 
 struct Layout {
-  size_t scs, th, tl, ph, pl, vec, total;
+  size_t scs, th, tl, ph, pl, fac, kt, total;
 };
 
-inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk) {
+inline Layout layout(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int chunk) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t mats = maxc * static_cast<size_t>(Hv);
@@ -661,7 +978,8 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk) {
   L.tl = off; off += up(mats * CT * CT * sizeof(bf16));
   L.ph = off; off += up(mats * CT * CT * sizeof(bf16));
   L.pl = off; off += up(mats * CT * CT * sizeof(bf16));
-  L.vec = off; off += up(mats * 3 * CT * sizeof(float));
+  L.fac = off; off += up(mats * (4 * CT + 4) * sizeof(float));
+  L.kt = off; off += up(maxc * static_cast<size_t>(Hk) * Dk * CT * sizeof(bf16));
   L.total = off;
   return L;
 }
@@ -676,7 +994,8 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
   bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
   bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
-  float* vec = reinterpret_cast<float*>(ws + L.vec);
+  float* fac = reinterpret_cast<float*>(ws + L.fac);
+  bf16* KTw = reinterpret_cast<bf16*>(ws + L.kt);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
   const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW));
@@ -685,11 +1004,17 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
   hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
-                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, vec);
-  hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
-                     dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
-                     Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, vec, static_cast<T*>(y));
+                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac, KTw);
+  if constexpr (std::is_same<T, bf16>::value)
+    hipLaunchKernelGGL((gdn_prefill_lds_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+                       dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
+                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, KTw, static_cast<bf16*>(y));
+  else
+    hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+                       dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
+                       Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, fac, static_cast<T*>(y));
   return launch_status();
 }
 
@@ -698,6 +1023,10 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
+  // bf16: the LDS-staged kernel; fp32 activations: the register-fragment
+  // kernel (its operands would not fit LDS twice).  64 value columns (four
+  // waves, up to 512 registers each) per workgroup, else 32.  Eight waves
+  // per workgroup would cap each wave at 256 registers and spill.
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
                                     chunk, scale, l2norm, y, ws, L, stream);
@@ -738,9 +1067,9 @@ inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk =
 
 extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int Dv,
                                               int chunk) {
-  (void)Hk; (void)Dk; (void)Dv;
-  if (T_tot < 0 || N_s < 0 || Hv <= 0 || !gdn::valid_chunk(chunk)) return 0;
-  return gdn::layout(T_tot, N_s, Hv, chunk).total;
+  (void)Dv;
+  if (T_tot < 0 || N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || !gdn::valid_chunk(chunk)) return 0;
+  return gdn::layout(T_tot, N_s, Hk, Hv, Dk, chunk).total;
 }
 
 extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -762,7 +1091,7 @@ extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, co
   if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(state_pool) || !aligned16(workspace))
     return GDN_ERR_ALIGN;
-  const Layout L = layout(T_tot, N_s, Hv, chunk);
+  const Layout L = layout(T_tot, N_s, Hk, Hv, Dk, chunk);
   if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   const size_t pool_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
   const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
