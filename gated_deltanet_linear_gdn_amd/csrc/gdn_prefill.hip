@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
     const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm,
     bf16* __restrict__ Th, bf16* __restrict__ Tl, bf16* __restrict__ Ph, bf16* __restrict__ Pl,
-    float* __restrict__ fac, bf16* __restrict__ KTw) {
+    float* __restrict__ fac) {
   constexpr bool PRECISE = std::is_same<T, float>::value;
   constexpr int MT = CT / 16, KB = DK / 32;
   __shared__ float sG[CT], srk[CT], srq[CT], sb[CT];
@@ -334,28 +334,6 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
     fp[3 * CT + lane] = __expf(GC - G) * srk[lane];
     if (lane == 0) fp[4 * CT] = __expf(GC);
   }
-  // K^T of the chunk for the bf16 chunk loop, written once per key head by
-  // the first value head of its group: KT[dk][t] (zero past the last token).
-  if constexpr (!PRECISE) {
-    if (hv % (Hv / Hk) == 0) {
-      bf16* kt = KTw + (static_cast<size_t>(c) * Hk + hk) * DK * CT;
-#pragma unroll
-      for (int I = 0; I < MT; ++I) {
-        const int t = I * 16 + l16;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 wk = __builtin_bit_cast(u32x4, kh[I][kb]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t word = wk[e >> 1];
-            const bf16 val = static_cast<bf16>((e & 1) ? (word >> 16) : (word & 0xffffu));
-            kt[(kb * 32 + kg * 8 + e) * CT + t] = t < n ? val : bf16(0);
-          }
-        }
-      }
-    }
-  }
-
   // Gram K K^T and Q K^T tiles (I, J), J <= I; A and P from them.
   bf16* ph = Ph + mat * CT * CT;
   bf16* pl = Pl + mat * CT * CT;
@@ -665,115 +643,134 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// 3b. The bf16 chunk loop with LDS-staged, double-buffered chunk operands.
+// 3b. The bf16 chunk loop, operands streamed through LDS.
 //
 // One workgroup per (sequence, value head, BV = 16 * NW value columns), a wave
-// per 16 columns.  What a chunk needs besides the state - K, Q, K^T, the V
-// block, T hi/lo and the per-token factors - is copied once per workgroup from
-// global memory straight into LDS (global_load_lds: no registers,
-// asynchronous) into the buffer the current chunk does not use; one wait and
-// barrier per chunk hands the two buffers over.  P is read from L2 into
-// registers at the start of the chunk that uses it.  Tile rows are padded by
-// 16 bytes, which makes every 8-byte fragment read of a 32-lane half-wave
-// bank-conflict free and leaves only a per-lane base plus an immediate offset
-// in each LDS read.
+// per 16 columns, so every chunk operand is fetched once per 16*NW columns.
+// Operands reach LDS by asynchronous buffer->LDS copies (no registers); each
+// tile is re-fetched for the next chunk right after the phase that last reads
+// it, so every copy has two or more phases of compute to land in:
+//
+//   step ci:  copy K, factors (ci+1)   [K and factors are double-buffered]
+//             X = K S, R                     -> copy V (ci+1)
+//             Delta = T R                    -> copy T hi/lo (ci+1)
+//             O = Q S + P Delta, y           -> copy Q, P (ci+1)
+//             S <- gamma_C S + K^T E
+//
+// Each hand-over is "wait for my own copies of the group the next phases
+// need, finish my LDS reads, barrier".  Copies are bounded by a buffer
+// descriptor per chunk: rows past the chunk's last token (and whole chunks
+// past the sequence) read as zero, so the ragged tail needs no clamping.
+// Tile rows are padded so that the 8-byte fragment reads of a half-wave hit
+// distinct banks; K^T and V are read with the transposing LDS load
+// (ds_read_b64_tr_b16), which hands each lane four rows of one column.
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
-typedef __attribute__((address_space(1))) void* gbl_vptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4p;
 
-// A ROWS x COLS bf16 tile stored with a 16-byte pad after every row.
-template <int ROWS, int COLS>
-struct PadTile {
-  static constexpr int PITCH = COLS + 8;          // elements
-  static constexpr int SPR = COLS / 8;            // 16-byte source items per row
-  static constexpr int SLOTS = ROWS * (SPR + 1);  // 16-byte LDS slots, pads included
-  static constexpr int NBLK = (SLOTS + 63) / 64;  // 1 KiB copy blocks
-  static constexpr int ELEMS = NBLK * 512;        // storage, whole blocks
-};
+// A copy offset beyond every bound used here: the copy fills zeros.
+constexpr uint32_t kOOB = 0x7ffffff0u;
 
-template <int DK, int CT, int BV>
-struct __attribute__((aligned(16))) ChunkBuf {
-  bf16 K[PadTile<CT, DK>::ELEMS];
-  bf16 Q[PadTile<CT, DK>::ELEMS];
-  bf16 KT[PadTile<DK, CT>::ELEMS];
-  bf16 Th[PadTile<CT, CT>::ELEMS];
-  bf16 Tl[PadTile<CT, CT>::ELEMS];
-  bf16 V[CT * BV];          // read two bytes at a time: no padding
-  // beta, beta gamma/|k|, gamma scale/|q|, exp(G_C-G)/|k|, gamma_C; rounded
-  // up to whole 64-float copy blocks so the last block stays inside.
-  float fac[(4 * CT + 4 + 63) / 64 * 64];
-};
-
-// Wave-wide asynchronous copy: lane i's `BYTES` (4 or 16) from `src` land at
-// `lds_block + i * BYTES`; completion is counted by vmcnt.
-template <int BYTES>
-__device__ __forceinline__ void copy_to_lds(const void* src, void* lds_block) {
-  static_assert(BYTES == 4 || BYTES == 16, "copy size");
-  if constexpr (BYTES == 16)
-    __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_block, 16, 0, 0);
-  else
-    __builtin_amdgcn_global_load_lds((gbl_vptr)src, (lds_vptr)lds_block, 4, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // data format 32 bits, stride 0: a raw byte-addressed buffer of `bytes`
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
 }
 
-// Copy a padded tile: row r of the source starts at row_ptr(r); pad slots
-// (and slots past the last row) fetch a valid dummy item.  Wave w copies
-// blocks w, w + NW, ...; w is wave-uniform so every branch here is too.
-template <int ROWS, int COLS, int NW, typename RowPtr>
-__device__ __forceinline__ void stage_padded(bf16* dst, int w, int lane, RowPtr row_ptr) {
-  using P = PadTile<ROWS, COLS>;
+// A tile of ROWS rows; row r is ITEMS 16-byte items at byte offset
+// r * src_stride of the source, stored in LDS with a pitch of PITCH bf16.
+// The copy runs in 1 KiB blocks of 64 consecutive 16-byte LDS slots, dealt
+// round-robin to the NW waves; each lane's source offset per block is fixed
+// for the whole sequence (only the descriptor changes per chunk).
+template <int ROWS, int ITEMS, int PITCH, int NW>
+struct TileCopy {
+  static constexpr int SPR = PITCH / 8;                 // LDS slots per row
+  static constexpr int NBLK = (ROWS * SPR + 63) / 64;
+  static constexpr int ELEMS = NBLK * 512;              // LDS bf16 to reserve
+  static constexpr int PER = (NBLK + NW - 1) / NW;      // blocks of the busiest wave
+  static constexpr int MIN = NBLK / NW;                 // blocks of every wave
+  static_assert(PITCH % 8 == 0 && PITCH >= 8 * ITEMS, "pitch");
+  uint32_t off[PER];
+  __device__ __forceinline__ void init(int w, int lane, uint32_t src_stride) {
 #pragma unroll
-  for (int j = 0; j < (P::NBLK + NW - 1) / NW; ++j) {
-    const int b = j * NW + w;
-    if (P::NBLK % NW == 0 || b < P::NBLK) {
-      const int slot = b * 64 + lane;
-      const int row = slot / (P::SPR + 1), item = slot % (P::SPR + 1);
-      const bool real = row < ROWS && item < P::SPR;
-      copy_to_lds<16>(row_ptr(real ? row : 0) + (real ? item : 0) * 8, dst + b * 512);
+    for (int j = 0; j < PER; ++j) {
+      const int slot = (j * NW + w) * 64 + lane;
+      const int row = slot / SPR, item = slot - row * SPR;
+      off[j] = (row < ROWS && item < ITEMS) ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
-}
-
-// Unpadded ROWS x COLS tile.
-template <int ROWS, int COLS, int NW, typename RowPtr>
-__device__ __forceinline__ void stage_plain(bf16* dst, int w, int lane, RowPtr row_ptr) {
-  constexpr int SPR = COLS / 8, NBLK = ROWS * SPR / 64;
-  static_assert(ROWS * SPR % 64 == 0, "whole blocks");
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, void* tile, int w) const {
 #pragma unroll
-  for (int j = 0; j < (NBLK + NW - 1) / NW; ++j) {
-    const int b = j * NW + w;
-    if (NBLK % NW == 0 || b < NBLK) {
-      const int slot = b * 64 + lane;
-      copy_to_lds<16>(row_ptr(slot / SPR) + (slot % SPR) * 8, dst + b * 512);
+    for (int j = 0; j < PER; ++j) {
+      const int b = j * NW + w;
+      if (MIN == PER || b < NBLK) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        // (device pass only: the host pass cannot check this gfx950 builtin
+        // and would silently drop the kernel's launch stub)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(static_cast<bf16*>(tile) + b * 512), 16,
+                                                 off[j], 0, 0, 0);
+#endif
+      }
     }
   }
+};
+
+// Wait until at most `VM` of this wave's vector-memory operations are in
+// flight and its LDS reads are done, then meet the workgroup.  The asm is a
+// compiler memory barrier too, so no LDS access moves across it.
+template <int VM>
+__device__ __forceinline__ void handover() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-// "pi"-order operand from row `row` of a padded tile (see acc_operand).
-template <int COLS>
+// "pi"-order operand from row `row` of a padded LDS tile (see acc_operand).
+template <int PITCH>
 __device__ __forceinline__ bf16x8v lds_pi(const bf16* tile, int row, int k0, int kg) {
-  constexpr int PITCH = COLS + 8;
   const bf16* p = tile + row * PITCH + k0 + kg * 4;
   const uint2 a = *reinterpret_cast<const uint2*>(p);
   const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
   return __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, b.x, b.y});
 }
 
+// Transposing read: for lane (l16, kg) whose address is
+//   tile + (r0 + kg*4 + l16/4) * PITCH + c0 + 4*(l16%4),
+// element e of the result is tile[r0 + kg*4 + e][c0 + l16].
+__device__ __forceinline__ s16x4 lds_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4p)(p));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(short x) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16);
+}
+
 template <int DK, int CT, int NW>
-__global__ __launch_bounds__(64 * NW) void gdn_prefill_lds_kernel(
+__global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
     int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
-    const bf16* __restrict__ Ph, const float* __restrict__ fac, const bf16* __restrict__ KTw,
-    bf16* __restrict__ y) {
+    const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
   constexpr int BV = 16 * NW;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
   constexpr int FSTR = 4 * CT + 4;
-  using Buf = ChunkBuf<DK, CT, BV>;
-  // Two distinct buffers (not an indexed pair): the compiler can then see
-  // that reads of one do not alias the asynchronous copies into the other
-  // and does not wait for the copies before every read.
-  __shared__ Buf buf0, buf1;
+  constexpr int KP = DK + 8, TPP = CT + 8, VP = BV + 16;  // LDS pitches (bf16)
+  using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
+  using Tcopy = TileCopy<CT, CT / 8, TPP, NW>;
+  using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
+  using Fcopy = TileCopy<1, CT, 8 * CT, NW>;  // 4*CT floats as CT 16-byte items
+  // Separate arrays (and the two K / factor buffers as separate arrays too):
+  // the compiler then knows which copies a read can depend on.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[KQcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[KQcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[KQcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sTh[Tcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sTl[Tcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sP[Tcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[Vcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sF0[Fcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sF1[Fcopy::ELEMS];
 
   const int nvb = Dv / BV;
   const int s = blockIdx.x / (Hv * nvb);
@@ -792,164 +789,175 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_lds_kernel(
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dvl = w * 16 + l16;  // value column within the block
-  const int dv = vb * BV + dvl;
 
-  auto chunk_rows = [&](int ci) {
-    const int64_t done = static_cast<int64_t>(ci) * C;
-    return static_cast<int>(len - done < C ? len - done : C);
-  };
-  // Start copying chunk ci into N.  Rows past the chunk's last token copy
-  // that token again; their factors are zero, so they add nothing.
-  auto fetch = [&](int ci, Buf& N) {
-    const int64_t t0 = b0 + static_cast<int64_t>(ci) * C;
-    const int last = chunk_rows(ci) - 1;
-    const size_t mat = static_cast<size_t>(cbase + ci) * Hv + hv;
-    const bf16* kb0 = k + (static_cast<size_t>(t0) * Hk + hk) * DK;
-    const bf16* qb0 = q + (static_cast<size_t>(t0) * Hk + hk) * DK;
-    const bf16* vb0 = v + (static_cast<size_t>(t0) * Hv + hv) * Dv + vb * BV;
-    const bf16* kt0 = KTw + (static_cast<size_t>(cbase + ci) * Hk + hk) * DK * CT;
-    const bf16* th0 = Th + mat * CT * CT;
-    const bf16* tl0 = Tl + mat * CT * CT;
-    stage_padded<CT, DK, NW>(N.K, w, lane, [&](int r) { return kb0 + min(r, last) * (Hk * DK); });
-    stage_padded<CT, DK, NW>(N.Q, w, lane, [&](int r) { return qb0 + min(r, last) * (Hk * DK); });
-    stage_padded<DK, CT, NW>(N.KT, w, lane, [&](int r) { return kt0 + r * CT; });
-    stage_padded<CT, CT, NW>(N.Th, w, lane, [&](int r) { return th0 + r * CT; });
-    stage_padded<CT, CT, NW>(N.Tl, w, lane, [&](int r) { return tl0 + r * CT; });
-    stage_plain<CT, BV, NW>(N.V, w, lane, [&](int r) { return vb0 + min(r, last) * (Hv * Dv); });
-    if (w == NW - 1) {
-      const float* fp = fac + mat * FSTR;
-#pragma unroll
-      for (int j = 0; j < (FSTR + 63) / 64; ++j)
-        copy_to_lds<4>(fp + min(j * 64 + lane, FSTR - 1), N.fac + j * 64);
-    }
-  };
+  const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
+  const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
+  KQcopy cKQ;
+  Tcopy cT;
+  Vcopy cV;
+  Fcopy cF;
+  cKQ.init(w, lane, kstride);
+  cT.init(w, lane, CT * 2);
+  cV.init(w, lane, vstride);
+  cF.init(w, lane, 0);
 
-  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(dv) * DK;
+  // rows of chunk ci that exist (0 past the sequence)
+  auto rows = [&](int ci) -> int {
+    if (ci >= nch) return 0;
+    const int64_t left = len - static_cast<int64_t>(ci) * C;
+    return static_cast<int>(left < C ? left : C);
+  };
+  auto tok0 = [&](int ci) -> int64_t { return b0 + static_cast<int64_t>(ci) * C; };
+  auto matix = [&](int ci) -> size_t { return static_cast<size_t>(cbase + ci) * Hv + hv; };
+  auto kq_rsrc = [&](const bf16* base, int ci) {
+    const int n = rows(ci);
+    return make_rsrc(base + (static_cast<size_t>(tok0(ci)) * Hk + hk) * DK,
+                     n > 0 ? (n - 1) * kstride + DK * 2 : 0u);
+  };
+  auto ws_rsrc = [&](const bf16* base, int ci) {
+    return make_rsrc(base + matix(ci) * CT * CT, rows(ci) > 0 ? CT * CT * 2 : 0u);
+  };
+  auto copy_K = [&](int ci, bf16* dk, bf16* df) {
+    cKQ.issue(kq_rsrc(k, ci), dk, w);
+    cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? 16 * CT : 0u), df, w);
+  };
+  auto copy_V = [&](int ci) {
+    const int n = rows(ci);
+    cV.issue(make_rsrc(v + (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV,
+                       n > 0 ? (n - 1) * vstride + BV * 2 : 0u),
+             sV, w);
+  };
+  auto copy_T = [&](int ci) {
+    cT.issue(ws_rsrc(Th, ci), sTh, w);
+    cT.issue(ws_rsrc(Tl, ci), sTl, w);
+  };
+  auto copy_QP = [&](int ci) {
+    cKQ.issue(kq_rsrc(q, ci), sQ, w);
+    cT.issue(ws_rsrc(Ph, ci), sP, w);
+  };
+  // Copies of the later groups each wave has surely issued (see the step
+  // order) when it waits for an earlier one.
+  constexpr int nKF = KQcopy::MIN + Fcopy::MIN, nV = Vcopy::MIN, nT = 2 * Tcopy::MIN,
+                nQP = KQcopy::MIN + Tcopy::MIN;
+
+  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
+              static_cast<size_t>(vb * BV + dvl) * DK;
   f32x4 S[DT];
 #pragma unroll
   for (int m = 0; m < DT; ++m) S[m] = *reinterpret_cast<const f32x4*>(Sp + m * 16 + kg * 4);
 
-  // One chunk: start copying chunk ci+1 into N, compute chunk ci from B,
-  // then wait for the copies and hand the buffers over.
-  auto step = [&](int ci, const Buf& B, Buf& N) {
-    const int n = chunk_rows(ci);
-    const int64_t t0 = b0 + static_cast<int64_t>(ci) * C;
-    const size_t mat = static_cast<size_t>(cbase + ci) * Hv + hv;
-    if (ci + 1 < nch) fetch(ci + 1, N);
-    // P rows for the lower-triangular (mt, cb) blocks, straight from L2
-    Raw<bf16> pf[MT][CKB];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int cb = 0; cb <= mt / 2; ++cb)
-        pf[mt][cb] = Raw<bf16>::load(Ph + mat * CT * CT + (mt * 16 + l16) * CT, cb * 32, kg);
+  // lane parts of the transposing reads
+  const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
 
-    // state operand over dk (hi/lo)
+  auto step = [&](int ci, const bf16* Kc, bf16* Kn, const bf16* Fcb, bf16* Fnb) {
+    const float* F = reinterpret_cast<const float*>(Fcb);
+    const int n = rows(ci);
+    const float gC = fac[matix(ci) * FSTR + 4 * CT];
+    copy_K(ci + 1, Kn, Fnb);
+
+    // ---- X = K S (state-grade: S as hi + lo), R = beta V - (beta gamma/|k|) X
     bf16x8v Sh[KB], Sl[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc_operand(S[2 * kb], S[2 * kb + 1], Sh[kb], Sl[kb]);
-
-    // X = K S (state-grade)
-    f32x4 X[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8v ak = lds_pi<DK>(B.K, mt * 16 + l16, kb * 32, kg);
-        X[mt] = mma(ak, Sh[kb], X[mt]);
-        X[mt] = mma(ak, Sl[kb], X[mt]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // R = diag(beta) V - diag(beta gamma / |k|) X   (rows t = mt*16 + kg*4 + r)
     f32x4 R[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 fb = *reinterpret_cast<const f32x4*>(B.fac + mt * 16 + kg * 4);
-      const f32x4 fk = *reinterpret_cast<const f32x4*>(B.fac + CT + mt * 16 + kg * 4);
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float vv = bf16_to_f32(B.V[(mt * 16 + kg * 4 + r) * BV + dvl]);
-        R[mt][r] = fb[r] * vv - fk[r] * X[mt][r];
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8v a = lds_pi<KP>(Kc, mt * 16 + l16, kb * 32, kg);
+        X = mma(a, Sh[kb], X);
+        X = mma(a, Sl[kb], X);
       }
+      const s16x4 vv = lds_tr(sV + (mt * 16 + tr_row) * VP + w * 16 + tr_col);
+      const f32x4 fb = *reinterpret_cast<const f32x4*>(F + mt * 16 + kg * 4);
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(F + CT + mt * 16 + kg * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[r];
     }
+    handover<nQP + nKF>();  // T of this chunk landed; V is free
+    copy_V(ci + 1);
+
+    // ---- Delta = T R (T lower triangular: blocks above the diagonal skipped)
     bf16x8v Rh[CKB], Rl[CKB];
 #pragma unroll
     for (int cb = 0; cb < CKB; ++cb) acc_operand(R[2 * cb], R[2 * cb + 1], Rh[cb], Rl[cb]);
-
-    // Delta = T R (T lower triangular: skip blocks above the diagonal)
     f32x4 D[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
-        const bf16x8v th = lds_pi<CT>(B.Th, mt * 16 + l16, cb * 32, kg);
-        const bf16x8v tl = lds_pi<CT>(B.Tl, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v th = lds_pi<TPP>(sTh, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v tl = lds_pi<TPP>(sTl, mt * 16 + l16, cb * 32, kg);
         D[mt] = mma(th, Rh[cb], D[mt]);
         D[mt] = mma(th, Rl[cb], D[mt]);
         D[mt] = mma(tl, Rh[cb], D[mt]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    handover<nKF + nV>();  // Q and P of this chunk landed; T is free
+    copy_T(ci + 1);
 
-    // O = diag(gamma scale / |q|) Q S + P Delta -> y   (output-grade: S hi only)
-    bf16x8v Dh[CKB];
+    // ---- O = (gamma scale/|q|) Q S + P Delta -> y   (output-grade: hi parts)
+    {
+      bf16x8v Dh[CKB];
 #pragma unroll
-    for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
+      for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
+      const int64_t t0 = tok0(ci);
+      const __amdgpu_buffer_rsrc_t yr =
+          make_rsrc(y + (static_cast<size_t>(t0) * Hv + hv) * Dv + vb * BV, n > 0 ? (n - 1) * vstride + BV * 2 : 0u);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<DK>(B.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
-      const f32x4 fq = *reinterpret_cast<const f32x4*>(B.fac + 2 * CT + mt * 16 + kg * 4);
-      f32x4 O = fq * Y;
+        for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<KP>(sQ, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
+        const f32x4 fq = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4);
+        f32x4 O = fq * Y;
 #pragma unroll
-      for (int cb = 0; cb <= mt / 2; ++cb) {
-        bf16x8v ph, unused;
-        pf[mt][cb].operand(ph, unused);
-        O = mma(ph, Dh[cb], O);
-      }
+        for (int cb = 0; cb <= mt / 2; ++cb) O = mma(lds_pi<TPP>(sP, mt * 16 + l16, cb * 32, kg), Dh[cb], O);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = mt * 16 + kg * 4 + r;
-        if (t < n)
-          y[(static_cast<size_t>(t0 + t) * Hv + hv) * Dv + dv] = __builtin_bit_cast(bf16, (__bf16)O[r]);
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t off = (static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride) + dvl * 2;
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)O[r]), yr, off, 0, 0);
+        }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    handover<nKF + nV + nT>();  // Q and P are free
+    copy_QP(ci + 1);
 
-    // S <- gamma_C S + K^T diag(exp(G_C - G) / |k|) Delta
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(B.fac + 3 * CT + mt * 16 + kg * 4);
+    // ---- S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
     bf16x8v Eh[CKB], El[CKB];
 #pragma unroll
+    for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
+#pragma unroll
     for (int cb = 0; cb < CKB; ++cb) acc_operand(D[2 * cb], D[2 * cb + 1], Eh[cb], El[cb]);
-    const float gC = B.fac[4 * CT];
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
       S[m] *= gC;
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) {
-        const bf16x8v a = lds_pi<CT>(B.KT, m * 16 + l16, cb * 32, kg);
+        const bf16* p = Kc + (cb * 32 + tr_row) * KP + m * 16 + tr_col;
+        const s16x4 lo4 = lds_tr(p), hi4 = lds_tr(p + 16 * KP);
+        const bf16x8v a = __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         S[m] = mma(a, Eh[cb], S[m]);
         S[m] = mma(a, El[cb], S[m]);
       }
     }
-
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next chunk landed
-    __syncthreads();                // ... and everyone's; the current buffer is free
+    handover<nT + nQP>();  // K, factors and V of the next chunk landed
   };
 
-  if (nch > 0) fetch(0, buf0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // prologue: all operands of chunk 0, then wait for K, factors and V
+  copy_K(0, sK0, sF0);
+  copy_V(0);
+  copy_T(0);
+  copy_QP(0);
+  handover<nT + nQP>();
   for (int ci = 0; ci < nch; ci += 2) {
-    step(ci, buf0, buf1);
-    if (ci + 1 < nch) step(ci + 1, buf1, buf0);
+    step(ci, sK0, sK1, sF0, sF1);
+    if (ci + 1 < nch) step(ci + 1, sK1, sK0, sF1, sF0);
   }
+  // no copy may still be landing in LDS when the workgroup retires
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
   for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
@@ -964,10 +972,10 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
 
 struct Layout {
-  size_t scs, th, tl, ph, pl, fac, kt, total;
+  size_t scs, th, tl, ph, pl, fac, total;
 };
 
-inline Layout layout(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int chunk) {
+inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t mats = maxc * static_cast<size_t>(Hv);
@@ -979,7 +987,6 @@ inline Layout layout(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int chunk) 
   L.ph = off; off += up(mats * CT * CT * sizeof(bf16));
   L.pl = off; off += up(mats * CT * CT * sizeof(bf16));
   L.fac = off; off += up(mats * (4 * CT + 4) * sizeof(float));
-  L.kt = off; off += up(maxc * static_cast<size_t>(Hk) * Dk * CT * sizeof(bf16));
   L.total = off;
   return L;
 }
@@ -995,7 +1002,6 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
   bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
   float* fac = reinterpret_cast<float*>(ws + L.fac);
-  bf16* KTw = reinterpret_cast<bf16*>(ws + L.kt);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
   const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW));
@@ -1004,12 +1010,12 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
   hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
-                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac, KTw);
+                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
   if constexpr (std::is_same<T, bf16>::value)
-    hipLaunchKernelGGL((gdn_prefill_lds_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
-                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, KTw, static_cast<bf16*>(y));
+                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y));
   else
     hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
@@ -1023,10 +1029,15 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
-  // bf16: the LDS-staged kernel; fp32 activations: the register-fragment
-  // kernel (its operands would not fit LDS twice).  64 value columns (four
-  // waves, up to 512 registers each) per workgroup, else 32.  Eight waves
-  // per workgroup would cap each wave at 256 registers and spill.
+  // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
+  // workgroup so each chunk operand is fetched once per 128 columns.  fp32
+  // activations: the register-fragment kernel, 64 (four waves, up to 512
+  // registers each) or 32 columns per workgroup.
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (Dv % 128 == 0)
+      return launch_all<T, DK, CT, 8>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
+                                      chunk, scale, l2norm, y, ws, L, stream);
+  }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
                                     chunk, scale, l2norm, y, ws, L, stream);
@@ -1069,7 +1080,7 @@ extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, in
                                               int chunk) {
   (void)Dv;
   if (T_tot < 0 || N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || !gdn::valid_chunk(chunk)) return 0;
-  return gdn::layout(T_tot, N_s, Hk, Hv, Dk, chunk).total;
+  return gdn::layout(T_tot, N_s, Hv, chunk).total;
 }
 
 extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -1089,9 +1100,13 @@ extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, co
   if (N_s == 0) return GDN_OK;
   if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
   if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(state_pool) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_pool) || !aligned16(workspace))
     return GDN_ERR_ALIGN;
-  const Layout L = layout(T_tot, N_s, Hk, Hv, Dk, chunk);
+  // per-chunk copy offsets are 32-bit: 64 token rows of q/k/v must span < 1 GiB
+  if (static_cast<uint64_t>(Hk) * Dk * 2 * 64 >= (1ull << 30) ||
+      static_cast<uint64_t>(Hv) * Dv * 2 * 64 >= (1ull << 30))
+    return GDN_ERR_UNSUPPORTED;
+  const Layout L = layout(T_tot, N_s, Hv, chunk);
   if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   const size_t pool_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
   const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);

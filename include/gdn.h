@@ -162,7 +162,9 @@ size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
  * workspace     device memory of at least gdn_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
  * Requirements: Dk in {32, 64, 128}; Dv a multiple of 32, <= 256;
- * Hv % Hk == 0; q, k, state_pool 16-byte aligned.  N_s == 0 is a no-op.
+ * Hv % Hk == 0; q, k, v, state_pool 16-byte aligned; 64 tokens of q/k
+ * (64 * Hk * Dk elements) and of v (64 * Hv * Dv) each under 1 GiB, else
+ * GDN_ERR_UNSUPPORTED.  N_s == 0 is a no-op.
  * On an in-kernel failure the referenced slots are unspecified (the update
  * is in place): callers that need to retry keep a copy of those slots.
  */

@@ -145,6 +145,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, cu=0) == NULL
     assert prefill(lib, q=0) == NULL
     assert prefill(lib, pool=A + 5 * BIG + 8) == ALIGN
+    assert prefill(lib, v=A + 2 * BIG + 2) == ALIGN
+    assert prefill(lib, Hv=65536, Hk=65536, Dv=256) == UNSUP  # 64 tokens of v span >= 1 GiB
     assert prefill(lib, ws_bytes=1024) == WORKSPACE
     assert prefill(lib, y=A + 5 * BIG + 64) == ALIAS      # y inside the pool
     assert prefill(lib, N_s=0, q=0, cu=0) == OK           # nothing to do
