@@ -69,7 +69,7 @@ def load_library():
     lib.gdn_prefill_gates.restype = _i
     lib.gdn_prefill_gates.argtypes = [_vp] * 6 + [_i64, _i, _i, _vp]
     lib.gdn_chunk_prefill_workspace.restype = ctypes.c_size_t
-    lib.gdn_chunk_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i]
+    lib.gdn_chunk_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i, _i]
     lib.gdn_chunk_prefill.restype = _i
     lib.gdn_chunk_prefill.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
                                       + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
@@ -202,9 +202,11 @@ def gdn_prefill_gates(a, b, A_log, dt_bias, g=None, beta=None):
 GDN_QK_L2NORM = 1
 
 
-def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64) -> int:
-    """Bytes of workspace ``gdn_chunk_prefill`` needs (0 for invalid sizes)."""
-    return int(load_library().gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk))
+def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace ``gdn_chunk_prefill`` needs for activations of
+    ``dtype`` (torch.bfloat16 by default; 0 for invalid sizes)."""
+    act = 0 if dtype == torch.float32 else 1
+    return int(load_library().gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act))
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, chunk=64,
@@ -235,7 +237,7 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
     _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
     _check("y", y, (T, Hv, Dv), act, dev)
-    need = gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk)
+    need = gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk, act)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():

@@ -407,6 +407,74 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// 2b. Chunk records for the fused bf16 loop: one wave per (chunk, key head).
+//
+// Lane t owns token t of the chunk.  The norms of its key and query rows are
+// shared by the value heads of the group; per value head the wave scans the
+// log-gates (G = inclusive in-chunk sum, flat past the last token) and writes
+// the record  [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| |
+// G | 1/|k| | scale/|q| | beta]  (CT floats each; zero past the last token
+// except G), then gamma_C = exp(G_C).
+
+template <int DK, int CT>
+__global__ __launch_bounds__(64) void gdn_chunk_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
+    int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm,
+    float* __restrict__ rec) {
+  constexpr int RSTR = 8 * CT + 4;
+  const int c = blockIdx.x / Hk;
+  const int hk = blockIdx.x - c * Hk;
+  if (c >= scs[N_s]) return;
+  int lo = 0, hi = N_s;  // largest s with scs[s] <= c
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (scs[mid] <= c) lo = mid; else hi = mid;
+  }
+  int64_t b0, len;
+  seq_bounds(cu, lo, T_tot, b0, len);
+  const int64_t j0 = static_cast<int64_t>(c - scs[lo]) * C;
+  const int64_t t0 = b0 + j0;
+  const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
+  const int t = threadIdx.x;
+  const bool ok = t < n;
+  // rows past the last token read it again (unconditional loads) and are
+  // masked afterwards
+  const size_t row = (static_cast<size_t>(t0 + min(t, n - 1)) * Hk + hk) * DK;
+  const float ssk = Frag<bf16>::sumsq(k + row, DK);
+  const float ssq = Frag<bf16>::sumsq(q + row, DK);
+  const float rk = ok ? (l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.0f) : 0.f;
+  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.0f) : 0.f;
+  const int HG = Hv / Hk;
+  for (int j = 0; j < HG; ++j) {
+    const int hv = hk * HG + j;
+    const size_t th = static_cast<size_t>(t0 + min(t, n - 1)) * Hv + hv;
+    const float gl = ok ? g[th] : 0.f;
+    const float bt = ok ? beta[th] : 0.f;
+    float G = gl;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float up = __shfl_up(G, off);
+      if (t >= off) G += up;
+    }
+    const float GC = __shfl(G, CT - 1);
+    const float gam = __expf(G);
+    if (t < CT) {
+      float* r = rec + (static_cast<size_t>(c) * Hv + hv) * RSTR;
+      r[t] = bt;
+      r[CT + t] = bt * gam * rk;
+      r[2 * CT + t] = gam * rq;
+      r[3 * CT + t] = __expf(GC - G) * rk;
+      r[4 * CT + t] = G;
+      r[5 * CT + t] = rk;
+      r[6 * CT + t] = rq;
+      r[7 * CT + t] = bt;
+      if (t == 0) r[8 * CT] = __expf(GC);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // 3. Sequential chunk loop per (sequence, value head, value block).
 
 template <typename T, int DK, int CT, int NW>
@@ -647,23 +715,27 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
 //
 // One workgroup per (sequence, value head, BV = 16 * NW value columns), a wave
 // per 16 columns, so every chunk operand is fetched once per 16*NW columns.
-// Operands reach LDS by asynchronous buffer->LDS copies (no registers); each
-// tile is re-fetched for the next chunk right after the phase that last reads
-// it, so every copy has two or more phases of compute to land in:
+// Operands reach LDS by asynchronous buffer->LDS copies (no registers).  K,
+// Q, T hi/lo, P and the per-token factors are double-buffered and copied for
+// chunk ci+1 as soon as step ci starts; V (single-buffered) is copied right
+// after the phase that reads it.  Per step:
 //
-//   step ci:  copy K, factors (ci+1)   [K and factors are double-buffered]
-//             X = K S, R                     -> copy V (ci+1)
-//             Delta = T R                    -> copy T hi/lo (ci+1)
-//             O = Q S + P Delta, y           -> copy Q, P (ci+1)
-//             S <- gamma_C S + K^T E
+//   copy K, Q, T, P, factors (ci+1)
+//   X = K S, R = beta V - (beta gamma/|k|) X       | barrier, copy V (ci+1)
+//   Delta = T R
+//   O = (gamma scale/|q|) Q S + P Delta
+//   S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
+//   wait for all copies; barrier; store y (ci)
 //
-// Each hand-over is "wait for my own copies of the group the next phases
-// need, finish my LDS reads, barrier".  Copies are bounded by a buffer
-// descriptor per chunk: rows past the chunk's last token (and whole chunks
-// past the sequence) read as zero, so the ragged tail needs no clamping.
+// Copies are bounded by a buffer descriptor per chunk: rows past the chunk's
+// last token (and whole chunks past the sequence) read as zero, so the
+// ragged tail needs no clamping, and y rows past it are dropped the same way.
 // Tile rows are padded so that the 8-byte fragment reads of a half-wave hit
 // distinct banks; K^T and V are read with the transposing LDS load
 // (ds_read_b64_tr_b16), which hands each lane four rows of one column.
+// Workgroups are dealt to the eight XCDs round-robin; the value heads that
+// share a key head get consecutive slots on one XCD, so their K and Q copies
+// are served by that XCD's L2.
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -672,10 +744,35 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4p;
 // A copy offset beyond every bound used here: the copy fills zeros.
 constexpr uint32_t kOOB = 0x7ffffff0u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // data format 32 bits, stride 0: a raw byte-addressed buffer of `bytes`
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base`: stride 0 (raw byte offsets),
+// 32-bit data format; offsets at or past `bytes` read zero / drop the write.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>((a >> 32) & 0xffffu),
+               static_cast<int>(bytes), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_vptr)(const_cast<void*>(p))));
+}
+
+// Asynchronous 16-byte-per-lane copy from the buffer to LDS: lane i's bytes
+// land at lds + 16 i.  Written as asm so that the compiler does not track
+// it: every wait for these copies is explicit (handover below), and the
+// compiler's own conservative waits would otherwise stall on them.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
+}
+
+// Buffer store of one bf16 (dropped at or past `bytes`).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), rsrc, voff, 0, 0);
 }
 
 // A tile of ROWS rows; row r is ITEMS 16-byte items at byte offset
@@ -700,18 +797,12 @@ struct TileCopy {
       off[j] = (row < ROWS && item < ITEMS) ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, void* tile, int w) const {
+  __device__ __forceinline__ void issue(i32x4 r, void* tile, int w) const {
+    const uint32_t base = lds_addr(tile);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int b = j * NW + w;
-      if (MIN == PER || b < NBLK) {
-#if defined(__HIP_DEVICE_COMPILE__)
-        // (device pass only: the host pass cannot check this gfx950 builtin
-        // and would silently drop the kernel's launch stub)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(static_cast<bf16*>(tile) + b * 512), 16,
-                                                 off[j], 0, 0, 0);
-#endif
-      }
+      if (MIN == PER || b < NBLK) dma16(r, base + b * 1024, off[j]);
     }
   }
 };
@@ -723,6 +814,9 @@ template <int VM>
 __device__ __forceinline__ void handover() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+__device__ __forceinline__ void lds_handover() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // "pi"-order operand from row `row` of a padded LDS tile (see acc_operand).
@@ -745,38 +839,81 @@ __device__ __forceinline__ float bf16_bits_to_f32(short x) {
   return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16);
 }
 
+// Two 16x16x16 products accumulate as C += A B with A, B fp32 fragments
+// split into bf16 hi + lo (the lo x lo term is below fp32 rounding).
+// A: row l16, k = kg*4 + e;  B and C: column l16, k/row = kg*4 + e.
+__device__ __forceinline__ void split4(f32x4 x, s16x4& h, s16x4& l) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 hb = (__bf16)x[e];
+    h[e] = __builtin_bit_cast(short, hb);
+    l[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)hb));
+  }
+}
+__device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
+  s16x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+  return c;
+}
+
 template <int DK, int CT, int NW>
-__global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
+struct FusedTiles {
+  static constexpr int BV = 16 * NW;
+  static constexpr int KP = DK + 8, TPP = CT + 8, VP = BV + 16;  // LDS pitches (bf16)
+  static constexpr int MT = CT / 16;
+  static constexpr int NPAIR = MT * (MT + 1) / 2;  // 16x16 blocks on or below the diagonal
+  static constexpr int RSTR = 8 * CT + 4;          // floats per (chunk, value head) record
+  using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
+  using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
+  using Rcopy = TileCopy<1, 2 * CT, 16 * CT, NW>;  // the record's first 8*CT floats
+  // one chunk's double-buffered operands
+  struct __attribute__((aligned(16))) Set {
+    bf16 K[KQcopy::ELEMS];
+    bf16 Q[KQcopy::ELEMS];
+    bf16 R[Rcopy::ELEMS];
+  };
+};
+
+template <int DK, int CT, int NW>
+__global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
-    int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
-    const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
-  constexpr int BV = 16 * NW;
+    int Hv, int Dv, int C, int maxc, const float* __restrict__ rec, bf16* __restrict__ y) {
+  using Tiles = FusedTiles<DK, CT, NW>;
+  using Set = typename Tiles::Set;
+  constexpr int BV = Tiles::BV, KP = Tiles::KP, TPP = Tiles::TPP, VP = Tiles::VP;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
-  constexpr int FSTR = 4 * CT + 4;
-  constexpr int KP = DK + 8, TPP = CT + 8, VP = BV + 16;  // LDS pitches (bf16)
-  using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
-  using Tcopy = TileCopy<CT, CT / 8, TPP, NW>;
-  using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
-  using Fcopy = TileCopy<1, CT, 8 * CT, NW>;  // 4*CT floats as CT 16-byte items
-  // Separate arrays (and the two K / factor buffers as separate arrays too):
-  // the compiler then knows which copies a read can depend on.
-  __shared__ __attribute__((aligned(16))) bf16 sK0[KQcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sK1[KQcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[KQcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sTh[Tcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sTl[Tcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sP[Tcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[Vcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sF0[Fcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sF1[Fcopy::ELEMS];
+  constexpr int NPAIR = Tiles::NPAIR, RSTR = Tiles::RSTR;
+  // Two distinct sets (not an indexed pair): the compiler then knows that
+  // reads of one never wait on copies into the other.
+  __shared__ Set setA, setB;
+  __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sTh[CT * TPP];
+  __shared__ __attribute__((aligned(16))) bf16 sTl[CT * TPP];
+  __shared__ __attribute__((aligned(16))) bf16 sP[CT * TPP];
+  __shared__ __attribute__((aligned(16))) float sA[NPAIR][16][20];  // A blocks, row-major
+  __shared__ __attribute__((aligned(16))) float sD[MT][16][20];     // (I + A_bb)^-1, row-major
+  __shared__ __attribute__((aligned(16))) float sDT[MT][16][20];    // ... and transposed
 
-  const int nvb = Dv / BV;
-  const int s = blockIdx.x / (Hv * nvb);
-  const int rem = blockIdx.x - s * (Hv * nvb);
-  const int hv = rem / nvb;
-  const int vb = rem - hv * nvb;
+  // block -> (sequence, key head, value block, value head of the group)
+  const int HG = Hv / Hk, nvb = Dv / BV;
+  int lid = blockIdx.x;
+  {
+    const int span = 8 * HG, G = static_cast<int>(gridDim.x);
+    if (lid < G / span * span) {
+      const int x = lid & 7, r = lid >> 3;
+      lid = ((r / HG) * 8 + x) * HG + r % HG;
+    }
+  }
+  const int grp = lid / HG;
+  const int hv = (grp / nvb) % Hk * HG + lid % HG;
+  const int vb = grp % nvb;
+  const int s = grp / (nvb * Hk);
   const int64_t slot = cache_indices[s];
   if (slot < 0 || slot >= pool_size) return;
   int64_t b0, len;
@@ -785,60 +922,143 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   const int cbase = scs[s];
   const int nch_all = static_cast<int>((len + C - 1) / C);
   const int nch = cbase + nch_all > maxc ? (maxc > cbase ? maxc - cbase : 0) : nch_all;
-  const int hk = hv / (Hv / Hk);
+  if (nch <= 0) return;
+  const int hk = hv / HG;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dvl = w * 16 + l16;  // value column within the block
 
   const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
   const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
-  KQcopy cKQ;
-  Tcopy cT;
-  Vcopy cV;
-  Fcopy cF;
+  typename Tiles::KQcopy cKQ;
+  typename Tiles::Vcopy cV;
+  typename Tiles::Rcopy cR;
   cKQ.init(w, lane, kstride);
-  cT.init(w, lane, CT * 2);
   cV.init(w, lane, vstride);
-  cF.init(w, lane, 0);
+  cR.init(w, lane, 0);
 
   // rows of chunk ci that exist (0 past the sequence)
-  auto rows = [&](int ci) -> int {
+  auto rows = [&](int ci) __attribute__((always_inline)) -> int {
     if (ci >= nch) return 0;
     const int64_t left = len - static_cast<int64_t>(ci) * C;
     return static_cast<int>(left < C ? left : C);
   };
-  auto tok0 = [&](int ci) -> int64_t { return b0 + static_cast<int64_t>(ci) * C; };
-  auto matix = [&](int ci) -> size_t { return static_cast<size_t>(cbase + ci) * Hv + hv; };
-  auto kq_rsrc = [&](const bf16* base, int ci) {
+  auto tok0 = [&](int ci) __attribute__((always_inline)) -> int64_t { return b0 + static_cast<int64_t>(ci) * C; };
+  auto matix = [&](int ci) __attribute__((always_inline)) -> size_t { return static_cast<size_t>(cbase + ci) * Hv + hv; };
+  auto kq_rsrc = [&](const bf16* base, int ci) __attribute__((always_inline)) {
     const int n = rows(ci);
     return make_rsrc(base + (static_cast<size_t>(tok0(ci)) * Hk + hk) * DK,
                      n > 0 ? (n - 1) * kstride + DK * 2 : 0u);
   };
-  auto ws_rsrc = [&](const bf16* base, int ci) {
-    return make_rsrc(base + matix(ci) * CT * CT, rows(ci) > 0 ? CT * CT * 2 : 0u);
+  auto vy_off = [&](int ci) __attribute__((always_inline)) -> size_t {
+    return (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV;
   };
-  auto copy_K = [&](int ci, bf16* dk, bf16* df) {
-    cKQ.issue(kq_rsrc(k, ci), dk, w);
-    cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? 16 * CT : 0u), df, w);
-  };
-  auto copy_V = [&](int ci) {
+  auto vy_bytes = [&](int ci) __attribute__((always_inline)) -> uint32_t {
     const int n = rows(ci);
-    cV.issue(make_rsrc(v + (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV,
-                       n > 0 ? (n - 1) * vstride + BV * 2 : 0u),
-             sV, w);
+    return n > 0 ? (n - 1) * vstride + BV * 2 : 0u;
   };
-  auto copy_T = [&](int ci) {
-    cT.issue(ws_rsrc(Th, ci), sTh, w);
-    cT.issue(ws_rsrc(Tl, ci), sTl, w);
+  auto copy_set = [&](int ci, Set& d) __attribute__((always_inline)) {
+    cKQ.issue(kq_rsrc(k, ci), d.K, w);
+    cKQ.issue(kq_rsrc(q, ci), d.Q, w);
+    cR.issue(make_rsrc(rec + matix(ci) * RSTR, rows(ci) > 0 ? 32 * CT : 0u), d.R, w);
   };
-  auto copy_QP = [&](int ci) {
-    cKQ.issue(kq_rsrc(q, ci), sQ, w);
-    cT.issue(ws_rsrc(Ph, ci), sP, w);
+  auto copy_V = [&](int ci) __attribute__((always_inline)) { cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w); };
+
+  // ---- the chunk's T = (I + A)^-1 and P from its K, Q and record (in d)
+  auto wy = [&](const Set& d) __attribute__((always_inline)) {
+    const float* Rv = reinterpret_cast<const float*>(d.R);
+    const float* G = Rv + 4 * CT;
+    const float* rk = Rv + 5 * CT;
+    const float* rq = Rv + 6 * CT;
+    const float* bt = Rv + 7 * CT;
+    // Gram K K^T and Q K^T blocks (I >= J) -> A blocks and P, a block per wave
+#pragma unroll
+    for (int I = 0; I < MT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        const int pidx = I * (I + 1) / 2 + J;
+        if (pidx % NW != w) continue;
+        f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8v kj = lds_pi<KP>(d.K, J * 16 + l16, kb * 32, kg);
+          gk = mma(lds_pi<KP>(d.K, I * 16 + l16, kb * 32, kg), kj, gk);
+          gq = mma(lds_pi<KP>(d.Q, I * 16 + l16, kb * 32, kg), kj, gq);
+        }
+        const int jj = J * 16 + l16;
+        const float Gj = G[jj], rkj = rk[jj];
+        const f32x4 Gi = *reinterpret_cast<const f32x4*>(G + I * 16 + kg * 4);
+        const f32x4 rki = *reinterpret_cast<const f32x4*>(rk + I * 16 + kg * 4);
+        const f32x4 rqi = *reinterpret_cast<const f32x4*>(rq + I * 16 + kg * 4);
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(bt + I * 16 + kg * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ii = I * 16 + kg * 4 + r;
+          const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
+          sA[pidx][kg * 4 + r][l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[r] : 0.f;
+          sP[ii * TPP + jj] = __builtin_bit_cast(bf16, (__bf16)(dec * rqi[r] * rkj * gq[r]));
+        }
+      }
+    lds_handover();
+    // diagonal blocks: lane (b, c) of wave 0 solves column c of (I + A_bb)^-1
+    // by forward substitution in fp32
+    if (w == 0) {
+      const int b = lane >> 4, c = l16;
+      if (b < MT) {
+        const int pd = b * (b + 1) / 2 + b;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float a0 = (i == c) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+          for (int j = 0; j + 3 < i; j += 4) {
+            const f32x4 ar = *reinterpret_cast<const f32x4*>(&sA[pd][i][j]);
+            a0 -= ar.x * x[j];
+            a1 -= ar.y * x[j + 1];
+            a2 -= ar.z * x[j + 2];
+            a3 -= ar.w * x[j + 3];
+          }
+#pragma unroll
+          for (int j = i & ~3; j < i; ++j) a0 -= sA[pd][i][j] * x[j];
+          x[i] = (a0 + a1) + (a2 + a3);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sD[b][i][c] = x[i];
+#pragma unroll
+        for (int i = 0; i < 16; i += 4)
+          *reinterpret_cast<f32x4*>(&sDT[b][c][i]) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+      }
+    }
+    lds_handover();
+    // block column j of T, by wave j % NW:  T_jj = D_j,
+    //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
+    auto put_T = [&](int i, int j, f32x4 t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int off = (i * 16 + kg * 4 + r) * TPP + j * 16 + l16;
+        const __bf16 h = (__bf16)t[r];
+        sTh[off] = __builtin_bit_cast(bf16, h);
+        sTl[off] = __builtin_bit_cast(bf16, (__bf16)(t[r] - (float)h));
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      if (j % NW != w) continue;
+      f32x4 Tc[MT];
+      Tc[j] = *reinterpret_cast<const f32x4*>(&sDT[j][l16][kg * 4]);
+      put_T(j, j, Tc[j]);
+#pragma unroll
+      for (int i = j + 1; i < MT; ++i) {
+        f32x4 M = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = j; kk < i; ++kk)
+          M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16][kg * 4]), Tc[kk], M);
+        const f32x4 Tn = mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16][kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
+        Tc[i] = -Tn;
+        put_T(i, j, Tc[i]);
+      }
+    }
   };
-  // Copies of the later groups each wave has surely issued (see the step
-  // order) when it waits for an earlier one.
-  constexpr int nKF = KQcopy::MIN + Fcopy::MIN, nV = Vcopy::MIN, nT = 2 * Tcopy::MIN,
-                nQP = KQcopy::MIN + Tcopy::MIN;
 
   float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
               static_cast<size_t>(vb * BV + dvl) * DK;
@@ -848,12 +1068,20 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   // lane parts of the transposing reads
   const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
+  f32x4 O[MT];  // the chunk's outputs, stored after the step's last wait
 
-  auto step = [&](int ci, const bf16* Kc, bf16* Kn, const bf16* Fcb, bf16* Fnb) {
-    const float* F = reinterpret_cast<const float*>(Fcb);
-    const int n = rows(ci);
-    const float gC = fac[matix(ci) * FSTR + 4 * CT];
-    copy_K(ci + 1, Kn, Fnb);
+  auto store_y = [&](int ci) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci), vy_bytes(ci));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store_b16(yr, static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride + dvl * 2, O[mt][r]);
+  };
+
+  auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
+    const float* F = reinterpret_cast<const float*>(c.R);
+    copy_set(ci + 1, nx);
 
     // ---- X = K S (state-grade: S as hi + lo), R = beta V - (beta gamma/|k|) X
     bf16x8v Sh[KB], Sl[KB];
@@ -865,7 +1093,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8v a = lds_pi<KP>(Kc, mt * 16 + l16, kb * 32, kg);
+        const bf16x8v a = lds_pi<KP>(c.K, mt * 16 + l16, kb * 32, kg);
         X = mma(a, Sh[kb], X);
         X = mma(a, Sl[kb], X);
       }
@@ -875,7 +1103,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) R[mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[r];
     }
-    handover<nQP + nKF>();  // T of this chunk landed; V is free
+    lds_handover();  // V is free
     copy_V(ci + 1);
 
     // ---- Delta = T R (T lower triangular: blocks above the diagonal skipped)
@@ -895,37 +1123,26 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         D[mt] = mma(tl, Rh[cb], D[mt]);
       }
     }
-    handover<nKF + nV>();  // Q and P of this chunk landed; T is free
-    copy_T(ci + 1);
 
-    // ---- O = (gamma scale/|q|) Q S + P Delta -> y   (output-grade: hi parts)
+    // ---- O = (gamma scale/|q|) Q S + P Delta   (output-grade: hi parts)
     {
       bf16x8v Dh[CKB];
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
-      const int64_t t0 = tok0(ci);
-      const __amdgpu_buffer_rsrc_t yr =
-          make_rsrc(y + (static_cast<size_t>(t0) * Hv + hv) * Dv + vb * BV, n > 0 ? (n - 1) * vstride + BV * 2 : 0u);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<KP>(sQ, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
-        const f32x4 fq = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4);
-        f32x4 O = fq * Y;
+        for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
+        O[mt] = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4) * Y;
 #pragma unroll
-        for (int cb = 0; cb <= mt / 2; ++cb) O = mma(lds_pi<TPP>(sP, mt * 16 + l16, cb * 32, kg), Dh[cb], O);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t off = (static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride) + dvl * 2;
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)O[r]), yr, off, 0, 0);
-        }
+        for (int cb = 0; cb <= mt / 2; ++cb)
+          O[mt] = mma(lds_pi<TPP>(sP, mt * 16 + l16, cb * 32, kg), Dh[cb], O[mt]);
       }
     }
-    handover<nKF + nV + nT>();  // Q and P are free
-    copy_QP(ci + 1);
 
-    // ---- S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
+    // ---- S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta  (G flat past the last token)
+    const float gC = __expf(F[5 * CT - 1]);
     bf16x8v Eh[CKB], El[CKB];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
@@ -936,28 +1153,40 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       S[m] *= gC;
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) {
-        const bf16* p = Kc + (cb * 32 + tr_row) * KP + m * 16 + tr_col;
+        const bf16* p = c.K + (cb * 32 + tr_row) * KP + m * 16 + tr_col;
         const s16x4 lo4 = lds_tr(p), hi4 = lds_tr(p + 16 * KP);
         const bf16x8v a = __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         S[m] = mma(a, Eh[cb], S[m]);
         S[m] = mma(a, El[cb], S[m]);
       }
     }
-    handover<nT + nQP>();  // K, factors and V of the next chunk landed
+    if (ci + 1 < nch) {
+      // K, Q and record of the next chunk landed (its V may still be in
+      // flight); every read of this chunk's T and P is done
+      handover<Tiles::Vcopy::MIN>();
+      wy(nx);
+    }
+    handover<0>();  // every copy of chunk ci+1 landed, its T and P are ready
+    store_y(ci);
   };
 
-  // prologue: all operands of chunk 0, then wait for K, factors and V
-  copy_K(0, sK0, sF0);
-  copy_V(0);
-  copy_T(0);
-  copy_QP(0);
-  handover<nT + nQP>();
-  for (int ci = 0; ci < nch; ci += 2) {
-    step(ci, sK0, sK1, sF0, sF1);
-    if (ci + 1 < nch) step(ci + 1, sK1, sK0, sF1, sF0);
+  // prologue: zero T and P (blocks above the diagonal stay zero), copy chunk
+  // 0, build its T and P
+  for (int i = tid; i < CT * TPP; i += 64 * NW) {
+    sTh[i] = 0;
+    sTl[i] = 0;
+    sP[i] = 0;
   }
-  // no copy may still be landing in LDS when the workgroup retires
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  copy_set(0, setA);
+  copy_V(0);
+  handover<Tiles::Vcopy::MIN>();
+  wy(setA);
+  handover<0>();
+  for (int ci = 0; ci < nch; ci += 2) {
+    step(ci, setA, setB);
+    if (ci + 1 < nch) step(ci + 1, setB, setA);
+  }
+  // (every copy has landed: each step ends waiting for all of them)
 
 #pragma unroll
   for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
@@ -971,22 +1200,26 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
 
+// Workspace: the chunk map, then per (chunk, value head) either the chunk
+// record (bf16: 8*CT+4 floats) or T hi/lo, P hi/lo and the factors (fp32
+// activations: the separate WY pass).
 struct Layout {
   size_t scs, th, tl, ph, pl, fac, total;
 };
 
-inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk) {
+inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool fused) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t mats = maxc * static_cast<size_t>(Hv);
+  const size_t tile = fused ? 0 : up(mats * CT * CT * sizeof(bf16));
   Layout L;
   size_t off = 0;
   L.scs = off; off += up(sizeof(int) * (static_cast<size_t>(N_s) + 1));
-  L.th = off; off += up(mats * CT * CT * sizeof(bf16));
-  L.tl = off; off += up(mats * CT * CT * sizeof(bf16));
-  L.ph = off; off += up(mats * CT * CT * sizeof(bf16));
-  L.pl = off; off += up(mats * CT * CT * sizeof(bf16));
-  L.fac = off; off += up(mats * (4 * CT + 4) * sizeof(float));
+  L.th = off; off += tile;
+  L.tl = off; off += tile;
+  L.ph = off; off += tile;
+  L.pl = off; off += tile;
+  L.fac = off; off += up(mats * (fused ? 8 * CT + 4 : 4 * CT + 4) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -997,10 +1230,6 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
                char* ws, const Layout& L, hipStream_t stream) {
   int* scs = reinterpret_cast<int*>(ws + L.scs);
-  bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
-  bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
-  bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
-  bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
   float* fac = reinterpret_cast<float*>(ws + L.fac);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
@@ -1008,19 +1237,28 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
-  hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
-                     stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
-                     T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
-  if constexpr (std::is_same<T, bf16>::value)
-    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+  if constexpr (std::is_same<T, bf16>::value) {
+    const size_t prep_blocks = maxc * static_cast<size_t>(Hk);
+    hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, CT>), dim3(static_cast<unsigned>(prep_blocks)), dim3(64), 0,
+                       stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
+                       N_s, T_tot, Hk, Hv, chunk, scale, l2norm, fac);
+    hipLaunchKernelGGL((gdn_prefill_fused_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
-                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y));
-  else
+                       chunk, static_cast<int>(maxc), fac, static_cast<bf16*>(y));
+  } else {
+    bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
+    bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
+    bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
+    bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
+    hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
+                       stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
+                       T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
     hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
                        Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, fac, static_cast<T*>(y));
+  }
   return launch_status();
 }
 
@@ -1077,10 +1315,12 @@ inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk =
 }  // namespace gdn
 
 extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int Dv,
-                                              int chunk) {
+                                              int chunk, gdn_dtype act) {
   (void)Dv;
-  if (T_tot < 0 || N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || !gdn::valid_chunk(chunk)) return 0;
-  return gdn::layout(T_tot, N_s, Hv, chunk).total;
+  if (T_tot < 0 || N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || !gdn::valid_chunk(chunk) ||
+      !gdn::is_act(act))
+    return 0;
+  return gdn::layout(T_tot, N_s, Hv, chunk, act == GDN_BF16).total;
 }
 
 extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -1106,7 +1346,7 @@ extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, co
   if (static_cast<uint64_t>(Hk) * Dk * 2 * 64 >= (1ull << 30) ||
       static_cast<uint64_t>(Hv) * Dv * 2 * 64 >= (1ull << 30))
     return GDN_ERR_UNSUPPORTED;
-  const Layout L = layout(T_tot, N_s, Hv, chunk);
+  const Layout L = layout(T_tot, N_s, Hv, chunk, act == GDN_BF16);
   if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
   const size_t pool_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
   const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);

@@ -121,11 +121,12 @@ int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
 
 /*
  * gdn_chunk_prefill_workspace - bytes of device workspace gdn_chunk_prefill
- * needs for these sizes (0 for invalid arguments).  It depends only on T_tot,
- * N_s, Hv and chunk; the other sizes are accepted for a stable signature.
+ * needs for these sizes and activation dtype (0 for invalid arguments).  It
+ * depends only on T_tot, N_s, Hv, chunk and act; the other sizes are
+ * accepted for a stable signature.
  */
 size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
-                                   int Dk, int Dv, int chunk);
+                                   int Dk, int Dv, int chunk, gdn_dtype act);
 
 /*
  * gdn_chunk_prefill - variable-length chunkwise (WY) prefill that advances a

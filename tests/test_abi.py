@@ -116,7 +116,7 @@ def prefill(lib, q=A, k=A + BIG, v=A + 2 * BIG, g=A + 3 * BIG, beta=A + 4 * BIG,
             P=4, ci=A + 6 * BIG, cu=A + 7 * BIG, N_s=2, T=100, Hk=2, Hv=4, Dk=128, Dv=128, chunk=64,
             flags=1, y=A + 8 * BIG, act=1, ws=A + 9 * BIG, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = lib.gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk)
+        ws_bytes = lib.gdn_chunk_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk, act if act in (0, 1) else 1)
     return lib.gdn_chunk_prefill(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(pool), P, _p(ci), _p(cu),
                                  N_s, T, Hk, Hv, Dk, Dv, chunk, ctypes.c_float(0.0), flags, _p(y), act,
                                  _p(ws), ws_bytes, None)
@@ -124,13 +124,17 @@ def prefill(lib, q=A, k=A + BIG, v=A + 2 * BIG, g=A + 3 * BIG, beta=A + 4 * BIG,
 
 def test_prefill_workspace_size(lib):
     f = lib.gdn_chunk_prefill_workspace
-    assert f(100, 2, 2, 4, 128, 128, 64) > 0
-    assert f(100, 2, 2, 4, 128, 128, 48) == 0          # unsupported chunk
-    assert f(-1, 2, 2, 4, 128, 128, 64) == 0
-    # grows with tokens, sequences and heads
-    assert f(1000, 2, 2, 4, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
-    assert f(100, 20, 2, 4, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
-    assert f(100, 2, 2, 8, 128, 128, 64) > f(100, 2, 2, 4, 128, 128, 64)
+    for act in (0, 1):
+        assert f(100, 2, 2, 4, 128, 128, 64, act) > 0
+        assert f(100, 2, 2, 4, 128, 128, 48, act) == 0          # unsupported chunk
+        assert f(-1, 2, 2, 4, 128, 128, 64, act) == 0
+        # grows with tokens, sequences and heads
+        assert f(1000, 2, 2, 4, 128, 128, 64, act) > f(100, 2, 2, 4, 128, 128, 64, act)
+        assert f(100, 20, 2, 4, 128, 128, 64, act) > f(100, 2, 2, 4, 128, 128, 64, act)
+        assert f(100, 2, 2, 8, 128, 128, 64, act) > f(100, 2, 2, 4, 128, 128, 64, act)
+    assert f(100, 2, 2, 4, 128, 128, 64, 7) == 0                 # unknown dtype
+    # bf16 builds T and P on chip: no per-chunk matrices in the workspace
+    assert f(1000, 2, 2, 4, 128, 128, 64, 1) < f(1000, 2, 2, 4, 128, 128, 64, 0)
 
 
 def test_prefill_validation(lib):
