@@ -407,74 +407,6 @@ __global__ __launch_bounds__(64) void gdn_wy_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// 2b. Chunk records for the fused bf16 loop: one wave per (chunk, key head).
-//
-// Lane t owns token t of the chunk.  The norms of its key and query rows are
-// shared by the value heads of the group; per value head the wave scans the
-// log-gates (G = inclusive in-chunk sum, flat past the last token) and writes
-// the record  [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| |
-// G | 1/|k| | scale/|q| | beta]  (CT floats each; zero past the last token
-// except G), then gamma_C = exp(G_C).
-
-template <int DK, int CT>
-__global__ __launch_bounds__(64) void gdn_chunk_prep_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
-    int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm,
-    float* __restrict__ rec) {
-  constexpr int RSTR = 8 * CT + 4;
-  const int c = blockIdx.x / Hk;
-  const int hk = blockIdx.x - c * Hk;
-  if (c >= scs[N_s]) return;
-  int lo = 0, hi = N_s;  // largest s with scs[s] <= c
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (scs[mid] <= c) lo = mid; else hi = mid;
-  }
-  int64_t b0, len;
-  seq_bounds(cu, lo, T_tot, b0, len);
-  const int64_t j0 = static_cast<int64_t>(c - scs[lo]) * C;
-  const int64_t t0 = b0 + j0;
-  const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
-  const int t = threadIdx.x;
-  const bool ok = t < n;
-  // rows past the last token read it again (unconditional loads) and are
-  // masked afterwards
-  const size_t row = (static_cast<size_t>(t0 + min(t, n - 1)) * Hk + hk) * DK;
-  const float ssk = Frag<bf16>::sumsq(k + row, DK);
-  const float ssq = Frag<bf16>::sumsq(q + row, DK);
-  const float rk = ok ? (l2norm ? 1.0f / sqrtf(ssk + kNormEps) : 1.0f) : 0.f;
-  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(ssq + kNormEps) : 1.0f) : 0.f;
-  const int HG = Hv / Hk;
-  for (int j = 0; j < HG; ++j) {
-    const int hv = hk * HG + j;
-    const size_t th = static_cast<size_t>(t0 + min(t, n - 1)) * Hv + hv;
-    const float gl = ok ? g[th] : 0.f;
-    const float bt = ok ? beta[th] : 0.f;
-    float G = gl;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float up = __shfl_up(G, off);
-      if (t >= off) G += up;
-    }
-    const float GC = __shfl(G, CT - 1);
-    const float gam = __expf(G);
-    if (t < CT) {
-      float* r = rec + (static_cast<size_t>(c) * Hv + hv) * RSTR;
-      r[t] = bt;
-      r[CT + t] = bt * gam * rk;
-      r[2 * CT + t] = gam * rq;
-      r[3 * CT + t] = __expf(GC - G) * rk;
-      r[4 * CT + t] = G;
-      r[5 * CT + t] = rk;
-      r[6 * CT + t] = rq;
-      r[7 * CT + t] = bt;
-      if (t == 0) r[8 * CT] = __expf(GC);
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
 // 3. Sequential chunk loop per (sequence, value head, value block).
 
 template <typename T, int DK, int CT, int NW>
@@ -780,7 +712,7 @@ __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // The copy runs in 1 KiB blocks of 64 consecutive 16-byte LDS slots, dealt
 // round-robin to the NW waves; each lane's source offset per block is fixed
 // for the whole sequence (only the descriptor changes per chunk).
-template <int ROWS, int ITEMS, int PITCH, int NW>
+template <int ROWS, int ITEMS, int PITCH, int NW, bool LOWER = false>
 struct TileCopy {
   static constexpr int SPR = PITCH / 8;                 // LDS slots per row
   static constexpr int NBLK = (ROWS * SPR + 63) / 64;
@@ -794,7 +726,10 @@ struct TileCopy {
     for (int j = 0; j < PER; ++j) {
       const int slot = (j * NW + w) * 64 + lane;
       const int row = slot / SPR, item = slot - row * SPR;
-      off[j] = (row < ROWS && item < ITEMS) ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
+      // LOWER: only 16x16 blocks on or below the diagonal are copied; the
+      // rest of the tile reads zero
+      const bool copy = row < ROWS && item < ITEMS && (!LOWER || item * 8 < (row / 16 + 1) * 16);
+      off[j] = copy ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
   __device__ __forceinline__ void issue(i32x4 r, void* tile, int w) const {
@@ -860,60 +795,273 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
   return c;
 }
 
+// ----------------------------------------------------------------------------
+// 4. bf16 WY pass: one independent wave per (chunk, value head).
+//
+// The wave holds every K and Q fragment of the chunk in registers (rows past
+// the last token read it again; their factors are zero), takes the row norms
+// from them, scans the gates (lane = token) and writes the per-token record
+// [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| | gamma_C,0,0,0].
+// The Gram blocks K K^T and Q K^T on MFMA give A and P; T = (I + A)^-1 is
+// built blockwise: the 16x16 diagonal blocks D_b by forward substitution in
+// fp32 (lane = (block, column)), then each block column j as
+//   T_jj = D_j,   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
+// with 16x16x16 MFMA on hi/lo-split operands.  T is written as bf16 hi/lo and
+// P as bf16, blocks on and below the diagonal only (the chunk loop reads the
+// blocks above as zero).  One wave needs no barriers, and small LDS lets
+// many waves share a CU to hide each other's latency.
+
+template <int DK, int CT>
+__global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
+    int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
+    bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac) {
+  constexpr int MT = CT / 16, KB = DK / 32;
+  constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 4 * CT + 4;
+  __shared__ __attribute__((aligned(16))) float sG[CT], sRK[CT], sRQ[CT], sB[CT];
+  // 16x16 fp32 blocks; a stride of 324 floats puts the four diagonal blocks
+  // (read together by lane groups of the diagonal solve) on distinct banks
+  __shared__ __attribute__((aligned(16))) float sA[NPAIR][324];
+  __shared__ __attribute__((aligned(16))) float sD[MT][324];   // D_b row-major, pitch 20
+  __shared__ __attribute__((aligned(16))) float sDT[MT][324];  // D_b transposed
+
+  const int c = blockIdx.x / Hv;
+  const int hv = blockIdx.x - c * Hv;
+  if (c >= scs[N_s]) return;
+  int lo = 0, hi = N_s;  // largest s with scs[s] <= c
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (scs[mid] <= c) lo = mid; else hi = mid;
+  }
+  int64_t b0, len;
+  seq_bounds(cu, lo, T_tot, b0, len);
+  const int64_t j0 = static_cast<int64_t>(c - scs[lo]) * C;
+  const int64_t t0 = b0 + j0;
+  const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
+  const int hk = hv / (Hv / Hk);
+  const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
+  const size_t mat = static_cast<size_t>(c) * Hv + hv;
+
+  // gates of token `lane`, then the K and Q fragments: lane (l16, kg) holds
+  // row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on both
+  // sides of every Gram product)
+  float gl = 0.f, bt = 0.f;
+  {
+    const size_t tg = static_cast<size_t>(t0 + min(lane, n - 1)) * Hv + hv;
+    gl = g[tg];
+    bt = beta[tg];
+  }
+  bf16x8v kf[MT][KB], qf[MT][KB];
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+    const size_t roff = (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      kf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(k + roff + kb * 32 + kg * 8));
+      qf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + roff + kb * 32 + kg * 8));
+    }
+  }
+  // row sums of squares: 8 elements per lane and k-block, then over kg
+  float ssk[MT], ssq[MT];
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 wk = __builtin_bit_cast(u32x4, kf[I][kb]), wq = __builtin_bit_cast(u32x4, qf[I][kb]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = __uint_as_float(wk[p] << 16), x1 = __uint_as_float(wk[p] & 0xffff0000u);
+        const float y0 = __uint_as_float(wq[p] << 16), y1 = __uint_as_float(wq[p] & 0xffff0000u);
+        a += x0 * x0 + x1 * x1;
+        b += y0 * y0 + y1 * y1;
+      }
+    }
+    a += __shfl_xor(a, 16);
+    a += __shfl_xor(a, 32);
+    b += __shfl_xor(b, 16);
+    b += __shfl_xor(b, 32);
+    ssk[I] = a;
+    ssq[I] = b;
+  }
+  // lane t = kg*16 + l16 takes row t's sums from register slot kg
+  float mk = ssk[0], mq = ssq[0];
+#pragma unroll
+  for (int I = 1; I < MT; ++I) {
+    mk = kg == I ? ssk[I] : mk;
+    mq = kg == I ? ssq[I] : mq;
+  }
+  const bool ok = lane < n;
+  const float rk = ok ? (l2norm ? 1.0f / sqrtf(mk + kNormEps) : 1.0f) : 0.f;
+  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(mq + kNormEps) : 1.0f) : 0.f;
+  float G = ok ? gl : 0.f;
+  bt = ok ? bt : 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float up = __shfl_up(G, off);
+    if (lane >= off) G += up;
+  }
+  const float GC = __shfl(G, CT - 1);
+  if (lane < CT) {
+    const float gam = __expf(G);
+    float* r = fac + mat * FSTR;
+    r[lane] = bt;
+    r[CT + lane] = bt * gam * rk;
+    r[2 * CT + lane] = gam * rq;
+    r[3 * CT + lane] = __expf(GC - G) * rk;
+    if (lane < 4) r[4 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
+    sG[lane] = G;
+    sRK[lane] = rk;
+    sRQ[lane] = rq;
+    sB[lane] = bt;
+  }
+
+  // ---- Gram blocks -> A (LDS, fp32) and P (global, bf16)
+  bf16* th = Th + mat * CT * CT;
+  bf16* tl = Tl + mat * CT * CT;
+  bf16* ph = Ph + mat * CT * CT;
+#pragma unroll
+  for (int I = 0; I < MT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      const int pidx = I * (I + 1) / 2 + J;
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        gk = mma(kf[I][kb], kf[J][kb], gk);
+        gq = mma(qf[I][kb], kf[J][kb], gq);
+      }
+      const int jj = J * 16 + l16;
+      const float Gj = sG[jj], rkj = sRK[jj];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = I * 16 + kg * 4 + r;
+        const float dec = jj <= ii ? __expf(sG[ii] - Gj) : 0.f;
+        sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? sB[ii] * dec * sRK[ii] * rkj * gk[r] : 0.f;
+        ph[ii * CT + jj] = __builtin_bit_cast(bf16, (__bf16)(dec * sRQ[ii] * rkj * gq[r]));
+      }
+    }
+
+  // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
+  {
+    const int b = lane >> 4, cc = l16;
+    if (b < MT) {
+      const float* Ab = sA[b * (b + 1) / 2 + b];
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float a0 = (i == cc) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int j = 0; j + 3 < i; j += 4) {
+          const f32x4 ar = *reinterpret_cast<const f32x4*>(Ab + i * 20 + j);
+          a0 -= ar.x * x[j];
+          a1 -= ar.y * x[j + 1];
+          a2 -= ar.z * x[j + 2];
+          a3 -= ar.w * x[j + 3];
+        }
+#pragma unroll
+        for (int j = i & ~3; j < i; ++j) a0 -= Ab[i * 20 + j] * x[j];
+        x[i] = (a0 + a1) + (a2 + a3);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sD[b][i * 20 + cc] = x[i];
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<f32x4*>(&sDT[b][cc * 20 + i]) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    }
+  }
+
+  // ---- block columns of T
+  auto put_T = [&](int i, int j, f32x4 t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int off = (i * 16 + kg * 4 + r) * CT + j * 16 + l16;
+      const __bf16 h = (__bf16)t[r];
+      th[off] = __builtin_bit_cast(bf16, h);
+      tl[off] = __builtin_bit_cast(bf16, (__bf16)(t[r] - (float)h));
+    }
+  };
+  f32x4 Tc[MT][MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    Tc[j][j] = *reinterpret_cast<const f32x4*>(&sDT[j][l16 * 20 + kg * 4]);
+    put_T(j, j, Tc[j][j]);
+  }
+  // level by level (i - j = 1, 2, ...) so the columns' chains interleave
+#pragma unroll
+  for (int d = 1; d < MT; ++d)
+#pragma unroll
+    for (int j = 0; j + d < MT; ++j) {
+      const int i = j + d;
+      f32x4 M = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = j; kk < i; ++kk)
+        M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16 * 20 + kg * 4]), Tc[kk][j], M);
+      Tc[i][j] = -mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
+      put_T(i, j, Tc[i][j]);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// 5. bf16 chunk loop: one workgroup per (sequence, value head, BV = 16 * NW
+// value columns), a wave per 16 columns, state in MFMA accumulators.
+//
+// Chunk operands reach LDS by asynchronous buffer->LDS copies.  K, Q, T
+// hi/lo, P and the factor record are double-buffered and copied for chunk
+// ci+1 when step ci starts; V is copied right after the phase that reads it.
+// Per step (products that do not depend on each other share a phase, so
+// their MFMA chains interleave):
+//   A: X = K S (S as hi + lo), Y = Q S (hi);  R = beta V - (beta gamma/|k|) X
+//      -- barrier, copy V (ci+1)
+//   B: Delta = T R                              (T lower triangular)
+//   C: O = (gamma scale/|q|) Y + P Delta;  S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
+//      -- wait for every copy, barrier, store y
+// Copies are bounded by a buffer descriptor per chunk: rows past the chunk's
+// last token (and whole chunks past the sequence) read as zero, and y rows
+// past it are dropped the same way.  K^T and V are read with the transposing
+// LDS load.
+
 template <int DK, int CT, int NW>
-struct FusedTiles {
+struct StreamTiles {
   static constexpr int BV = 16 * NW;
   static constexpr int KP = DK + 8, TPP = CT + 8, VP = BV + 16;  // LDS pitches (bf16)
-  static constexpr int MT = CT / 16;
-  static constexpr int NPAIR = MT * (MT + 1) / 2;  // 16x16 blocks on or below the diagonal
-  static constexpr int RSTR = 8 * CT + 4;          // floats per (chunk, value head) record
+  static constexpr int FSTR = 4 * CT + 4;                        // floats per record
   using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
+  using Tcopy = TileCopy<CT, CT / 8, TPP, NW, true>;
   using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
-  using Rcopy = TileCopy<1, 2 * CT, 16 * CT, NW>;  // the record's first 8*CT floats
-  // one chunk's double-buffered operands
+  using Fcopy = TileCopy<1, CT + 1, 8 * CT + 8, NW>;  // the record as CT+1 16-byte items
   struct __attribute__((aligned(16))) Set {
     bf16 K[KQcopy::ELEMS];
     bf16 Q[KQcopy::ELEMS];
-    bf16 R[Rcopy::ELEMS];
+    bf16 Th[Tcopy::ELEMS];
+    bf16 Tl[Tcopy::ELEMS];
+    bf16 P[Tcopy::ELEMS];
+    bf16 F[Fcopy::ELEMS];
   };
 };
 
 template <int DK, int CT, int NW>
-__global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
+__global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
-    int Hv, int Dv, int C, int maxc, const float* __restrict__ rec, bf16* __restrict__ y) {
-  using Tiles = FusedTiles<DK, CT, NW>;
+    int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
+    const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
+  using Tiles = StreamTiles<DK, CT, NW>;
   using Set = typename Tiles::Set;
-  constexpr int BV = Tiles::BV, KP = Tiles::KP, TPP = Tiles::TPP, VP = Tiles::VP;
+  constexpr int BV = Tiles::BV, KP = Tiles::KP, TPP = Tiles::TPP, VP = Tiles::VP, FSTR = Tiles::FSTR;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
-  constexpr int NPAIR = Tiles::NPAIR, RSTR = Tiles::RSTR;
-  // Two distinct sets (not an indexed pair): the compiler then knows that
-  // reads of one never wait on copies into the other.
+  // Two distinct sets (not an indexed pair): reads of one never depend on
+  // copies into the other.
   __shared__ Set setA, setB;
   __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 sTh[CT * TPP];
-  __shared__ __attribute__((aligned(16))) bf16 sTl[CT * TPP];
-  __shared__ __attribute__((aligned(16))) bf16 sP[CT * TPP];
-  __shared__ __attribute__((aligned(16))) float sA[NPAIR][16][20];  // A blocks, row-major
-  __shared__ __attribute__((aligned(16))) float sD[MT][16][20];     // (I + A_bb)^-1, row-major
-  __shared__ __attribute__((aligned(16))) float sDT[MT][16][20];    // ... and transposed
 
-  // block -> (sequence, key head, value block, value head of the group)
-  const int HG = Hv / Hk, nvb = Dv / BV;
-  int lid = blockIdx.x;
-  {
-    const int span = 8 * HG, G = static_cast<int>(gridDim.x);
-    if (lid < G / span * span) {
-      const int x = lid & 7, r = lid >> 3;
-      lid = ((r / HG) * 8 + x) * HG + r % HG;
-    }
-  }
-  const int grp = lid / HG;
-  const int hv = (grp / nvb) % Hk * HG + lid % HG;
-  const int vb = grp % nvb;
-  const int s = grp / (nvb * Hk);
+  const int nvb = Dv / BV;
+  const int s = blockIdx.x / (Hv * nvb);
+  const int rem = blockIdx.x - s * (Hv * nvb);
+  const int hv = rem / nvb;
+  const int vb = rem - hv * nvb;
   const int64_t slot = cache_indices[s];
   if (slot < 0 || slot >= pool_size) return;
   int64_t b0, len;
@@ -923,7 +1071,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
   const int nch_all = static_cast<int>((len + C - 1) / C);
   const int nch = cbase + nch_all > maxc ? (maxc > cbase ? maxc - cbase : 0) : nch_all;
   if (nch <= 0) return;
-  const int hk = hv / HG;
+  const int hk = hv / (Hv / Hk);
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dvl = w * 16 + l16;  // value column within the block
@@ -931,11 +1079,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
   const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
   const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
   typename Tiles::KQcopy cKQ;
+  typename Tiles::Tcopy cT;
   typename Tiles::Vcopy cV;
-  typename Tiles::Rcopy cR;
+  typename Tiles::Fcopy cF;
   cKQ.init(w, lane, kstride);
+  cT.init(w, lane, CT * 2);
   cV.init(w, lane, vstride);
-  cR.init(w, lane, 0);
+  cF.init(w, lane, 0);
 
   // rows of chunk ci that exist (0 past the sequence)
   auto rows = [&](int ci) __attribute__((always_inline)) -> int {
@@ -943,12 +1093,19 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
     const int64_t left = len - static_cast<int64_t>(ci) * C;
     return static_cast<int>(left < C ? left : C);
   };
-  auto tok0 = [&](int ci) __attribute__((always_inline)) -> int64_t { return b0 + static_cast<int64_t>(ci) * C; };
-  auto matix = [&](int ci) __attribute__((always_inline)) -> size_t { return static_cast<size_t>(cbase + ci) * Hv + hv; };
+  auto tok0 = [&](int ci) __attribute__((always_inline)) -> int64_t {
+    return b0 + static_cast<int64_t>(ci) * C;
+  };
+  auto matix = [&](int ci) __attribute__((always_inline)) -> size_t {
+    return static_cast<size_t>(cbase + ci) * Hv + hv;
+  };
   auto kq_rsrc = [&](const bf16* base, int ci) __attribute__((always_inline)) {
     const int n = rows(ci);
     return make_rsrc(base + (static_cast<size_t>(tok0(ci)) * Hk + hk) * DK,
                      n > 0 ? (n - 1) * kstride + DK * 2 : 0u);
+  };
+  auto ws_rsrc = [&](const bf16* base, int ci) __attribute__((always_inline)) {
+    return make_rsrc(base + matix(ci) * CT * CT, rows(ci) > 0 ? CT * CT * 2 : 0u);
   };
   auto vy_off = [&](int ci) __attribute__((always_inline)) -> size_t {
     return (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV;
@@ -960,104 +1117,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
   auto copy_set = [&](int ci, Set& d) __attribute__((always_inline)) {
     cKQ.issue(kq_rsrc(k, ci), d.K, w);
     cKQ.issue(kq_rsrc(q, ci), d.Q, w);
-    cR.issue(make_rsrc(rec + matix(ci) * RSTR, rows(ci) > 0 ? 32 * CT : 0u), d.R, w);
+    cT.issue(ws_rsrc(Th, ci), d.Th, w);
+    cT.issue(ws_rsrc(Tl, ci), d.Tl, w);
+    cT.issue(ws_rsrc(Ph, ci), d.P, w);
+    cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u), d.F, w);
   };
-  auto copy_V = [&](int ci) __attribute__((always_inline)) { cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w); };
-
-  // ---- the chunk's T = (I + A)^-1 and P from its K, Q and record (in d)
-  auto wy = [&](const Set& d) __attribute__((always_inline)) {
-    const float* Rv = reinterpret_cast<const float*>(d.R);
-    const float* G = Rv + 4 * CT;
-    const float* rk = Rv + 5 * CT;
-    const float* rq = Rv + 6 * CT;
-    const float* bt = Rv + 7 * CT;
-    // Gram K K^T and Q K^T blocks (I >= J) -> A blocks and P, a block per wave
-#pragma unroll
-    for (int I = 0; I < MT; ++I)
-#pragma unroll
-      for (int J = 0; J <= I; ++J) {
-        const int pidx = I * (I + 1) / 2 + J;
-        if (pidx % NW != w) continue;
-        f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const bf16x8v kj = lds_pi<KP>(d.K, J * 16 + l16, kb * 32, kg);
-          gk = mma(lds_pi<KP>(d.K, I * 16 + l16, kb * 32, kg), kj, gk);
-          gq = mma(lds_pi<KP>(d.Q, I * 16 + l16, kb * 32, kg), kj, gq);
-        }
-        const int jj = J * 16 + l16;
-        const float Gj = G[jj], rkj = rk[jj];
-        const f32x4 Gi = *reinterpret_cast<const f32x4*>(G + I * 16 + kg * 4);
-        const f32x4 rki = *reinterpret_cast<const f32x4*>(rk + I * 16 + kg * 4);
-        const f32x4 rqi = *reinterpret_cast<const f32x4*>(rq + I * 16 + kg * 4);
-        const f32x4 bi = *reinterpret_cast<const f32x4*>(bt + I * 16 + kg * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ii = I * 16 + kg * 4 + r;
-          const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
-          sA[pidx][kg * 4 + r][l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[r] : 0.f;
-          sP[ii * TPP + jj] = __builtin_bit_cast(bf16, (__bf16)(dec * rqi[r] * rkj * gq[r]));
-        }
-      }
-    lds_handover();
-    // diagonal blocks: lane (b, c) of wave 0 solves column c of (I + A_bb)^-1
-    // by forward substitution in fp32
-    if (w == 0) {
-      const int b = lane >> 4, c = l16;
-      if (b < MT) {
-        const int pd = b * (b + 1) / 2 + b;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float a0 = (i == c) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-          for (int j = 0; j + 3 < i; j += 4) {
-            const f32x4 ar = *reinterpret_cast<const f32x4*>(&sA[pd][i][j]);
-            a0 -= ar.x * x[j];
-            a1 -= ar.y * x[j + 1];
-            a2 -= ar.z * x[j + 2];
-            a3 -= ar.w * x[j + 3];
-          }
-#pragma unroll
-          for (int j = i & ~3; j < i; ++j) a0 -= sA[pd][i][j] * x[j];
-          x[i] = (a0 + a1) + (a2 + a3);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sD[b][i][c] = x[i];
-#pragma unroll
-        for (int i = 0; i < 16; i += 4)
-          *reinterpret_cast<f32x4*>(&sDT[b][c][i]) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
-      }
-    }
-    lds_handover();
-    // block column j of T, by wave j % NW:  T_jj = D_j,
-    //   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
-    auto put_T = [&](int i, int j, f32x4 t) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int off = (i * 16 + kg * 4 + r) * TPP + j * 16 + l16;
-        const __bf16 h = (__bf16)t[r];
-        sTh[off] = __builtin_bit_cast(bf16, h);
-        sTl[off] = __builtin_bit_cast(bf16, (__bf16)(t[r] - (float)h));
-      }
-    };
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      if (j % NW != w) continue;
-      f32x4 Tc[MT];
-      Tc[j] = *reinterpret_cast<const f32x4*>(&sDT[j][l16][kg * 4]);
-      put_T(j, j, Tc[j]);
-#pragma unroll
-      for (int i = j + 1; i < MT; ++i) {
-        f32x4 M = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = j; kk < i; ++kk)
-          M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16][kg * 4]), Tc[kk], M);
-        const f32x4 Tn = mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16][kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
-        Tc[i] = -Tn;
-        put_T(i, j, Tc[i]);
-      }
-    }
+  auto copy_V = [&](int ci) __attribute__((always_inline)) {
+    cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w);
   };
 
   float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
@@ -1080,33 +1146,35 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
   };
 
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
-    const float* F = reinterpret_cast<const float*>(c.R);
+    const float* F = reinterpret_cast<const float*>(c.F);
     copy_set(ci + 1, nx);
 
-    // ---- X = K S (state-grade: S as hi + lo), R = beta V - (beta gamma/|k|) X
+    // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
     bf16x8v Sh[KB], Sl[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) acc_operand(S[2 * kb], S[2 * kb + 1], Sh[kb], Sl[kb]);
     f32x4 R[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+      f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8v a = lds_pi<KP>(c.K, mt * 16 + l16, kb * 32, kg);
         X = mma(a, Sh[kb], X);
+        Y = mma(lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
         X = mma(a, Sl[kb], X);
       }
       const s16x4 vv = lds_tr(sV + (mt * 16 + tr_row) * VP + w * 16 + tr_col);
       const f32x4 fb = *reinterpret_cast<const f32x4*>(F + mt * 16 + kg * 4);
       const f32x4 fk = *reinterpret_cast<const f32x4*>(F + CT + mt * 16 + kg * 4);
+      O[mt] = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4) * Y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) R[mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[r];
     }
     lds_handover();  // V is free
     copy_V(ci + 1);
 
-    // ---- Delta = T R (T lower triangular: blocks above the diagonal skipped)
+    // ---- B: Delta = T R (blocks above the diagonal skipped)
     bf16x8v Rh[CKB], Rl[CKB];
 #pragma unroll
     for (int cb = 0; cb < CKB; ++cb) acc_operand(R[2 * cb], R[2 * cb + 1], Rh[cb], Rl[cb]);
@@ -1116,38 +1184,28 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
       D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
-        const bf16x8v th = lds_pi<TPP>(sTh, mt * 16 + l16, cb * 32, kg);
-        const bf16x8v tl = lds_pi<TPP>(sTl, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v th = lds_pi<TPP>(c.Th, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v tl = lds_pi<TPP>(c.Tl, mt * 16 + l16, cb * 32, kg);
         D[mt] = mma(th, Rh[cb], D[mt]);
         D[mt] = mma(th, Rl[cb], D[mt]);
         D[mt] = mma(tl, Rh[cb], D[mt]);
       }
     }
 
-    // ---- O = (gamma scale/|q|) Q S + P Delta   (output-grade: hi parts)
-    {
-      bf16x8v Dh[CKB];
+    // ---- C: O += P Delta (hi parts);  S <- gamma_C S + K^T diag(fD) Delta
+    bf16x8v Dh[CKB], Eh[CKB], El[CKB];
 #pragma unroll
-      for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) Y = mma(lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
-        O[mt] = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4) * Y;
-#pragma unroll
-        for (int cb = 0; cb <= mt / 2; ++cb)
-          O[mt] = mma(lds_pi<TPP>(sP, mt * 16 + l16, cb * 32, kg), Dh[cb], O[mt]);
-      }
-    }
-
-    // ---- S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta  (G flat past the last token)
-    const float gC = __expf(F[5 * CT - 1]);
-    bf16x8v Eh[CKB], El[CKB];
+    for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
 #pragma unroll
     for (int cb = 0; cb < CKB; ++cb) acc_operand(D[2 * cb], D[2 * cb + 1], Eh[cb], El[cb]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int cb = 0; cb <= mt / 2; ++cb)
+        O[mt] = mma(lds_pi<TPP>(c.P, mt * 16 + l16, cb * 32, kg), Dh[cb], O[mt]);
+    const float gC = F[4 * CT];
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
       S[m] *= gC;
@@ -1160,27 +1218,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_fused_kernel(
         S[m] = mma(a, El[cb], S[m]);
       }
     }
-    if (ci + 1 < nch) {
-      // K, Q and record of the next chunk landed (its V may still be in
-      // flight); every read of this chunk's T and P is done
-      handover<Tiles::Vcopy::MIN>();
-      wy(nx);
-    }
-    handover<0>();  // every copy of chunk ci+1 landed, its T and P are ready
+    handover<0>();  // every copy of chunk ci+1 landed; this chunk's set is free
     store_y(ci);
   };
 
-  // prologue: zero T and P (blocks above the diagonal stay zero), copy chunk
-  // 0, build its T and P
-  for (int i = tid; i < CT * TPP; i += 64 * NW) {
-    sTh[i] = 0;
-    sTl[i] = 0;
-    sP[i] = 0;
-  }
+  // prologue: all operands of chunk 0
   copy_set(0, setA);
   copy_V(0);
-  handover<Tiles::Vcopy::MIN>();
-  wy(setA);
   handover<0>();
   for (int ci = 0; ci < nch; ci += 2) {
     step(ci, setA, setB);
@@ -1200,26 +1244,25 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
 
-// Workspace: the chunk map, then per (chunk, value head) either the chunk
-// record (bf16: 8*CT+4 floats) or T hi/lo, P hi/lo and the factors (fp32
-// activations: the separate WY pass).
+// Workspace: the chunk map, then per (chunk, value head) T hi/lo and P (hi;
+// plus P lo for fp32 activations) as CT x CT bf16 and the factor record.
 struct Layout {
   size_t scs, th, tl, ph, pl, fac, total;
 };
 
-inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool fused) {
+inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t mats = maxc * static_cast<size_t>(Hv);
-  const size_t tile = fused ? 0 : up(mats * CT * CT * sizeof(bf16));
+  const size_t tile = up(mats * CT * CT * sizeof(bf16));
   Layout L;
   size_t off = 0;
   L.scs = off; off += up(sizeof(int) * (static_cast<size_t>(N_s) + 1));
   L.th = off; off += tile;
   L.tl = off; off += tile;
   L.ph = off; off += tile;
-  L.pl = off; off += tile;
-  L.fac = off; off += up(mats * (fused ? 8 * CT + 4 : 4 * CT + 4) * sizeof(float));
+  L.pl = off; off += bf16_act ? 0 : tile;
+  L.fac = off; off += up(mats * (4 * CT + 4) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -1230,6 +1273,10 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
                char* ws, const Layout& L, hipStream_t stream) {
   int* scs = reinterpret_cast<int*>(ws + L.scs);
+  bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
+  bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
+  bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
+  bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
   float* fac = reinterpret_cast<float*>(ws + L.fac);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
@@ -1238,19 +1285,14 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   (void)hipGetLastError();
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
   if constexpr (std::is_same<T, bf16>::value) {
-    const size_t prep_blocks = maxc * static_cast<size_t>(Hk);
-    hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, CT>), dim3(static_cast<unsigned>(prep_blocks)), dim3(64), 0,
+    hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
-                       N_s, T_tot, Hk, Hv, chunk, scale, l2norm, fac);
-    hipLaunchKernelGGL((gdn_prefill_fused_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+                       N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac);
+    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
-                       chunk, static_cast<int>(maxc), fac, static_cast<bf16*>(y));
+                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y));
   } else {
-    bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
-    bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
-    bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
-    bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
                        T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
