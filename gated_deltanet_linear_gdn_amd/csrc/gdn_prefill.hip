@@ -712,7 +712,7 @@ __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // The copy runs in 1 KiB blocks of 64 consecutive 16-byte LDS slots, dealt
 // round-robin to the NW waves; each lane's source offset per block is fixed
 // for the whole sequence (only the descriptor changes per chunk).
-template <int ROWS, int ITEMS, int PITCH, int NW, bool LOWER = false>
+template <int ROWS, int ITEMS, int PITCH, int NW, bool UPPER = false>
 struct TileCopy {
   static constexpr int SPR = PITCH / 8;                 // LDS slots per row
   static constexpr int NBLK = (ROWS * SPR + 63) / 64;
@@ -726,9 +726,9 @@ struct TileCopy {
     for (int j = 0; j < PER; ++j) {
       const int slot = (j * NW + w) * 64 + lane;
       const int row = slot / SPR, item = slot - row * SPR;
-      // LOWER: only 16x16 blocks on or below the diagonal are copied; the
+      // UPPER: only 16x16 blocks on or above the diagonal are copied; the
       // rest of the tile reads zero
-      const bool copy = row < ROWS && item < ITEMS && (!LOWER || item * 8 < (row / 16 + 1) * 16);
+      const bool copy = row < ROWS && item < ITEMS && (!UPPER || item * 8 >= (row / 16) * 16);
       off[j] = copy ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
@@ -770,6 +770,17 @@ __device__ __forceinline__ s16x4 lds_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4p)(p));
 }
 
+// "pi"-order operand of M^T from a tile holding M row-major: rows r and
+// r + 16 of the tile (r = k0 + kg*4 + l16/4) at column c (= m0 + 4*(l16%4))
+// give elements 0..3 and 4..7, i.e. M[k0 + kg*4 + e][m0 + l16] and
+// M[k0 + 16 + kg*4 + e][m0 + l16].
+template <int PITCH>
+__device__ __forceinline__ bf16x8v lds_trT(const bf16* tile, int r, int c) {
+  const bf16* p = tile + r * PITCH + c;
+  const s16x4 lo4 = lds_tr(p), hi4 = lds_tr(p + 16 * PITCH);
+  return __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(short x) {
   return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16);
 }
@@ -806,9 +817,10 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 // built blockwise: the 16x16 diagonal blocks D_b by forward substitution in
 // fp32 (lane = (block, column)), then each block column j as
 //   T_jj = D_j,   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
-// with 16x16x16 MFMA on hi/lo-split operands.  T is written as bf16 hi/lo and
-// P as bf16, blocks on and below the diagonal only (the chunk loop reads the
-// blocks above as zero).  One wave needs no barriers, and small LDS lets
+// with 16x16x16 MFMA on hi/lo-split operands.  T is written transposed as
+// bf16 hi/lo and P transposed as bf16 (each lane's four accumulator rows are
+// then one 8-byte store), blocks on and below the diagonal of T and P only:
+// the chunk loop reads the others as zero.  One wave needs no barriers, and small LDS lets
 // many waves share a CU to hide each other's latency.
 
 template <int DK, int CT>
@@ -934,13 +946,20 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
       }
       const int jj = J * 16 + l16;
       const float Gj = sG[jj], rkj = sRK[jj];
+      const f32x4 Gi = *reinterpret_cast<const f32x4*>(sG + I * 16 + kg * 4);
+      const f32x4 rki = *reinterpret_cast<const f32x4*>(sRK + I * 16 + kg * 4);
+      const f32x4 rqi = *reinterpret_cast<const f32x4*>(sRQ + I * 16 + kg * 4);
+      const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + I * 16 + kg * 4);
+      s16x4 pv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ii = I * 16 + kg * 4 + r;
-        const float dec = jj <= ii ? __expf(sG[ii] - Gj) : 0.f;
-        sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? sB[ii] * dec * sRK[ii] * rkj * gk[r] : 0.f;
-        ph[ii * CT + jj] = __builtin_bit_cast(bf16, (__bf16)(dec * sRQ[ii] * rkj * gq[r]));
+        const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
+        sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[r] : 0.f;
+        pv[r] = __builtin_bit_cast(short, (__bf16)(dec * rqi[r] * rkj * gq[r]));
       }
+      // P^T row jj, columns I*16 + kg*4 .. +3
+      *reinterpret_cast<s16x4*>(ph + jj * CT + I * 16 + kg * 4) = pv;
     }
 
   // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
@@ -973,14 +992,13 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
   }
 
   // ---- block columns of T
+  // T^T row j*16 + l16, columns i*16 + kg*4 .. +3: one 8-byte store per part
   auto put_T = [&](int i, int j, f32x4 t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int off = (i * 16 + kg * 4 + r) * CT + j * 16 + l16;
-      const __bf16 h = (__bf16)t[r];
-      th[off] = __builtin_bit_cast(bf16, h);
-      tl[off] = __builtin_bit_cast(bf16, (__bf16)(t[r] - (float)h));
-    }
+    s16x4 h, l;
+    split4(t, h, l);
+    const int off = (j * 16 + l16) * CT + i * 16 + kg * 4;
+    *reinterpret_cast<s16x4*>(th + off) = h;
+    *reinterpret_cast<s16x4*>(tl + off) = l;
   };
   f32x4 Tc[MT][MT];
 #pragma unroll
@@ -1025,8 +1043,11 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
 template <int DK, int CT, int NW>
 struct StreamTiles {
   static constexpr int BV = 16 * NW;
-  static constexpr int KP = DK + 8, TPP = CT + 8, VP = BV + 16;  // LDS pitches (bf16)
-  static constexpr int FSTR = 4 * CT + 4;                        // floats per record
+  // LDS pitches (bf16): K and Q rows take 8-byte fragment reads, T^T, P^T
+  // and V rows transposing reads; each pitch keeps a half-wave's reads on
+  // distinct banks
+  static constexpr int KP = DK + 8, TPP = CT + 16, VP = BV + 16;
+  static constexpr int FSTR = 4 * CT + 4;  // floats per record
   using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
   using Tcopy = TileCopy<CT, CT / 8, TPP, NW, true>;
   using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
@@ -1114,13 +1135,22 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const int n = rows(ci);
     return n > 0 ? (n - 1) * vstride + BV * 2 : 0u;
   };
-  auto copy_set = [&](int ci, Set& d) __attribute__((always_inline)) {
-    cKQ.issue(kq_rsrc(k, ci), d.K, w);
-    cKQ.issue(kq_rsrc(q, ci), d.Q, w);
-    cT.issue(ws_rsrc(Th, ci), d.Th, w);
-    cT.issue(ws_rsrc(Tl, ci), d.Tl, w);
-    cT.issue(ws_rsrc(Ph, ci), d.P, w);
-    cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u), d.F, w);
+  // The copies of a chunk's set in three groups (0: K and the record, 1: T,
+  // 2: Q and P; -1: all), issued at different points of a step so that the
+  // CU's memory pipeline drains them while the MFMAs run.
+  auto copy_set = [&](int ci, Set& d, int part) __attribute__((always_inline)) {
+    if (part <= 0) {
+      cKQ.issue(kq_rsrc(k, ci), d.K, w);
+      cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u), d.F, w);
+    }
+    if (part == -1 || part == 1) {
+      cT.issue(ws_rsrc(Th, ci), d.Th, w);
+      cT.issue(ws_rsrc(Tl, ci), d.Tl, w);
+    }
+    if (part == -1 || part == 2) {
+      cKQ.issue(kq_rsrc(q, ci), d.Q, w);
+      cT.issue(ws_rsrc(Ph, ci), d.P, w);
+    }
   };
   auto copy_V = [&](int ci) __attribute__((always_inline)) {
     cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w);
@@ -1147,7 +1177,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
     const float* F = reinterpret_cast<const float*>(c.F);
-    copy_set(ci + 1, nx);
+    copy_set(ci + 1, nx, 0);
 
     // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
     bf16x8v Sh[KB], Sl[KB];
@@ -1173,6 +1203,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     }
     lds_handover();  // V is free
     copy_V(ci + 1);
+    copy_set(ci + 1, nx, 1);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
     bf16x8v Rh[CKB], Rl[CKB];
@@ -1184,13 +1215,15 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
-        const bf16x8v th = lds_pi<TPP>(c.Th, mt * 16 + l16, cb * 32, kg);
-        const bf16x8v tl = lds_pi<TPP>(c.Tl, mt * 16 + l16, cb * 32, kg);
+        const bf16x8v th = lds_trT<TPP>(c.Th, cb * 32 + tr_row, mt * 16 + tr_col);
+        const bf16x8v tl = lds_trT<TPP>(c.Tl, cb * 32 + tr_row, mt * 16 + tr_col);
         D[mt] = mma(th, Rh[cb], D[mt]);
         D[mt] = mma(th, Rl[cb], D[mt]);
         D[mt] = mma(tl, Rh[cb], D[mt]);
       }
     }
+
+    copy_set(ci + 1, nx, 2);
 
     // ---- C: O += P Delta (hi parts);  S <- gamma_C S + K^T diag(fD) Delta
     bf16x8v Dh[CKB], Eh[CKB], El[CKB];
@@ -1204,16 +1237,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb)
-        O[mt] = mma(lds_pi<TPP>(c.P, mt * 16 + l16, cb * 32, kg), Dh[cb], O[mt]);
+        O[mt] = mma(lds_trT<TPP>(c.P, cb * 32 + tr_row, mt * 16 + tr_col), Dh[cb], O[mt]);
     const float gC = F[4 * CT];
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
       S[m] *= gC;
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) {
-        const bf16* p = c.K + (cb * 32 + tr_row) * KP + m * 16 + tr_col;
-        const s16x4 lo4 = lds_tr(p), hi4 = lds_tr(p + 16 * KP);
-        const bf16x8v a = __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8v a = lds_trT<KP>(c.K, cb * 32 + tr_row, m * 16 + tr_col);
         S[m] = mma(a, Eh[cb], S[m]);
         S[m] = mma(a, El[cb], S[m]);
       }
@@ -1223,7 +1254,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   };
 
   // prologue: all operands of chunk 0
-  copy_set(0, setA);
+  copy_set(0, setA, -1);
   copy_V(0);
   handover<0>();
   for (int ci = 0; ci < nch; ci += 2) {
