@@ -38,6 +38,27 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 
+# HBM bytes per B=256 decode launch from two rocprofv3 PMC runs of this bench
+# (FETCH_SIZE x 2 + WRITE_SIZE x 1; the factors are what the same counters
+# read for a 2 GiB device copy), valid for the kernel built from these
+# sources only: after any change to them the figure is reported as null.
+DECODE_TRAFFIC = {
+    "bytes": 1624392499,
+    "sources_sha256": {
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "c1c5cfcfcc6bf5f4856adbfb1790d16c610588750dbdac4f52ff6640b6740595",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "dba007333ce8708713001b4524a494916ff0b0e7a70406cf145e1271f616b6d5",
+    },
+}
+
+
+def _decode_traffic():
+    import hashlib
+    for rel, want in DECODE_TRAFFIC["sources_sha256"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != want:
+                return None
+    return DECODE_TRAFFIC["bytes"]
+
 
 def _dev(x, dtype, device):
     import torch
@@ -283,7 +304,8 @@ def main():
                    **dec["shape"], "state_bytes_per_step": dec["state_bytes"],
                    "activation_bytes_per_step": dec["act_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": _decode_traffic()},
         "copy_GBps": round(copy_gbps, 1),
         "decode_frac_of_copy": round(gbps / copy_gbps, 4),
         "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
