@@ -10,13 +10,15 @@
 //   of state (Dk = 128), the shared k and q, and v_j.  A row is spread over
 //   Dk/4 lanes, one float4 per lane, so each load/store instruction of a
 //   wave moves whole rows with 16-byte accesses (global_load_dwordx4).
-// * A workgroup (512 threads, 8 waves) owns ROWS = (512 / (Dk/4)) * NV rows
-//   of one slice (NV <= 8; Dk = Dv = 128 is one workgroup per 64 KiB slice);
-//   each lane keeps its NV float4s in registers from the load to the store,
-//   so the state crosses HBM exactly twice (read once, written once), with NV
-//   independent 16-byte loads in flight per lane.  Measured on MI355X this
-//   shape streams as fast as a plain 16-byte copy kernel of the same bytes;
-//   16 rows per lane (fewer, fatter waves) was ~9% slower.
+// * A workgroup of 128 threads (two waves) owns ROWS = (128 / (Dk/4)) * 2
+//   rows of one slice, two per lane-row group: 4 KiB of state (8 rows at
+//   Dk = 128, 16 workgroups per 64 KiB slice).  Each lane keeps its two
+//   float4s in registers from the load to the store, so the state crosses
+//   HBM exactly twice (read once, written once).  Measured on MI355X at
+//   B=256, Hv=48, Dk=Dv=128 this fine grain streams within 2% of a one-load,
+//   one-store copy kernel of the same bytes (6.44 vs 6.58 TB/s); one slice
+//   per 512-thread workgroup with 8 rows per lane was 7% slower, and more
+//   rows per lane or larger workgroups were slower still.
 // * Both row reductions (S.k and S.q, before the update) run together as
 //   lane-group sums; the readout then uses the exact identity
 //   y_j = a (S_j . q) + d_j (k . q), so no second pass over the updated row
@@ -32,7 +34,8 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 128;
+constexpr int kRowsPerLane = 2;
 
 template <int DK, int NV, bool FULL, typename T>
 __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
@@ -100,34 +103,23 @@ template <int DK, typename T>
 int launch_dk(const float* state_in, float* state_out, const void* q, const void* k,
               const void* v, const float* g, const void* beta, void* y, int B, int Hk,
               int Hv, int Dv, hipStream_t stream) {
-  constexpr int RPS = kThreads / (DK / 4);
-  // Register slots per lane: enough rows in flight without starving occupancy.
-  const int need = (Dv + RPS - 1) / RPS;
-  const long slices = static_cast<long>(B) * Hv;
-  auto go = [&](auto nv_tag) -> int {
-    constexpr int NV = decltype(nv_tag)::value;
-    const int parts = (Dv + RPS * NV - 1) / (RPS * NV);
-    const long blocks = slices * parts;
-    if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
-    (void)hipGetLastError();
-    if (Dv % (RPS * NV) == 0)
-      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, true, T>), dim3(static_cast<unsigned>(blocks)),
-                         dim3(kThreads), 0, stream, state_in, state_out,
-                         static_cast<const T*>(q), static_cast<const T*>(k),
-                         static_cast<const T*>(v), g, static_cast<const T*>(beta),
-                         static_cast<T*>(y), Hk, Hv, Dv, parts);
-    else
-      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, false, T>), dim3(static_cast<unsigned>(blocks)),
-                         dim3(kThreads), 0, stream, state_in, state_out,
-                         static_cast<const T*>(q), static_cast<const T*>(k),
-                         static_cast<const T*>(v), g, static_cast<const T*>(beta),
-                         static_cast<T*>(y), Hk, Hv, Dv, parts);
-    return launch_status();
-  };
-  if (need <= 1) return go(std::integral_constant<int, 1>{});
-  if (need <= 2) return go(std::integral_constant<int, 2>{});
-  if (need <= 4) return go(std::integral_constant<int, 4>{});
-  return go(std::integral_constant<int, 8>{});
+  constexpr int NV = kRowsPerLane;
+  constexpr int ROWS = kThreads / (DK / 4) * NV;
+  const int parts = (Dv + ROWS - 1) / ROWS;
+  const long blocks = static_cast<long>(B) * Hv * parts;
+  if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
+  (void)hipGetLastError();
+  if (Dv % ROWS == 0)
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, true, T>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g,
+                       static_cast<const T*>(beta), static_cast<T*>(y), Hk, Hv, Dv, parts);
+  else
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, false, T>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g,
+                       static_cast<const T*>(beta), static_cast<T*>(y), Hk, Hv, Dv, parts);
+  return launch_status();
 }
 
 template <typename T>
