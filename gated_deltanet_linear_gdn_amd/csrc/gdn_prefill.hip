@@ -1040,9 +1040,9 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
 // past it are dropped the same way.  K^T and V are read with the transposing
 // LDS load.
 
-template <int DK, int CT, int NW>
+template <int DK, int CT, int NW, int CW>
 struct StreamTiles {
-  static constexpr int BV = 16 * NW;
+  static constexpr int BV = 16 * CW * NW;
   // LDS pitches (bf16): K and Q rows take 8-byte fragment reads, T^T, P^T
   // and V rows transposing reads; each pitch keeps a half-wave's reads on
   // distinct banks
@@ -1062,14 +1062,14 @@ struct StreamTiles {
   };
 };
 
-template <int DK, int CT, int NW>
+template <int DK, int CT, int NW, int CW>
 __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
     int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
     const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
-  using Tiles = StreamTiles<DK, CT, NW>;
+  using Tiles = StreamTiles<DK, CT, NW, CW>;
   using Set = typename Tiles::Set;
   constexpr int BV = Tiles::BV, KP = Tiles::KP, TPP = Tiles::TPP, VP = Tiles::VP, FSTR = Tiles::FSTR;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
@@ -1095,7 +1095,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   const int hk = hv / (Hv / Hk);
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dvl = w * 16 + l16;  // value column within the block
+  // wave w owns value columns (w*CW + t)*16 + l16 of the block, t < CW
+  auto dvl = [&](int t) __attribute__((always_inline)) { return (w * CW + t) * 16 + l16; };
 
   const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
   const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
@@ -1156,97 +1157,138 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w);
   };
 
-  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
-              static_cast<size_t>(vb * BV + dvl) * DK;
-  f32x4 S[DT];
+  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(vb * BV) * DK;
+  f32x4 S[CW][DT];
 #pragma unroll
-  for (int m = 0; m < DT; ++m) S[m] = *reinterpret_cast<const f32x4*>(Sp + m * 16 + kg * 4);
+  for (int t = 0; t < CW; ++t)
+#pragma unroll
+    for (int m = 0; m < DT; ++m)
+      S[t][m] = *reinterpret_cast<const f32x4*>(Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4);
 
   // lane parts of the transposing reads
   const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
-  f32x4 O[MT];  // the chunk's outputs, stored after the step's last wait
+  f32x4 O[CW][MT];  // the chunk's outputs, stored after the step's last wait
 
   auto store_y = [&](int ci) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci), vy_bytes(ci));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < CW; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        store_b16(yr, static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride + dvl * 2, O[mt][r]);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          store_b16(yr, static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride + dvl(t) * 2, O[t][mt][r]);
   };
 
+  // Every operand fragment read from LDS feeds the CW column tiles of the
+  // wave; the tiles' MFMA chains are independent and interleave.
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
     const float* F = reinterpret_cast<const float*>(c.F);
     copy_set(ci + 1, nx, 0);
 
     // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
-    bf16x8v Sh[KB], Sl[KB];
+    f32x4 X[CW][MT], Y[CW][MT];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) acc_operand(S[2 * kb], S[2 * kb + 1], Sh[kb], Sl[kb]);
-    f32x4 R[MT];
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        X[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Y[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8v Sh[CW], Sl[CW];
+#pragma unroll
+      for (int t = 0; t < CW; ++t) acc_operand(S[t][2 * kb], S[t][2 * kb + 1], Sh[t], Sl[t]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8v a = lds_pi<KP>(c.K, mt * 16 + l16, kb * 32, kg);
+        const bf16x8v aq = lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg);
+#pragma unroll
+        for (int t = 0; t < CW; ++t) {
+          X[t][mt] = mma(a, Sh[t], X[t][mt]);
+          Y[t][mt] = mma(aq, Sh[t], Y[t][mt]);
+          X[t][mt] = mma(a, Sl[t], X[t][mt]);
+        }
+      }
+    }
+    f32x4 R[CW][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8v a = lds_pi<KP>(c.K, mt * 16 + l16, kb * 32, kg);
-        X = mma(a, Sh[kb], X);
-        Y = mma(lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg), Sh[kb], Y);
-        X = mma(a, Sl[kb], X);
-      }
-      const s16x4 vv = lds_tr(sV + (mt * 16 + tr_row) * VP + w * 16 + tr_col);
       const f32x4 fb = *reinterpret_cast<const f32x4*>(F + mt * 16 + kg * 4);
       const f32x4 fk = *reinterpret_cast<const f32x4*>(F + CT + mt * 16 + kg * 4);
-      O[mt] = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4) * Y;
+      const f32x4 fq = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R[mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[r];
+      for (int t = 0; t < CW; ++t) {
+        const s16x4 vv = lds_tr(sV + (mt * 16 + tr_row) * VP + (w * CW + t) * 16 + tr_col);
+        O[t][mt] = fq * Y[t][mt];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[t][mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[t][mt][r];
+      }
     }
     lds_handover();  // V is free
     copy_V(ci + 1);
     copy_set(ci + 1, nx, 1);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
-    bf16x8v Rh[CKB], Rl[CKB];
+    bf16x8v Rh[CW][CKB], Rl[CW][CKB];
 #pragma unroll
-    for (int cb = 0; cb < CKB; ++cb) acc_operand(R[2 * cb], R[2 * cb + 1], Rh[cb], Rl[cb]);
-    f32x4 D[MT];
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int cb = 0; cb < CKB; ++cb) acc_operand(R[t][2 * cb], R[t][2 * cb + 1], Rh[t][cb], Rl[t][cb]);
+    f32x4 D[CW][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      D[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < CW; ++t) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
         const bf16x8v th = lds_trT<TPP>(c.Th, cb * 32 + tr_row, mt * 16 + tr_col);
         const bf16x8v tl = lds_trT<TPP>(c.Tl, cb * 32 + tr_row, mt * 16 + tr_col);
-        D[mt] = mma(th, Rh[cb], D[mt]);
-        D[mt] = mma(th, Rl[cb], D[mt]);
-        D[mt] = mma(tl, Rh[cb], D[mt]);
+#pragma unroll
+        for (int t = 0; t < CW; ++t) {
+          D[t][mt] = mma(th, Rh[t][cb], D[t][mt]);
+          D[t][mt] = mma(th, Rl[t][cb], D[t][mt]);
+          D[t][mt] = mma(tl, Rh[t][cb], D[t][mt]);
+        }
       }
     }
 
     copy_set(ci + 1, nx, 2);
 
     // ---- C: O += P Delta (hi parts);  S <- gamma_C S + K^T diag(fD) Delta
-    bf16x8v Dh[CKB], Eh[CKB], El[CKB];
+    bf16x8v Dh[CW][CKB], Eh[CW][CKB], El[CW][CKB];
 #pragma unroll
-    for (int cb = 0; cb < CKB; ++cb) Dh[cb] = acc_operand_hi(D[2 * cb], D[2 * cb + 1]);
+    for (int t = 0; t < CW; ++t) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) D[mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
+      for (int cb = 0; cb < CKB; ++cb) Dh[t][cb] = acc_operand_hi(D[t][2 * cb], D[t][2 * cb + 1]);
 #pragma unroll
-    for (int cb = 0; cb < CKB; ++cb) acc_operand(D[2 * cb], D[2 * cb + 1], Eh[cb], El[cb]);
+      for (int mt = 0; mt < MT; ++mt)
+        D[t][mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
+#pragma unroll
+      for (int cb = 0; cb < CKB; ++cb) acc_operand(D[t][2 * cb], D[t][2 * cb + 1], Eh[t][cb], El[t][cb]);
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int cb = 0; cb <= mt / 2; ++cb)
-        O[mt] = mma(lds_trT<TPP>(c.P, cb * 32 + tr_row, mt * 16 + tr_col), Dh[cb], O[mt]);
+      for (int cb = 0; cb <= mt / 2; ++cb) {
+        const bf16x8v pa = lds_trT<TPP>(c.P, cb * 32 + tr_row, mt * 16 + tr_col);
+#pragma unroll
+        for (int t = 0; t < CW; ++t) O[t][mt] = mma(pa, Dh[t][cb], O[t][mt]);
+      }
     const float gC = F[4 * CT];
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
-      S[m] *= gC;
+#pragma unroll
+      for (int t = 0; t < CW; ++t) S[t][m] *= gC;
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) {
         const bf16x8v a = lds_trT<KP>(c.K, cb * 32 + tr_row, m * 16 + tr_col);
-        S[m] = mma(a, Eh[cb], S[m]);
-        S[m] = mma(a, El[cb], S[m]);
+#pragma unroll
+        for (int t = 0; t < CW; ++t) {
+          S[t][m] = mma(a, Eh[t][cb], S[t][m]);
+          S[t][m] = mma(a, El[t][cb], S[t][m]);
+        }
       }
     }
     handover<0>();  // every copy of chunk ci+1 landed; this chunk's set is free
@@ -1264,7 +1306,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   // (every copy has landed: each step ends waiting for all of them)
 
 #pragma unroll
-  for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
+  for (int t = 0; t < CW; ++t)
+#pragma unroll
+    for (int m = 0; m < DT; ++m)
+      *reinterpret_cast<f32x4*>(Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4) = S[t][m];
 }
 
 // ----------------------------------------------------------------------------
@@ -1298,7 +1343,7 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   return L;
 }
 
-template <typename T, int DK, int CT, int NW>
+template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
@@ -1311,7 +1356,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   float* fac = reinterpret_cast<float*>(ws + L.fac);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
-  const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW));
+  const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW * CW));
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
@@ -1319,7 +1364,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
     hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
                        N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac);
-    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
+    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
                        chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y));
@@ -1346,8 +1391,8 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   // registers each) or 32 columns per workgroup.
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
-      return launch_all<T, DK, CT, 8>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                      chunk, scale, l2norm, y, ws, L, stream);
+      return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
+                                         chunk, scale, l2norm, y, ws, L, stream);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,

@@ -100,6 +100,7 @@ CASES = [
     ([40, 9], 1, 2, 128, 32, 8, "bf16"),
     ([70, 3, 128], 2, 4, 128, 64, 64, "f32"),
     ([45, 16], 1, 1, 64, 32, 32, "f32"),
+    ([100, 300], 1, 2, 128, 256, 64, "bf16"),      # two value blocks per head
 ]
 
 
@@ -112,6 +113,22 @@ def test_prefill_parity(lengths, Hk, Hv, Dk, Dv, chunk, act):
     pool, y = _run_gpu(inp, pool0, chunk, act)
     P_ref, y_ref = _run_oracle(inp, pool0)
     _check(pool, y, P_ref, y_ref, pool0, inp, act)
+
+
+def test_prefill_long_memory():
+    """Slowly decaying heads (A_log = -7: log-gates of about -6e-4 per token)
+    over 1900 tokens: the state carries information across all 30 chunks, so
+    every chunk's state-side product must keep fp32-grade accuracy."""
+    rng = np.random.default_rng(5)
+    Hk, Hv, Dk, Dv = 1, 2, 128, 128
+    pool0 = _warm_pool(rng, 3, Hk, Hv, Dk, Dv, steps=4)
+    inp = synth.prefill_inputs(rng, [700, 1200], Hk, Hv, Dk, Dv, pool_size=3)
+    inp["A_log"] = np.full(Hv, -7.0, dtype=np.float32)
+    g, _ = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    assert g.sum(axis=0).max() > -2.0          # the memory really is long
+    pool, y = _run_gpu(inp, pool0, 64, "bf16")
+    P_ref, y_ref = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
 
 
 def test_prefill_without_l2norm_and_explicit_scale():
