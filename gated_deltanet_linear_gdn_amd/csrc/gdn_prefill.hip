@@ -807,21 +807,22 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 }
 
 // ----------------------------------------------------------------------------
-// 4. bf16 WY pass: one independent wave per (chunk, value head).
+// 4. bf16 WY pass: one independent wave per (chunk, key head).
 //
 // The wave holds every K and Q fragment of the chunk in registers (rows past
 // the last token read it again; their factors are zero), takes the row norms
-// from them, scans the gates (lane = token) and writes the per-token record
-// [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| | gamma_C,0,0,0].
-// The Gram blocks K K^T and Q K^T on MFMA give A and P; T = (I + A)^-1 is
-// built blockwise: the 16x16 diagonal blocks D_b by forward substitution in
-// fp32 (lane = (block, column)), then each block column j as
+// from them and the Gram blocks K K^T and Q K^T on MFMA, once for the value
+// heads of the key head.  Then, per value head: the gate scan (lane = token),
+// the record [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| |
+// gamma_C,0,0,0], A and P from the Gram blocks, and T = (I + A)^-1 built
+// blockwise: the 16x16 diagonal blocks D_b by forward substitution in fp32
+// (lane = (block, column)), then level by level
 //   T_jj = D_j,   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
 // with 16x16x16 MFMA on hi/lo-split operands.  T is written transposed as
 // bf16 hi/lo and P transposed as bf16 (each lane's four accumulator rows are
-// then one 8-byte store), blocks on and below the diagonal of T and P only:
-// the chunk loop reads the others as zero.  One wave needs no barriers, and small LDS lets
-// many waves share a CU to hide each other's latency.
+// then one 8-byte store), blocks on and below the diagonal only: the chunk
+// loop reads the others as zero.  One wave needs no barriers, and a small
+// LDS footprint lets eight waves share a CU and hide each other's latency.
 
 template <int DK, int CT>
 __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
@@ -832,14 +833,14 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
   constexpr int MT = CT / 16, KB = DK / 32;
   constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 4 * CT + 4;
   __shared__ __attribute__((aligned(16))) float sG[CT], sRK[CT], sRQ[CT], sB[CT];
-  // 16x16 fp32 blocks; a stride of 324 floats puts the four diagonal blocks
-  // (read together by lane groups of the diagonal solve) on distinct banks
+  // 16x16 fp32 blocks with a row pitch of 20; a block stride of 324 floats
+  // puts the four diagonal blocks (read together by lane groups of the
+  // diagonal solve) on distinct banks
   __shared__ __attribute__((aligned(16))) float sA[NPAIR][324];
-  __shared__ __attribute__((aligned(16))) float sD[MT][324];   // D_b row-major, pitch 20
-  __shared__ __attribute__((aligned(16))) float sDT[MT][324];  // D_b transposed
+  __shared__ __attribute__((aligned(16))) float sD[MT][324];
 
-  const int c = blockIdx.x / Hv;
-  const int hv = blockIdx.x - c * Hv;
+  const int c = blockIdx.x / Hk;
+  const int hk = blockIdx.x - c * Hk;
   if (c >= scs[N_s]) return;
   int lo = 0, hi = N_s;  // largest s with scs[s] <= c
   while (hi - lo > 1) {
@@ -851,174 +852,182 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
   const int64_t j0 = static_cast<int64_t>(c - scs[lo]) * C;
   const int64_t t0 = b0 + j0;
   const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
-  const int hk = hv / (Hv / Hk);
+  const int HG = Hv / Hk;
   const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
-  const size_t mat = static_cast<size_t>(c) * Hv + hv;
-
-  // gates of token `lane`, then the K and Q fragments: lane (l16, kg) holds
-  // row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on both
-  // sides of every Gram product)
-  float gl = 0.f, bt = 0.f;
-  {
-    const size_t tg = static_cast<size_t>(t0 + min(lane, n - 1)) * Hv + hv;
-    gl = g[tg];
-    bt = beta[tg];
-  }
-  bf16x8v kf[MT][KB], qf[MT][KB];
-#pragma unroll
-  for (int I = 0; I < MT; ++I) {
-    const size_t roff = (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      kf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(k + roff + kb * 32 + kg * 8));
-      qf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + roff + kb * 32 + kg * 8));
-    }
-  }
-  // row sums of squares: 8 elements per lane and k-block, then over kg
-  float ssk[MT], ssq[MT];
-#pragma unroll
-  for (int I = 0; I < MT; ++I) {
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 wk = __builtin_bit_cast(u32x4, kf[I][kb]), wq = __builtin_bit_cast(u32x4, qf[I][kb]);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float x0 = __uint_as_float(wk[p] << 16), x1 = __uint_as_float(wk[p] & 0xffff0000u);
-        const float y0 = __uint_as_float(wq[p] << 16), y1 = __uint_as_float(wq[p] & 0xffff0000u);
-        a += x0 * x0 + x1 * x1;
-        b += y0 * y0 + y1 * y1;
-      }
-    }
-    a += __shfl_xor(a, 16);
-    a += __shfl_xor(a, 32);
-    b += __shfl_xor(b, 16);
-    b += __shfl_xor(b, 32);
-    ssk[I] = a;
-    ssq[I] = b;
-  }
-  // lane t = kg*16 + l16 takes row t's sums from register slot kg
-  float mk = ssk[0], mq = ssq[0];
-#pragma unroll
-  for (int I = 1; I < MT; ++I) {
-    mk = kg == I ? ssk[I] : mk;
-    mq = kg == I ? ssq[I] : mq;
-  }
   const bool ok = lane < n;
-  const float rk = ok ? (l2norm ? 1.0f / sqrtf(mk + kNormEps) : 1.0f) : 0.f;
-  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(mq + kNormEps) : 1.0f) : 0.f;
-  float G = ok ? gl : 0.f;
-  bt = ok ? bt : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float up = __shfl_up(G, off);
-    if (lane >= off) G += up;
-  }
-  const float GC = __shfl(G, CT - 1);
-  if (lane < CT) {
-    const float gam = __expf(G);
-    float* r = fac + mat * FSTR;
-    r[lane] = bt;
-    r[CT + lane] = bt * gam * rk;
-    r[2 * CT + lane] = gam * rq;
-    r[3 * CT + lane] = __expf(GC - G) * rk;
-    if (lane < 4) r[4 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
-    sG[lane] = G;
-    sRK[lane] = rk;
-    sRQ[lane] = rq;
-    sB[lane] = bt;
-  }
+  const size_t tg = static_cast<size_t>(t0 + min(lane, n - 1)) * Hv + hk * HG;  // gates of token `lane`
 
-  // ---- Gram blocks -> A (LDS, fp32) and P (global, bf16)
-  bf16* th = Th + mat * CT * CT;
-  bf16* tl = Tl + mat * CT * CT;
-  bf16* ph = Ph + mat * CT * CT;
+  // gates of the first value head, then the K fragments: lane (l16, kg)
+  // holds row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on
+  // both sides of every Gram product); Q fragments follow one row block at a
+  // time, as the Q K^T blocks of that row need them
+  float gl = g[tg], bl = beta[tg];
+  auto row_off = [&](int I) __attribute__((always_inline)) {
+    return (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK + kg * 8;
+  };
+  bf16x8v kf[MT][KB];
 #pragma unroll
   for (int I = 0; I < MT; ++I)
 #pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      kf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(k + row_off(I) + kb * 32));
+  // row sums of squares: 8 elements per lane and k-block, then over kg
+  auto sumsq = [&](const bf16x8v (&f)[KB]) __attribute__((always_inline)) {
+    float a = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 wv = __builtin_bit_cast(u32x4, f[kb]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = __uint_as_float(wv[p] << 16), x1 = __uint_as_float(wv[p] & 0xffff0000u);
+        a += x0 * x0 + x1 * x1;
+      }
+    }
+    a += __shfl_xor(a, 16);
+    return a + __shfl_xor(a, 32);
+  };
+  // Gram blocks (I >= J), kept for every value head of the group; lane
+  // t = kg*16 + l16 takes row t's sums of squares from row block kg
+  f32x4 gk[NPAIR], gq[NPAIR];
+  float mk = 0.f, mq = 0.f;
+#pragma unroll
+  for (int I = 0; I < MT; ++I) {
+    bf16x8v qf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + row_off(I) + kb * 32));
+    const float sk = sumsq(kf[I]), sq = sumsq(qf);
+    mk = kg == I ? sk : mk;
+    mq = kg == I ? sq : mq;
+#pragma unroll
     for (int J = 0; J <= I; ++J) {
       const int pidx = I * (I + 1) / 2 + J;
-      f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+      gk[pidx] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gq[pidx] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        gk = mma(kf[I][kb], kf[J][kb], gk);
-        gq = mma(qf[I][kb], kf[J][kb], gq);
+        gk[pidx] = mma(kf[I][kb], kf[J][kb], gk[pidx]);
+        gq[pidx] = mma(qf[kb], kf[J][kb], gq[pidx]);
       }
-      const int jj = J * 16 + l16;
-      const float Gj = sG[jj], rkj = sRK[jj];
-      const f32x4 Gi = *reinterpret_cast<const f32x4*>(sG + I * 16 + kg * 4);
-      const f32x4 rki = *reinterpret_cast<const f32x4*>(sRK + I * 16 + kg * 4);
-      const f32x4 rqi = *reinterpret_cast<const f32x4*>(sRQ + I * 16 + kg * 4);
-      const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + I * 16 + kg * 4);
-      s16x4 pv;
+    }
+  }
+  const float rk = ok ? (l2norm ? 1.0f / sqrtf(mk + kNormEps) : 1.0f) : 0.f;
+  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(mq + kNormEps) : 1.0f) : 0.f;
+  if (lane < CT) {
+    sRK[lane] = rk;
+    sRQ[lane] = rq;
+  }
+
+  for (int j = 0; j < HG; ++j) {
+    const int hv = hk * HG + j;
+    const size_t mat = static_cast<size_t>(c) * Hv + hv;
+    float G = ok ? gl : 0.f;
+    const float bt = ok ? bl : 0.f;
+    if (j + 1 < HG) {  // the next head's gates, in flight during this head
+      gl = g[tg + j + 1];
+      bl = beta[tg + j + 1];
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ii = I * 16 + kg * 4 + r;
-        const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
-        sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[r] : 0.f;
-        pv[r] = __builtin_bit_cast(short, (__bf16)(dec * rqi[r] * rkj * gq[r]));
-      }
-      // P^T row jj, columns I*16 + kg*4 .. +3
-      *reinterpret_cast<s16x4*>(ph + jj * CT + I * 16 + kg * 4) = pv;
+    for (int off = 1; off < 64; off <<= 1) {
+      const float up = __shfl_up(G, off);
+      if (lane >= off) G += up;
+    }
+    const float GC = __shfl(G, CT - 1);
+    if (lane < CT) {
+      const float gam = __expf(G);
+      float* r = fac + mat * FSTR;
+      r[lane] = bt;
+      r[CT + lane] = bt * gam * rk;
+      r[2 * CT + lane] = gam * rq;
+      r[3 * CT + lane] = __expf(GC - G) * rk;
+      if (lane < 4) r[4 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
+      sG[lane] = G;
+      sB[lane] = bt;
     }
 
-  // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
-  {
-    const int b = lane >> 4, cc = l16;
-    if (b < MT) {
-      const float* Ab = sA[b * (b + 1) / 2 + b];
-      float x[16];
+    // ---- A (LDS, fp32) and P (global, bf16, transposed) from the Gram blocks
+    bf16* th = Th + mat * CT * CT;
+    bf16* tl = Tl + mat * CT * CT;
+    bf16* ph = Ph + mat * CT * CT;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float a0 = (i == cc) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int I = 0; I < MT; ++I)
 #pragma unroll
-        for (int j = 0; j + 3 < i; j += 4) {
-          const f32x4 ar = *reinterpret_cast<const f32x4*>(Ab + i * 20 + j);
-          a0 -= ar.x * x[j];
-          a1 -= ar.y * x[j + 1];
-          a2 -= ar.z * x[j + 2];
-          a3 -= ar.w * x[j + 3];
+      for (int J = 0; J <= I; ++J) {
+        const int pidx = I * (I + 1) / 2 + J;
+        const int jj = J * 16 + l16;
+        const float Gj = sG[jj], rkj = sRK[jj];
+        const f32x4 Gi = *reinterpret_cast<const f32x4*>(sG + I * 16 + kg * 4);
+        const f32x4 rki = *reinterpret_cast<const f32x4*>(sRK + I * 16 + kg * 4);
+        const f32x4 rqi = *reinterpret_cast<const f32x4*>(sRQ + I * 16 + kg * 4);
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + I * 16 + kg * 4);
+        s16x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ii = I * 16 + kg * 4 + r;
+          const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
+          sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[pidx][r] : 0.f;
+          pv[r] = __builtin_bit_cast(short, (__bf16)(dec * rqi[r] * rkj * gq[pidx][r]));
+        }
+        // P^T row jj, columns I*16 + kg*4 .. +3
+        *reinterpret_cast<s16x4*>(ph + jj * CT + I * 16 + kg * 4) = pv;
+      }
+
+    // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
+    {
+      const int b = lane >> 4, cc = l16;
+      if (b < MT) {
+        const float* Ab = sA[b * (b + 1) / 2 + b];
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float a0 = (i == cc) ? 1.f : 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+          for (int jx = 0; jx + 3 < i; jx += 4) {
+            const f32x4 ar = *reinterpret_cast<const f32x4*>(Ab + i * 20 + jx);
+            a0 -= ar.x * x[jx];
+            a1 -= ar.y * x[jx + 1];
+            a2 -= ar.z * x[jx + 2];
+            a3 -= ar.w * x[jx + 3];
+          }
+#pragma unroll
+          for (int jx = i & ~3; jx < i; ++jx) a0 -= Ab[i * 20 + jx] * x[jx];
+          x[i] = (a0 + a1) + (a2 + a3);
         }
 #pragma unroll
-        for (int j = i & ~3; j < i; ++j) a0 -= Ab[i * 20 + j] * x[j];
-        x[i] = (a0 + a1) + (a2 + a3);
+        for (int i = 0; i < 16; ++i) sD[b][i * 20 + cc] = x[i];
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sD[b][i * 20 + cc] = x[i];
-#pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<f32x4*>(&sDT[b][cc * 20 + i]) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
     }
-  }
 
-  // ---- block columns of T
-  // T^T row j*16 + l16, columns i*16 + kg*4 .. +3: one 8-byte store per part
-  auto put_T = [&](int i, int j, f32x4 t) __attribute__((always_inline)) {
-    s16x4 h, l;
-    split4(t, h, l);
-    const int off = (j * 16 + l16) * CT + i * 16 + kg * 4;
-    *reinterpret_cast<s16x4*>(th + off) = h;
-    *reinterpret_cast<s16x4*>(tl + off) = l;
-  };
-  f32x4 Tc[MT][MT];
+    // ---- block columns of T
+    auto put_T = [&](int i, int jb, f32x4 t) __attribute__((always_inline)) {
+      s16x4 h, l;
+      split4(t, h, l);
+      const int off = (jb * 16 + l16) * CT + i * 16 + kg * 4;  // T^T row jb*16 + l16
+      *reinterpret_cast<s16x4*>(th + off) = h;
+      *reinterpret_cast<s16x4*>(tl + off) = l;
+    };
+    f32x4 Tc[MT][MT];
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    Tc[j][j] = *reinterpret_cast<const f32x4*>(&sDT[j][l16 * 20 + kg * 4]);
-    put_T(j, j, Tc[j][j]);
-  }
-  // level by level (i - j = 1, 2, ...) so the columns' chains interleave
+    for (int jb = 0; jb < MT; ++jb) {
+      // D_jb in accumulator layout: column l16, rows kg*4 .. +3
 #pragma unroll
-  for (int d = 1; d < MT; ++d)
-#pragma unroll
-    for (int j = 0; j + d < MT; ++j) {
-      const int i = j + d;
-      f32x4 M = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = j; kk < i; ++kk)
-        M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16 * 20 + kg * 4]), Tc[kk][j], M);
-      Tc[i][j] = -mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
-      put_T(i, j, Tc[i][j]);
+      for (int r = 0; r < 4; ++r) Tc[jb][jb][r] = sD[jb][(kg * 4 + r) * 20 + l16];
+      put_T(jb, jb, Tc[jb][jb]);
     }
+    // level by level (i - jb = 1, 2, ...) so the columns' chains interleave
+#pragma unroll
+    for (int d = 1; d < MT; ++d)
+#pragma unroll
+      for (int jb = 0; jb + d < MT; ++jb) {
+        const int i = jb + d;
+        f32x4 M = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = jb; kk < i; ++kk)
+          M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16 * 20 + kg * 4]), Tc[kk][jb], M);
+        Tc[i][jb] = -mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
+        put_T(i, jb, Tc[i][jb]);
+      }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1361,7 +1370,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   (void)hipGetLastError();
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
+    hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
                        N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac);
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
