@@ -15,27 +15,29 @@
 // which is the page's w/u~ construction, S_0 W, triu(K^T Q) and state update
 // rescaled by the cumulative decay (no 1/gamma anywhere).
 //
-// Kernels (gfx950, wave64, v_mfma_f32_16x16x32_bf16 for every contraction):
+// Kernels (gfx950, wave64, v_mfma_f32_16x16x32_bf16 for the contractions):
 //  1. gdn_chunk_map_kernel: scan over cu_seqlens -> first chunk of each
 //     sequence (device side, no host sync).
-//  2. gdn_wy_kernel, one wave per (chunk, value head), all chunks of all
-//     sequences in parallel: q/k row norms, G, the Gram K K^T and Q K^T on
-//     MFMA, A and P, and T by column-parallel forward substitution in fp32.
-//     Writes T and P as bf16 hi/lo pairs and G, 1/|k|, scale/|q| to the
-//     workspace.  Nothing here depends on the state.
-//  3. gdn_prefill_kernel, one workgroup per (sequence, value head, 16*NW
-//     value columns): each wave owns 16 value columns and keeps its Dk x 16
-//     slice of S in MFMA accumulators across the sequential chunk loop.  Per
-//     chunk it stages K^T in LDS (the only operand needed transposed), then
-//     runs X = K S, Y = Q S, Delta = T R, O = Y' + P Delta and the state
-//     update as chained MFMAs: every product's right operand is the
-//     previous product's accumulator converted to bf16, with the contraction
-//     index permuted identically on both sides so no data moves between
-//     lanes.  Raw bf16 q/k/v enter the MFMAs exactly; the per-row norm and
-//     decay factors are applied to fp32 accumulators.  Operands that carry
-//     the state (S, R, Delta, T) are split into bf16 hi + lo halves so the
-//     state keeps fp32-grade accuracy; with fp32 activations every product
-//     uses hi/lo on both sides.
+//  2. The WY pass, all chunks of all sequences in parallel (nothing here
+//     depends on the state): q/k row norms, G, the Gram blocks K K^T and
+//     Q K^T on MFMA, A and P, T = (I + A)^-1, and per-token factors.
+//     bf16 activations: gdn_wy_wave_kernel (section 4), one wave per
+//     (chunk, key head), blocked inverse.  fp32 activations: gdn_wy_kernel
+//     (section 2), one wave per (chunk, value head), column-parallel forward
+//     substitution.
+//  3. The sequential chunk loop per (sequence, value head, value columns),
+//     each wave keeping its Dk x 16 slice of S in MFMA accumulators:
+//     X = K S, Y = Q S, Delta = T R, O = Y' + P Delta and the state update as
+//     chained MFMAs (every product's right operand is the previous product's
+//     accumulator converted to bf16, with the contraction index permuted
+//     identically on both sides so no data moves between lanes).  Raw q/k/v
+//     enter the MFMAs exactly; norms and decays scale fp32 accumulators;
+//     operands that carry the state (S, R, Delta, T, and the scaled Delta of
+//     the update) are split into bf16 hi + lo halves so the state keeps
+//     fp32-grade accuracy.  bf16 activations: gdn_prefill_stream_kernel
+//     (section 5), operands streamed through LDS by asynchronous copies.
+//     fp32 activations: gdn_prefill_kernel (section 3), register fragments
+//     from global memory, hi/lo on both sides of every product.
 
 #include <type_traits>
 
