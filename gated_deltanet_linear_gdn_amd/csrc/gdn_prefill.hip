@@ -50,6 +50,7 @@ namespace {
 typedef __bf16 bf16x8v __attribute__((__vector_size__(16)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNormEps = 1e-6f;
 
@@ -711,26 +712,25 @@ __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 
 // A tile of ROWS rows; row r is ITEMS 16-byte items at byte offset
 // r * src_stride of the source, stored in LDS with a pitch of PITCH bf16.
+// SKEW: rows with bit 3 set start one 16-byte slot (8 bf16) later.
 // The copy runs in 1 KiB blocks of 64 consecutive 16-byte LDS slots, dealt
 // round-robin to the NW waves; each lane's source offset per block is fixed
 // for the whole sequence (only the descriptor changes per chunk).
-template <int ROWS, int ITEMS, int PITCH, int NW, bool UPPER = false>
+template <int ROWS, int ITEMS, int PITCH, int NW, bool SKEW = false>
 struct TileCopy {
   static constexpr int SPR = PITCH / 8;                 // LDS slots per row
   static constexpr int NBLK = (ROWS * SPR + 63) / 64;
   static constexpr int ELEMS = NBLK * 512;              // LDS bf16 to reserve
   static constexpr int PER = (NBLK + NW - 1) / NW;      // blocks of the busiest wave
   static constexpr int MIN = NBLK / NW;                 // blocks of every wave
-  static_assert(PITCH % 8 == 0 && PITCH >= 8 * ITEMS, "pitch");
+  static_assert(PITCH % 8 == 0 && PITCH >= 8 * (ITEMS + SKEW), "pitch");
   uint32_t off[PER];
   __device__ __forceinline__ void init(int w, int lane, uint32_t src_stride) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int slot = (j * NW + w) * 64 + lane;
-      const int row = slot / SPR, item = slot - row * SPR;
-      // UPPER: only 16x16 blocks on or above the diagonal are copied; the
-      // rest of the tile reads zero
-      const bool copy = row < ROWS && item < ITEMS && (!UPPER || item * 8 >= (row / 16) * 16);
+      const int row = slot / SPR, item = slot - row * SPR - (SKEW ? (row >> 3) & 1 : 0);
+      const bool copy = row < ROWS && item >= 0 && item < ITEMS;
       off[j] = copy ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
@@ -757,11 +757,16 @@ __device__ __forceinline__ void lds_handover() {
 }
 
 // "pi"-order operand from row `row` of a padded LDS tile (see acc_operand).
+// The two halves are separate 8-byte reads (volatile, so they are not fused
+// into one paired read): on gfx950 a half-wave of single 8-byte reads over
+// 16 rows at an odd 16-byte-slot pitch hits every bank once, while the
+// paired form serves the two addresses of a lane together and conflicts.
 template <int PITCH>
 __device__ __forceinline__ bf16x8v lds_pi(const bf16* tile, int row, int k0, int kg) {
   const bf16* p = tile + row * PITCH + k0 + kg * 4;
-  const uint2 a = *reinterpret_cast<const uint2*>(p);
-  const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+  typedef const volatile __attribute__((address_space(3))) u32x2* lds_u32x2p;
+  const u32x2 a = *(lds_u32x2p)(p);
+  const u32x2 b = *(lds_u32x2p)(p + 16);
   return __builtin_bit_cast(bf16x8v, u32x4{a.x, a.y, b.x, b.y});
 }
 
@@ -780,6 +785,30 @@ template <int PITCH>
 __device__ __forceinline__ bf16x8v lds_trT(const bf16* tile, int r, int c) {
   const bf16* p = tile + r * PITCH + c;
   const s16x4 lo4 = lds_tr(p), hi4 = lds_tr(p + 16 * PITCH);
+  return __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Compact upper-triangular storage of a CT x CT bf16 matrix (bf16
+// activations): only the 16x16 blocks (a, b) with a <= b, block-row-major,
+// each block 16 rows of 32 bytes.  Block (a, b) starts at element
+// 256 * tri_block<CT>(a, b).
+template <int CT>
+__host__ __device__ constexpr int tri_blocks() { return (CT / 16) * (CT / 16 + 1) / 2; }
+template <int CT>
+__device__ __forceinline__ constexpr int tri_block(int a, int b) {
+  return a * (CT / 16) - a * (a - 1) / 2 + (b - a);
+}
+
+// The same operand of M^T from M in compact upper-triangular blocks
+// (tri_block): rows 32 cb + kg*4 + e and 32 cb + 16 + kg*4 + e of M at
+// column 16 mt + l16; lane_off = (kg*4 + l16/4) * 16 + 4*(l16%4).  The second
+// half is zero when block (2cb + 1, mt) lies below the diagonal.  Within a
+// block, the 8 rows of a half-wave's read are 256 contiguous bytes.
+template <int CT>
+__device__ __forceinline__ bf16x8v tri_trT(const bf16* tile, int cb, int mt, int lane_off) {
+  const s16x4 lo4 = lds_tr(tile + tri_block<CT>(2 * cb, mt) * 256 + lane_off);
+  s16x4 hi4 = {0, 0, 0, 0};
+  if (2 * cb + 1 <= mt) hi4 = lds_tr(tile + tri_block<CT>(2 * cb + 1, mt) * 256 + lane_off);
   return __builtin_bit_cast(bf16x8v, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -822,9 +851,10 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 //   T_jj = D_j,   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
 // with 16x16x16 MFMA on hi/lo-split operands.  T is written transposed as
 // bf16 hi/lo and P transposed as bf16 (each lane's four accumulator rows are
-// then one 8-byte store), blocks on and below the diagonal only: the chunk
-// loop reads the others as zero.  One wave needs no barriers, and a small
-// LDS footprint lets eight waves share a CU and hide each other's latency.
+// then one 8-byte store), blocks on and below the diagonal only, in the
+// compact upper-triangular form of the transposes (tri_block).  One wave
+// needs no barriers, and a small LDS footprint lets eight waves share a CU
+// and hide each other's latency.
 
 template <int DK, int CT>
 __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
@@ -948,9 +978,9 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
     }
 
     // ---- A (LDS, fp32) and P (global, bf16, transposed) from the Gram blocks
-    bf16* th = Th + mat * CT * CT;
-    bf16* tl = Tl + mat * CT * CT;
-    bf16* ph = Ph + mat * CT * CT;
+    bf16* th = Th + mat * NPAIR * 256;
+    bf16* tl = Tl + mat * NPAIR * 256;
+    bf16* ph = Ph + mat * NPAIR * 256;
 #pragma unroll
     for (int I = 0; I < MT; ++I)
 #pragma unroll
@@ -970,8 +1000,8 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
           sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[pidx][r] : 0.f;
           pv[r] = __builtin_bit_cast(short, (__bf16)(dec * rqi[r] * rkj * gq[pidx][r]));
         }
-        // P^T row jj, columns I*16 + kg*4 .. +3
-        *reinterpret_cast<s16x4*>(ph + jj * CT + I * 16 + kg * 4) = pv;
+        // P^T row jj, columns I*16 + kg*4 .. +3: block (J, I), row l16
+        *reinterpret_cast<s16x4*>(ph + tri_block<CT>(J, I) * 256 + l16 * 16 + kg * 4) = pv;
       }
 
     // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
@@ -1004,7 +1034,7 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
     auto put_T = [&](int i, int jb, f32x4 t) __attribute__((always_inline)) {
       s16x4 h, l;
       split4(t, h, l);
-      const int off = (jb * 16 + l16) * CT + i * 16 + kg * 4;  // T^T row jb*16 + l16
+      const int off = tri_block<CT>(jb, i) * 256 + l16 * 16 + kg * 4;  // T^T row jb*16 + l16
       *reinterpret_cast<s16x4*>(th + off) = h;
       *reinterpret_cast<s16x4*>(tl + off) = l;
     };
@@ -1045,27 +1075,43 @@ __global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
 //      -- barrier, copy V (ci+1)
 //   B: Delta = T R                              (T lower triangular)
 //   C: O = (gamma scale/|q|) Y + P Delta;  S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
-//      -- wait for every copy, barrier, store y
+//      -- wait for every copy, barrier, O -> LDS (bf16, row-major)
+// and the previous chunk's y leaves LDS after barrier b of the next step,
+// each wave storing whole rows (16-byte pieces, 4 rows per instruction).
 // Copies are bounded by a buffer descriptor per chunk: rows past the chunk's
 // last token (and whole chunks past the sequence) read as zero, and y rows
-// past it are dropped the same way.  K^T and V are read with the transposing
-// LDS load.
+// past it are dropped the same way.  K^T, T^T, P^T and V are read with the
+// transposing LDS load.
 
 template <int DK, int CT, int NW, int CW>
 struct StreamTiles {
   static constexpr int BV = 16 * CW * NW;
-  // LDS pitches (bf16): K and Q rows take 8-byte fragment reads, T^T, P^T
-  // and V rows transposing reads; each pitch keeps a half-wave's reads on
-  // distinct banks
-  static constexpr int KP = DK + 8, TPP = CT + 16, VP = BV + 16;
+  // LDS layouts (bf16), chosen so that each half-wave of reads touches
+  // every bank once (64 banks of 4 bytes, i.e. 16 slots of 16 bytes):
+  // * Q rows take 8-byte fragment reads, 16 rows by one slot: an odd slot
+  //   pitch (DK + 8) spreads them.
+  // * V takes transposing reads, 8 rows by 2 slots: a pitch of twice an odd
+  //   number of slots (BV + 16) spreads them.
+  // * T^T hi/lo and P^T arrive as their compact upper-triangular blocks
+  //   (tri_block), one linear copy each; a transposing read stays inside
+  //   one block, whose rows are 32 contiguous bytes.
+  // * K takes both kinds of read.  Its pitch is DK + 16 (2 x odd slots) and
+  //   rows with bit 3 set start one slot later, which moves rows 8..15 of
+  //   every 16 onto the odd slots the even pitch leaves free: fragment
+  //   reads cover 16 distinct slots and transposing reads (rows 0..7 or
+  //   8..15 of a block) 8 distinct slot pairs.
+  // * y waits in sY (CT rows of BV + 8): 16-byte row reads for the stores.
+  static constexpr int KP = DK + 16, QP = DK + 8, VP = BV + 16, YP = BV + 8;
   static constexpr int FSTR = 4 * CT + 4;  // floats per record
-  using KQcopy = TileCopy<CT, DK / 8, KP, NW>;
-  using Tcopy = TileCopy<CT, CT / 8, TPP, NW, true>;
+  static constexpr int NTB = tri_blocks<CT>();
+  using Kcopy = TileCopy<CT, DK / 8, KP, NW, true>;
+  using Qcopy = TileCopy<CT, DK / 8, QP, NW>;
+  using Tcopy = TileCopy<1, NTB * 32, NTB * 256, NW>;  // NTB blocks of 32 16-byte items
   using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
   using Fcopy = TileCopy<1, CT + 1, 8 * CT + 8, NW>;  // the record as CT+1 16-byte items
   struct __attribute__((aligned(16))) Set {
-    bf16 K[KQcopy::ELEMS];
-    bf16 Q[KQcopy::ELEMS];
+    bf16 K[Kcopy::ELEMS];
+    bf16 Q[Qcopy::ELEMS];
     bf16 Th[Tcopy::ELEMS];
     bf16 Tl[Tcopy::ELEMS];
     bf16 P[Tcopy::ELEMS];
@@ -1082,12 +1128,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
   using Tiles = StreamTiles<DK, CT, NW, CW>;
   using Set = typename Tiles::Set;
-  constexpr int BV = Tiles::BV, KP = Tiles::KP, TPP = Tiles::TPP, VP = Tiles::VP, FSTR = Tiles::FSTR;
+  constexpr int BV = Tiles::BV, KP = Tiles::KP, QP = Tiles::QP, VP = Tiles::VP, YP = Tiles::YP,
+                FSTR = Tiles::FSTR, NTB = Tiles::NTB;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
   // Two distinct sets (not an indexed pair): reads of one never depend on
   // copies into the other.
   __shared__ Set setA, setB;
   __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 sY[CT * YP];
 
   const int nvb = Dv / BV;
   const int s = blockIdx.x / (Hv * nvb);
@@ -1111,12 +1159,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
   const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
-  typename Tiles::KQcopy cKQ;
+  typename Tiles::Kcopy cK;
+  typename Tiles::Qcopy cQ;
   typename Tiles::Tcopy cT;
   typename Tiles::Vcopy cV;
   typename Tiles::Fcopy cF;
-  cKQ.init(w, lane, kstride);
-  cT.init(w, lane, CT * 2);
+  cK.init(w, lane, kstride);
+  cQ.init(w, lane, kstride);
+  cT.init(w, lane, 0);
   cV.init(w, lane, vstride);
   cF.init(w, lane, 0);
 
@@ -1138,7 +1188,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
                      n > 0 ? (n - 1) * kstride + DK * 2 : 0u);
   };
   auto ws_rsrc = [&](const bf16* base, int ci) __attribute__((always_inline)) {
-    return make_rsrc(base + matix(ci) * CT * CT, rows(ci) > 0 ? CT * CT * 2 : 0u);
+    return make_rsrc(base + matix(ci) * NTB * 256, rows(ci) > 0 ? NTB * 512 : 0u);
   };
   auto vy_off = [&](int ci) __attribute__((always_inline)) -> size_t {
     return (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV;
@@ -1152,7 +1202,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   // CU's memory pipeline drains them while the MFMAs run.
   auto copy_set = [&](int ci, Set& d, int part) __attribute__((always_inline)) {
     if (part <= 0) {
-      cKQ.issue(kq_rsrc(k, ci), d.K, w);
+      cK.issue(kq_rsrc(k, ci), d.K, w);
       cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u), d.F, w);
     }
     if (part == -1 || part == 1) {
@@ -1160,7 +1210,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       cT.issue(ws_rsrc(Tl, ci), d.Tl, w);
     }
     if (part == -1 || part == 2) {
-      cKQ.issue(kq_rsrc(q, ci), d.Q, w);
+      cQ.issue(kq_rsrc(q, ci), d.Q, w);
       cT.issue(ws_rsrc(Ph, ci), d.P, w);
     }
   };
@@ -1178,17 +1228,35 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   // lane parts of the transposing reads
   const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
-  f32x4 O[CW][MT];  // the chunk's outputs, stored after the step's last wait
+  // the skew of K rows read by this lane: fragment reads take row l16 of a
+  // block, transposing reads rows kg*4 + l16/4 (+16)
+  const int kfrag = ((l16 >> 3) & 1) * 8, ktr = (kg >> 1) * 8;
+  const int tri_off = tr_row * 16 + tr_col;  // lane part of tri_trT
+  f32x4 O[CW][MT];  // the chunk's outputs, staged after the step's last wait
 
-  auto store_y = [&](int ci) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci), vy_bytes(ci));
+  // O -> sY as bf16 rows (token, value column)
+  auto stage_y = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < CW; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          store_b16(yr, static_cast<uint32_t>(mt * 16 + kg * 4 + r) * vstride + dvl(t) * 2, O[t][mt][r]);
+          sY[(mt * 16 + kg * 4 + r) * YP + dvl(t)] = __builtin_bit_cast(bf16, (__bf16)O[t][mt][r]);
+  };
+  // sY -> y rows of chunk ci: wave w stores CT/NW whole rows, 16 bytes per lane
+  auto store_y = [&](int ci) __attribute__((always_inline)) {
+    constexpr int SPR = BV / 8;              // 16-byte pieces per row
+    constexpr int PIECES = CT * SPR / NW;    // per wave, a multiple of 64
+    static_assert(PIECES % 64 == 0, "y pieces");
+    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci), vy_bytes(ci));
+#pragma unroll
+    for (int it = 0; it < PIECES / 64; ++it) {
+      const int pc = w * PIECES + it * 64 + lane;
+      const int row = pc / SPR, col = (pc - row * SPR) * 8;
+      const u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
+      __builtin_amdgcn_raw_buffer_store_b128(d, yr, static_cast<uint32_t>(row) * vstride + col * 2, 0, 0);
+    }
   };
 
   // Every operand fragment read from LDS feeds the CW column tiles of the
@@ -1213,8 +1281,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int t = 0; t < CW; ++t) acc_operand(S[t][2 * kb], S[t][2 * kb + 1], Sh[t], Sl[t]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8v a = lds_pi<KP>(c.K, mt * 16 + l16, kb * 32, kg);
-        const bf16x8v aq = lds_pi<KP>(c.Q, mt * 16 + l16, kb * 32, kg);
+        const bf16x8v a = lds_pi<KP>(c.K + kfrag, mt * 16 + l16, kb * 32, kg);
+        const bf16x8v aq = lds_pi<QP>(c.Q, mt * 16 + l16, kb * 32, kg);
 #pragma unroll
         for (int t = 0; t < CW; ++t) {
           X[t][mt] = mma(a, Sh[t], X[t][mt]);
@@ -1237,9 +1305,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         for (int r = 0; r < 4; ++r) R[t][mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[t][mt][r];
       }
     }
-    lds_handover();  // V is free
+    lds_handover();  // V is free; every wave staged chunk ci-1's y
     copy_V(ci + 1);
     copy_set(ci + 1, nx, 1);
+    if (ci > 0) store_y(ci - 1);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
     bf16x8v Rh[CW][CKB], Rl[CW][CKB];
@@ -1254,8 +1323,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int t = 0; t < CW; ++t) D[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
-        const bf16x8v th = lds_trT<TPP>(c.Th, cb * 32 + tr_row, mt * 16 + tr_col);
-        const bf16x8v tl = lds_trT<TPP>(c.Tl, cb * 32 + tr_row, mt * 16 + tr_col);
+        const bf16x8v th = tri_trT<CT>(c.Th, cb, mt, tri_off);
+        const bf16x8v tl = tri_trT<CT>(c.Tl, cb, mt, tri_off);
 #pragma unroll
         for (int t = 0; t < CW; ++t) {
           D[t][mt] = mma(th, Rh[t][cb], D[t][mt]);
@@ -1283,7 +1352,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int cb = 0; cb <= mt / 2; ++cb) {
-        const bf16x8v pa = lds_trT<TPP>(c.P, cb * 32 + tr_row, mt * 16 + tr_col);
+        const bf16x8v pa = tri_trT<CT>(c.P, cb, mt, tri_off);
 #pragma unroll
         for (int t = 0; t < CW; ++t) O[t][mt] = mma(pa, Dh[t][cb], O[t][mt]);
       }
@@ -1294,7 +1363,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int t = 0; t < CW; ++t) S[t][m] *= gC;
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) {
-        const bf16x8v a = lds_trT<KP>(c.K, cb * 32 + tr_row, m * 16 + tr_col);
+        const bf16x8v a = lds_trT<KP>(c.K + ktr, cb * 32 + tr_row, m * 16 + tr_col);
 #pragma unroll
         for (int t = 0; t < CW; ++t) {
           S[t][m] = mma(a, Eh[t][cb], S[t][m]);
@@ -1302,8 +1371,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         }
       }
     }
-    handover<0>();  // every copy of chunk ci+1 landed; this chunk's set is free
-    store_y(ci);
+    handover<0>();  // every copy of chunk ci+1 landed; this chunk's set and sY are free
+    stage_y();
   };
 
   // prologue: all operands of chunk 0
@@ -1315,6 +1384,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     if (ci + 1 < nch) step(ci + 1, setB, setA);
   }
   // (every copy has landed: each step ends waiting for all of them)
+  lds_handover();
+  store_y(nch - 1);
 
 #pragma unroll
   for (int t = 0; t < CW; ++t)
@@ -1332,7 +1403,9 @@ inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int chunk_tile(int chunk) { return chunk <= 32 ? 32 : 64; }
 
 // Workspace: the chunk map, then per (chunk, value head) T hi/lo and P (hi;
-// plus P lo for fp32 activations) as CT x CT bf16 and the factor record.
+// plus P lo for fp32 activations) and the factor record.  The matrices are
+// CT x CT bf16 for fp32 activations and compact upper-triangular blocks
+// (tri_block) for bf16 activations.
 struct Layout {
   size_t scs, th, tl, ph, pl, fac, total;
 };
@@ -1341,7 +1414,8 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t mats = maxc * static_cast<size_t>(Hv);
-  const size_t tile = up(mats * CT * CT * sizeof(bf16));
+  const size_t per = bf16_act ? static_cast<size_t>(CT / 16) * (CT / 16 + 1) / 2 * 256 : static_cast<size_t>(CT) * CT;
+  const size_t tile = up(mats * per * sizeof(bf16));
   Layout L;
   size_t off = 0;
   L.scs = off; off += up(sizeof(int) * (static_cast<size_t>(N_s) + 1));
