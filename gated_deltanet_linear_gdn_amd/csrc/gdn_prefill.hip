@@ -734,13 +734,13 @@ struct TileCopy {
       off[j] = copy ? static_cast<uint32_t>(row) * src_stride + item * 16 : kOOB;
     }
   }
+  // the wave's j-th block (none past the tile)
+  __device__ __forceinline__ void issue_one(i32x4 r, void* tile, int w, int j) const {
+    if (j < MIN || (j < PER && j * NW + w < NBLK)) dma16(r, lds_addr(tile) + (j * NW + w) * 1024, off[j]);
+  }
   __device__ __forceinline__ void issue(i32x4 r, void* tile, int w) const {
-    const uint32_t base = lds_addr(tile);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = j * NW + w;
-      if (MIN == PER || b < NBLK) dma16(r, base + b * 1024, off[j]);
-    }
+    for (int j = 0; j < PER; ++j) issue_one(r, tile, w, j);
   }
 };
 
@@ -1197,26 +1197,29 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const int n = rows(ci);
     return n > 0 ? (n - 1) * vstride + BV * 2 : 0u;
   };
-  // The copies of a chunk's set in three groups (0: K and the record, 1: T,
-  // 2: Q and P; -1: all), issued at different points of a step so that the
-  // CU's memory pipeline drains them while the MFMAs run.
-  auto copy_set = [&](int ci, Set& d, int part) __attribute__((always_inline)) {
-    if (part <= 0) {
-      cK.issue(kq_rsrc(k, ci), d.K, w);
-      cF.issue(make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u), d.F, w);
-    }
-    if (part == -1 || part == 1) {
-      cT.issue(ws_rsrc(Th, ci), d.Th, w);
-      cT.issue(ws_rsrc(Tl, ci), d.Tl, w);
-    }
-    if (part == -1 || part == 2) {
-      cQ.issue(kq_rsrc(q, ci), d.Q, w);
-      cT.issue(ws_rsrc(Ph, ci), d.P, w);
-    }
+  // The copies of chunk ci's set are a per-wave list of single 1 KiB copies
+  // (K, the record, T hi, T lo, Q, P); a step issues them one at a time
+  // between its products, so no wave stalls on a burst of memory
+  // instructions while its MFMAs wait.
+  using Tiles_ = Tiles;
+  constexpr int J0 = Tiles_::Kcopy::PER, J1 = J0 + Tiles_::Fcopy::PER, J2 = J1 + Tiles_::Tcopy::PER,
+                J3 = J2 + Tiles_::Tcopy::PER, J4 = J3 + Tiles_::Qcopy::PER, NJOBS = J4 + Tiles_::Tcopy::PER;
+  struct Rsrc {
+    i32x4 K, F, Th, Tl, Q, P;
   };
-  auto copy_V = [&](int ci) __attribute__((always_inline)) {
-    cV.issue(make_rsrc(v + vy_off(ci), vy_bytes(ci)), sV, w);
+  auto set_rsrc = [&](int ci) __attribute__((always_inline)) {
+    return Rsrc{kq_rsrc(k, ci), make_rsrc(fac + matix(ci) * FSTR, rows(ci) > 0 ? FSTR * 4 : 0u),
+                ws_rsrc(Th, ci), ws_rsrc(Tl, ci), kq_rsrc(q, ci), ws_rsrc(Ph, ci)};
   };
+  auto copy_job = [&](const Rsrc& r, Set& d, int n) __attribute__((always_inline)) {
+    if (n < J0) cK.issue_one(r.K, d.K, w, n);
+    else if (n < J1) cF.issue_one(r.F, d.F, w, n - J0);
+    else if (n < J2) cT.issue_one(r.Th, d.Th, w, n - J1);
+    else if (n < J3) cT.issue_one(r.Tl, d.Tl, w, n - J2);
+    else if (n < J4) cQ.issue_one(r.Q, d.Q, w, n - J3);
+    else if (n < NJOBS) cT.issue_one(r.P, d.P, w, n - J4);
+  };
+  auto v_rsrc = [&](int ci) __attribute__((always_inline)) { return make_rsrc(v + vy_off(ci), vy_bytes(ci)); };
 
   float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(vb * BV) * DK;
   f32x4 S[CW][DT];
@@ -1244,26 +1247,24 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         for (int r = 0; r < 4; ++r)
           sY[(mt * 16 + kg * 4 + r) * YP + dvl(t)] = __builtin_bit_cast(bf16, (__bf16)O[t][mt][r]);
   };
-  // sY -> y rows of chunk ci: wave w stores CT/NW whole rows, 16 bytes per lane
-  auto store_y = [&](int ci) __attribute__((always_inline)) {
-    constexpr int SPR = BV / 8;              // 16-byte pieces per row
-    constexpr int PIECES = CT * SPR / NW;    // per wave, a multiple of 64
-    static_assert(PIECES % 64 == 0, "y pieces");
-    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci), vy_bytes(ci));
-#pragma unroll
-    for (int it = 0; it < PIECES / 64; ++it) {
-      const int pc = w * PIECES + it * 64 + lane;
-      const int row = pc / SPR, col = (pc - row * SPR) * 8;
-      const u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
-      __builtin_amdgcn_raw_buffer_store_b128(d, yr, static_cast<uint32_t>(row) * vstride + col * 2, 0, 0);
-    }
+  // sY -> y rows of chunk ci: wave w stores CT/NW whole rows, 16 bytes per
+  // lane, in NYS instructions
+  constexpr int SPR = BV / 8;              // 16-byte pieces per row
+  constexpr int PIECES = CT * SPR / NW;    // per wave, a multiple of 64
+  constexpr int NYS = PIECES / 64;
+  static_assert(PIECES % 64 == 0, "y pieces");
+  auto store_y_one = [&](__amdgpu_buffer_rsrc_t yr, int it) __attribute__((always_inline)) {
+    const int pc = w * PIECES + it * 64 + lane;
+    const int row = pc / SPR, col = (pc - row * SPR) * 8;
+    const u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
+    __builtin_amdgcn_raw_buffer_store_b128(d, yr, static_cast<uint32_t>(row) * vstride + col * 2, 0, 0);
   };
 
   // Every operand fragment read from LDS feeds the CW column tiles of the
   // wave; the tiles' MFMA chains are independent and interleave.
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
     const float* F = reinterpret_cast<const float*>(c.F);
-    copy_set(ci + 1, nx, 0);
+    const Rsrc rn = set_rsrc(ci + 1);
 
     // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
     f32x4 X[CW][MT], Y[CW][MT];
@@ -1289,8 +1290,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           Y[t][mt] = mma(aq, Sh[t], Y[t][mt]);
           X[t][mt] = mma(a, Sl[t], X[t][mt]);
         }
+        copy_job(rn, nx, kb * MT + mt);  // chunk ci+1's set, one copy per product group
       }
     }
+#pragma unroll
+    for (int n = KB * MT; n < NJOBS; ++n) copy_job(rn, nx, n);
     f32x4 R[CW][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -1306,9 +1310,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       }
     }
     lds_handover();  // V is free; every wave staged chunk ci-1's y
-    copy_V(ci + 1);
-    copy_set(ci + 1, nx, 1);
-    if (ci > 0) store_y(ci - 1);
+    const i32x4 rv = v_rsrc(ci + 1);
+    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci > 0 ? ci - 1 : 0), ci > 0 ? vy_bytes(ci - 1) : 0u);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
     bf16x8v Rh[CW][CKB], Rl[CW][CKB];
@@ -1332,9 +1335,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           D[t][mt] = mma(tl, Rh[t][cb], D[t][mt]);
         }
       }
+      cV.issue_one(rv, sV, w, mt);  // chunk ci+1's V
     }
-
-    copy_set(ci + 1, nx, 2);
+#pragma unroll
+    for (int j = MT; j < Tiles_::Vcopy::PER; ++j) cV.issue_one(rv, sV, w, j);
 
     // ---- C: O += P Delta (hi parts);  S <- gamma_C S + K^T diag(fD) Delta
     bf16x8v Dh[CW][CKB], Eh[CW][CKB], El[CW][CKB];
@@ -1370,14 +1374,20 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           S[t][m] = mma(a, El[t][cb], S[t][m]);
         }
       }
+      // chunk ci-1's y, spread over the update
+      if (m % (DT / NYS) == 0 && m / (DT / NYS) < NYS && ci > 0) store_y_one(yr, m / (DT / NYS));
     }
     handover<0>();  // every copy of chunk ci+1 landed; this chunk's set and sY are free
     stage_y();
   };
 
   // prologue: all operands of chunk 0
-  copy_set(0, setA, -1);
-  copy_V(0);
+  {
+    const Rsrc r0 = set_rsrc(0);
+#pragma unroll
+    for (int n = 0; n < NJOBS; ++n) copy_job(r0, setA, n);
+    cV.issue(v_rsrc(0), sV, w);
+  }
   handover<0>();
   for (int ci = 0; ci < nch; ci += 2) {
     step(ci, setA, setB);
@@ -1385,7 +1395,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   }
   // (every copy has landed: each step ends waiting for all of them)
   lds_handover();
-  store_y(nch - 1);
+  {
+    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(nch - 1), vy_bytes(nch - 1));
+#pragma unroll
+    for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
+  }
 
 #pragma unroll
   for (int t = 0; t < CW; ++t)
