@@ -853,11 +853,12 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 // bf16 hi/lo and P transposed as bf16 (each lane's four accumulator rows are
 // then one 8-byte store), blocks on and below the diagonal only, in the
 // compact upper-triangular form of the transposes (tri_block).  One wave
-// needs no barriers, and a small LDS footprint lets eight waves share a CU
-// and hide each other's latency.
+// needs no barriers; the LDS footprint (19 KB) and a register budget of 256
+// (two waves per SIMD, requested from the compiler) let eight waves share a
+// CU and hide each other's latency.
 
 template <int DK, int CT>
-__global__ __launch_bounds__(64) void gdn_wy_wave_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gdn_wy_wave_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
