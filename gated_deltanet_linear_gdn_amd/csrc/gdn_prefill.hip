@@ -63,16 +63,23 @@ __device__ __forceinline__ uint32_t pk(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float hi_part(float x) { return (float)(__bf16)x; }
+// Two fp32 values -> packed bf16 hi (round to nearest even) and lo =
+// bf16(x - hi).  The hi halves come back to fp32 from the packed word (a
+// shift and a mask), not from a second conversion.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& h, uint32_t& l) {
+  h = pk(a, b);
+  l = pk(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
 
 // Eight fp32 values -> bf16 hi (and lo = bf16(x - hi)) operand vectors.
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8v& hi, bf16x8v& lo) {
   u32x4 h, l;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const float a = x[2 * p], b = x[2 * p + 1];
-    h[p] = pk(a, b);
-    l[p] = pk(a - hi_part(a), b - hi_part(b));
+    uint32_t hp, lp;
+    split_pair(x[2 * p], x[2 * p + 1], hp, lp);
+    h[p] = hp;
+    l[p] = lp;
   }
   hi = __builtin_bit_cast(bf16x8v, h);
   lo = __builtin_bit_cast(bf16x8v, l);
@@ -820,12 +827,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(short x) {
 // split into bf16 hi + lo (the lo x lo term is below fp32 rounding).
 // A: row l16, k = kg*4 + e;  B and C: column l16, k/row = kg*4 + e.
 __device__ __forceinline__ void split4(f32x4 x, s16x4& h, s16x4& l) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 hb = (__bf16)x[e];
-    h[e] = __builtin_bit_cast(short, hb);
-    l[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)hb));
-  }
+  uint32_t h0, l0, h1, l1;
+  split_pair(x[0], x[1], h0, l0);
+  split_pair(x[2], x[3], h1, l1);
+  h = __builtin_bit_cast(s16x4, u32x2{h0, h1});
+  l = __builtin_bit_cast(s16x4, u32x2{l0, l1});
 }
 __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
   s16x4 ah, al, bh, bl;
@@ -844,15 +850,17 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 // the last token read it again; their factors are zero), takes the row norms
 // from them and the Gram blocks K K^T and Q K^T on MFMA, once for the value
 // heads of the key head.  Then, per value head: the gate scan (lane = token),
-// the record [beta | beta gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| |
-// gamma_C,0,0,0], A and P from the Gram blocks, and T = (I + A)^-1 built
-// blockwise: the 16x16 diagonal blocks D_b by forward substitution in fp32
-// (lane = (block, column)), then level by level
+// the record [gamma/|k| | gamma scale/|q| | exp(G_C - G)/|k| | gamma_C,0,0,0],
+// A and P from the Gram blocks, and T = (I + A)^-1 built blockwise: the
+// 16x16 diagonal blocks D_b by forward substitution in fp32 (lane = (block,
+// column)), then level by level
 //   T_jj = D_j,   T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj   (i > j)
-// with 16x16x16 MFMA on hi/lo-split operands.  T is written transposed as
-// bf16 hi/lo and P transposed as bf16 (each lane's four accumulator rows are
-// then one 8-byte store), blocks on and below the diagonal only, in the
-// compact upper-triangular form of the transposes (tri_block).  One wave
+// with 16x16x16 MFMA on hi/lo-split operands.  T diag(beta) is written, so
+// that Delta = T diag(beta) (V - diag(gamma/|k|) K S) needs no beta in the
+// chunk loop: transposed as bf16 hi/lo, and P transposed as bf16 (each
+// lane's four accumulator rows are then one 8-byte store), blocks on and
+// below the diagonal only, in the compact upper-triangular form of the
+// transposes (tri_block).  One wave
 // needs no barriers; the LDS footprint (19 KB) and a register budget of 256
 // (two waves per SIMD, requested from the compiler) let eight waves share a
 // CU and hide each other's latency.
@@ -864,7 +872,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
     bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac) {
   constexpr int MT = CT / 16, KB = DK / 32;
-  constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 4 * CT + 4;
+  constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 3 * CT + 4;
   __shared__ __attribute__((aligned(16))) float sG[CT], sRK[CT], sRQ[CT], sB[CT];
   // 16x16 fp32 blocks with a row pitch of 20; a block stride of 324 floats
   // puts the four diagonal blocks (read together by lane groups of the
@@ -969,11 +977,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     if (lane < CT) {
       const float gam = __expf(G);
       float* r = fac + mat * FSTR;
-      r[lane] = bt;
-      r[CT + lane] = bt * gam * rk;
-      r[2 * CT + lane] = gam * rq;
-      r[3 * CT + lane] = __expf(GC - G) * rk;
-      if (lane < 4) r[4 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
+      r[lane] = gam * rk;
+      r[CT + lane] = gam * rq;
+      r[2 * CT + lane] = __expf(GC - G) * rk;
+      if (lane < 4) r[3 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
       sG[lane] = G;
       sB[lane] = bt;
     }
@@ -1031,10 +1038,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
       }
     }
 
-    // ---- block columns of T
+    // ---- block columns of T; stored as T diag(beta) (column jb*16 + l16 of
+    // this lane scaled by its beta)
+    float bcol[MT];
+#pragma unroll
+    for (int jb = 0; jb < MT; ++jb) bcol[jb] = sB[jb * 16 + l16];
     auto put_T = [&](int i, int jb, f32x4 t) __attribute__((always_inline)) {
       s16x4 h, l;
-      split4(t, h, l);
+      split4(t * bcol[jb], h, l);
       const int off = tri_block<CT>(jb, i) * 256 + l16 * 16 + kg * 4;  // T^T row jb*16 + l16
       *reinterpret_cast<s16x4*>(th + off) = h;
       *reinterpret_cast<s16x4*>(tl + off) = l;
@@ -1072,9 +1083,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
 // ci+1 when step ci starts; V is copied right after the phase that reads it.
 // Per step (products that do not depend on each other share a phase, so
 // their MFMA chains interleave):
-//   A: X = K S (S as hi + lo), Y = Q S (hi);  R = beta V - (beta gamma/|k|) X
+//   A: X = K S (S as hi + lo), Y = Q S (hi);  R = V - (gamma/|k|) X
 //      -- barrier, copy V (ci+1)
-//   B: Delta = T R                              (T lower triangular)
+//   B: Delta = (T diag(beta)) R                 (lower triangular)
 //   C: O = (gamma scale/|q|) Y + P Delta;  S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
 //      -- wait for every copy, barrier, O -> LDS (bf16, row-major)
 // and the previous chunk's y leaves LDS after barrier b of the next step,
@@ -1103,13 +1114,13 @@ struct StreamTiles {
   //   8..15 of a block) 8 distinct slot pairs.
   // * y waits in sY (CT rows of BV + 8): 16-byte row reads for the stores.
   static constexpr int KP = DK + 16, QP = DK + 8, VP = BV + 16, YP = BV + 8;
-  static constexpr int FSTR = 4 * CT + 4;  // floats per record
+  static constexpr int FSTR = 3 * CT + 4;  // floats per record
   static constexpr int NTB = tri_blocks<CT>();
   using Kcopy = TileCopy<CT, DK / 8, KP, NW, true>;
   using Qcopy = TileCopy<CT, DK / 8, QP, NW>;
   using Tcopy = TileCopy<1, NTB * 32, NTB * 256, NW>;  // NTB blocks of 32 16-byte items
   using Vcopy = TileCopy<CT, BV / 8, VP, NW>;
-  using Fcopy = TileCopy<1, CT + 1, 8 * CT + 8, NW>;  // the record as CT+1 16-byte items
+  using Fcopy = TileCopy<1, FSTR / 4, 2 * FSTR, NW>;  // the record as 16-byte items
   struct __attribute__((aligned(16))) Set {
     bf16 K[Kcopy::ELEMS];
     bf16 Q[Qcopy::ELEMS];
@@ -1299,15 +1310,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     f32x4 R[CW][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 fb = *reinterpret_cast<const f32x4*>(F + mt * 16 + kg * 4);
-      const f32x4 fk = *reinterpret_cast<const f32x4*>(F + CT + mt * 16 + kg * 4);
-      const f32x4 fq = *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4);
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(F + mt * 16 + kg * 4);
+      const f32x4 fq = *reinterpret_cast<const f32x4*>(F + CT + mt * 16 + kg * 4);
 #pragma unroll
       for (int t = 0; t < CW; ++t) {
         const s16x4 vv = lds_tr(sV + (mt * 16 + tr_row) * VP + (w * CW + t) * 16 + tr_col);
         O[t][mt] = fq * Y[t][mt];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[t][mt][r] = fb[r] * bf16_bits_to_f32(vv[r]) - fk[r] * X[t][mt][r];
+        for (int r = 0; r < 4; ++r) R[t][mt][r] = bf16_bits_to_f32(vv[r]) - fk[r] * X[t][mt][r];
       }
     }
     lds_handover();  // V is free; every wave staged chunk ci-1's y
@@ -1349,7 +1359,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int cb = 0; cb < CKB; ++cb) Dh[t][cb] = acc_operand_hi(D[t][2 * cb], D[t][2 * cb + 1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        D[t][mt] *= *reinterpret_cast<const f32x4*>(F + 3 * CT + mt * 16 + kg * 4);
+        D[t][mt] *= *reinterpret_cast<const f32x4*>(F + 2 * CT + mt * 16 + kg * 4);
 #pragma unroll
       for (int cb = 0; cb < CKB; ++cb) acc_operand(D[t][2 * cb], D[t][2 * cb + 1], Eh[t][cb], El[t][cb]);
     }
@@ -1361,7 +1371,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 #pragma unroll
         for (int t = 0; t < CW; ++t) O[t][mt] = mma(pa, Dh[t][cb], O[t][mt]);
       }
-    const float gC = F[4 * CT];
+    const float gC = F[3 * CT];
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
 #pragma unroll
@@ -1438,7 +1448,7 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   L.tl = off; off += tile;
   L.ph = off; off += tile;
   L.pl = off; off += bf16_act ? 0 : tile;
-  L.fac = off; off += up(mats * (4 * CT + 4) * sizeof(float));
+  L.fac = off; off += up(mats * ((bf16_act ? 3 : 4) * CT + 4) * sizeof(float));
   L.total = off;
   return L;
 }
