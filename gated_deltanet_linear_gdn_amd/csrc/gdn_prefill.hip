@@ -68,6 +68,7 @@ __device__ __forceinline__ uint32_t pk(float a, float b) {
 // shift and a mask), not from a second conversion.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& h, uint32_t& l) {
   h = pk(a, b);
+  asm("" : "+v"(h));  // opaque: otherwise the low half is converted again on its own
   l = pk(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
 }
 
@@ -1256,8 +1257,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sY[(mt * 16 + kg * 4 + r) * YP + dvl(t)] = __builtin_bit_cast(bf16, (__bf16)O[t][mt][r]);
+        for (int r = 0; r < 4; r += 2) {
+          // one conversion for two rows: low half to row r, high half to r + 1
+          uint32_t p = pk(O[t][mt][r], O[t][mt][r + 1]);
+          asm("" : "+v"(p));
+          sY[(mt * 16 + kg * 4 + r) * YP + dvl(t)] = static_cast<bf16>(p);
+          sY[(mt * 16 + kg * 4 + r + 1) * YP + dvl(t)] = static_cast<bf16>(p >> 16);
+        }
   };
   // sY -> y rows of chunk ci: wave w stores CT/NW whole rows, 16 bytes per
   // lane, in NYS instructions
