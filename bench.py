@@ -148,6 +148,35 @@ def prefill_flops_per_token(Hv, Dk, Dv, C):
     return Hv * (6 * Dk * Dv + C * (6 * Dk + 4 * Dv))
 
 
+def prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C):
+    """FLOPs the bf16 prefill kernels actually issue as MFMAs, hi/lo extra
+    products included.  Chunk loop, per (chunk, value head) and per wave of 16
+    value columns: X = K S (hi + lo) and Y = Q S (hi) take 3 (C/16)(Dk/32)
+    16x16x32 products; Delta = (T diag beta) R takes 3 per lower 32-row block
+    pair; P Delta one per pair; the state update 2 (Dk/16)(C/32).  WY pass, per
+    (chunk, key head): the Gram blocks K K^T and Q K^T (2 (Dk/32) per lower
+    16x16 block), and per value head 3 16x16x16 products per step of the
+    blocked inverse.  Counts for C = 64 (the only tile the bench runs)."""
+    assert C == 64
+    MT, KB, DT, CKB = C // 16, Dk // 32, Dk // 16, C // 32
+    pairs = sum(mt // 2 + 1 for mt in range(MT))
+    per_wave = 3 * MT * KB + 3 * pairs + pairs + 2 * DT * CKB
+    chunks = sum(-(-int(L) // C) for L in lengths)
+    loop = chunks * Hv * (Dv // 16) * per_wave * 16 * 16 * 32 * 2
+    npair = MT * (MT + 1) // 2
+    inverse_steps = sum(d + 1 for d in range(1, MT) for _ in range(MT - d))  # mm3 calls
+    wy = chunks * Hk * (npair * KB * 2 * 16 * 16 * 32 * 2
+                        + (Hv // Hk) * inverse_steps * 3 * 16 * 16 * 16 * 2)
+    return loop + wy
+
+
+def prefill_min_bytes(T, n_seq, Hk, Hv, Dk, Dv, act_bytes=2):
+    """Bytes a fused prefill must move: q, k, v, y and the raw gates a, b per
+    token, and each sequence's state slot read and written once."""
+    per_token = act_bytes * (2 * Hk * Dk + 2 * Hv * Dv + 2 * Hv)
+    return T * per_token + n_seq * 2 * Hv * Dv * Dk * 4
+
+
 def bench_prefill(steps, warmup, device):
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
@@ -184,6 +213,8 @@ def bench_prefill(steps, warmup, device):
     sec = _timed(step, steps, warmup)
     flops = prefill_flops_per_token(Hv, Dk, Dv, C) * T
     return dict(sec=sec, tokens=T, flops=flops, lengths=[int(x) for x in lengths],
+                issued=prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C),
+                min_bytes=prefill_min_bytes(T, len(lengths), Hk, Hv, Dk, Dv),
                 shape=dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, chunk=C, pool=P))
 
 
@@ -321,7 +352,10 @@ def main():
                     "us_per_call": round(pre["sec"] * 1e6, 2),
                     "tokens_per_s": round(pre["tokens"] / pre["sec"], 1),
                     "canonical_TFLOPs": round(pre["flops"] / pre["sec"] / 1e12, 2),
-                    "mfma_frac_of_bf16_peak": round(pre["flops"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                    "mfma_frac_of_bf16_peak": round(pre["flops"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "min_bytes": pre["min_bytes"],
+                    "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
