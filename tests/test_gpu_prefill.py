@@ -101,6 +101,9 @@ CASES = [
     ([70, 3, 128], 2, 4, 128, 64, 64, "f32"),
     ([45, 16], 1, 1, 64, 32, 32, "f32"),
     ([100, 300], 1, 2, 128, 256, 64, "bf16"),      # two value blocks per head
+    ([37, 100, 5], 2, 4, 128, 128, 32, "bf16"),    # 32-row tiles, eight waves
+    ([90, 20], 1, 2, 64, 128, 64, "bf16"),         # Dk = 64 with eight waves
+    ([77, 64], 1, 1, 32, 128, 16, "bf16"),         # Dk = 32, chunk 16, eight waves
 ]
 
 
