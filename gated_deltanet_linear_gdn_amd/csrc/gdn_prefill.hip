@@ -654,31 +654,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// 3b. The bf16 chunk loop, operands streamed through LDS.
-//
-// One workgroup per (sequence, value head, BV = 16 * NW value columns), a wave
-// per 16 columns, so every chunk operand is fetched once per 16*NW columns.
-// Operands reach LDS by asynchronous buffer->LDS copies (no registers).  K,
-// Q, T hi/lo, P and the per-token factors are double-buffered and copied for
-// chunk ci+1 as soon as step ci starts; V (single-buffered) is copied right
-// after the phase that reads it.  Per step:
-//
-//   copy K, Q, T, P, factors (ci+1)
-//   X = K S, R = beta V - (beta gamma/|k|) X       | barrier, copy V (ci+1)
-//   Delta = T R
-//   O = (gamma scale/|q|) Q S + P Delta
-//   S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
-//   wait for all copies; barrier; store y (ci)
-//
-// Copies are bounded by a buffer descriptor per chunk: rows past the chunk's
-// last token (and whole chunks past the sequence) read as zero, so the
-// ragged tail needs no clamping, and y rows past it are dropped the same way.
-// Tile rows are padded so that the 8-byte fragment reads of a half-wave hit
-// distinct banks; K^T and V are read with the transposing LDS load
-// (ds_read_b64_tr_b16), which hands each lane four rows of one column.
-// Workgroups are dealt to the eight XCDs round-robin; the value heads that
-// share a key head get consecutive slots on one XCD, so their K and Q copies
-// are served by that XCD's L2.
+// 3b. Helpers of the bf16 chunk loop (section 5): buffer descriptors,
+// asynchronous buffer->LDS copies, LDS operand reads (fragment and
+// transposing), hi/lo splits for 16x16x16 products.
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
