@@ -15,6 +15,10 @@ Functions (each cites the page it follows in ``gdn_oracle.c``):
   gdn_prefill   varlen prefill over a pool, per token  (pymllm gdn_chunkwise API)
   comba_step    one Comba step, state [B,H,K,V]         (KBench comba_decode_step)
   gates         g (log-space) and beta from a, b        (regolith gdn.metal header)
+  conv_silu     4-tap causal conv + SiLU with a rolling history per pool slot
+                                                        (regolith gdn.metal conv block)
+  gated_rmsnorm y = o rsqrt(mean(o^2) + eps) gamma sigmoid(z) per (token, head)
+                                                        (regolith gdn.metal output block)
 """
 from __future__ import annotations
 
@@ -60,6 +64,12 @@ def _load():
         lib.oracle_comba_step.argtypes = [_dp] * 7 + [ctypes.c_double, _dp] + [ctypes.c_int] * 4
         lib.oracle_gates.restype = None
         lib.oracle_gates.argtypes = [_dp] * 6 + [ctypes.c_int64, ctypes.c_int]
+        lib.oracle_conv_silu.restype = ctypes.c_int
+        lib.oracle_conv_silu.argtypes = [_dp, _dp, _dp, ctypes.c_int64, _i64p, _i64p, ctypes.c_int,
+                                         ctypes.c_int64, ctypes.c_int, _dp]
+        lib.oracle_gated_rmsnorm.restype = None
+        lib.oracle_gated_rmsnorm.argtypes = [_dp, _dp, _dp, ctypes.c_double, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_int, _dp]
         _lib = lib
     return _lib
 
@@ -151,3 +161,34 @@ def gates(a, b, A_log, dt_bias):
     beta = np.zeros((T, Hv), dtype=np.float64)
     lib.oracle_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta), T, Hv)
     return g, beta
+
+
+def conv_silu(x, W, hist, cache_indices, cu_seqlens):
+    """4-tap causal conv + SiLU per channel with a rolling history.  x [T,C],
+    W [C,4] (tap 3 = current token), hist [P,C,3] (oldest first).  Returns
+    (out [T,C], hist_new) in float64; hist is not modified."""
+    lib = _load()
+    x, W = _f64(x), _f64(W)
+    H = _f64(hist).copy()
+    ci = np.ascontiguousarray(np.asarray(cache_indices, dtype=np.int64))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    T, C = x.shape
+    assert W.shape == (C, 4) and H.shape[1:] == (C, 3) and cu.shape == (ci.shape[0] + 1,)
+    out = np.zeros((T, C), dtype=np.float64)
+    rc = lib.oracle_conv_silu(_ptr(x), _ptr(W), _ptr(H), H.shape[0], ci.ctypes.data_as(_i64p),
+                              cu.ctypes.data_as(_i64p), ci.shape[0], T, C, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_conv_silu: invalid shape or index")
+    return out, H
+
+
+def gated_rmsnorm(o, z, gamma, eps=1e-6):
+    """y = o rsqrt(mean_j(o^2) + eps) gamma[j] sigmoid(z) over the last axis
+    of o, z [T,Hv,Dv]; gamma [Dv].  Returns y in float64."""
+    lib = _load()
+    o, z, gamma = _f64(o), _f64(z), _f64(gamma)
+    T, Hv, Dv = o.shape
+    assert z.shape == o.shape and gamma.shape == (Dv,)
+    y = np.zeros_like(o)
+    lib.oracle_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(gamma), float(eps), T, Hv, Dv, _ptr(y))
+    return y

@@ -229,3 +229,69 @@ void oracle_gates(const double* a, const double* b, const double* A_log,
     }
   }
 }
+
+/*
+ * Short causal convolution + SiLU of the layer's q/k/v channels, with a
+ * rolling history per pool slot (regolith `gdn.metal`: header comment and
+ * the conv/SiLU block of its kernel; 4 taps, history [channels][3] oldest
+ * first).  x and out are [T][C] (C channels per token); W is [C][4], tap 3
+ * weighting the current token; hist is [pool][C][3].  For each sequence s
+ * (tokens cu[s] .. cu[s+1]-1) with slot = cache_indices[s], and each
+ * channel c, the window at token t is (x[t-3], x[t-2], x[t-1], x[t]), where
+ * inputs before the sequence's first token are the slot's history
+ * (hist[0] the oldest, hist[2] the newest).  Then
+ *   pre = sum_m window[m] W[c][m],   out[t][c] = pre / (1 + exp(-pre)),
+ * and afterwards the slot's history holds the newest three entries of
+ * (old history, the sequence's inputs), oldest first.  A zero-length
+ * sequence leaves its slot untouched; other slots are never touched.
+ */
+int oracle_conv_silu(const double* x, const double* W, double* hist, int64_t pool,
+                     const int64_t* cache_indices, const int64_t* cu, int N_s, int64_t T,
+                     int C, double* out) {
+  if (N_s < 0 || T < 0 || C <= 0 || pool < 0) return -1;
+  for (int s = 0; s < N_s; ++s) {
+    const int64_t t0 = cu[s], t1 = cu[s + 1];
+    const int64_t slot = cache_indices[s];
+    if (t0 < 0 || t1 < t0 || t1 > T) return -1;
+    if (t1 == t0) continue;
+    if (slot < 0 || slot >= pool) return -1;
+    for (int c = 0; c < C; ++c) {
+      double* h = hist + ((size_t)slot * C + c) * 3;
+      double win[4] = {h[0], h[1], h[2], 0.0};  /* win[0..2]: the three previous inputs */
+      for (int64_t t = t0; t < t1; ++t) {
+        win[3] = x[(size_t)t * C + c];
+        double pre = 0.0;
+        for (int m = 0; m < 4; ++m) pre += win[m] * W[(size_t)c * 4 + m];
+        out[(size_t)t * C + c] = pre / (1.0 + exp(-pre));
+        win[0] = win[1];
+        win[1] = win[2];
+        win[2] = win[3];
+      }
+      h[0] = win[0];
+      h[1] = win[1];
+      h[2] = win[2];
+    }
+  }
+  return 0;
+}
+
+/*
+ * Gated RMS norm of the recurrence output (regolith `gdn.metal` header
+ * comment and the kernel's output block): per (token, value head), over the
+ * Dv outputs o_j of that head,
+ *   y_j = o_j / sqrt(mean_j(o_j^2) + eps) * gamma[j] * sigmoid(z_j),
+ * with gamma [Dv] shared by every head.  o, z, y are [T][Hv][Dv].
+ */
+void oracle_gated_rmsnorm(const double* o, const double* z, const double* gamma, double eps,
+                          int64_t T, int Hv, int Dv, double* y) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int h = 0; h < Hv; ++h) {
+      const size_t base = ((size_t)t * Hv + h) * Dv;
+      double ss = 0.0;
+      for (int j = 0; j < Dv; ++j) ss += o[base + j] * o[base + j];
+      const double r = 1.0 / sqrt(ss / Dv + eps);
+      for (int j = 0; j < Dv; ++j)
+        y[base + j] = o[base + j] * r * gamma[j] * (1.0 / (1.0 + exp(-z[base + j])));
+    }
+  }
+}

@@ -411,3 +411,148 @@ def test_printed_w_recursion_fails_from_three_tokens():
     assert np.max(np.abs(S2 - S_ref)) < 1e-12
     O6, S6 = wy.chunked_head(S0, Q, K, V, g, beta, 6, form="page", printed_w=True)
     assert np.max(np.abs(S6 - S_ref)) > 1e-3
+
+
+# ---------------------------------------- layer prologue: conv1d (4 taps) + SiLU
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def test_conv_impulse_response_reads_taps_oldest_first():
+    """A unit impulse at a sequence's first token, zero history: the
+    pre-activation at token t is the weight of the tap t steps back, i.e.
+    W[c][3 - t] (tap 3 = current token), and zero from t = 4 on."""
+    rng = np.random.default_rng(3)
+    T, C = 7, 5
+    W = rng.standard_normal((C, 4))
+    x = np.zeros((T, C))
+    x[0, :] = 1.0
+    out, hist = oracle.conv_silu(x, W, np.zeros((1, C, 3)), [0], [0, T])
+    for t in range(4):
+        np.testing.assert_allclose(out[t], _silu(W[:, 3 - t]), rtol=0, atol=1e-15)
+    assert np.all(out[4:] == 0.0)
+    assert np.all(hist[0] == 0.0)  # the impulse left the 3-token window
+
+
+def test_conv_oldest_tap_reads_history_then_inputs():
+    """W = (1, 0, 0, 0): out[t] = SiLU(x[t - 3]), the first three coming from
+    the slot's history in order hist[0], hist[1], hist[2]."""
+    rng = np.random.default_rng(4)
+    T, C = 6, 3
+    W = np.zeros((C, 4))
+    W[:, 0] = 1.0
+    x = rng.standard_normal((T, C))
+    h0 = rng.standard_normal((2, C, 3))
+    out, hist = oracle.conv_silu(x, W, h0, [1], [0, T])
+    for t in range(3):
+        np.testing.assert_allclose(out[t], _silu(h0[1, :, t]), rtol=1e-15)
+    for t in range(3, T):
+        np.testing.assert_allclose(out[t], _silu(x[t - 3]), rtol=1e-15)
+    np.testing.assert_array_equal(hist[1], x[T - 3:].T)  # newest three inputs, oldest first
+    np.testing.assert_array_equal(hist[0], h0[0])         # another slot: untouched
+
+
+def test_conv_identity_tap_is_silu():
+    rng = np.random.default_rng(5)
+    T, C = 9, 4
+    W = np.zeros((C, 4))
+    W[:, 3] = 1.0
+    x = 4.0 * rng.standard_normal((T, C))
+    out, _ = oracle.conv_silu(x, W, rng.standard_normal((1, C, 3)), [0], [0, T])
+    np.testing.assert_allclose(out, x * (1.0 / (1.0 + np.exp(-x))), rtol=1e-14)
+    # SiLU special values
+    o0, _ = oracle.conv_silu(np.zeros((1, 1)), np.array([[0, 0, 0, 1.0]]), np.zeros((1, 1, 3)), [0], [0, 1])
+    assert o0[0, 0] == 0.0
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 5])
+def test_conv_history_after_short_sequences(L):
+    """The new history is the newest three of (old history, inputs)."""
+    rng = np.random.default_rng(6 + L)
+    C = 4
+    W = rng.standard_normal((C, 4))
+    x = rng.standard_normal((max(L, 1), C))[:L]
+    h0 = rng.standard_normal((1, C, 3))
+    _, hist = oracle.conv_silu(x.reshape(L, C), W, h0, [0], [0, L])
+    expect = np.concatenate([h0[0], x.T], axis=1)[:, -3:]
+    np.testing.assert_array_equal(hist[0], expect)
+
+
+def test_conv_split_sequence_equals_whole():
+    """Brute force: a sequence run in two calls, the history carried through
+    the pool slot, gives the same outputs and final history as one call."""
+    rng = np.random.default_rng(8)
+    T, C = 11, 6
+    W = rng.standard_normal((C, 4))
+    x = rng.standard_normal((T, C))
+    h0 = rng.standard_normal((3, C, 3))
+    whole, hw = oracle.conv_silu(x, W, h0, [2], [0, T])
+    for a in (1, 2, 3, 7):
+        first, h1 = oracle.conv_silu(x[:a], W, h0, [2], [0, a])
+        second, h2 = oracle.conv_silu(x[a:], W, h1, [2], [0, T - a])
+        np.testing.assert_array_equal(np.concatenate([first, second]), whole)
+        np.testing.assert_array_equal(h2, hw)
+
+
+def test_conv_varlen_packing_matches_separate_calls():
+    """Packed sequences with their own slots equal one call per sequence."""
+    rng = np.random.default_rng(9)
+    lens, slots, C = [4, 0, 1, 6], [3, 0, 1, 2], 5
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    W = rng.standard_normal((C, 4))
+    x = rng.standard_normal((cu[-1], C))
+    h0 = rng.standard_normal((5, C, 3))
+    out, hist = oracle.conv_silu(x, W, h0, slots, cu)
+    ref_h = h0.copy()
+    for s, L in enumerate(lens):
+        o_s, h_s = oracle.conv_silu(x[cu[s]:cu[s + 1]], W, ref_h, [slots[s]], [0, L])
+        np.testing.assert_array_equal(out[cu[s]:cu[s + 1]], o_s)
+        ref_h = h_s
+    np.testing.assert_array_equal(hist, ref_h)
+    np.testing.assert_array_equal(hist[0], h0[0])  # zero-length sequence: slot untouched
+    np.testing.assert_array_equal(hist[4], h0[4])  # slot nobody uses
+
+
+# ---------------------------------------------- layer epilogue: gated RMS norm
+
+
+def test_gated_rmsnorm_worked_example():
+    """By hand: o = (3, 4) has mean square 12.5; with gamma = (1, 2) and
+    z = (0, ln 3) (sigmoid 1/2 and 3/4), eps = 0:
+    y = (3 * 0.5, 4 * 2 * 0.75) / sqrt(12.5)."""
+    y = oracle.gated_rmsnorm(np.array([[[3.0, 4.0]]]), np.array([[[0.0, np.log(3.0)]]]),
+                             np.array([1.0, 2.0]), eps=0.0)
+    np.testing.assert_allclose(y[0, 0], [1.5 / np.sqrt(12.5), 6.0 / np.sqrt(12.5)], rtol=1e-15)
+
+
+def test_gated_rmsnorm_unit_rms_and_scale_invariance():
+    """With eps = 0, gamma = 1 and a saturated gate the output has unit RMS
+    per (token, head) and is invariant to scaling o by c > 0 (odd in c)."""
+    rng = np.random.default_rng(10)
+    o = rng.standard_normal((3, 4, 32))
+    z = np.full(o.shape, 60.0)  # sigmoid(60) = 1 in double
+    y = oracle.gated_rmsnorm(o, z, np.ones(32), eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * o, z, np.ones(32), eps=0.0), y, rtol=1e-14)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(-2.0 * o, z, np.ones(32), eps=0.0), -y, rtol=1e-14)
+
+
+def test_gated_rmsnorm_gate_and_eps():
+    """gamma and sigmoid(z) multiply column-wise; eps enters the mean square
+    (a zero row stays zero)."""
+    rng = np.random.default_rng(11)
+    o = rng.standard_normal((2, 3, 16))
+    z = rng.standard_normal(o.shape)
+    gam = rng.standard_normal(16)
+    eps = 0.25
+    y = oracle.gated_rmsnorm(o, z, gam, eps=eps)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    np.testing.assert_allclose(y, o / np.sqrt(ms + eps) * gam / (1.0 + np.exp(-z)), rtol=1e-13)
+    y0 = oracle.gated_rmsnorm(np.zeros((1, 1, 8)), np.zeros((1, 1, 8)), np.ones(8), eps=1e-6)
+    assert np.all(y0 == 0.0)
+    # eps inside the root, beside the mean square: a row of ones with eps = 3
+    # gives 1 / sqrt(1 + 3) = 1/2 exactly
+    y1 = oracle.gated_rmsnorm(np.ones((1, 1, 8)), np.full((1, 1, 8), 60.0), np.ones(8), eps=3.0)
+    np.testing.assert_array_equal(y1, 0.5)
