@@ -75,6 +75,10 @@ def load_library():
                                       + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.gdn_validate_varlen.restype = _i
     lib.gdn_validate_varlen.argtypes = [_vp, _vp, _i, _i64, _i64, _vp]
+    lib.gdn_conv_silu.restype = _i
+    lib.gdn_conv_silu.argtypes = [_vp] * 3 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4 + [_vp] * 3 + [_i, _vp]
+    lib.gdn_gated_rmsnorm.restype = _i
+    lib.gdn_gated_rmsnorm.argtypes = [_vp] * 3 + [_f, _vp, _i64, _i, _i, _i, _vp]
     _lib = lib
     return lib
 
@@ -247,6 +251,49 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
           GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q), _ptr(workspace),
           workspace.numel(), _stream())
+    return y
+
+
+def gdn_conv_silu(qkv, conv_w, conv_state, cache_indices, cu_seqlens, Hk, Hv, Dk, Dv,
+                  q=None, k=None, v=None):
+    """Layer prologue: 4-tap causal conv + SiLU of the q/k/v channels with the
+    per-slot history ``conv_state`` [pool, C, 3] f32 updated in place
+    (see ``gdn_conv_silu`` in include/gdn.h).  qkv [T_tot, 2*Hk*Dk + Hv*Dv];
+    returns (q [T,Hk,Dk], k [T,Hk,Dk], v [T,Hv,Dv]) in qkv's dtype."""
+    T, C = qkv.shape
+    dev, dt = qkv.device, qkv.dtype
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError(f"qkv has {C} channels, expected 2*Hk*Dk + Hv*Dv = {2 * Hk * Dk + Hv * Dv}")
+    N_s = cache_indices.shape[0]
+    q = torch.empty((T, Hk, Dk), dtype=dt, device=dev) if q is None else q
+    k = torch.empty((T, Hk, Dk), dtype=dt, device=dev) if k is None else k
+    v = torch.empty((T, Hv, Dv), dtype=dt, device=dev) if v is None else v
+    _check("qkv", qkv, (T, C), dt, dev)
+    _check("conv_w", conv_w, (C, 4), torch.float32, dev)
+    _check("conv_state", conv_state, (conv_state.shape[0], C, 3), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    _check("q", q, (T, Hk, Dk), dt, dev)
+    _check("k", k, (T, Hk, Dk), dt, dev)
+    _check("v", v, (T, Hv, Dv), dt, dev)
+    _call("gdn_conv_silu", _ptr(qkv), _ptr(conv_w), _ptr(conv_state), conv_state.shape[0],
+          _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v),
+          _act_of(qkv), _stream())
+    return q, k, v
+
+
+def gdn_gated_rmsnorm(o, z, gamma, eps=1e-6, y=None):
+    """Layer epilogue: y = o rsqrt(mean(o^2) + eps) gamma sigmoid(z) per
+    (token, value head); o, z [T,Hv,Dv], gamma [Dv] f32; y may be o."""
+    T, Hv, Dv = o.shape
+    dev, dt = o.device, o.dtype
+    y = torch.empty_like(o) if y is None else y
+    _check("o", o, (T, Hv, Dv), dt, dev)
+    _check("z", z, (T, Hv, Dv), dt, dev)
+    _check("gamma", gamma, (Dv,), torch.float32, dev)
+    _check("y", y, (T, Hv, Dv), dt, dev)
+    _call("gdn_gated_rmsnorm", _ptr(o), _ptr(z), _ptr(gamma), float(eps), _ptr(y), T, Hv, Dv,
+          _act_of(o), _stream())
     return y
 
 

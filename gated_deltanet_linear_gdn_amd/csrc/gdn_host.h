@@ -23,6 +23,11 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 inline bool pow2_head(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
+// The gated RMS norm epilogue (gdn_layer.hip), also used by the prefill
+// when a value head spans several chunk-loop workgroups.
+int gated_rmsnorm_launch(const void* o, const void* z, const float* gamma, float eps, long rows,
+                         int Dv, void* y, gdn_dtype act, hipStream_t stream);
+
 // Status of the launch just enqueued.
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;

@@ -186,6 +186,53 @@ int gdn_validate_varlen(const int64_t* cu_seqlens,
                         const int64_t* cache_indices, int N_s, int64_t T_tot,
                         int64_t pool_size, hipStream_t stream);
 
+/*
+ * gdn_conv_silu - the layer prologue: 4-tap causal convolution + SiLU of the
+ * q, k and v channels of every token, with a rolling history per state slot.
+ * Source: regolith `gdn.metal`, header comment and the conv/SiLU block of its
+ * kernel (4 taps, history [channels][3] oldest first).  Per token the
+ * C = 2*Hk*Dk + Hv*Dv input channels are [q heads | k heads | v heads].
+ * For sequence s (packed tokens cu_seqlens[s] .. cu_seqlens[s+1]-1, slot
+ * cache_indices[s]) and channel c, with inputs before the sequence's first
+ * token read from the slot's history (conv_state[slot][c][0] the oldest):
+ *     pre = x[t-3] w[c][0] + x[t-2] w[c][1] + x[t-1] w[c][2] + x[t] w[c][3]
+ *     out[t][c] = pre / (1 + exp(-pre))
+ * and afterwards the slot's history holds the newest three of (history,
+ * the sequence's inputs).  A decode step is one token per sequence
+ * (cu_seqlens = 0, 1, ..., B).
+ *
+ * qkv           [T_tot, C] act, read.
+ * conv_w        [C, 4] float32 (tap 3 weighs the current token).
+ * conv_state    [pool_size, C, 3] float32, read and written in place; only
+ *               the slots of non-empty sequences are accessed.
+ * cache_indices, cu_seqlens: as for gdn_chunk_prefill (device arrays, same
+ *               contract, not checked here).
+ * q, k          [T_tot, Hk, Dk] act, written (channels 0 .. 2*Hk*Dk-1).
+ * v             [T_tot, Hv, Dv] act, written.
+ * Requirements: Dk and Dv multiples of 8; qkv, conv_w, q, k, v 16-byte
+ * aligned; no two of qkv, conv_state, q, k, v overlap.  Two kernels are
+ * enqueued (outputs, then the history update).
+ */
+int gdn_conv_silu(const void* qkv, const float* conv_w, float* conv_state,
+                  int64_t pool_size, const int64_t* cache_indices,
+                  const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk,
+                  int Hv, int Dk, int Dv, void* q, void* k, void* v,
+                  gdn_dtype act, hipStream_t stream);
+
+/*
+ * gdn_gated_rmsnorm - the layer epilogue: per (token, value head), over its
+ * Dv outputs o_j,
+ *     y_j = o_j / sqrt(mean_j(o_j^2) + eps) * gamma[j] * sigmoid(z_j)
+ * Source: regolith `gdn.metal`, header comment and the kernel's output block
+ * (gamma indexed by the column only, shared by every head).
+ * o, z, y       [T_tot, Hv, Dv] act; y may equal o (in place), nothing else
+ *               may overlap.   gamma: [Dv] float32.   eps >= 0.
+ * Requirements: Dv in {32, 64, 128, 256}; o, z, gamma, y 16-byte aligned.
+ */
+int gdn_gated_rmsnorm(const void* o, const void* z, const float* gamma,
+                      float eps, void* y, int64_t T_tot, int Hv, int Dv,
+                      gdn_dtype act, hipStream_t stream);
+
 /* Human-readable name of a gdn_status value (static string, never NULL). */
 const char* gdn_status_string(int status);
 

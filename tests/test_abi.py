@@ -162,3 +162,41 @@ def test_validate_varlen_rejects_before_any_copy(lib):
     assert f(_p(0), _p(A + BIG), 2, 10, 4, None) == NULL
     assert f(_p(A), _p(A + BIG), 0, 0, 4, None) == OK
     assert f(_p(A), _p(A + BIG), 0, 5, 4, None) == SHAPE
+
+
+def conv(lib, x=A, w=A + BIG, hist=A + 2 * BIG, P=4, ci=A + 3 * BIG, cu=A + 4 * BIG, N_s=2, T=100,
+         Hk=2, Hv=4, Dk=128, Dv=128, q=A + 5 * BIG, k=A + 6 * BIG, v=A + 7 * BIG, act=1):
+    return lib.gdn_conv_silu(_p(x), _p(w), _p(hist), P, _p(ci), _p(cu), N_s, T, Hk, Hv, Dk, Dv,
+                             _p(q), _p(k), _p(v), act, None)
+
+
+def test_conv_silu_validation(lib):
+    # every check returns before any HIP call (fake device addresses)
+    assert conv(lib, N_s=-1) == SHAPE
+    assert conv(lib, Hk=0) == SHAPE
+    assert conv(lib, act=7) == DTYPE
+    assert conv(lib, Dk=100) == UNSUP      # channels per head not a multiple of 8
+    assert conv(lib, x=0) == NULL
+    assert conv(lib, hist=0) == NULL
+    assert conv(lib, q=A + 5 * BIG + 2) == ALIGN
+    assert conv(lib, k=A + 5 * BIG + 16) == ALIAS   # k overlaps q
+    assert conv(lib, v=A + 2) == ALIGN
+    assert conv(lib, v=A + 16) == ALIAS             # v overlaps qkv
+    assert conv(lib, N_s=0, x=0) == OK              # nothing to do
+    assert conv(lib, T=0, x=0) == OK
+
+
+def norm(lib, o=A, z=A + BIG, gamma=A + 2 * BIG, eps=1e-6, y=A + 3 * BIG, T=10, Hv=4, Dv=128, act=1):
+    return lib.gdn_gated_rmsnorm(_p(o), _p(z), _p(gamma), ctypes.c_float(eps), _p(y), T, Hv, Dv, act, None)
+
+
+def test_gated_rmsnorm_validation(lib):
+    assert norm(lib, T=-1) == SHAPE
+    assert norm(lib, eps=-1.0) == SHAPE
+    assert norm(lib, act=3) == DTYPE
+    assert norm(lib, Dv=96) == UNSUP
+    assert norm(lib, z=0) == NULL
+    assert norm(lib, gamma=A + 2 * BIG + 4) == ALIGN
+    assert norm(lib, y=A + BIG + 16) == ALIAS       # y overlaps z
+    assert norm(lib, y=A + 16) == ALIAS             # partial overlap with o
+    assert norm(lib, T=0, o=0) == OK
