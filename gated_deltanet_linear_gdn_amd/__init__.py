@@ -75,6 +75,9 @@ def load_library():
                                       + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.gdn_validate_varlen.restype = _i
     lib.gdn_validate_varlen.argtypes = [_vp, _vp, _i, _i64, _i64, _vp]
+    lib.gdn_chunk_prefill_gated.restype = _i
+    lib.gdn_chunk_prefill_gated.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
+                                            + [_f, ctypes.c_uint, _vp, _vp, _f, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.gdn_conv_silu.restype = _i
     lib.gdn_conv_silu.argtypes = [_vp] * 3 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4 + [_vp] * 3 + [_i, _vp]
     lib.gdn_gated_rmsnorm.restype = _i
@@ -214,7 +217,7 @@ def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64, dtype=None
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, chunk=64,
-                      scale=None, l2norm=True, y=None, workspace=None):
+                      scale=None, l2norm=True, y=None, workspace=None, z=None, gamma=None, eps=1e-6):
     """Varlen chunkwise prefill, ``state_pool`` updated in place (see
     ``gdn_chunk_prefill`` in include/gdn.h).
 
@@ -223,7 +226,8 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     [N_s+1] int64 (device tensors, contract not checked here: see
     ``gdn_validate_varlen``); y [T,Hv,Dv] or None; workspace: a uint8 device
     tensor of at least ``gdn_chunk_prefill_workspace`` bytes, or None.
-    Returns y."""
+    With z [T,Hv,Dv] and gamma [Dv] f32 given, y is the gated RMS norm of the
+    output (``gdn_chunk_prefill_gated``).  Returns y."""
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     P = state_pool.shape[0]
@@ -247,10 +251,20 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
     sc = 0.0 if scale is None else float(scale)
-    _call("gdn_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
-          _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
-          GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q), _ptr(workspace),
-          workspace.numel(), _stream())
+    flags = GDN_QK_L2NORM if l2norm else 0
+    if z is None and gamma is None:
+        _call("gdn_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+              _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
+              flags, _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(), _stream())
+        return y
+    if z is None or gamma is None:
+        raise ValueError("the gated output needs both z and gamma")
+    _check("z", z, (T, Hv, Dv), act, dev)
+    _check("gamma", gamma, (Dv,), torch.float32, dev)
+    _call("gdn_chunk_prefill_gated", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+          _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags,
+          _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
+          _stream())
     return y
 
 

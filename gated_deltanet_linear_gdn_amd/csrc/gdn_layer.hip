@@ -41,11 +41,15 @@ template <> struct Vec8<bf16> {
       x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
     }
   }
+  // round to nearest even, two values per v_cvt_pk_bf16_f32
   static __device__ __forceinline__ void store(bf16* p, const float (&x)[8]) {
     uint32_t u[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      u[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 lo = static_cast<__bf16>(x[2 * i]), hi = static_cast<__bf16>(x[2 * i + 1]);
+      u[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
     *reinterpret_cast<uint4*>(p) = uint4{u[0], u[1], u[2], u[3]};
   }
 };
@@ -61,7 +65,39 @@ template <> struct Vec8<float> {
   }
 };
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+// One input row of kVec channels kept as loaded (packed for bf16).
+template <typename T> struct Row8;
+template <> struct Row8<bf16> {
+  uint32_t w[4];
+  __device__ __forceinline__ void load(const bf16* p) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
+  }
+};
+template <> struct Row8<float> {
+  float f[8];
+  __device__ __forceinline__ void load(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ __forceinline__ float get(int i) const { return f[i]; }
+};
+
+// e[k] for a run-time k in 0..2 without indexing a register array.
+__device__ __forceinline__ float pick3(const float (&e)[3], int k) {
+  return k == 0 ? e[0] : (k == 1 ? e[1] : e[2]);
+}
+
+// sigmoid and SiLU on the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32; a few ulp): the elementwise kernels are otherwise bound by the
+// instruction sequences of an exact exp and an IEEE division.  Saturates
+// correctly: a large -x gives exp = inf and a reciprocal of 0.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigmoid_fast(x); }
 
 // Sequence bounds clamped to [0, T): out-of-contract entries never index
 // outside the buffers.
@@ -83,27 +119,47 @@ __device__ __forceinline__ int seq_of(const int64_t* cu, int N_s, int64_t t) {
   return lo;
 }
 
-// Outputs for TT consecutive tokens x kVec channels per thread.  The window
-// w[0..2] holds the three inputs before the current token of the current
-// sequence (history entries before its first token).
+// The 3 history entries of kVec channels: 24 consecutive floats, 16-byte
+// aligned (C is a multiple of 8), as six 16-byte accesses.
+struct Hist8 {
+  float h[kVec][3];
+  __device__ __forceinline__ void load(const float* p) {
+    f32x4 a[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) a[i] = *reinterpret_cast<const f32x4*>(p + 4 * i);
+#pragma unroll
+    for (int e = 0; e < 24; ++e) h[e / 3][e % 3] = a[e / 4][e % 4];
+  }
+  __device__ __forceinline__ void store(float* p) const {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      f32x4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = h[(4 * i + e) / 3][(4 * i + e) % 3];
+      *reinterpret_cast<f32x4*>(p + 4 * i) = a;
+    }
+  }
+};
+
+// Outputs for the TT tokens of one tile x kVec channels per thread.  The
+// tile's input rows and the three before it are loaded up front; window
+// entries before a sequence's first token come from the slot's history.
+// A sequence lying wholly inside the tile has all its history reads in this
+// thread, which then also writes its new history; the history of every
+// other sequence is written by gdn_conv_history_kernel after this kernel.
 template <typename T, int TT>
 __global__ __launch_bounds__(kThreads) void gdn_conv_silu_kernel(
-    const T* __restrict__ x, const float* __restrict__ W, const float* __restrict__ hist,
+    const T* __restrict__ x, const float* __restrict__ W, float* __restrict__ hist,
     int64_t pool_size, const int64_t* __restrict__ cache_indices, const int64_t* __restrict__ cu,
     int N_s, int64_t T_tot, int C, int Cq, int Cv, int gx, T* __restrict__ q, T* __restrict__ k,
     T* __restrict__ v) {
-  const int tile = blockIdx.x / gx;  // TT tokens
+  constexpr int R = TT + 3;  // rows ts-3 .. ts+TT-1
+  const int tile = blockIdx.x / gx;
   const int c0 = ((blockIdx.x - tile * gx) * kThreads + threadIdx.x) * kVec;
   if (c0 >= C) return;
   const int64_t ts = static_cast<int64_t>(tile) * TT;
   const int64_t te = ts + TT < T_tot ? ts + TT : T_tot;
 
-  float w4[kVec][4];
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(W + static_cast<size_t>(c0 + i) * 4);
-    w4[i][0] = a.x; w4[i][1] = a.y; w4[i][2] = a.z; w4[i][3] = a.w;
-  }
   // output row: q, k ([T, Cq]) or v ([T, Cv]) and the channel inside it
   T* orow;
   int oc, ostride;
@@ -114,55 +170,107 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_silu_kernel(
   int s = seq_of(cu, N_s, ts);
   int64_t t0, t1;
   seq_range(cu, s, T_tot, t0, t1);
-  float win[3][kVec];
-  bool fresh = true;  // the window must be (re)built for token t
-  for (int64_t t = ts; t < te; ++t) {
-    while (t >= t1 && s + 1 < N_s) {  // next non-empty sequence holding t
+  float w4[kVec][4];
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(W + static_cast<size_t>(c0 + i) * 4);
+    w4[i][0] = a.x; w4[i][1] = a.y; w4[i][2] = a.z; w4[i][3] = a.w;
+  }
+  if (te == ts + TT && t0 <= ts - 3 && t1 >= te) {
+    // the common case: a full tile inside one sequence whose windows never
+    // reach its history -- straight-line loads, products and stores
+    Row8<T> rr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rr[r].load(x + static_cast<size_t>(ts - 3 + r) * C + c0);
+    // every row load is issued before the first use (loads complete in order)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      float out[kVec];
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        float pre = rr[j].get(i) * w4[i][0];
+        pre = fmaf(rr[j + 1].get(i), w4[i][1], pre);
+        pre = fmaf(rr[j + 2].get(i), w4[i][2], pre);
+        pre = fmaf(rr[j + 3].get(i), w4[i][3], pre);
+        out[i] = silu(pre);
+      }
+      Vec8<T>::store(orow + static_cast<size_t>(ts + j) * ostride + oc, out);
+    }
+    return;
+  }
+  // rows any window of this tile reads start at max(first sequence start, ts-3)
+  const int64_t lo = t0 > ts - 3 ? t0 : ts - 3;
+  Row8<T> rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t p = ts - 3 + r;
+    if (p >= lo && p < te) rows[r].load(x + static_cast<size_t>(p) * C + c0);
+  }
+
+  Hist8 hs;      // the current sequence's old history (when it is needed)
+  int hs_seq = -1;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < TT; ++j) {
+    const int64_t t = ts + j;
+    while (t < te && t >= t1 && s + 1 < N_s) {  // next sequence holding t
       ++s;
       seq_range(cu, s, T_tot, t0, t1);
-      fresh = true;
     }
-    if (t < t0 || t >= t1) continue;  // outside every sequence (contract broken)
-    const int64_t slot = cache_indices[s];
-    const bool slot_ok = slot >= 0 && slot < pool_size;
-    if (fresh) {
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {  // positions t-3+m
-        const int64_t p = t - 3 + m;
-        if (p >= t0) {
-          Vec8<T>::load(x + static_cast<size_t>(p) * C + c0, win[m]);
+    // (no token past the tile, none outside every sequence)
+    if (t < te && t >= t0 && t < t1) {
+      const int64_t slot = cache_indices[s];
+      const bool slot_ok = slot >= 0 && slot < pool_size;
+      const bool need_hist = t - 3 < t0;
+      if (need_hist && hs_seq != s) {
+        if (slot_ok) {
+          hs.load(hist + (static_cast<size_t>(slot) * C + c0) * 3);
         } else {
 #pragma unroll
-          for (int i = 0; i < kVec; ++i)
-            win[m][i] = slot_ok ? hist[(static_cast<size_t>(slot) * C + c0 + i) * 3 + (p - t0 + 3)] : 0.f;
+          for (int i = 0; i < kVec; ++i) hs.h[i][0] = hs.h[i][1] = hs.h[i][2] = 0.f;
         }
+        hs_seq = s;
       }
-      fresh = false;
-    }
-    float cur[kVec], out[kVec];
-    Vec8<T>::load(x + static_cast<size_t>(t) * C + c0, cur);
+      float out[kVec];
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      float pre = win[0][i] * w4[i][0];
-      pre = fmaf(win[1][i], w4[i][1], pre);
-      pre = fmaf(win[2][i], w4[i][2], pre);
-      pre = fmaf(cur[i], w4[i][3], pre);
-      out[i] = silu(pre);
-      win[0][i] = win[1][i];
-      win[1][i] = win[2][i];
-      win[2][i] = cur[i];
+      for (int i = 0; i < kVec; ++i) {
+        float win[3];
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {  // position t-3+m
+          const int64_t p = t - 3 + m;
+          win[m] = p >= t0 ? rows[j + m].get(i) : pick3(hs.h[i], static_cast<int>(p - t0 + 3));
+        }
+        float pre = win[0] * w4[i][0];
+        pre = fmaf(win[1], w4[i][1], pre);
+        pre = fmaf(win[2], w4[i][2], pre);
+        pre = fmaf(rows[j + 3].get(i), w4[i][3], pre);
+        out[i] = silu(pre);
+      }
+      Vec8<T>::store(orow + static_cast<size_t>(t) * ostride + oc, out);
+      // the whole sequence lies in this tile: its new history, from here
+      if (t == t1 - 1 && t0 >= ts && slot_ok) {
+        Hist8 nw;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {  // position t1-3+m = t-2+m
+          const int64_t p = t - 2 + m;
+#pragma unroll
+          for (int i = 0; i < kVec; ++i)
+            nw.h[i][m] = p >= t0 ? rows[j + 1 + m].get(i) : pick3(hs.h[i], static_cast<int>(p - t0 + 3));
+        }
+        nw.store(hist + (static_cast<size_t>(slot) * C + c0) * 3);
+      }
     }
-    Vec8<T>::store(orow + static_cast<size_t>(t) * ostride + oc, out);
   }
 }
 
-// New history per (sequence, channel group): the newest three of (old
-// history, the sequence's inputs).  Runs after the outputs kernel.
+// New history per (sequence, channel group) for the sequences that span
+// more than one tile of TT tokens: the newest three of (old history, the
+// sequence's inputs).  Runs after the outputs kernel.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gdn_conv_history_kernel(
     const T* __restrict__ x, float* __restrict__ hist, int64_t pool_size,
     const int64_t* __restrict__ cache_indices, const int64_t* __restrict__ cu, int N_s,
-    int64_t T_tot, int C, int gx) {
+    int64_t T_tot, int C, int gx, int TT) {
   const int s = blockIdx.x / gx;
   const int c0 = ((blockIdx.x - s * gx) * kThreads + threadIdx.x) * kVec;
   if (c0 >= C || s >= N_s) return;
@@ -170,26 +278,24 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_history_kernel(
   seq_range(cu, s, T_tot, t0, t1);
   const int64_t slot = cache_indices[s];
   if (t1 == t0 || slot < 0 || slot >= pool_size) return;
+  if (t0 / TT == (t1 - 1) / TT) return;  // written by the outputs kernel
   float* h = hist + (static_cast<size_t>(slot) * C + c0) * 3;
-  float old[kVec][3], nw[3][kVec];
-#pragma unroll
-  for (int i = 0; i < kVec; ++i)
-#pragma unroll
-    for (int m = 0; m < 3; ++m) old[i][m] = h[i * 3 + m];
+  Hist8 old, nw;
+  old.load(h);
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const int64_t p = t1 - 3 + m;
     if (p >= t0) {
-      Vec8<T>::load(x + static_cast<size_t>(p) * C + c0, nw[m]);
+      float r[kVec];
+      Vec8<T>::load(x + static_cast<size_t>(p) * C + c0, r);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) nw.h[i][m] = r[i];
     } else {
 #pragma unroll
-      for (int i = 0; i < kVec; ++i) nw[m][i] = old[i][p - t0 + 3];
+      for (int i = 0; i < kVec; ++i) nw.h[i][m] = pick3(old.h[i], static_cast<int>(p - t0 + 3));
     }
   }
-#pragma unroll
-  for (int i = 0; i < kVec; ++i)
-#pragma unroll
-    for (int m = 0; m < 3; ++m) h[i * 3 + m] = nw[m][i];
+  nw.store(h);
 }
 
 template <typename T, int TT>
@@ -206,7 +312,7 @@ int launch_conv_tt(const void* x, const float* W, float* hist, int64_t pool_size
   if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
   hipLaunchKernelGGL((gdn_conv_history_kernel<T>), dim3(static_cast<unsigned>(static_cast<int64_t>(N_s) * gx)),
                      dim3(kThreads), 0, stream, static_cast<const T*>(x), hist, pool_size, ci, cu, N_s, T_tot,
-                     C, gx);
+                     C, gx, TT);
   return launch_status();
 }
 
@@ -217,7 +323,8 @@ int launch_conv(const void* x, const float* W, float* hist, int64_t pool_size, c
   // a few tokens per thread amortise the weight loads; one keeps small
   // (decode-sized) batches spread over the CUs
   if (T_tot >= 8192)
-    return launch_conv_tt<T, 16>(x, W, hist, pool_size, ci, cu, N_s, T_tot, C, Cq, Cv, q, k, v, stream);
+    return launch_conv_tt<T, sizeof(T) == 2 ? 16 : 8>(x, W, hist, pool_size, ci, cu, N_s, T_tot, C, Cq, Cv, q, k,
+                                                       v, stream);
   if (T_tot >= 2048)
     return launch_conv_tt<T, 4>(x, W, hist, pool_size, ci, cu, N_s, T_tot, C, Cq, Cv, q, k, v, stream);
   return launch_conv_tt<T, 1>(x, W, hist, pool_size, ci, cu, N_s, T_tot, C, Cq, Cv, q, k, v, stream);
@@ -225,39 +332,51 @@ int launch_conv(const void* x, const float* W, float* hist, int64_t pool_size, c
 
 // ------------------------------------------------------------ gated RMS norm
 
-// G = Dv/8 lanes per row, 8 values per lane; 64/G rows per wave.
+// G = Dv/8 lanes per row, 8 values per lane; a workgroup takes RPT groups
+// of kThreads/G rows, and each lane issues the loads of its RPT rows before
+// using any of them.
+constexpr int kNormRPT = 4;
+
 template <typename T, int G>
 __global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(
     const T* o, const T* __restrict__ z, const float* __restrict__ gamma, float eps, long rows,
     T* y) {
-  constexpr int RPB = kThreads / G;  // rows per workgroup
+  constexpr int RPB = kThreads / G;  // rows per group
   const int lane_in_row = threadIdx.x % G;
-  const long row = static_cast<long>(blockIdx.x) * RPB + threadIdx.x / G;
-  const bool ok = row < rows;
-  const long r = ok ? row : rows - 1;  // idle lanes repeat the last row (their sums are discarded)
-  const size_t base = static_cast<size_t>(r) * (G * kVec) + lane_in_row * kVec;
-  float ov[kVec], zv[kVec];
-  Vec8<T>::load(o + base, ov);
-  Vec8<T>::load(z + base, zv);
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) ss = fmaf(ov[i], ov[i], ss);
-  ss = group_sum<G>(ss);
-  const float rs = 1.0f / sqrtf(ss / static_cast<float>(G * kVec) + eps);
   const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + lane_in_row * kVec);
   const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + lane_in_row * kVec + 4);
   const float gm[kVec] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-  float out[kVec];
+  float ov[kNormRPT][kVec], zv[kNormRPT][kVec];
+  size_t base[kNormRPT];
+  bool ok[kNormRPT];
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) out[i] = ov[i] * rs * gm[i] * (1.0f / (1.0f + expf(-zv[i])));
-  if (ok) Vec8<T>::store(y + base, out);
+  for (int u = 0; u < kNormRPT; ++u) {
+    const long row = (static_cast<long>(blockIdx.x) * kNormRPT + u) * RPB + threadIdx.x / G;
+    ok[u] = row < rows;
+    const long r = ok[u] ? row : rows - 1;  // idle lanes repeat the last row (not stored)
+    base[u] = static_cast<size_t>(r) * (G * kVec) + lane_in_row * kVec;
+    Vec8<T>::load(o + base[u], ov[u]);
+    Vec8<T>::load(z + base[u], zv[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kNormRPT; ++u) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) ss = fmaf(ov[u][i], ov[u][i], ss);
+    ss = group_sum<G>(ss);
+    const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / static_cast<float>(G * kVec)) + eps);
+    float out[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) out[i] = ov[u][i] * rs * gm[i] * sigmoid_fast(zv[u][i]);
+    if (ok[u]) Vec8<T>::store(y + base[u], out);
+  }
 }
 
 template <typename T, int G>
 int launch_norm_g(const void* o, const void* z, const float* gamma, float eps, long rows, void* y,
                   hipStream_t stream) {
-  constexpr int RPB = kThreads / G;
-  const long blocks = (rows + RPB - 1) / RPB;
+  constexpr long RPW = static_cast<long>(kThreads / G) * kNormRPT;  // rows per workgroup
+  const long blocks = (rows + RPW - 1) / RPW;
   if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
   hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<T, G>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
@@ -304,7 +423,8 @@ extern "C" int gdn_conv_silu(const void* qkv, const float* conv_w, float* conv_s
   if (N_s == 0 || T_tot == 0) return GDN_OK;
   if (!qkv || !conv_w || !conv_state || !cache_indices || !cu_seqlens || !q || !k || !v)
     return GDN_ERR_NULL;
-  if (!aligned16(qkv) || !aligned16(conv_w) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+  if (!aligned16(qkv) || !aligned16(conv_w) || !aligned16(conv_state) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v))
     return GDN_ERR_ALIGN;
   const size_t ab = act_bytes(act);
   const size_t xb = static_cast<size_t>(T_tot) * C64 * ab;

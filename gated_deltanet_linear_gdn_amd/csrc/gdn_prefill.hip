@@ -1110,13 +1110,14 @@ struct StreamTiles {
   };
 };
 
-template <int DK, int CT, int NW, int CW>
+template <int DK, int CT, int NW, int CW, bool GATED = false>
 __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
     int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
-    const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y) {
+    const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y,
+    const bf16* __restrict__ z, const float* __restrict__ gamma, float eps) {
   using Tiles = StreamTiles<DK, CT, NW, CW>;
   using Set = typename Tiles::Set;
   constexpr int BV = Tiles::BV, KP = Tiles::KP, QP = Tiles::QP, VP = Tiles::VP, YP = Tiles::YP,
@@ -1127,6 +1128,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   __shared__ Set setA, setB;
   __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sY[CT * YP];
+  // the gated epilogue's z tile (one element when unused)
+  __shared__ __attribute__((aligned(16))) bf16 sZ[GATED ? CT * BV : 8];
 
   const int nvb = Dv / BV;
   const int s = blockIdx.x / (Hv * nvb);
@@ -1249,11 +1252,58 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   constexpr int PIECES = CT * SPR / NW;    // per wave, a multiple of 64
   constexpr int NYS = PIECES / 64;
   static_assert(PIECES % 64 == 0, "y pieces");
+  auto y_off = [&](int it) __attribute__((always_inline)) -> uint32_t {
+    const int pc = w * PIECES + it * 64 + lane;
+    const int row = pc / SPR, col = (pc - row * SPR) * 8;
+    return static_cast<uint32_t>(row) * vstride + col * 2;
+  };
+  // GATED: y = o / sqrt(mean(o^2) + eps) * gamma * sigmoid(z) over the
+  // head's BV = Dv columns, i.e. over the 16 lanes that store one row.  Each
+  // wave copies the z pieces of its own y pieces into sZ when the step
+  // starts (so no other wave is involved); gamma for the lane's 8 columns is
+  // loaded once.
+  static_assert(!GATED || SPR == 16, "the gated epilogue needs one 128-column head per workgroup");
+  float gm[8];
+  if constexpr (GATED) {
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + (lane % SPR) * 8);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + (lane % SPR) * 8 + 4);
+    gm[0] = g0.x; gm[1] = g0.y; gm[2] = g0.z; gm[3] = g0.w;
+    gm[4] = g1.x; gm[5] = g1.y; gm[6] = g1.z; gm[7] = g1.w;
+  }
   auto store_y_one = [&](__amdgpu_buffer_rsrc_t yr, int it) __attribute__((always_inline)) {
     const int pc = w * PIECES + it * 64 + lane;
     const int row = pc / SPR, col = (pc - row * SPR) * 8;
-    const u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
-    __builtin_amdgcn_raw_buffer_store_b128(d, yr, static_cast<uint32_t>(row) * vstride + col * 2, 0, 0);
+    u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
+    if constexpr (GATED) {
+      float o8[8], ss = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        o8[2 * p] = __uint_as_float(d[p] << 16);
+        o8[2 * p + 1] = __uint_as_float(d[p] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(o8[i], o8[i], ss);
+      ss = group_sum<16>(ss);
+      const float rs = __builtin_amdgcn_rsqf(ss * (1.0f / BV) + eps);
+      const u32x4 zv = *reinterpret_cast<const u32x4*>(sZ + pc * 8);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float z0 = __uint_as_float(zv[p] << 16), z1 = __uint_as_float(zv[p] & 0xffff0000u);
+        // sigmoid on the hardware exponential and reciprocal (a few ulp)
+        d[p] = pk(o8[2 * p] * rs * gm[2 * p] * __builtin_amdgcn_rcpf(1.0f + __expf(-z0)),
+                  o8[2 * p + 1] * rs * gm[2 * p + 1] * __builtin_amdgcn_rcpf(1.0f + __expf(-z1)));
+      }
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(d, yr, y_off(it), 0, 0);
+  };
+  // z pieces of chunk ci -> sZ slot pc (one 1 KiB copy per y instruction).
+  // The reads wait with vmcnt(N): at most N of this wave's later loads
+  // outstanding (loads complete in order), which covers z without waiting
+  // for the copies issued after it.
+  auto z_load = [&](int ci) __attribute__((always_inline)) {
+    const i32x4 zr = make_rsrc(z + vy_off(ci), vy_bytes(ci));
+#pragma unroll
+    for (int it = 0; it < NYS; ++it) dma16(zr, lds_addr(sZ) + (w * PIECES + it * 64) * 16, y_off(it));
   };
 
   // Every operand fragment read from LDS feeds the CW column tiles of the
@@ -1261,6 +1311,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
     const float* F = reinterpret_cast<const float*>(c.F);
     const Rsrc rn = set_rsrc(ci + 1);
+    if constexpr (GATED) {
+      if (ci > 0) z_load(ci - 1);
+    }
 
     // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
     f32x4 X[CW][MT], Y[CW][MT];
@@ -1370,6 +1423,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         }
       }
       // chunk ci-1's y, spread over the update
+      if constexpr (GATED) {
+        // every wave issued at least these copies after its z loads
+        constexpr int VMZ = Tiles_::Kcopy::MIN + Tiles_::Fcopy::MIN + 3 * Tiles_::Tcopy::MIN +
+                            Tiles_::Qcopy::MIN + Tiles_::Vcopy::MIN;
+        static_assert(VMZ < 64, "z wait");
+        if (m == 0 && ci > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VMZ) : "memory");
+      }
       if (m % (DT / NYS) == 0 && m / (DT / NYS) < NYS && ci > 0) store_y_one(yr, m / (DT / NYS));
     }
     handover<0>();  // every copy of chunk ci+1 landed; this chunk's set and sY are free
@@ -1391,6 +1451,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   // (every copy has landed: each step ends waiting for all of them)
   lds_handover();
   {
+    if constexpr (GATED) {
+      z_load(nch - 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(nch - 1), vy_bytes(nch - 1));
 #pragma unroll
     for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
@@ -1437,11 +1501,18 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   return L;
 }
 
+// The optional gated RMS norm of y (gdn_chunk_prefill_gated).
+struct Epilogue {
+  const void* z;
+  const float* gamma;
+  float eps;
+};
+
 template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
-               char* ws, const Layout& L, hipStream_t stream) {
+               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
   int* scs = reinterpret_cast<int*>(ws + L.scs);
   bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
   bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
@@ -1458,10 +1529,22 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
     hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
                        N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac);
+    // the epilogue is fused when one workgroup covers a whole 128-column head
+    if constexpr (NW == 8 && CW == 1) {
+      if (epi && Dv == 128) {
+        hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW, true>), dim3(static_cast<unsigned>(main_blocks)),
+                           dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                           static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
+                           chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
+                           static_cast<const bf16*>(epi->z), epi->gamma, epi->eps);
+        return launch_status();
+      }
+    }
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
-                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y));
+                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
+                       static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
   } else {
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
@@ -1471,14 +1554,19 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                        static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
                        Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, fac, static_cast<T*>(y));
   }
-  return launch_status();
+  if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
+  // otherwise the separate norm kernel, in place on y
+  if (epi)
+    return gated_rmsnorm_launch(y, epi->z, epi->gamma, epi->eps, static_cast<long>(T_tot) * Hv, Dv, y,
+                                std::is_same<T, bf16>::value ? GDN_BF16 : GDN_F32, stream);
+  return GDN_OK;
 }
 
 template <typename T, int DK, int CT>
 int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
   // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
   // workgroup so each chunk operand is fetched once per 128 columns.  fp32
   // activations: the register-fragment kernel, 64 (four waves, up to 512
@@ -1486,25 +1574,25 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
       return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                         chunk, scale, l2norm, y, ws, L, stream);
+                                         chunk, scale, l2norm, y, ws, L, epi, stream);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                    chunk, scale, l2norm, y, ws, L, stream);
+                                    chunk, scale, l2norm, y, ws, L, epi, stream);
   return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                  chunk, scale, l2norm, y, ws, L, stream);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream);
 }
 
 template <typename T, int DK>
 int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, hipStream_t stream) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
   if (CT == 32)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, stream);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream);
   return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                chunk, scale, l2norm, y, ws, L, stream);
+                                chunk, scale, l2norm, y, ws, L, epi, stream);
 }
 
 template <typename T>
@@ -1512,11 +1600,11 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
                 const float* g, const float* beta, float* pool, int64_t pool_size,
                 const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
                 int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
-                hipStream_t stream) {
+                const Epilogue* epi, hipStream_t stream) {
   switch (Dk) {
-    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
-    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
-    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, stream);
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -1535,13 +1623,14 @@ extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, in
   return gdn::layout(T_tot, N_s, Hv, chunk, act == GDN_BF16).total;
 }
 
-extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
-                                 const float* beta, float* state_pool, int64_t pool_size,
-                                 const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
-                                 int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk,
-                                 float scale, unsigned flags, void* y, gdn_dtype act,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  using namespace gdn;
+namespace gdn {
+namespace {
+
+int chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  float* state_pool, int64_t pool_size, const int64_t* cache_indices,
+                  const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
+                  int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
+                  size_t workspace_bytes, const Epilogue* epi, hipStream_t stream) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
@@ -1565,15 +1654,55 @@ extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, co
   if (overlaps(y, y_bytes, state_pool, pool_bytes) || overlaps(workspace, L.total, state_pool, pool_bytes) ||
       overlaps(workspace, L.total, y, y_bytes))
     return GDN_ERR_ALIAS;
+  if (epi && (overlaps(epi->z, y_bytes, state_pool, pool_bytes) || overlaps(epi->z, y_bytes, workspace, L.total)))
+    return GDN_ERR_ALIAS;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(Dk));
   const int l2 = (flags & GDN_QK_L2NORM) ? 1 : 0;
   const int CT = chunk_tile(chunk);
   char* ws = static_cast<char*>(workspace);
   if (act == GDN_BF16)
     return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, stream);
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream);
   return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, stream);
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream);
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, float* state_pool, int64_t pool_size,
+                                 const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
+                                 int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk,
+                                 float scale, unsigned flags, void* y, gdn_dtype act,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return gdn::chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s,
+                            T_tot, Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, workspace_bytes,
+                            nullptr, stream);
+}
+
+extern "C" int gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g,
+                                       const float* beta, float* state_pool, int64_t pool_size,
+                                       const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
+                                       int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk,
+                                       float scale, unsigned flags, const void* z, const float* gamma,
+                                       float eps, void* y, gdn_dtype act, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdn;
+  if (N_s < 0 || T_tot < 0 || Hv <= 0 || Dv <= 0) return GDN_ERR_SHAPE;
+  if (!(eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if (!pow2_head(Dv)) return GDN_ERR_UNSUPPORTED;
+  if (N_s > 0 && T_tot > 0) {
+    if (!z || !gamma) return GDN_ERR_NULL;
+    if (!aligned16(z) || !aligned16(gamma)) return GDN_ERR_ALIGN;
+    if (is_act(act)) {
+      const size_t nb = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
+      if (y && overlaps(z, nb, y, nb)) return GDN_ERR_ALIAS;
+    }
+  }
+  const Epilogue epi{z, gamma, eps};
+  return chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot, Hk,
+                       Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, workspace_bytes, &epi, stream);
 }
 
 extern "C" int gdn_validate_varlen(const int64_t* cu_seqlens, const int64_t* cache_indices, int N_s,

@@ -178,6 +178,30 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill_gated - gdn_chunk_prefill followed by the layer's gated
+ * RMS norm of every output row (gdn_gated_rmsnorm below): y receives
+ *     o_j / sqrt(mean_j(o_j^2) + eps) * gamma[j] * sigmoid(z_j)
+ * per (token, value head), o being what gdn_chunk_prefill writes.  Source:
+ * regolith `gdn.metal` output block, fused into the recurrence's output as
+ * that kernel does.  With bf16 activations and Dv == 128 the norm runs inside
+ * the chunk loop's store of y (o is not written to memory); otherwise the
+ * norm kernel runs afterwards on y in place (o rounded to act first).
+ * z [T_tot, Hv, Dv] act; gamma [Dv] float32; eps >= 0.  Requirements: those
+ * of gdn_chunk_prefill, Dv in {32, 64, 128, 256}, z and gamma 16-byte
+ * aligned, z overlapping none of y, state_pool and the workspace.
+ */
+int gdn_chunk_prefill_gated(const void* q, const void* k, const void* v,
+                            const float* g, const float* beta,
+                            float* state_pool, int64_t pool_size,
+                            const int64_t* cache_indices,
+                            const int64_t* cu_seqlens, int N_s, int64_t T_tot,
+                            int Hk, int Hv, int Dk, int Dv, int chunk,
+                            float scale, unsigned flags, const void* z,
+                            const float* gamma, float eps, void* y,
+                            gdn_dtype act, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * gdn_validate_varlen - debug/test helper: copies cu_seqlens and
  * cache_indices to the host (synchronising `stream`) and checks the
  * gdn_chunk_prefill contract above.  GDN_OK, or GDN_ERR_SHAPE if violated.
@@ -209,9 +233,9 @@ int gdn_validate_varlen(const int64_t* cu_seqlens,
  *               contract, not checked here).
  * q, k          [T_tot, Hk, Dk] act, written (channels 0 .. 2*Hk*Dk-1).
  * v             [T_tot, Hv, Dv] act, written.
- * Requirements: Dk and Dv multiples of 8; qkv, conv_w, q, k, v 16-byte
- * aligned; no two of qkv, conv_state, q, k, v overlap.  Two kernels are
- * enqueued (outputs, then the history update).
+ * Requirements: Dk and Dv multiples of 8; qkv, conv_w, conv_state, q, k, v
+ * 16-byte aligned; no two of qkv, conv_state, q, k, v overlap.  Two kernels
+ * are enqueued (outputs, then the history update of the longer sequences).
  */
 int gdn_conv_silu(const void* qkv, const float* conv_w, float* conv_state,
                   int64_t pool_size, const int64_t* cache_indices,

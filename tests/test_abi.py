@@ -200,3 +200,20 @@ def test_gated_rmsnorm_validation(lib):
     assert norm(lib, y=A + BIG + 16) == ALIAS       # y overlaps z
     assert norm(lib, y=A + 16) == ALIAS             # partial overlap with o
     assert norm(lib, T=0, o=0) == OK
+
+
+def test_gated_prefill_validation(lib):
+    def gated(z=A + 10 * BIG, gamma=A + 11 * BIG, eps=1e-6, Dv=128, y=A + 8 * BIG, N_s=2, T=100):
+        ws = lib.gdn_chunk_prefill_workspace(T, N_s, 2, 4, 128, Dv, 64, 1)
+        return lib.gdn_chunk_prefill_gated(
+            _p(A), _p(A + BIG), _p(A + 2 * BIG), _p(A + 3 * BIG), _p(A + 4 * BIG), _p(A + 5 * BIG), 4,
+            _p(A + 6 * BIG), _p(A + 7 * BIG), N_s, T, 2, 4, 128, Dv, 64, ctypes.c_float(0.0), 1,
+            _p(z), _p(gamma), ctypes.c_float(eps), _p(y), 1, _p(A + 9 * BIG), ws, None)
+    assert gated(eps=-1.0) == SHAPE
+    assert gated(Dv=96) == UNSUP
+    assert gated(z=0) == NULL
+    assert gated(gamma=0) == NULL
+    assert gated(z=A + 10 * BIG + 8) == ALIGN
+    assert gated(z=A + 8 * BIG + 16) == ALIAS        # z overlaps y
+    assert gated(z=A + 5 * BIG + 64) == ALIAS        # z overlaps the state pool
+    assert gated(N_s=0, z=0) == OK

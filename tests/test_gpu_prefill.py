@@ -252,3 +252,48 @@ def test_varlen_prefill_workload_sampled():
     untouched = sorted(set(range(P)) - set(int(x) for x in inp["cache_indices"]))
     for slot in untouched:
         assert np.array_equal(to_np(pool[slot]).astype(np.float32), pool0[slot])
+
+
+GATED_CASES = [
+    # lengths, Hk, Hv, Dk, Dv, chunk, act   (bf16 with Dv = 128: norm fused in the chunk loop)
+    ([1, 64, 130, 0, 77], 2, 4, 128, 128, 64, "bf16"),
+    ([90, 33], 1, 2, 64, 128, 32, "bf16"),
+    ([70, 5], 1, 2, 128, 256, 64, "bf16"),     # two workgroups per head: separate norm kernel
+    ([40, 9], 1, 2, 64, 64, 16, "bf16"),
+    ([45, 16], 1, 1, 64, 32, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("lengths,Hk,Hv,Dk,Dv,chunk,act", GATED_CASES)
+def test_gated_prefill_parity(lengths, Hk, Hv, Dk, Dv, chunk, act):
+    """y of gdn_chunk_prefill_gated equals the oracle's prefill output put
+    through the oracle's gated RMS norm; the pool is bitwise that of the
+    ungated call."""
+    rng = np.random.default_rng(7 * sum(lengths) + Dv)
+    P = len(lengths) + 2
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=4)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P, act=act)
+    T = int(sum(lengths))
+    d = DT[act]
+    z = torch.from_numpy(rng.standard_normal((T, Hv, Dv)).astype(np.float32)).to(d)
+    gam = torch.from_numpy((1.0 + 0.2 * rng.standard_normal(Dv)).astype(np.float32))
+    pool_plain, _ = _run_gpu(inp, pool0, chunk, act)
+    a, b = to_dev(inp["a"], d, DEV), to_dev(inp["b"], d, DEV)
+    g, beta = gdn.gdn_prefill_gates(a, b, to_dev(inp["A_log"], torch.float32, DEV),
+                                    to_dev(inp["dt_bias"], torch.float32, DEV))
+    pool = to_dev(pool0, torch.float32, DEV)
+    y = torch.full((T, Hv, Dv), float("nan"), dtype=d, device=DEV)
+    gdn.gdn_chunk_prefill(to_dev(inp["q"], d, DEV), to_dev(inp["k"], d, DEV), to_dev(inp["v"], d, DEV),
+                          g, beta, pool, to_dev(inp["cache_indices"], torch.int64, DEV),
+                          to_dev(inp["cu_seqlens"], torch.int64, DEV), chunk=chunk, y=y,
+                          z=z.to(DEV), gamma=gam.to(DEV), eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool_plain)
+    P_ref, o_ref = _run_oracle(inp, pool0)
+    y_ref = oracle.gated_rmsnorm(o_ref, z.to(torch.float32).numpy(), gam.numpy(), eps=1e-6)
+    yv = to_np(y)
+    assert not np.isnan(yv).any()
+    if act == "f32":
+        assert maxrel(yv, y_ref) <= 1e-3
+    else:
+        assert relF(yv, y_ref) <= 2e-2
