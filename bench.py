@@ -218,6 +218,67 @@ def bench_prefill(steps, warmup, device):
                 shape=dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, chunk=C, pool=P))
 
 
+def bench_layer(steps, warmup, device):
+    """The layer steps around the recurrence at the varlen prefill workload
+    (and the decode batch for the conv): conv + SiLU prologue, the gated RMS
+    norm epilogue on its own, and the prefill with the norm fused into its
+    output against prefill followed by the norm kernel."""
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.PREFILL_VARLEN
+    Hk, Hv, Dk, Dv, P, C = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"], c["chunk"]
+    rng = np.random.default_rng(0)
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    T = int(inp["cu_seqlens"][-1])
+    lay = synth.layer_inputs(rng, T, Hk, Hv, Dk, Dv, P)
+    bf = torch.bfloat16
+    ci = _dev(inp["cache_indices"], torch.int64, device)
+    cu = _dev(inp["cu_seqlens"], torch.int64, device)
+    qkv = _dev(lay["qkv"], bf, device)
+    w = _dev(lay["conv_w"], torch.float32, device)
+    hist = _dev(lay["conv_state"], torch.float32, device)
+    z = _dev(lay["z"], bf, device)
+    gam = _dev(lay["gamma"], torch.float32, device)
+    q = torch.empty((T, Hk, Dk), dtype=bf, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty((T, Hv, Dv), dtype=bf, device=device)
+    a, b = _dev(inp["a"], bf, device), _dev(inp["b"], bf, device)
+    g, beta = gdn.gdn_prefill_gates(a, b, _dev(inp["A_log"], torch.float32, device),
+                                    _dev(inp["dt_bias"], torch.float32, device))
+    pool = torch.zeros((P, Hv, Dv, Dk), dtype=torch.float32, device=device)
+    y = torch.empty((T, Hv, Dv), dtype=bf, device=device)
+    ws = torch.empty(gdn.gdn_chunk_prefill_workspace(T, len(lengths), Hk, Hv, Dk, Dv, C),
+                     dtype=torch.uint8, device=device)
+    gdn.gdn_conv_silu(qkv, w, hist, ci, cu, Hk, Hv, Dk, Dv, q, k, v)  # real q/k/v for the prefill
+    Cch = 2 * Hk * Dk + Hv * Dv
+    conv_sec = _timed(lambda i: gdn.gdn_conv_silu(qkv, w, hist, ci, cu, Hk, Hv, Dk, Dv, q, k, v),
+                      steps, warmup)
+    norm_sec = _timed(lambda i: gdn.gdn_gated_rmsnorm(y, z, gam, y=y), steps, warmup)
+    plain_sec = _timed(lambda i: gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y,
+                                                       workspace=ws), steps, warmup)
+    fused_sec = _timed(lambda i: gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y,
+                                                       workspace=ws, z=z, gamma=gam), steps, warmup)
+    # decode step of the conv: one token for each of 256 sequences
+    B = synth.DECODE_B256["B"]
+    qkv_d = _dev(synth.layer_inputs(rng, B, Hk, Hv, Dk, Dv, 1)["qkv"], bf, device)
+    hist_d = torch.zeros((B, Cch, 3), dtype=torch.float32, device=device)
+    ci_d = torch.arange(B, dtype=torch.int64, device=device)
+    cu_d = torch.arange(B + 1, dtype=torch.int64, device=device)
+    qd = torch.empty((B, Hk, Dk), dtype=bf, device=device)
+    kd = torch.empty_like(qd)
+    vd = torch.empty((B, Hv, Dv), dtype=bf, device=device)
+    convd_sec = _timed(lambda i: gdn.gdn_conv_silu(qkv_d, w, hist_d, ci_d, cu_d, Hk, Hv, Dk, Dv, qd, kd, vd),
+                       steps, warmup)
+    conv_bytes = 2 * T * Cch * 2 + len(lengths) * Cch * 3 * 4 * 2 + Cch * 16
+    convd_bytes = 2 * B * Cch * 2 + B * Cch * 3 * 4 * 2 + Cch * 16
+    norm_bytes = 3 * T * Hv * Dv * 2 + Dv * 4
+    return dict(T=T, conv_sec=conv_sec, conv_bytes=conv_bytes, convd_sec=convd_sec,
+                convd_bytes=convd_bytes, norm_sec=norm_sec, norm_bytes=norm_bytes,
+                plain_sec=plain_sec, fused_sec=fused_sec)
+
+
 def bench_comba_hbm(steps, warmup, device, B=896, H=16, K=128, V=128):
     """Comba at one of the KBench measure shapes (0.94 GB state per copy,
     well beyond the 256 MB MALL)."""
@@ -314,6 +375,7 @@ def main():
     com = bench_comba(args.steps, args.warmup, device)
     com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
+    lay = bench_layer(max(5, args.steps // 50), 3, device)
     copy_gbps = bench_copy(device)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
@@ -356,6 +418,18 @@ def main():
                     "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
                     "min_bytes": pre["min_bytes"],
                     "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+        "layer": {"workload": "prologue gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per "
+                              "slot) and epilogue gdn_gated_rmsnorm around the varlen prefill; conv "
+                              "also as a decode step of 256 sequences",
+                  "conv_us": round(lay["conv_sec"] * 1e6, 2),
+                  "conv_GBps": round(lay["conv_bytes"] / lay["conv_sec"] / 1e9, 1),
+                  "conv_decode_B256_us": round(lay["convd_sec"] * 1e6, 2),
+                  "conv_decode_B256_GBps": round(lay["convd_bytes"] / lay["convd_sec"] / 1e9, 1),
+                  "norm_us": round(lay["norm_sec"] * 1e6, 2),
+                  "norm_GBps": round(lay["norm_bytes"] / lay["norm_sec"] / 1e9, 1),
+                  "prefill_us": round(lay["plain_sec"] * 1e6, 2),
+                  "prefill_gated_fused_us": round(lay["fused_sec"] * 1e6, 2),
+                  "prefill_then_norm_us": round((lay["plain_sec"] + lay["norm_sec"]) * 1e6, 2)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

@@ -101,6 +101,21 @@ def prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size, act="bf16"):
                 cache_indices=cache_indices, cu_seqlens=cu_from_lengths(lengths))
 
 
+def layer_inputs(rng, T, Hk, Hv, Dk, Dv, pool_size, act="bf16"):
+    """Inputs of the layer steps around the recurrence: qkv [T, C] with
+    C = 2*Hk*Dk + Hv*Dv channels ([q heads | k heads | v heads]) ~ N(0,1);
+    conv weights [C, 4] ~ N(0, 0.5^2) (fp32); conv history [pool, C, 3] ~
+    N(0,1) (fp32); z [T, Hv, Dv] ~ N(0,1); gamma [Dv] ~ 1 + N(0, 0.1^2)
+    (fp32).  No trained weights: only the shapes and scales matter here."""
+    C = 2 * Hk * Dk + Hv * Dv
+    qkv = _act(rng.standard_normal((T, C), dtype=np.float32), act)
+    conv_w = (0.5 * rng.standard_normal((C, 4), dtype=np.float32)).astype(np.float32)
+    conv_state = rng.standard_normal((pool_size, C, 3), dtype=np.float32)
+    z = _act(rng.standard_normal((T, Hv, Dv), dtype=np.float32), act)
+    gamma = (1.0 + 0.1 * rng.standard_normal(Dv, dtype=np.float32)).astype(np.float32)
+    return dict(qkv=qkv, conv_w=conv_w, conv_state=conv_state, z=z, gamma=gamma)
+
+
 # Workload shapes (seed 0 for each).
 TINY = dict(B=2, Hk=2, Hv=4, Dk=32, Dv=32, act="f32", prefill_len=16, chunk=8)
 DECODE_B64 = dict(B=64, Hk=16, Hv=48, Dk=128, Dv=128, act="bf16")
