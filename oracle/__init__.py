@@ -19,6 +19,8 @@ Functions (each cites the page it follows in ``gdn_oracle.c``):
                                                         (regolith gdn.metal conv block)
   gated_rmsnorm y = o rsqrt(mean(o^2) + eps) gamma sigmoid(z) per (token, head)
                                                         (regolith gdn.metal output block)
+  gdn_window    T decode tokens per sequence, committing the state after the
+                first k (metaltile mt_gated_delta_chunk; regolith commit rule)
 """
 from __future__ import annotations
 
@@ -192,3 +194,25 @@ def gated_rmsnorm(o, z, gamma, eps=1e-6):
     y = np.zeros_like(o)
     lib.oracle_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(gamma), float(eps), T, Hv, Dv, _ptr(y))
     return y
+
+
+def gdn_window(state, q, k, v, g, beta, commit=None):
+    """A decode window of T tokens per sequence: the pinned single step
+    (``gdn_step``) applied token by token.  q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv];
+    g, beta [B,T,Hv].  Returns (state after the first ``commit`` tokens,
+    y [B,T,Hv,Dv]); commit None means all T, 0 returns the state unchanged
+    (a verify window), in float64."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    T = q.shape[1]
+    commit = T if commit is None else int(commit)
+    if not 0 <= commit <= T:
+        raise ValueError("commit must be in [0, T]")
+    S = _f64(state).copy()
+    kept = S.copy()
+    ys = []
+    for t in range(T):
+        S, y = gdn_step(S, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t])
+        ys.append(y)
+        if t + 1 == commit:
+            kept = S.copy()
+    return kept, np.stack(ys, axis=1)

@@ -556,3 +556,54 @@ def test_gated_rmsnorm_gate_and_eps():
     # gives 1 / sqrt(1 + 3) = 1/2 exactly
     y1 = oracle.gated_rmsnorm(np.ones((1, 1, 8)), np.full((1, 1, 8), 60.0), np.ones(8), eps=3.0)
     np.testing.assert_array_equal(y1, 0.5)
+
+
+# ------------------------------------------------ multi-token decode windows
+
+
+def _window_inputs(rng, B, T, Hk, Hv, Dk, Dv):
+    toks = [synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act="f32") for _ in range(T)]
+    return {n: np.stack([t[n] for t in toks], axis=1) for n in toks[0]}
+
+
+def test_window_verify_keeps_the_state_and_commit_prefixes():
+    """A verify window (commit 0) returns the input state and the same
+    outputs as a committed one; committing after k tokens gives the state of
+    a k-token window; outputs are causal (a token's y is the same in every
+    window that contains it)."""
+    rng = np.random.default_rng(12)
+    B, T, Hk, Hv, Dk, Dv = 2, 5, 1, 2, 32, 16
+    S0 = 0.3 * rng.standard_normal((B, Hv, Dv, Dk))
+    w = _window_inputs(rng, B, T, Hk, Hv, Dk, Dv)
+    S_all, y_all = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"])
+    S_ver, y_ver = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"], commit=0)
+    np.testing.assert_array_equal(S_ver, S0)
+    np.testing.assert_array_equal(y_ver, y_all)
+    for kk in range(1, T + 1):
+        S_k, y_k = oracle.gdn_window(S0, *(w[n][:, :kk] for n in ("q", "k", "v", "g", "beta")))
+        S_c, _ = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"], commit=kk)
+        np.testing.assert_array_equal(S_c, S_k)
+        np.testing.assert_array_equal(y_k, y_all[:, :kk])
+    assert not np.allclose(S_all, S0)
+
+
+def test_window_closed_form_unit_keys():
+    """beta = 1, log-gate 0 and orthonormal keys across the window: token t
+    overwrites the state along k_t with v_t, so after the window S k_t = v_t
+    for every t, and y_t = S_t q_t with S_t built the same way."""
+    rng = np.random.default_rng(13)
+    B, T, Hk, Hv, Dk, Dv = 1, 4, 1, 1, 16, 8
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    k = Qm[:, :T].T.reshape(B, T, Hk, Dk)
+    v = rng.standard_normal((B, T, Hv, Dv))
+    q = rng.standard_normal((B, T, Hk, Dk))
+    S0 = rng.standard_normal((B, Hv, Dv, Dk))
+    S, y = oracle.gdn_window(S0, q, k, v, np.zeros((B, T, Hv)), np.ones((B, T, Hv)))
+    for t in range(T):
+        np.testing.assert_allclose(S[0, 0] @ k[0, t, 0], v[0, t, 0], atol=1e-12)
+    # the state after t tokens: S0 with its component along k_0..k_t replaced
+    St = S0[0, 0].copy()
+    for t in range(T):
+        kt = k[0, t, 0]
+        St = St - np.outer(St @ kt, kt) + np.outer(v[0, t, 0], kt)
+        np.testing.assert_allclose(y[0, t, 0], St @ q[0, t, 0], atol=1e-12)
