@@ -64,6 +64,8 @@ def load_library():
     lib.gdn_status_string.argtypes = [_i]
     lib.gdn_decode_step.restype = _i
     lib.gdn_decode_step.argtypes = [_vp] * 8 + [_i] * 6 + [_vp]
+    lib.gdn_decode_window.restype = _i
+    lib.gdn_decode_window.argtypes = [_vp] * 8 + [_i] * 8 + [_vp]
     lib.comba_decode_step.restype = _i
     lib.comba_decode_step.argtypes = [_vp] * 9 + [_i] * 4 + [_f, _i, _vp]
     lib.gdn_prefill_gates.restype = _i
@@ -154,6 +156,36 @@ def gdn_decode_step(state_in, state_out, q, k, v, g, beta, y=None):
     _check("y", y, (B, Hv, Dv), act, dev)
     _call("gdn_decode_step", _ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
           _ptr(g), _ptr(beta), _ptr(y), B, Hk, Hv, Dk, Dv, _act_of(q), _stream())
+    return state_out, y
+
+
+def gdn_decode_window(state_in, state_out, q, k, v, g, beta, commit=None, y=None):
+    """T decode tokens per sequence with the state kept on chip (see
+    ``gdn_decode_window`` in include/gdn.h).  q,k [B,T,Hk,Dk]; v [B,T,Hv,Dv];
+    g [B,T,Hv] f32; beta [B,T,Hv]; state_in [B,Hv,Dv,Dk] f32.  state_out
+    receives the state after the first ``commit`` tokens (None: all T; 0: a
+    verify window that writes no state; state_out None allocates one, or
+    pass state_in for in place).  Returns (state_out, y [B,T,Hv,Dv])."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev, act = q.device, q.dtype
+    commit = T if commit is None else int(commit)
+    if state_out is None and commit > 0:
+        state_out = torch.empty_like(state_in)
+    if y is None:
+        y = torch.empty((B, T, Hv, Dv), dtype=act, device=dev)
+    _check("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    if state_out is not None:
+        _check("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("q", q, (B, T, Hk, Dk), act, dev)
+    _check("k", k, (B, T, Hk, Dk), act, dev)
+    _check("v", v, (B, T, Hv, Dv), act, dev)
+    _check("g", g, (B, T, Hv), torch.float32, dev)
+    _check("beta", beta, (B, T, Hv), act, dev)
+    _check("y", y, (B, T, Hv, Dv), act, dev)
+    out_ptr = _ptr(state_out) if state_out is not None else ctypes.c_void_p(0)
+    _call("gdn_decode_window", _ptr(state_in), out_ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(y), B, T, Hk, Hv, Dk, Dv, commit, _act_of(q), _stream())
     return state_out, y
 
 

@@ -135,8 +135,186 @@ int launch(const float* state_in, float* state_out, const void* q, const void* k
   return GDN_ERR_UNSUPPORTED;
 }
 
+// ------------------------------------------------------------ decode windows
+//
+// T tokens per sequence in one pass (metaltile `mt_gated_delta_chunk`: the
+// state stays in registers across an inner token loop; regolith commit
+// rule): the same per-token arithmetic as gdn_decode_kernel, token after
+// token, on the lane's two state rows.  Every token's activations are
+// loaded before the state (kept as loaded, converted on use); the state
+// after the first `commit` tokens is kept in registers and stored at the
+// end (commit 0: a verify window, no state write).  The state crosses HBM
+// once per window instead of once per token.
+
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ f32x4 f() const {
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+};
+template <> struct Raw4<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ f32x4 f() const { return w; }
+};
+
+template <int DK, int NV, bool FULL, typename T, int NT>
+__global__ __launch_bounds__(kThreads) void gdn_window_kernel(
+    const float* state_in, float* state_out, const T* __restrict__ q,
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
+    const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
+    int parts_per_slice, int Tn, int commit) {
+  constexpr int LPR = DK / 4;            // lanes per row
+  constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
+  constexpr int ROWS = RPS * NV;         // rows per workgroup
+
+  const int slice = blockIdx.x / parts_per_slice;  // n = b * Hv + hv
+  const int part = blockIdx.x - slice * parts_per_slice;
+  const int b = slice / Hv;
+  const int hv = slice - b * Hv;
+  const int hk = hv / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int c4 = tid % LPR;
+  const int row0 = part * ROWS + tid / LPR;
+  auto rowc = [&](int n) { return FULL ? row0 + n * RPS : min(row0 + n * RPS, Dv - 1); };
+
+  const size_t slice_off = static_cast<size_t>(slice) * Dv * DK;
+  const float* sin = state_in + slice_off + c4 * 4;
+  float* sout = state_out + slice_off + c4 * 4;
+
+  // every token's activations first (token t of sequence b is row b*Tn + t)
+  Raw4<T> kr[NT], qr[NT];
+  float vv[NT][NV], graw[NT], bt[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < Tn) {
+      const size_t bt_ = static_cast<size_t>(b) * Tn + t;
+      const size_t qk_off = (bt_ * Hk + hk) * DK + c4 * 4;
+      kr[t].load(k + qk_off);
+      qr[t].load(q + qk_off);
+      graw[t] = g[bt_ * Hv + hv];
+      bt[t] = Act<T>::load(beta + bt_ * Hv + hv);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) vv[t][n] = Act<T>::load(v + (bt_ * Hv + hv) * Dv + rowc(n));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 s[NV], kept[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) s[n] = load_stream(sin + static_cast<size_t>(rowc(n)) * DK);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NV; ++n) kept[n] = s[n];
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t < Tn) {
+      const f32x4 kk = kr[t].f(), qq = qr[t].f();
+      const float gate = expf(graw[t]);
+      const float kq = group_sum<LPR>(dot4(kk, qq));
+      const size_t yrow = ((static_cast<size_t>(b) * Tn + t) * Hv + hv) * Dv;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const int row = row0 + n * RPS;
+        const float sk = group_sum<LPR>(dot4(s[n], kk));
+        const float sq = group_sum<LPR>(dot4(s[n], qq));
+        const float d = bt[t] * (vv[t][n] - gate * sk);
+        s[n] = gate * s[n] + d * kk;
+        if ((FULL || row < Dv) && c4 == 0) Act<T>::store(y + yrow + row, gate * sq + d * kq);
+      }
+      if (t + 1 == commit) {
+#pragma unroll
+        for (int n = 0; n < NV; ++n) kept[n] = s[n];
+      }
+    }
+  }
+  if (commit > 0) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const int row = row0 + n * RPS;
+      if (FULL || row < Dv) store_stream(sout + static_cast<size_t>(row) * DK, kept[n]);
+    }
+  }
+}
+
+template <int DK, typename T, int NT>
+int launch_window_nt(const float* state_in, float* state_out, const void* q, const void* k, const void* v,
+                     const float* g, const void* beta, void* y, int B, int Hk, int Hv, int Dv, int Tn,
+                     int commit, hipStream_t stream) {
+  constexpr int NV = kRowsPerLane;
+  constexpr int ROWS = kThreads / (DK / 4) * NV;
+  const int parts = (Dv + ROWS - 1) / ROWS;
+  const long blocks = static_cast<long>(B) * Hv * parts;
+  if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
+  (void)hipGetLastError();
+  if (Dv % ROWS == 0)
+    hipLaunchKernelGGL((gdn_window_kernel<DK, NV, true, T, NT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, static_cast<const T*>(beta),
+                       static_cast<T*>(y), Hk, Hv, Dv, parts, Tn, commit);
+  else
+    hipLaunchKernelGGL((gdn_window_kernel<DK, NV, false, T, NT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, static_cast<const T*>(beta),
+                       static_cast<T*>(y), Hk, Hv, Dv, parts, Tn, commit);
+  return launch_status();
+}
+
+template <int DK, typename T>
+int launch_window(const float* state_in, float* state_out, const void* q, const void* k, const void* v,
+                  const float* g, const void* beta, void* y, int B, int Hk, int Hv, int Dv, int Tn,
+                  int commit, hipStream_t stream) {
+  // the smallest built token capacity that holds the window
+  if (Tn <= 2)
+    return launch_window_nt<DK, T, 2>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+  if (Tn <= 4)
+    return launch_window_nt<DK, T, 4>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+  return launch_window_nt<DK, T, 8>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+}
+
+template <typename T>
+int launch_window_dk(const float* state_in, float* state_out, const void* q, const void* k, const void* v,
+                     const float* g, const void* beta, void* y, int B, int Hk, int Hv, int Dk, int Dv,
+                     int Tn, int commit, hipStream_t stream) {
+  switch (Dk) {
+    case 32: return launch_window<32, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 64: return launch_window<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 128: return launch_window<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 256: return launch_window<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 }  // namespace gdn
+
+extern "C" int gdn_decode_window(const float* state_in, float* state_out, const void* q,
+                                 const void* k, const void* v, const float* g,
+                                 const void* beta, void* y, int B, int T, int Hk, int Hv, int Dk,
+                                 int Dv, int commit, gdn_dtype act, hipStream_t stream) {
+  using namespace gdn;
+  if (B < 0 || T < 1 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0 || commit < 0 ||
+      commit > T)
+    return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (!pow2_head(Dk) || Dv % 32 != 0 || Dv > 256 || T > 8) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  if (!state_in || !q || !k || !v || !g || !beta || !y || (commit > 0 && !state_out)) return GDN_ERR_NULL;
+  if (!aligned16(state_in) || (state_out && !aligned16(state_out)) || !aligned16(q) || !aligned16(k))
+    return GDN_ERR_ALIGN;
+  const size_t state_bytes = static_cast<size_t>(B) * Hv * Dv * Dk * sizeof(float);
+  if (state_out && state_out != state_in && overlaps(state_in, state_bytes, state_out, state_bytes))
+    return GDN_ERR_ALIAS;
+  const size_t y_bytes = static_cast<size_t>(B) * T * Hv * Dv * act_bytes(act);
+  if (overlaps(y, y_bytes, state_in, state_bytes) || (state_out && overlaps(y, y_bytes, state_out, state_bytes)))
+    return GDN_ERR_ALIAS;
+  if (act == GDN_BF16)
+    return launch_window_dk<bf16>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, T, commit, stream);
+  return launch_window_dk<float>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, T, commit, stream);
+}
 
 extern "C" int gdn_decode_step(const float* state_in, float* state_out, const void* q,
                                const void* k, const void* v, const float* g,

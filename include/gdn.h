@@ -77,6 +77,28 @@ int gdn_decode_step(const float* state_in, float* state_out, const void* q,
                     int Dv, gdn_dtype act, hipStream_t stream);
 
 /*
+ * gdn_decode_window - T decode tokens per sequence in one pass, with the
+ * state kept on chip across them (metaltile `mt_gated_delta_chunk`: the
+ * recurrent state lives in registers across an inner token loop; regolith
+ * `gdn.metal` commit rule for verify windows).  Token t of sequence b is
+ * the gdn_decode_step above applied to the state after tokens 0..t-1.
+ * q, k          [B, T, Hk, Dk] act.     v, y: [B, T, Hv, Dv] act.
+ * g, beta       [B, T, Hv] (g float32 log-space, beta act).
+ * state_in      [B, Hv, Dv, Dk] float32, read.
+ * state_out     [B, Hv, Dv, Dk] float32: receives the state after the first
+ *               `commit` tokens (0 <= commit <= T); commit == 0 is a verify
+ *               window (state_out not written, may be NULL); may equal
+ *               state_in; every token's y is written in all cases.
+ * Requirements: 1 <= T <= 8 and the gdn_decode_step sizes; q, k,
+ * state_in, state_out 16-byte aligned.
+ */
+int gdn_decode_window(const float* state_in, float* state_out, const void* q,
+                      const void* k, const void* v, const float* g,
+                      const void* beta, void* y, int B, int T, int Hk, int Hv,
+                      int Dk, int Dv, int commit, gdn_dtype act,
+                      hipStream_t stream);
+
+/*
  * comba_decode_step - one Comba step (gated delta rule with a decoupled read
  * key) for a dense batch.  Source: KBench `comba_decode_step` spec, sections
  * spec_md and contract_md.  For every (b, h), S the [K, V] state slice:

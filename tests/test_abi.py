@@ -217,3 +217,20 @@ def test_gated_prefill_validation(lib):
     assert gated(z=A + 8 * BIG + 16) == ALIAS        # z overlaps y
     assert gated(z=A + 5 * BIG + 64) == ALIAS        # z overlaps the state pool
     assert gated(N_s=0, z=0) == OK
+
+
+def test_decode_window_validation(lib):
+    def win(sin=A, sout=A + BIG, q=A + 2 * BIG, k=A + 3 * BIG, v=A + 4 * BIG, g=A + 5 * BIG,
+            beta=A + 6 * BIG, y=A + 7 * BIG, B=4, T=4, Hk=2, Hv=4, Dk=128, Dv=128, commit=4, act=1):
+        return lib.gdn_decode_window(_p(sin), _p(sout), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(y),
+                                     B, T, Hk, Hv, Dk, Dv, commit, act, None)
+    assert win(T=0) == SHAPE
+    assert win(commit=5) == SHAPE
+    assert win(commit=-1) == SHAPE
+    assert win(T=9, commit=2) == UNSUP
+    assert win(act=2) == DTYPE
+    assert win(sout=0) == NULL                   # committing needs state_out
+    assert win(sout=0, commit=0, B=0) == OK
+    assert win(q=A + 2 * BIG + 4) == ALIGN
+    assert win(sout=A + 64) == ALIAS             # partial overlap with state_in
+    assert win(y=A + 16) == ALIAS

@@ -163,3 +163,68 @@ def test_decode_batch_b256_sampled():
         got = bufs[(step + 1) % 2][torch.from_numpy(sample).to(DEV)]
         assert maxrel(to_np(got), S_ref) <= 1e-5, step
         _check_y(to_np(y)[sample], y_ref, "bf16")
+
+
+# ------------------------------------------------------------ decode windows
+
+WINDOW_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, commit, act
+    (3, 1, 1, 3, 32, 32, 1, "f32"),
+    (2, 3, 2, 6, 64, 96, 2, "bf16"),
+    (3, 4, 2, 4, 128, 128, 4, "bf16"),
+    (2, 4, 2, 4, 128, 128, 0, "bf16"),       # verify: no state write
+    (1, 8, 1, 2, 128, 160, 5, "f32"),        # Dv not a multiple of a workgroup's rows
+    (2, 8, 1, 1, 256, 64, 8, "bf16"),
+]
+
+
+def _window_tokens(rng, B, T, Hk, Hv, Dk, Dv, act):
+    toks = [synth.decode_token(rng, B, Hk, Hv, Dk, Dv, act=act) for _ in range(T)]
+    return {n: np.stack([t[n] for t in toks], axis=1) for n in toks[0]}
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,commit,act", WINDOW_CASES)
+def test_decode_window_parity(B, T, Hk, Hv, Dk, Dv, commit, act):
+    rng = np.random.default_rng(B * 100 + T * 10 + Dk + Dv + commit)
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    w = _window_tokens(rng, B, T, Hk, Hv, Dk, Dv, act)
+    d = DT[act]
+    dw = {n: to_dev(x, torch.float32 if n == "g" else d, DEV) for n, x in w.items()}
+    s_in = to_dev(S0, torch.float32, DEV)
+    s_out = torch.full_like(s_in, float("nan"))
+    _, y = gdn.gdn_decode_window(s_in, s_out, dw["q"], dw["k"], dw["v"], dw["g"], dw["beta"], commit=commit)
+    torch.cuda.synchronize()
+    S_ref, y_ref = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"], commit=commit)
+    if commit == 0:
+        assert torch.isnan(s_out).all()          # a verify window writes no state
+    else:
+        assert maxrel(to_np(s_out), S_ref) <= 1e-5
+    yv = to_np(y)
+    if act == "f32":
+        assert maxrel(yv, y_ref) <= 1e-5
+    else:
+        assert relF(yv, y_ref) <= 2e-2
+    assert np.array_equal(to_np(s_in).astype(np.float32), S0)  # state_in untouched
+
+
+def test_decode_window_matches_single_steps_and_runs_in_place():
+    """A committed 4-token window equals four gdn_decode_step calls (up to
+    rounding order) and gives the same result in place."""
+    rng = np.random.default_rng(31)
+    B, T, Hk, Hv, Dk, Dv = 4, 4, 2, 6, 128, 128
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    w = _window_tokens(rng, B, T, Hk, Hv, Dk, Dv, "bf16")
+    dw = {n: to_dev(x, torch.float32 if n == "g" else torch.bfloat16, DEV) for n, x in w.items()}
+    S, ys = to_dev(S0, torch.float32, DEV), []
+    for t in range(T):
+        S, yt = gdn.gdn_decode_step(S, None, dw["q"][:, t].contiguous(), dw["k"][:, t].contiguous(),
+                                    dw["v"][:, t].contiguous(), dw["g"][:, t].contiguous(),
+                                    dw["beta"][:, t].contiguous())
+        ys.append(yt)
+    y_steps = torch.stack(ys, dim=1)
+    s_io = to_dev(S0, torch.float32, DEV)
+    _, y_win = gdn.gdn_decode_window(s_io, s_io, dw["q"], dw["k"], dw["v"], dw["g"], dw["beta"])
+    torch.cuda.synchronize()
+    assert maxrel(to_np(s_io), to_np(S)) <= 1e-6
+    assert maxrel(to_np(y_win), to_np(y_steps)) <= 1e-2  # bf16 outputs of near-identical fp32 values
+    assert relF(to_np(y_win), to_np(y_steps)) <= 1e-3
