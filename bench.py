@@ -112,6 +112,35 @@ def bench_decode(steps, warmup, device):
                 shape=dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv))
 
 
+def bench_window(steps, warmup, device, T):
+    """Decode windows of T tokens per sequence at the B=256 decode batch,
+    committing all T (functional ping-pong, like the decode step)."""
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.DECODE_B256
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    rng = np.random.default_rng(0)
+    wins = []
+    for _ in range(4):
+        toks = [synth.decode_token(rng, B, Hk, Hv, Dk, Dv) for _ in range(T)]
+        wins.append({n: _dev(np.stack([t[n] for t in toks], axis=1),
+                             torch.float32 if n == "g" else torch.bfloat16, device) for n in toks[0]})
+    bufs = [torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=device),
+            torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=device)]
+    y = torch.empty((B, T, Hv, Dv), dtype=torch.bfloat16, device=device)
+
+    def step(i):
+        w = wins[i % 4]
+        gdn.gdn_decode_window(bufs[i % 2], bufs[(i + 1) % 2], w["q"], w["k"], w["v"], w["g"], w["beta"],
+                              y=y)
+
+    for i in range(4):
+        step(i)
+    sec = _timed(step, steps, warmup)
+    return dict(sec=sec, tokens=B * T, state_bytes=2 * B * Hv * Dv * Dk * 4)
+
+
 def bench_comba(steps, warmup, device):
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
@@ -376,6 +405,7 @@ def main():
     com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
+    wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
     copy_gbps = bench_copy(device)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
@@ -401,6 +431,12 @@ def main():
                      "traffic": _decode_traffic()},
         "copy_GBps": round(copy_gbps, 1),
         "decode_frac_of_copy": round(gbps / copy_gbps, 4),
+        "decode_window": {"workload": "gdn_decode_window at the B=256 decode batch, all T tokens committed",
+                          "tokens_per_s_single_step": round(dec["shape"]["B"] / dec["sec"], 1),
+                          **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
+                                       "tokens_per_s": round(w["tokens"] / w["sec"], 1),
+                                       "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
+                             for T, w in wins.items()}},
         "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
                   "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
                   "us_per_step": round(com["sec"] * 1e6, 2),
