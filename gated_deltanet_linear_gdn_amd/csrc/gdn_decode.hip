@@ -36,22 +36,34 @@ namespace {
 
 constexpr int kThreads = 128;
 constexpr int kRowsPerLane = 2;
+// grid z holds at most this many sequences: larger batches launch in slices
+constexpr int kMaxGridZ = 65535;
+
+// ceil(2^32 / G) for the kernels' multiply-high hk = hv / G; 0 for G == 1,
+// whose reciprocal does not fit 32 bits.  Exact for every hv < 2^16: the
+// reciprocal's rounding error m*G - 2^32 is below G <= 2^16.
+unsigned hk_reciprocal(int G) {
+  return G == 1 ? 0u : static_cast<unsigned>(((1ull << 32) + G - 1) / static_cast<unsigned>(G));
+}
 
 template <int DK, int NV, bool FULL, typename T>
 __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const float* state_in, float* state_out, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
-    int parts_per_slice) {
+    unsigned hk_mul) {
   constexpr int LPR = DK / 4;            // lanes per row
   constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
   constexpr int ROWS = RPS * NV;         // rows per workgroup
 
-  const int slice = blockIdx.x / parts_per_slice;  // n = b * Hv + hv
-  const int part = blockIdx.x - slice * parts_per_slice;
-  const int b = slice / Hv;
-  const int hv = slice - b * Hv;
-  const int hk = hv / (Hv / Hk);
+  // grid (part, hv, b): the same dispatch order as slice-major with parts
+  // innermost, and no integer division on the way in (hk = hv / (Hv/Hk) as a
+  // multiply-high by hk_mul, the host's hk_reciprocal(Hv/Hk)).
+  const int part = blockIdx.x;
+  const int hv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int slice = b * Hv + hv;  // n = b * Hv + hv
+  const int hk = hk_mul ? static_cast<int>(__umulhi(static_cast<unsigned>(hv), hk_mul)) : hv;
   const int tid = threadIdx.x;
   const int c4 = tid % LPR;                        // float4 column within the row
   const int row0 = part * ROWS + tid / LPR;
@@ -106,19 +118,28 @@ int launch_dk(const float* state_in, float* state_out, const void* q, const void
   constexpr int NV = kRowsPerLane;
   constexpr int ROWS = kThreads / (DK / 4) * NV;
   const int parts = (Dv + ROWS - 1) / ROWS;
-  const long blocks = static_cast<long>(B) * Hv * parts;
-  if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
+  if (Hv > 65535) return GDN_ERR_SHAPE;  // grid y
+  const unsigned hk_mul = hk_reciprocal(Hv / Hk);
+  const T* qa = static_cast<const T*>(q);
+  const T* ka = static_cast<const T*>(k);
+  const T* va = static_cast<const T*>(v);
+  const T* ba = static_cast<const T*>(beta);
+  T* ya = static_cast<T*>(y);
   (void)hipGetLastError();
-  if (Dv % ROWS == 0)
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, true, T>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), g,
-                       static_cast<const T*>(beta), static_cast<T*>(y), Hk, Hv, Dv, parts);
-  else
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, false, T>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), g,
-                       static_cast<const T*>(beta), static_cast<T*>(y), Hk, Hv, Dv, parts);
+  for (int b0 = 0; b0 < B; b0 += kMaxGridZ) {
+    const int nb = std::min(B - b0, kMaxGridZ);
+    const size_t sv = static_cast<size_t>(b0) * Hv;  // value-head slices before this one
+    const size_t sk = static_cast<size_t>(b0) * Hk * DK;
+    const dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(Hv), static_cast<unsigned>(nb));
+    if (Dv % ROWS == 0)
+      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, true, T>), grid, dim3(kThreads), 0, stream,
+                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + sk, ka + sk,
+                         va + sv * Dv, g + sv, ba + sv, ya + sv * Dv, Hk, Hv, Dv, hk_mul);
+    else
+      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, false, T>), grid, dim3(kThreads), 0, stream,
+                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + sk, ka + sk,
+                         va + sv * Dv, g + sv, ba + sv, ya + sv * Dv, Hk, Hv, Dv, hk_mul);
+  }
   return launch_status();
 }
 
@@ -166,16 +187,17 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
     const float* state_in, float* state_out, const T* __restrict__ q,
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
-    int parts_per_slice, int Tn, int commit) {
+    unsigned hk_mul, int Tn, int commit) {
   constexpr int LPR = DK / 4;            // lanes per row
   constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
   constexpr int ROWS = RPS * NV;         // rows per workgroup
 
-  const int slice = blockIdx.x / parts_per_slice;  // n = b * Hv + hv
-  const int part = blockIdx.x - slice * parts_per_slice;
-  const int b = slice / Hv;
-  const int hv = slice - b * Hv;
-  const int hk = hv / (Hv / Hk);
+  // grid (part, hv, b) and the key head as in the single-step kernel
+  const int part = blockIdx.x;
+  const int hv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int slice = b * Hv + hv;
+  const int hk = hk_mul ? static_cast<int>(__umulhi(static_cast<unsigned>(hv), hk_mul)) : hv;
   const int tid = threadIdx.x;
   const int c4 = tid % LPR;
   const int row0 = part * ROWS + tid / LPR;
@@ -247,19 +269,29 @@ int launch_window_nt(const float* state_in, float* state_out, const void* q, con
   constexpr int NV = kRowsPerLane;
   constexpr int ROWS = kThreads / (DK / 4) * NV;
   const int parts = (Dv + ROWS - 1) / ROWS;
-  const long blocks = static_cast<long>(B) * Hv * parts;
-  if (blocks > 0x7fffffffL) return GDN_ERR_SHAPE;
+  if (Hv > 65535) return GDN_ERR_SHAPE;  // grid y
+  const unsigned hk_mul = hk_reciprocal(Hv / Hk);
+  const T* qa = static_cast<const T*>(q);
+  const T* ka = static_cast<const T*>(k);
+  const T* va = static_cast<const T*>(v);
+  const T* ba = static_cast<const T*>(beta);
+  T* ya = static_cast<T*>(y);
   (void)hipGetLastError();
-  if (Dv % ROWS == 0)
-    hipLaunchKernelGGL((gdn_window_kernel<DK, NV, true, T, NT>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), g, static_cast<const T*>(beta),
-                       static_cast<T*>(y), Hk, Hv, Dv, parts, Tn, commit);
-  else
-    hipLaunchKernelGGL((gdn_window_kernel<DK, NV, false, T, NT>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, state_in, state_out, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), g, static_cast<const T*>(beta),
-                       static_cast<T*>(y), Hk, Hv, Dv, parts, Tn, commit);
+  for (int b0 = 0; b0 < B; b0 += kMaxGridZ) {
+    const int nb = std::min(B - b0, kMaxGridZ);
+    const size_t sv = static_cast<size_t>(b0) * Hv;        // state slices before this batch slice
+    const size_t tv = static_cast<size_t>(b0) * Tn * Hv;   // token x value-head rows before it
+    const size_t tk = static_cast<size_t>(b0) * Tn * Hk * DK;
+    const dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(Hv), static_cast<unsigned>(nb));
+    if (Dv % ROWS == 0)
+      hipLaunchKernelGGL((gdn_window_kernel<DK, NV, true, T, NT>), grid, dim3(kThreads), 0, stream,
+                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + tk, ka + tk,
+                         va + tv * Dv, g + tv, ba + tv, ya + tv * Dv, Hk, Hv, Dv, hk_mul, Tn, commit);
+    else
+      hipLaunchKernelGGL((gdn_window_kernel<DK, NV, false, T, NT>), grid, dim3(kThreads), 0, stream,
+                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + tk, ka + tk,
+                         va + tv * Dv, g + tv, ba + tv, ya + tv * Dv, Hk, Hv, Dv, hk_mul, Tn, commit);
+  }
   return launch_status();
 }
 

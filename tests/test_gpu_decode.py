@@ -59,6 +59,8 @@ SHAPES = [
     (2, 3, 3, 256, 64),
     (1, 1, 1, 256, 256),
     (5, 4, 8, 128, 32),
+    (2, 1, 48, 32, 32),    # 48 value heads read one key head
+    (1, 6, 48, 64, 64),    # groups of 8
 ]
 
 
@@ -163,6 +165,31 @@ def test_decode_batch_b256_sampled():
         got = bufs[(step + 1) % 2][torch.from_numpy(sample).to(DEV)]
         assert maxrel(to_np(got), S_ref) <= 1e-5, step
         _check_y(to_np(y)[sample], y_ref, "bf16")
+
+
+def test_batch_beyond_one_launch_grid():
+    """65,538 sequences: more than one launch's grid holds (65,535 sequences),
+    so the batch runs in two slices.  The oracle follows the sequences on both
+    sides of the seam and at the ends, for one step and for a 2-token window."""
+    rng = np.random.default_rng(41)
+    B, Hk, Hv, Dk, Dv = 65538, 1, 2, 32, 32
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk), dtype=np.float32)).astype(np.float32)
+    tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
+    sample = np.array([0, 1, 30000, 65533, 65534, 65535, 65536, 65537])
+    S_dev, y = _step(to_dev(S0, torch.float32, DEV), _dev_token(tok, "bf16"))
+    S_ref, y_ref = oracle_decode_batched(S0[sample].astype(np.float64), {n: a[sample] for n, a in tok.items()})
+    idx = torch.from_numpy(sample).to(DEV)
+    assert maxrel(to_np(S_dev[idx]), S_ref) <= 1e-5
+    _check_y(to_np(y)[sample], y_ref, "bf16")
+    del S_dev, y
+    w = _window_tokens(rng, B, 2, Hk, Hv, Dk, Dv, "bf16")
+    dw = {n: to_dev(x, torch.float32 if n == "g" else torch.bfloat16, DEV) for n, x in w.items()}
+    s_io = to_dev(S0, torch.float32, DEV)
+    _, yw = gdn.gdn_decode_window(s_io, s_io, dw["q"], dw["k"], dw["v"], dw["g"], dw["beta"])
+    torch.cuda.synchronize()
+    Sw, yw_ref = oracle.gdn_window(S0[sample], *(w[n][sample] for n in ("q", "k", "v", "g", "beta")))
+    assert maxrel(to_np(s_io[idx]), Sw) <= 1e-5
+    assert relF(to_np(yw)[sample], yw_ref) <= 2e-2
 
 
 # ------------------------------------------------------------ decode windows
