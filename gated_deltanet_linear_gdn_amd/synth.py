@@ -101,6 +101,24 @@ def prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size, act="bf16"):
                 cache_indices=cache_indices, cu_seqlens=cu_from_lengths(lengths))
 
 
+def comba_prefill_inputs(rng, lengths, H, K, V, pool_size, act="bf16"):
+    """Packed Comba batch with the Comba token distributions: q [T,H,K];
+    k [T,H,K] (unit rows); v [T,H,V]; p [T,H,K] (unit rows); beta [T,H]
+    (activation dtype); g [T,H] (fp32); cache_indices = first N_s entries of
+    a random permutation of the pool; cu_seqlens from the lengths."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    q = _act(rng.standard_normal((T, H, K), dtype=np.float32), act)
+    k = _act(_unit_rows(rng.standard_normal((T, H, K), dtype=np.float32)), act)
+    v = _act(rng.standard_normal((T, H, V), dtype=np.float32), act)
+    p = _act(_unit_rows(rng.standard_normal((T, H, K), dtype=np.float32)), act)
+    beta = _act(_sigmoid(rng.random((T, H), dtype=np.float32)), act)
+    g = (_logsigmoid(rng.standard_normal((T, H), dtype=np.float32)) / 4.0).astype(np.float32)
+    cache_indices = rng.permutation(pool_size)[: lengths.shape[0]].astype(np.int64)
+    return dict(q=q, k=k, v=v, p=p, beta=beta, g=g, cache_indices=cache_indices,
+                cu_seqlens=cu_from_lengths(lengths))
+
+
 def layer_inputs(rng, T, Hk, Hv, Dk, Dv, pool_size, act="bf16"):
     """Inputs of the layer steps around the recurrence: qkv [T, C] with
     C = 2*Hk*Dk + Hv*Dv channels ([q heads | k heads | v heads]) ~ N(0,1);
@@ -123,4 +141,6 @@ DECODE_B256 = dict(B=256, Hk=16, Hv=48, Dk=128, Dv=128, act="bf16")
 PREFILL_VARLEN = dict(n_seq=8, len_lo=512, len_hi=4096, Hk=16, Hv=48, Dk=128, Dv=128,
                       pool=16, chunk=64, act="bf16")
 COMBA_B128 = dict(B=128, H=32, K=128, V=128, act="bf16")
+COMBA_PREFILL_VARLEN = dict(n_seq=8, len_lo=512, len_hi=4096, H=32, K=128, V=128, pool=16,
+                            chunk=64, act="bf16")
 WARMUP_STEPS = 16

@@ -21,6 +21,8 @@ Functions (each cites the page it follows in ``gdn_oracle.c``):
                                                         (regolith gdn.metal output block)
   gdn_window    T decode tokens per sequence, committing the state after the
                 first k (metaltile mt_gated_delta_chunk; regolith commit rule)
+  comba_prefill varlen Comba forward over a pool, per token (KBench
+                comba_decode_step: the step run over every token)
 """
 from __future__ import annotations
 
@@ -216,3 +218,32 @@ def gdn_window(state, q, k, v, g, beta, commit=None):
         if t + 1 == commit:
             kept = S.copy()
     return kept, np.stack(ys, axis=1)
+
+
+def comba_prefill(q, k, v, p, beta, g, pool, cache_indices, cu_seqlens, scale=None):
+    """Varlen Comba forward over a state pool: the pinned single step
+    (``comba_step``) applied token by token to each sequence's slot, as the
+    KBench spec describes the forward task (the step run once per token).
+    q, k, p [T,H,K]; v [T,H,V]; beta, g [T,H]; pool [P,H,K,V].  Sequence s
+    owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and slot cache_indices[s].
+    Returns (pool_new, o [T,H,V]) in float64; scale None -> K^-1/2."""
+    q, k, v, p, beta, g = map(_f64, (q, k, v, p, beta, g))
+    P = _f64(pool).copy()
+    ci = np.asarray(cache_indices, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, K = q.shape
+    V = v.shape[2]
+    if P.ndim != 4 or P.shape[1:] != (H, K, V) or cu.shape != (ci.shape[0] + 1,):
+        raise ValueError("comba_prefill: inconsistent shapes")
+    if (cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0) or np.any(ci < 0)
+            or np.any(ci >= P.shape[0]) or len(set(ci.tolist())) != ci.shape[0]):
+        raise ValueError("comba_prefill: invalid cu_seqlens or cache_indices")
+    o = np.zeros((T, H, V), dtype=np.float64)
+    for s in range(ci.shape[0]):
+        S = P[ci[s]][None].copy()
+        for t in range(int(cu[s]), int(cu[s + 1])):
+            S, ot = comba_step(S, q[t][None], k[t][None], v[t][None], p[t][None], beta[t][None],
+                               g[t][None], scale=scale, inplace=True)
+            o[t] = ot[0]
+        P[ci[s]] = S[0]
+    return P, o

@@ -607,3 +607,84 @@ def test_window_closed_form_unit_keys():
         kt = k[0, t, 0]
         St = St - np.outer(St @ kt, kt) + np.outer(v[0, t, 0], kt)
         np.testing.assert_allclose(y[0, t, 0], St @ q[0, t, 0], atol=1e-12)
+
+
+# ------------------------------------------------------------ comba prefill
+
+
+def test_comba_prefill_with_p_equal_k_is_the_gdn_prefill():
+    """Reading with p = k makes the Comba forward the (unnormalised) gated
+    delta-rule prefill on the transposed pool with q pre-scaled: two
+    independently written oracle functions, including their varlen plumbing."""
+    rng = np.random.default_rng(61)
+    lengths, H, K, V, P = [6, 0, 9, 1], 3, 16, 8, 6
+    inp = synth.comba_prefill_inputs(rng, lengths, H, K, V, P, act="f32")
+    P0 = _rand_state(rng, P, H, K, V)
+    sc = 0.29
+    Pc, oc = oracle.comba_prefill(inp["q"], inp["k"], inp["v"], inp["k"], inp["beta"], inp["g"], P0,
+                                  inp["cache_indices"], inp["cu_seqlens"], scale=sc)
+    Pg, yg = oracle.gdn_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                np.swapaxes(P0, -1, -2), inp["cache_indices"], inp["cu_seqlens"],
+                                scale=sc, l2norm=False)
+    np.testing.assert_allclose(Pc, np.swapaxes(Pg, -1, -2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oc, yg, rtol=1e-11, atol=1e-12)
+
+
+def test_comba_prefill_one_hot_keys_closed_form():
+    """Zero state, read key e0 then e1... worked by hand: token 1 writes row a1
+    with u1 = beta1 v1; token 2 decays it by alpha2, reads row b2 and writes
+    u2 = beta2 (v2 - [b2 == a1] alpha2 beta1 v1) into row a2.  The read and
+    write roles are distinguishable: swapping p and k changes the result."""
+    K, V, s = 4, 3, 0.5
+    rng = np.random.default_rng(62)
+    v = rng.standard_normal((2, 1, V))
+    q = rng.standard_normal((2, 1, K))
+    e = np.eye(K)
+    k = np.stack([e[0], e[1]])[:, None, :]     # write rows 0 then 1
+    p = np.stack([e[2], e[0]])[:, None, :]     # read row 2 (empty) then row 0
+    beta = np.array([[0.8], [0.6]])
+    g = np.array([[-0.3], [-0.7]])
+    a1, a2 = np.exp(g[0, 0]), np.exp(g[1, 0])
+    P, o = oracle.comba_prefill(q, k, v, p, beta, g, np.zeros((1, 1, K, V)), [0], [0, 2], scale=s)
+    u1 = 0.8 * v[0, 0]
+    row0 = a2 * u1
+    u2 = 0.6 * (v[1, 0] - row0)
+    ref = np.zeros((K, V))
+    ref[0], ref[1] = row0, u2
+    np.testing.assert_allclose(P[0, 0], ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0], s * q[0, 0, 0] * u1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(o[1, 0], s * (q[1, 0, 0] * row0 + q[1, 0, 1] * u2), rtol=1e-14, atol=1e-15)
+    Pswap, _ = oracle.comba_prefill(q, p, v, k, beta, g, np.zeros((1, 1, K, V)), [0], [0, 2], scale=s)
+    assert not np.allclose(Pswap, P)
+
+
+def test_comba_prefill_split_and_index_handling():
+    """Running a sequence in two calls equals one call; unnamed slots are
+    bitwise untouched; zero-length sequences are no-ops."""
+    rng = np.random.default_rng(63)
+    H, K, V, P = 2, 8, 8, 5
+    inp = synth.comba_prefill_inputs(rng, [7, 0, 3], H, K, V, P, act="f32")
+    P0 = _rand_state(rng, P, H, K, V)
+    ci, cu = inp["cache_indices"], inp["cu_seqlens"]
+    args = [inp[n] for n in ("q", "k", "v", "p", "beta", "g")]
+    Pw, ow = oracle.comba_prefill(*args, P0, ci, cu)
+    for slot in set(range(P)) - {int(ci[0]), int(ci[2])}:
+        assert np.array_equal(Pw[slot], P0[slot])
+    # first sequence split after 4 tokens
+    first = [a[:4] for a in args]
+    rest = [np.concatenate([a[4:7], a[7:]]) for a in args]
+    P1, o1 = oracle.comba_prefill(*first, P0, ci[:1], [0, 4])
+    P2, o2 = oracle.comba_prefill(*rest, P1, ci, [0, 3, 3, 6])
+    np.testing.assert_array_equal(P2, Pw)
+    np.testing.assert_array_equal(np.concatenate([o1, o2]), ow)
+
+
+def test_comba_prefill_rejects_bad_indices():
+    z = np.zeros((2, 1, 4))
+    zz = np.zeros((2, 1))
+    with pytest.raises(ValueError):
+        oracle.comba_prefill(z, z, z, z, zz, zz, np.zeros((2, 1, 4, 4)), [0, 0], [0, 1, 2])
+    with pytest.raises(ValueError):
+        oracle.comba_prefill(z, z, z, z, zz, zz, np.zeros((2, 1, 4, 4)), [2], [0, 2])
+    with pytest.raises(ValueError):
+        oracle.comba_prefill(z, z, z, z, zz, zz, np.zeros((2, 1, 4, 4)), [0], [0, 1])
