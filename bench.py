@@ -247,6 +247,48 @@ def bench_prefill(steps, warmup, device):
                 shape=dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, chunk=C, pool=P))
 
 
+def comba_prefill_min_bytes(T, n_seq, H, K, V, act_bytes=2):
+    """Bytes the Comba forward must move: q, k, p, v, o and beta in the
+    activation dtype and g (fp32) per token, and each sequence's state slot
+    read and written once."""
+    per_token = act_bytes * (3 * H * K + 2 * H * V + H) + 4 * H
+    return T * per_token + n_seq * 2 * H * K * V * 4
+
+
+def bench_comba_prefill(steps, warmup, device):
+    """comba_chunk_prefill at the varlen token mix with H=32, K=V=128."""
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.COMBA_PREFILL_VARLEN
+    H, K, V, P, C = c["H"], c["K"], c["V"], c["pool"], c["chunk"]
+    rng = np.random.default_rng(0)
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    inp = synth.comba_prefill_inputs(rng, lengths, H, K, V, P)
+    T = int(inp["cu_seqlens"][-1])
+    bf = torch.bfloat16
+    d = {n: _dev(inp[n], torch.float32 if n == "g" else bf, device) for n in ("q", "k", "v", "p", "beta", "g")}
+    ci = _dev(inp["cache_indices"], torch.int64, device)
+    cu = _dev(inp["cu_seqlens"], torch.int64, device)
+    pool = torch.zeros((P, H, K, V), dtype=torch.float32, device=device)
+    for _ in range(synth.WARMUP_STEPS):  # slots warmed by 16 Comba steps
+        t = synth.comba_token(rng, P, H, K, V)
+        td = {n: _dev(x, torch.float32 if n == "g" else bf, device) for n, x in t.items()}
+        gdn.comba_decode_step(pool, pool, td["q"], td["k"], td["v"], td["p"], td["beta"], td["g"])
+    o = torch.empty((T, H, V), dtype=bf, device=device)
+    ws = torch.empty(gdn.comba_chunk_prefill_workspace(T, len(lengths), H, K, V, C), dtype=torch.uint8,
+                     device=device)
+
+    def step(i):
+        gdn.comba_chunk_prefill(d["q"], d["k"], d["v"], d["p"], d["beta"], d["g"], pool, ci, cu, chunk=C,
+                                o=o, workspace=ws)
+
+    sec = _timed(step, steps, warmup)
+    return dict(sec=sec, tokens=T, flops=prefill_flops_per_token(H, K, V, C) * T,
+                issued=prefill_issued_flops(lengths, H, H, K, V, C),
+                min_bytes=comba_prefill_min_bytes(T, len(lengths), H, K, V))
+
+
 def bench_layer(steps, warmup, device):
     """The layer steps around the recurrence at the varlen prefill workload
     (and the decode batch for the conv): conv + SiLU prologue, the gated RMS
@@ -404,6 +446,7 @@ def main():
     com = bench_comba(args.steps, args.warmup, device)
     com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
+    cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
     copy_gbps = bench_copy(device)
@@ -454,6 +497,17 @@ def main():
                     "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
                     "min_bytes": pre["min_bytes"],
                     "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+        "comba_prefill": {"workload": "comba_chunk_prefill, the same 8 sequences, H=32 K=V=128, bf16, "
+                                      "chunk 64, pool 16",
+                          "tokens": cpre["tokens"],
+                          "us_per_call": round(cpre["sec"] * 1e6, 2),
+                          "tokens_per_s": round(cpre["tokens"] / cpre["sec"], 1),
+                          "canonical_TFLOPs": round(cpre["flops"] / cpre["sec"] / 1e12, 2),
+                          "mfma_frac_of_bf16_peak": round(cpre["flops"] / cpre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "issued_mfma_frac_of_bf16_peak": round(cpre["issued"] / cpre["sec"] / 1e12
+                                                                 / BF16_PEAK_TFLOPS, 4),
+                          "min_bytes": cpre["min_bytes"],
+                          "hbm_frac_of_peak": round(cpre["min_bytes"] / cpre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
         "layer": {"workload": "prologue gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per "
                               "slot) and epilogue gdn_gated_rmsnorm around the varlen prefill; conv "
                               "also as a decode step of 256 sequences",

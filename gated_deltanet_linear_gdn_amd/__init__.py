@@ -23,6 +23,8 @@ __all__ = [
     "GdnError", "library_path", "load_library",
     "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
     "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
+    "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
+    "comba_chunk_prefill_workspace", "comba_chunk_prefill",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +86,11 @@ def load_library():
     lib.gdn_conv_silu.argtypes = [_vp] * 3 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4 + [_vp] * 3 + [_i, _vp]
     lib.gdn_gated_rmsnorm.restype = _i
     lib.gdn_gated_rmsnorm.argtypes = [_vp] * 3 + [_f, _vp, _i64, _i, _i, _i, _vp]
+    lib.comba_chunk_prefill_workspace.restype = ctypes.c_size_t
+    lib.comba_chunk_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i]
+    lib.comba_chunk_prefill.restype = _i
+    lib.comba_chunk_prefill.argtypes = ([_vp] * 7 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4
+                                        + [_f, _vp, _i, _vp, ctypes.c_size_t, _vp])
     _lib = lib
     return lib
 
@@ -298,6 +305,46 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
           _stream())
     return y
+
+
+def comba_chunk_prefill_workspace(T_tot, N_s, H, K, V, chunk=64) -> int:
+    """Bytes of workspace ``comba_chunk_prefill`` needs (bf16 activations)."""
+    return int(load_library().comba_chunk_prefill_workspace(T_tot, N_s, H, K, V, chunk, 1))
+
+
+def comba_chunk_prefill(q, k, v, p, beta, g, state_pool, cache_indices, cu_seqlens, chunk=64,
+                        scale=None, o=None, workspace=None):
+    """Varlen Comba forward, chunkwise, ``state_pool`` updated in place (see
+    ``comba_chunk_prefill`` in include/gdn.h).
+
+    q, k, p [T,H,K] bf16; v [T,H,V] bf16; beta [T,H] bf16; g [T,H] f32;
+    state_pool [P,H,K,V] f32; cache_indices [N_s], cu_seqlens [N_s+1] int64
+    device tensors; o [T,H,V] bf16 or None; workspace a uint8 device tensor of
+    at least ``comba_chunk_prefill_workspace`` bytes, or None.  Returns o."""
+    T, H, K = q.shape
+    V = v.shape[2]
+    P = state_pool.shape[0]
+    N_s = cache_indices.shape[0]
+    dev, act = q.device, q.dtype
+    if o is None:
+        o = torch.empty((T, H, V), dtype=act, device=dev)
+    for name, t, shape in (("q", q, (T, H, K)), ("k", k, (T, H, K)), ("p", p, (T, H, K)),
+                           ("v", v, (T, H, V)), ("beta", beta, (T, H)), ("o", o, (T, H, V))):
+        _check(name, t, shape, act, dev)
+    _check("g", g, (T, H), torch.float32, dev)
+    _check("state_pool", state_pool, (P, H, K, V), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    need = comba_chunk_prefill_workspace(T, N_s, H, K, V, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    _call("comba_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(beta), _ptr(g), _ptr(state_pool),
+          P, _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, H, K, V, int(chunk), sc, _ptr(o),
+          _act_of(q), _ptr(workspace), workspace.numel(), _stream())
+    return o
 
 
 def gdn_conv_silu(qkv, conv_w, conv_state, cache_indices, cu_seqlens, Hk, Hv, Dk, Dv,

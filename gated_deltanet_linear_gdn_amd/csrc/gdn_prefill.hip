@@ -843,11 +843,23 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 // needs no barriers; the LDS footprint (19 KB) and a register budget of 256
 // (two waves per SIMD, requested from the compiler) let eight waves share a
 // CU and hide each other's latency.
+//
+// COMBA: the Comba forward (read key p, write key k; KBench
+// `comba_decode_step` spec run over every token).  Its chunk form is the
+// same with A_ij = beta_i exp(G_i - G_j) p_i . k_j (the read key of the
+// later token against the write key of the earlier one) and the read term
+// R = V - diag(gamma) P S; keys are taken as given (no norms) and q is only
+// scaled.  The Gram blocks are then P K^T instead of K K^T, and beta comes
+// in the activation dtype.
 
-template <int DK, int CT>
+__device__ __forceinline__ float ld_beta(const float* b, size_t i) { return b[i]; }
+__device__ __forceinline__ float ld_beta(const bf16* b, size_t i) { return bf16_to_f32(b[i]); }
+
+template <int DK, int CT, bool COMBA = false, typename BT = float>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gdn_wy_wave_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int64_t* __restrict__ cu, const int* __restrict__ scs,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
+    const float* __restrict__ g, const BT* __restrict__ beta, const int64_t* __restrict__ cu,
+    const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
     bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac) {
   constexpr int MT = CT / 16, KB = DK / 32;
@@ -881,7 +893,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   // holds row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on
   // both sides of every Gram product); Q fragments follow one row block at a
   // time, as the Q K^T blocks of that row need them
-  float gl = g[tg], bl = beta[tg];
+  float gl = g[tg], bl = ld_beta(beta, tg);
   auto row_off = [&](int I) __attribute__((always_inline)) {
     return (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK + kg * 8;
   };
@@ -912,13 +924,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   float mk = 0.f, mq = 0.f;
 #pragma unroll
   for (int I = 0; I < MT; ++I) {
-    bf16x8v qf[KB];
+    bf16x8v qf[KB], lf[KB];  // lf: the left factor of the A Gram blocks (k, or Comba's p)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
       qf[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + row_off(I) + kb * 32));
-    const float sk = sumsq(kf[I]), sq = sumsq(qf);
-    mk = kg == I ? sk : mk;
-    mq = kg == I ? sq : mq;
+      lf[kb] = COMBA ? __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(pr + row_off(I) + kb * 32))
+                     : kf[I][kb];
+    }
+    if constexpr (!COMBA) {
+      const float sk = sumsq(kf[I]), sq = sumsq(qf);
+      mk = kg == I ? sk : mk;
+      mq = kg == I ? sq : mq;
+    }
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       const int pidx = I * (I + 1) / 2 + J;
@@ -926,13 +943,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
       gq[pidx] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        gk[pidx] = mma(kf[I][kb], kf[J][kb], gk[pidx]);
+        gk[pidx] = mma(lf[kb], kf[J][kb], gk[pidx]);
         gq[pidx] = mma(qf[kb], kf[J][kb], gq[pidx]);
       }
     }
   }
-  const float rk = ok ? (l2norm ? 1.0f / sqrtf(mk + kNormEps) : 1.0f) : 0.f;
-  const float rq = ok ? scale * (l2norm ? 1.0f / sqrtf(mq + kNormEps) : 1.0f) : 0.f;
+  const bool nrm = !COMBA && l2norm;
+  const float rk = ok ? (nrm ? 1.0f / sqrtf(mk + kNormEps) : 1.0f) : 0.f;
+  const float rq = ok ? scale * (nrm ? 1.0f / sqrtf(mq + kNormEps) : 1.0f) : 0.f;
   if (lane < CT) {
     sRK[lane] = rk;
     sRQ[lane] = rq;
@@ -945,7 +963,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     const float bt = ok ? bl : 0.f;
     if (j + 1 < HG) {  // the next head's gates, in flight during this head
       gl = g[tg + j + 1];
-      bl = beta[tg + j + 1];
+      bl = ld_beta(beta, tg + j + 1);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1073,6 +1091,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
 // last token (and whole chunks past the sequence) read as zero, and y rows
 // past it are dropped the same way.  K^T, T^T, P^T and V are read with the
 // transposing LDS load.
+//
+// COMBA (the Comba forward): phase A reads the state with the read keys
+// (X = Pr S, Pr the chunk's p rows) and phase C writes it with k.  Pr has
+// one single-buffered tile (it is only read in phase A) copied beside V.
+// The state slot is stored [K, V] (value index contiguous), the Comba
+// layout, instead of [Dv, Dk].
 
 template <int DK, int CT, int NW, int CW>
 struct StreamTiles {
@@ -1110,9 +1134,10 @@ struct StreamTiles {
   };
 };
 
-template <int DK, int CT, int NW, int CW, bool GATED = false>
+template <int DK, int CT, int NW, int CW, bool GATED = false, bool COMBA = false>
 __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
+    const bf16* __restrict__ v,
     float* __restrict__ pool, int64_t pool_size, const int64_t* __restrict__ cache_indices,
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
     int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
@@ -1128,8 +1153,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   __shared__ Set setA, setB;
   __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sY[CT * YP];
-  // the gated epilogue's z tile (one element when unused)
+  // the gated epilogue's z tile and Comba's read-key tile (8 elements when unused)
+  static_assert(!(GATED && COMBA), "no fused epilogue for the Comba forward");
   __shared__ __attribute__((aligned(16))) bf16 sZ[GATED ? CT * BV : 8];
+  __shared__ __attribute__((aligned(16))) bf16 sPr[COMBA ? Tiles::Qcopy::ELEMS : 8];
 
   const int nvb = Dv / BV;
   const int s = blockIdx.x / (Hv * nvb);
@@ -1158,7 +1185,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   typename Tiles::Tcopy cT;
   typename Tiles::Vcopy cV;
   typename Tiles::Fcopy cF;
+  typename Tiles::Qcopy cPr;  // Comba's read keys (same layout as Q)
   cK.init(w, lane, kstride);
+  if constexpr (COMBA) cPr.init(w, lane, kstride);
   cQ.init(w, lane, kstride);
   cT.init(w, lane, 0);
   cV.init(w, lane, vstride);
@@ -1215,13 +1244,25 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   };
   auto v_rsrc = [&](int ci) __attribute__((always_inline)) { return make_rsrc(v + vy_off(ci), vy_bytes(ci)); };
 
-  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK + static_cast<size_t>(vb * BV) * DK;
+  // S[t][m][r] is the state at key index m*16 + kg*4 + r, value column dvl(t)
+  float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
+              (COMBA ? static_cast<size_t>(vb * BV) : static_cast<size_t>(vb * BV) * DK);
+  auto s_at = [&](int t, int m, int r) __attribute__((always_inline)) -> float* {
+    return COMBA ? Sp + static_cast<size_t>(m * 16 + kg * 4 + r) * Dv + dvl(t)
+                 : Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4 + r;
+  };
   f32x4 S[CW][DT];
 #pragma unroll
   for (int t = 0; t < CW; ++t)
 #pragma unroll
-    for (int m = 0; m < DT; ++m)
-      S[t][m] = *reinterpret_cast<const f32x4*>(Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4);
+    for (int m = 0; m < DT; ++m) {
+      if constexpr (COMBA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[t][m][r] = *s_at(t, m, r);
+      } else {
+        S[t][m] = *reinterpret_cast<const f32x4*>(s_at(t, m, 0));
+      }
+    }
 
   // lane parts of the transposing reads
   const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
@@ -1331,7 +1372,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int t = 0; t < CW; ++t) acc_operand(S[t][2 * kb], S[t][2 * kb + 1], Sh[t], Sl[t]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8v a = lds_pi<KP>(c.K + kfrag, mt * 16 + l16, kb * 32, kg);
+        const bf16x8v a = COMBA ? lds_pi<QP>(sPr, mt * 16 + l16, kb * 32, kg)
+                                : lds_pi<KP>(c.K + kfrag, mt * 16 + l16, kb * 32, kg);
         const bf16x8v aq = lds_pi<QP>(c.Q, mt * 16 + l16, kb * 32, kg);
 #pragma unroll
         for (int t = 0; t < CW; ++t) {
@@ -1357,8 +1399,10 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         for (int r = 0; r < 4; ++r) R[t][mt][r] = bf16_bits_to_f32(vv[r]) - fk[r] * X[t][mt][r];
       }
     }
-    lds_handover();  // V is free; every wave staged chunk ci-1's y
+    lds_handover();  // V (and Comba's Pr) is free; every wave staged chunk ci-1's y
     const i32x4 rv = v_rsrc(ci + 1);
+    i32x4 rp;
+    if constexpr (COMBA) rp = kq_rsrc(pr, ci + 1);
     const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci > 0 ? ci - 1 : 0), ci > 0 ? vy_bytes(ci - 1) : 0u);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
@@ -1384,9 +1428,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         }
       }
       cV.issue_one(rv, sV, w, mt);  // chunk ci+1's V
+      if constexpr (COMBA) cPr.issue_one(rp, sPr, w, mt);
     }
 #pragma unroll
     for (int j = MT; j < Tiles_::Vcopy::PER; ++j) cV.issue_one(rv, sV, w, j);
+    if constexpr (COMBA) {
+#pragma unroll
+      for (int j = MT; j < Tiles_::Qcopy::PER; ++j) cPr.issue_one(rp, sPr, w, j);
+    }
 
     // ---- C: O += P Delta (hi parts);  S <- gamma_C S + K^T diag(fD) Delta
     bf16x8v Dh[CW][CKB], Eh[CW][CKB], El[CW][CKB];
@@ -1442,6 +1491,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 #pragma unroll
     for (int n = 0; n < NJOBS; ++n) copy_job(r0, setA, n);
     cV.issue(v_rsrc(0), sV, w);
+    if constexpr (COMBA) cPr.issue(kq_rsrc(pr, 0), sPr, w);
   }
   handover<0>();
   for (int ci = 0; ci < nch; ci += 2) {
@@ -1463,8 +1513,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 #pragma unroll
   for (int t = 0; t < CW; ++t)
 #pragma unroll
-    for (int m = 0; m < DT; ++m)
-      *reinterpret_cast<f32x4*>(Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4) = S[t][m];
+    for (int m = 0; m < DT; ++m) {
+      if constexpr (COMBA) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *s_at(t, m, r) = S[t][m][r];
+      } else {
+        *reinterpret_cast<f32x4*>(s_at(t, m, 0)) = S[t][m];
+      }
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -1527,14 +1583,15 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
-                       stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k), g, beta, cu, scs,
-                       N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac);
+                       stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(nullptr), g, beta, cu, scs, N_s, T_tot, Hk, Hv, chunk, scale,
+                       l2norm, Th, Tl, Ph, fac);
     // the epilogue is fused when one workgroup covers a whole 128-column head
     if constexpr (NW == 8 && CW == 1) {
       if (epi && Dv == 128) {
         hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW, true>), dim3(static_cast<unsigned>(main_blocks)),
                            dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                           static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
+                           static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
                            chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
                            static_cast<const bf16*>(epi->z), epi->gamma, epi->eps);
         return launch_status();
@@ -1542,9 +1599,10 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
     }
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
-                       chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
-                       static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+                       static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu,
+                       scs, N_s, T_tot, Hk, Hv, Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, fac,
+                       static_cast<bf16*>(y), static_cast<const bf16*>(nullptr),
+                       static_cast<const float*>(nullptr), 0.0f);
   } else {
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
@@ -1610,6 +1668,57 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
 }
 
 inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk == 32 || chunk == 64; }
+
+// The Comba forward (bf16 activations): the WY pass on P K^T Gram blocks and
+// the chunk loop reading with p, over a [K, V] state pool; one key head per
+// value head.
+struct CombaArgs {
+  const bf16 *q, *k, *v, *p, *beta;
+  const float* g;
+  float* pool;
+  int64_t pool_size;
+  const int64_t *ci, *cu;
+  int N_s;
+  int64_t T_tot;
+  int H, V, chunk;
+  float scale;
+  bf16* o;
+};
+
+template <int DK, int CT, int NW>
+int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stream) {
+  int* scs = reinterpret_cast<int*>(ws + L.scs);
+  bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
+  bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
+  bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
+  float* fac = reinterpret_cast<float*>(ws + L.fac);
+  const size_t maxc = static_cast<size_t>(a.T_tot / a.chunk) + static_cast<size_t>(a.N_s);
+  const size_t wy_blocks = maxc * static_cast<size_t>(a.H);
+  const size_t main_blocks = static_cast<size_t>(a.N_s) * a.H * (a.V / (16 * NW));
+  if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.N_s, a.T_tot, a.chunk, scs);
+  hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
+                     stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
+                     Th, Tl, Ph, fac);
+  hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true>), dim3(static_cast<unsigned>(main_blocks)),
+                     dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool, a.pool_size, a.ci, a.cu, scs, a.N_s,
+                     a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, a.o,
+                     static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+  return launch_status();
+}
+
+template <int DK, int CT>
+int comba_dispatch_nw(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stream) {
+  if (a.V % 128 == 0) return comba_launch<DK, CT, 8>(a, ws, L, stream);
+  if (a.V % 64 == 0) return comba_launch<DK, CT, 4>(a, ws, L, stream);
+  return comba_launch<DK, CT, 2>(a, ws, L, stream);
+}
+
+template <int DK>
+int comba_dispatch_ct(int CT, const CombaArgs& a, char* ws, const Layout& L, hipStream_t stream) {
+  return CT == 32 ? comba_dispatch_nw<DK, 32>(a, ws, L, stream) : comba_dispatch_nw<DK, 64>(a, ws, L, stream);
+}
 
 }  // namespace
 }  // namespace gdn
@@ -1731,4 +1840,53 @@ extern "C" int gdn_validate_varlen(const int64_t* cu_seqlens, const int64_t* cac
   }
   free(h);
   return rc;
+}
+
+extern "C" size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K, int V, int chunk,
+                                                gdn_dtype act) {
+  (void)K;
+  (void)V;
+  if (T_tot < 0 || N_s < 0 || H <= 0 || !gdn::valid_chunk(chunk) || act != GDN_BF16) return 0;
+  return gdn::layout(T_tot, N_s, H, chunk, true).total;
+}
+
+extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, const void* p,
+                                   const void* beta, const float* g, float* state_pool, int64_t pool_size,
+                                   const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
+                                   int64_t T_tot, int H, int K, int V, int chunk, float scale, void* o,
+                                   gdn_dtype act, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  using namespace gdn;
+  if (N_s < 0 || T_tot < 0 || pool_size < 0 || H <= 0 || K <= 0 || V <= 0) return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (act != GDN_BF16 || !(K == 32 || K == 64 || K == 128) || V % 32 != 0 || V > 256 ||
+      !valid_chunk(chunk))
+    return GDN_ERR_UNSUPPORTED;
+  if (N_s == 0) return GDN_OK;
+  if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
+  if (T_tot > 0 && (!q || !k || !v || !p || !beta || !g || !o)) return GDN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(p) || !aligned16(state_pool) ||
+      !aligned16(workspace))
+    return GDN_ERR_ALIGN;
+  // per-chunk copy offsets are 32-bit: 64 token rows of q/k/p/v must span < 1 GiB
+  if (static_cast<uint64_t>(H) * K * 2 * 64 >= (1ull << 30) || static_cast<uint64_t>(H) * V * 2 * 64 >= (1ull << 30))
+    return GDN_ERR_UNSUPPORTED;
+  const Layout L = layout(T_tot, N_s, H, chunk, true);
+  if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  const size_t pool_bytes = static_cast<size_t>(pool_size) * H * K * V * sizeof(float);
+  const size_t o_bytes = static_cast<size_t>(T_tot) * H * V * sizeof(bf16);
+  if (overlaps(o, o_bytes, state_pool, pool_bytes) || overlaps(workspace, L.total, state_pool, pool_bytes) ||
+      overlaps(workspace, L.total, o, o_bytes))
+    return GDN_ERR_ALIAS;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(K));
+  const CombaArgs a{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                    static_cast<const bf16*>(p), static_cast<const bf16*>(beta), g, state_pool, pool_size,
+                    cache_indices, cu_seqlens, N_s, T_tot, H, V, chunk, scale, static_cast<bf16*>(o)};
+  char* ws = static_cast<char*>(workspace);
+  const int CT = chunk_tile(chunk);
+  switch (K) {
+    case 32: return comba_dispatch_ct<32>(CT, a, ws, L, stream);
+    case 64: return comba_dispatch_ct<64>(CT, a, ws, L, stream);
+    default: return comba_dispatch_ct<128>(CT, a, ws, L, stream);
+  }
 }

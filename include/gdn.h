@@ -279,6 +279,53 @@ int gdn_gated_rmsnorm(const void* o, const void* z, const float* gamma,
                       float eps, void* y, int64_t T_tot, int Hv, int Dv,
                       gdn_dtype act, hipStream_t stream);
 
+/*
+ * comba_chunk_prefill_workspace - bytes of device workspace
+ * comba_chunk_prefill needs (0 for invalid arguments or act != GDN_BF16).
+ * Depends only on T_tot, N_s, H and chunk.
+ */
+size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
+                                     int V, int chunk, gdn_dtype act);
+
+/*
+ * comba_chunk_prefill - the Comba forward over a variable-length batch,
+ * chunkwise (WY), advancing a pool of [K, V] states in place.  Source: KBench
+ * `comba_decode_step` spec, spec_md (the step, and the forward task as that
+ * step run over every token) and contract_md (argument order and dtypes).
+ * Sequence s owns the packed tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and
+ * the slot state_pool[cache_indices[s]]; for every head the result equals
+ * running comba_decode_step token by token from the slot's contents:
+ *     S <- exp(g) S;  u = beta (v - S^T p);  S <- S + k u^T;  o = S^T (scale q)
+ * and writing the final S back.  In chunk form the WY factor is
+ * (I + A)^-1 with A_ij = beta_i exp(G_i - G_j) (p_i . k_j), j < i, G the
+ * in-chunk cumulative log-gate.  Results depend on `chunk` only through
+ * rounding.  Keys are used as given (no normalisation).
+ *
+ * q, k, p       [T_tot, H, K] bf16.   v, o [T_tot, H, V] bf16 (o written).
+ * beta          [T_tot, H] bf16.      g [T_tot, H] float32 (log-decay, <= 0
+ *               expected; the chunk form may overflow for g > 0).
+ * state_pool    [pool_size, H, K, V] float32 (value index contiguous, the
+ *               comba_decode_step layout), read and written in place.
+ * cache_indices [N_s] int64, cu_seqlens [N_s + 1] int64: device arrays with
+ *               the contract of gdn_chunk_prefill (gdn_validate_varlen
+ *               checks it); zero-length sequences leave their slot untouched.
+ * chunk         8, 16, 32 or 64 tokens.   scale: <= 0 selects K^-1/2.
+ * workspace     device memory of at least comba_chunk_prefill_workspace()
+ *               bytes, 16-byte aligned; its contents are scratch.
+ * Requirements: act == GDN_BF16 (else GDN_ERR_UNSUPPORTED); K in {32, 64,
+ * 128}; V a multiple of 32, <= 256; q, k, p, v, state_pool 16-byte aligned;
+ * 64 tokens of q (64 * H * K elements) and of v each under 1 GiB.
+ * N_s == 0 is a no-op.  On an in-kernel failure the referenced slots are
+ * unspecified (the update is in place).
+ */
+int comba_chunk_prefill(const void* q, const void* k, const void* v,
+                        const void* p, const void* beta, const float* g,
+                        float* state_pool, int64_t pool_size,
+                        const int64_t* cache_indices, const int64_t* cu_seqlens,
+                        int N_s, int64_t T_tot, int H, int K, int V, int chunk,
+                        float scale, void* o, gdn_dtype act, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a gdn_status value (static string, never NULL). */
 const char* gdn_status_string(int status);
 

@@ -234,3 +234,33 @@ def test_decode_window_validation(lib):
     assert win(q=A + 2 * BIG + 4) == ALIGN
     assert win(sout=A + 64) == ALIAS             # partial overlap with state_in
     assert win(y=A + 16) == ALIAS
+
+
+def test_comba_prefill_validation(lib):
+    def cp(q=A, k=A + BIG, v=A + 2 * BIG, p=A + 3 * BIG, beta=A + 4 * BIG, g=A + 5 * BIG,
+           pool=A + 6 * BIG, ci=A + 7 * BIG, cu=A + 8 * BIG, o=A + 9 * BIG, ws=A + 10 * BIG,
+           N_s=2, T=100, H=4, K=128, V=128, chunk=64, act=1, ws_bytes=None, P=4):
+        if ws_bytes is None:
+            ws_bytes = lib.comba_chunk_prefill_workspace(T, N_s, H, K, V, chunk, 1)
+        return lib.comba_chunk_prefill(_p(q), _p(k), _p(v), _p(p), _p(beta), _p(g), _p(pool), P, _p(ci),
+                                       _p(cu), N_s, T, H, K, V, chunk, ctypes.c_float(0.0), _p(o), act,
+                                       _p(ws), ws_bytes, None)
+    f = lib.comba_chunk_prefill_workspace
+    assert f(100, 2, 4, 128, 128, 64, 1) == lib.gdn_chunk_prefill_workspace(100, 2, 4, 4, 128, 128, 64, 1)
+    assert f(100, 2, 4, 128, 128, 64, 0) == 0            # bf16 activations only
+    assert f(100, 2, 4, 128, 128, 48, 1) == 0
+    assert cp(N_s=-1) == SHAPE
+    assert cp(H=0) == SHAPE
+    assert cp(act=9) == DTYPE
+    assert cp(act=0) == UNSUP                             # fp32 activations
+    assert cp(K=256) == UNSUP
+    assert cp(V=40) == UNSUP
+    assert cp(chunk=128) == UNSUP
+    assert cp(p=0) == NULL
+    assert cp(ws=0) == NULL
+    assert cp(p=A + 3 * BIG + 8) == ALIGN
+    assert cp(pool=A + 6 * BIG + 4) == ALIGN
+    assert cp(ws_bytes=1024) == WORKSPACE
+    assert cp(o=A + 6 * BIG + 64) == ALIAS                # o inside the pool
+    assert cp(ws=A + 9 * BIG + 64) == ALIAS               # workspace inside o
+    assert cp(N_s=0, q=0, p=0) == OK

@@ -44,3 +44,10 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_comba_prefill_min_bytes_per_token():
+    # q, k, p (32 heads x 128), v, o (32 x 128) and beta (32) in bf16, g (32)
+    # in fp32: 2 * (3*4096 + 2*4096 + 32) + 128 = 41,152 bytes per token
+    assert bench.comba_prefill_min_bytes(1, 0, 32, 128, 128) == 41_152
+    assert bench.comba_prefill_min_bytes(0, 1, 32, 128, 128) == 2 * 32 * 128 * 128 * 4
