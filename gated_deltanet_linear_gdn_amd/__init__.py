@@ -24,6 +24,7 @@ __all__ = [
     "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
     "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
+    "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
     "comba_chunk_prefill_workspace", "comba_chunk_prefill",
 ]
 
@@ -86,6 +87,11 @@ def load_library():
     lib.gdn_conv_silu.argtypes = [_vp] * 3 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4 + [_vp] * 3 + [_i, _vp]
     lib.gdn_gated_rmsnorm.restype = _i
     lib.gdn_gated_rmsnorm.argtypes = [_vp] * 3 + [_f, _vp, _i64, _i, _i, _i, _vp]
+    lib.gdn_chunk_prefill_fixed_workspace.restype = ctypes.c_size_t
+    lib.gdn_chunk_prefill_fixed_workspace.argtypes = [_i, _i64, _i, _i, _i, _i, _i, _i]
+    lib.gdn_chunk_prefill_fixed.restype = _i
+    lib.gdn_chunk_prefill_fixed.argtypes = ([_vp] * 6 + [_i, _i64] + [_i] * 5
+                                            + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.comba_chunk_prefill_workspace.restype = ctypes.c_size_t
     lib.comba_chunk_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i]
     lib.comba_chunk_prefill.restype = _i
@@ -304,6 +310,43 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags,
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
           _stream())
+    return y
+
+
+def gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace ``gdn_chunk_prefill_fixed`` needs (torch.bfloat16
+    activations by default)."""
+    act = 0 if dtype == torch.float32 else 1
+    return int(load_library().gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk, act))
+
+
+def gdn_chunk_prefill_fixed(q, k, v, g, beta, state, chunk=64, scale=None, l2norm=True, y=None,
+                            workspace=None):
+    """Chunkwise prefill of a fixed-length batch, ``state`` updated in place
+    (see ``gdn_chunk_prefill_fixed`` in include/gdn.h).  q, k [B,T,Hk,Dk];
+    v [B,T,Hv,Dv]; g, beta [B,T,Hv] f32; state [B,Hv,Dv,Dk] f32; y [B,T,Hv,Dv]
+    or None.  Returns y."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev, act = q.device, q.dtype
+    if y is None:
+        y = torch.empty((B, T, Hv, Dv), dtype=act, device=dev)
+    _check("q", q, (B, T, Hk, Dk), act, dev)
+    _check("k", k, (B, T, Hk, Dk), act, dev)
+    _check("v", v, (B, T, Hv, Dv), act, dev)
+    _check("g", g, (B, T, Hv), torch.float32, dev)
+    _check("beta", beta, (B, T, Hv), torch.float32, dev)
+    _check("state", state, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("y", y, (B, T, Hv, Dv), act, dev)
+    need = gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk, act)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    _call("gdn_chunk_prefill_fixed", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T,
+          Hk, Hv, Dk, Dv, int(chunk), sc, GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q),
+          _ptr(workspace), workspace.numel(), _stream())
     return y
 
 

@@ -198,6 +198,16 @@ __device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_t
   len = b - a;
 }
 
+// The fixed-T batch layout as a varlen batch: sequence s owns tokens
+// s*T .. s*T + T - 1 and state slot s.
+__global__ __launch_bounds__(256) void gdn_fixed_index_kernel(int64_t* __restrict__ cu,
+                                                              int64_t* __restrict__ ci, int B,
+                                                              int64_t T) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i <= B) cu[i] = static_cast<int64_t>(i) * T;
+  if (i < B) ci[i] = i;
+}
+
 __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
                                                              int N_s, int64_t T_tot, int C,
                                                              int* __restrict__ scs) {
@@ -1646,11 +1656,16 @@ int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, con
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
-  if (CT == 32)
+  if constexpr (DK == 256) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
                                   chunk, scale, l2norm, y, ws, L, epi, stream);
-  return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                chunk, scale, l2norm, y, ws, L, epi, stream);
+  } else {
+    if (CT == 32)
+      return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
+                                    chunk, scale, l2norm, y, ws, L, epi, stream);
+    return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
+                                  chunk, scale, l2norm, y, ws, L, epi, stream);
+  }
 }
 
 template <typename T>
@@ -1663,11 +1678,21 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
     case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
     case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
     case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+    case 256:  // bf16 activations only (the fp32 kernels would spill at this width)
+      if constexpr (std::is_same<T, bf16>::value)
+        return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+      else
+        return GDN_ERR_UNSUPPORTED;
   }
   return GDN_ERR_UNSUPPORTED;
 }
 
 inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk == 32 || chunk == 64; }
+
+// Dk = 256 runs chunks of at most 32 tokens: two 64-row K and Q tiles of
+// that width (plus their double buffers) do not fit in a CU's LDS, 32-row
+// ones do.  The chunk size changes results only through rounding.
+inline int effective_chunk(int Dk, int chunk) { return Dk == 256 && chunk > 32 ? 32 : chunk; }
 
 // The Comba forward (bf16 activations): the WY pass on P K^T Gram blocks and
 // the chunk loop reading with p, over a [K, V] state pool; one key head per
@@ -1717,7 +1742,10 @@ int comba_dispatch_nw(const CombaArgs& a, char* ws, const Layout& L, hipStream_t
 
 template <int DK>
 int comba_dispatch_ct(int CT, const CombaArgs& a, char* ws, const Layout& L, hipStream_t stream) {
-  return CT == 32 ? comba_dispatch_nw<DK, 32>(a, ws, L, stream) : comba_dispatch_nw<DK, 64>(a, ws, L, stream);
+  if constexpr (DK == 256)  // 32-row tiles only (effective_chunk)
+    return comba_dispatch_nw<DK, 32>(a, ws, L, stream);
+  else
+    return CT == 32 ? comba_dispatch_nw<DK, 32>(a, ws, L, stream) : comba_dispatch_nw<DK, 64>(a, ws, L, stream);
 }
 
 }  // namespace
@@ -1729,24 +1757,27 @@ extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, in
   if (T_tot < 0 || N_s < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || !gdn::valid_chunk(chunk) ||
       !gdn::is_act(act))
     return 0;
-  return gdn::layout(T_tot, N_s, Hv, chunk, act == GDN_BF16).total;
+  return gdn::layout(T_tot, N_s, Hv, gdn::effective_chunk(Dk, chunk), act == GDN_BF16).total;
 }
 
 namespace gdn {
 namespace {
 
+// Every host-side check, then (unless check_only) the launches.
 int chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   float* state_pool, int64_t pool_size, const int64_t* cache_indices,
                   const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
                   int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
-                  size_t workspace_bytes, const Epilogue* epi, hipStream_t stream) {
+                  size_t workspace_bytes, const Epilogue* epi, hipStream_t stream,
+                  bool check_only = false) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!(Dk == 32 || Dk == 64 || Dk == 128) || Dv % 32 != 0 || Dv > 256 || !valid_chunk(chunk) ||
-      (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
+  if (!(Dk == 32 || Dk == 64 || Dk == 128 || (Dk == 256 && act == GDN_BF16)) || Dv % 32 != 0 ||
+      Dv > 256 || !valid_chunk(chunk) || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
     return GDN_ERR_UNSUPPORTED;
+  chunk = effective_chunk(Dk, chunk);
   if (N_s == 0) return GDN_OK;
   if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
   if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
@@ -1765,6 +1796,7 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
     return GDN_ERR_ALIAS;
   if (epi && (overlaps(epi->z, y_bytes, state_pool, pool_bytes) || overlaps(epi->z, y_bytes, workspace, L.total)))
     return GDN_ERR_ALIAS;
+  if (check_only) return GDN_OK;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(Dk));
   const int l2 = (flags & GDN_QK_L2NORM) ? 1 : 0;
   const int CT = chunk_tile(chunk);
@@ -1844,10 +1876,9 @@ extern "C" int gdn_validate_varlen(const int64_t* cu_seqlens, const int64_t* cac
 
 extern "C" size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K, int V, int chunk,
                                                 gdn_dtype act) {
-  (void)K;
   (void)V;
-  if (T_tot < 0 || N_s < 0 || H <= 0 || !gdn::valid_chunk(chunk) || act != GDN_BF16) return 0;
-  return gdn::layout(T_tot, N_s, H, chunk, true).total;
+  if (T_tot < 0 || N_s < 0 || H <= 0 || K <= 0 || !gdn::valid_chunk(chunk) || act != GDN_BF16) return 0;
+  return gdn::layout(T_tot, N_s, H, gdn::effective_chunk(K, chunk), true).total;
 }
 
 extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, const void* p,
@@ -1859,9 +1890,10 @@ extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, 
   using namespace gdn;
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || H <= 0 || K <= 0 || V <= 0) return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (act != GDN_BF16 || !(K == 32 || K == 64 || K == 128) || V % 32 != 0 || V > 256 ||
+  if (act != GDN_BF16 || !(K == 32 || K == 64 || K == 128 || K == 256) || V % 32 != 0 || V > 256 ||
       !valid_chunk(chunk))
     return GDN_ERR_UNSUPPORTED;
+  chunk = effective_chunk(K, chunk);
   if (N_s == 0) return GDN_OK;
   if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
   if (T_tot > 0 && (!q || !k || !v || !p || !beta || !g || !o)) return GDN_ERR_NULL;
@@ -1887,6 +1919,63 @@ extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, 
   switch (K) {
     case 32: return comba_dispatch_ct<32>(CT, a, ws, L, stream);
     case 64: return comba_dispatch_ct<64>(CT, a, ws, L, stream);
-    default: return comba_dispatch_ct<128>(CT, a, ws, L, stream);
+    case 128: return comba_dispatch_ct<128>(CT, a, ws, L, stream);
+    default: return comba_dispatch_ct<256>(CT, a, ws, L, stream);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-T batch layout: q, k [B, T, Hk, Dk], v, y [B, T, Hv, Dv], g, beta
+// [B, T, Hv], state [B, Hv, Dv, Dk] -- the packed varlen layout with B
+// sequences of T tokens and state slot b for sequence b.  The index arrays
+// go to the end of the workspace (written by a small kernel on the stream),
+// then the varlen path runs.
+
+namespace gdn {
+namespace {
+inline size_t fixed_index_bytes(int B) { return up(sizeof(int64_t) * (2 * static_cast<size_t>(B) + 1)); }
+}  // namespace
+}  // namespace gdn
+
+extern "C" size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv, int Dk, int Dv,
+                                                    int chunk, gdn_dtype act) {
+  if (B < 0 || T < 0 || (T > 0 && B > INT64_MAX / T)) return 0;
+  const size_t main = gdn_chunk_prefill_workspace(static_cast<int64_t>(B) * T, B, Hk, Hv, Dk, Dv, chunk, act);
+  return main ? main + gdn::fixed_index_bytes(B) : 0;
+}
+
+extern "C" int gdn_chunk_prefill_fixed(const void* q, const void* k, const void* v, const float* g,
+                                       const float* beta, float* state, int B, int64_t T, int Hk,
+                                       int Hv, int Dk, int Dv, int chunk, float scale, unsigned flags,
+                                       void* y, gdn_dtype act, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  using namespace gdn;
+  if (B < 0 || T < 0 || (T > 0 && B > INT64_MAX / T) || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
+      Hv % Hk != 0)
+    return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (B == 0 || T == 0) return GDN_OK;
+  if (!workspace) return GDN_ERR_NULL;
+  const size_t total = gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk, act);
+  if (total == 0) return GDN_ERR_UNSUPPORTED;
+  if (workspace_bytes < total) return GDN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GDN_ERR_ALIGN;
+  const size_t main = total - fixed_index_bytes(B);
+  int64_t* cu = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + main);
+  int64_t* ci = cu + B + 1;
+  // the index arrays must not overlap the state or y (the varlen call checks the rest)
+  const size_t state_bytes = static_cast<size_t>(B) * Hv * Dv * Dk * sizeof(float);
+  const size_t y_bytes = static_cast<size_t>(B) * T * Hv * Dv * act_bytes(act);
+  if (overlaps(cu, total - main, state, state_bytes) || overlaps(cu, total - main, y, y_bytes))
+    return GDN_ERR_ALIAS;
+  // everything the varlen call checks, before the index kernel touches the device
+  const int rc = chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk,
+                               Dv, chunk, scale, flags, y, act, workspace, main, nullptr, stream, true);
+  if (rc != GDN_OK) return rc;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(gdn_fixed_index_kernel, dim3(static_cast<unsigned>((B + 1 + 255) / 256)), dim3(256), 0,
+                     stream, cu, ci, B, T);
+  if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
+  return chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk, Dv,
+                       chunk, scale, flags, y, act, workspace, main, nullptr, stream);
 }

@@ -144,8 +144,9 @@ int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
 /*
  * gdn_chunk_prefill_workspace - bytes of device workspace gdn_chunk_prefill
  * needs for these sizes and activation dtype (0 for invalid arguments).  It
- * depends only on T_tot, N_s, Hv, chunk and act; the other sizes are
- * accepted for a stable signature.
+ * depends only on T_tot, N_s, Hv, chunk, act and (through the chunk of at
+ * most 32 tokens that Dk = 256 runs) Dk; the other sizes are accepted for a
+ * stable signature.
  */
 size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
                                    int Dk, int Dv, int chunk, gdn_dtype act);
@@ -184,8 +185,10 @@ size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
  * flags         0 or GDN_QK_L2NORM.
  * workspace     device memory of at least gdn_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
- * Requirements: Dk in {32, 64, 128}; Dv a multiple of 32, <= 256;
- * Hv % Hk == 0; q, k, v, state_pool 16-byte aligned; 64 tokens of q/k
+ * Requirements: Dk in {32, 64, 128, 256} (256 with bf16 activations only;
+ * it runs chunks of at most 32 tokens whatever `chunk` asks for: two 64-row
+ * operand tiles of that width do not fit in LDS); Dv a multiple of 32,
+ * <= 256; Hv % Hk == 0; q, k, v, state_pool 16-byte aligned; 64 tokens of q/k
  * (64 * Hk * Dk elements) and of v (64 * Hv * Dv) each under 1 GiB, else
  * GDN_ERR_UNSUPPORTED.  N_s == 0 is a no-op.
  * On an in-kernel failure the referenced slots are unspecified (the update
@@ -280,9 +283,43 @@ int gdn_gated_rmsnorm(const void* o, const void* z, const float* gamma,
                       gdn_dtype act, hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill_fixed_workspace - bytes of device workspace
+ * gdn_chunk_prefill_fixed needs (0 for invalid arguments): that of
+ * gdn_chunk_prefill for B sequences of T tokens, plus the index arrays.
+ */
+size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv,
+                                         int Dk, int Dv, int chunk,
+                                         gdn_dtype act);
+
+/*
+ * gdn_chunk_prefill_fixed - gdn_chunk_prefill over a fixed-length batch in
+ * the metaltile layouts (metaltile-std `gated_delta.rs`, "Layouts" of
+ * `mt_gated_delta_chunk`): B sequences of T tokens each, the state one slice
+ * per (b, hv) updated in place.  The same computation as gdn_chunk_prefill
+ * with cu_seqlens = {0, T, 2T, ..., BT} and cache_indices = {0, ..., B-1}.
+ *
+ * q, k          [B, T, Hk, Dk] act.     v, y [B, T, Hv, Dv] act (y written).
+ * g, beta       [B, T, Hv] float32.
+ * state         [B, Hv, Dv, Dk] float32 (the gdn_decode_step layout), read
+ *               and written in place.
+ * chunk, scale, flags: as for gdn_chunk_prefill.
+ * workspace     device memory of at least gdn_chunk_prefill_fixed_workspace()
+ *               bytes, 16-byte aligned; its contents are scratch (the call
+ *               writes the index arrays into its end before the kernels run).
+ * Requirements: those of gdn_chunk_prefill.  B == 0 or T == 0 is a no-op.
+ */
+int gdn_chunk_prefill_fixed(const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state,
+                            int B, int64_t T, int Hk, int Hv, int Dk, int Dv,
+                            int chunk, float scale, unsigned flags, void* y,
+                            gdn_dtype act, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * comba_chunk_prefill_workspace - bytes of device workspace
  * comba_chunk_prefill needs (0 for invalid arguments or act != GDN_BF16).
- * Depends only on T_tot, N_s, H and chunk.
+ * Depends only on T_tot, N_s, H, chunk and (K = 256 runs chunks of at most
+ * 32 tokens) K.
  */
 size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
                                      int V, int chunk, gdn_dtype act);
@@ -313,7 +350,8 @@ size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
  * workspace     device memory of at least comba_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
  * Requirements: act == GDN_BF16 (else GDN_ERR_UNSUPPORTED); K in {32, 64,
- * 128}; V a multiple of 32, <= 256; q, k, p, v, state_pool 16-byte aligned;
+ * 128, 256} (256 runs chunks of at most 32 tokens); V a multiple of 32,
+ * <= 256; q, k, p, v, state_pool 16-byte aligned;
  * 64 tokens of q (64 * H * K elements) and of v each under 1 GiB.
  * N_s == 0 is a no-op.  On an in-kernel failure the referenced slots are
  * unspecified (the update is in place).

@@ -135,13 +135,17 @@ def test_prefill_workspace_size(lib):
     assert f(100, 2, 2, 4, 128, 128, 64, 7) == 0                 # unknown dtype
     # bf16 builds T and P on chip: no per-chunk matrices in the workspace
     assert f(1000, 2, 2, 4, 128, 128, 64, 1) < f(1000, 2, 2, 4, 128, 128, 64, 0)
+    # Dk = 256 runs 32-token chunks whatever chunk asks for
+    assert f(1000, 2, 2, 4, 256, 128, 64, 1) == f(1000, 2, 2, 4, 128, 128, 32, 1)
+    assert f(1000, 2, 2, 4, 256, 128, 16, 1) == f(1000, 2, 2, 4, 128, 128, 16, 1)
 
 
 def test_prefill_validation(lib):
     assert prefill(lib, N_s=-1) == SHAPE
     assert prefill(lib, Hk=3) == SHAPE
     assert prefill(lib, act=9) == DTYPE
-    assert prefill(lib, Dk=256) == UNSUP
+    assert prefill(lib, Dk=512) == UNSUP
+    assert prefill(lib, Dk=256, act=0) == UNSUP            # Dk = 256 with bf16 activations only
     assert prefill(lib, Dv=40) == UNSUP
     assert prefill(lib, chunk=128) == UNSUP
     assert prefill(lib, flags=2) == UNSUP
@@ -253,7 +257,7 @@ def test_comba_prefill_validation(lib):
     assert cp(H=0) == SHAPE
     assert cp(act=9) == DTYPE
     assert cp(act=0) == UNSUP                             # fp32 activations
-    assert cp(K=256) == UNSUP
+    assert cp(K=512) == UNSUP
     assert cp(V=40) == UNSUP
     assert cp(chunk=128) == UNSUP
     assert cp(p=0) == NULL
@@ -264,3 +268,32 @@ def test_comba_prefill_validation(lib):
     assert cp(o=A + 6 * BIG + 64) == ALIAS                # o inside the pool
     assert cp(ws=A + 9 * BIG + 64) == ALIAS               # workspace inside o
     assert cp(N_s=0, q=0, p=0) == OK
+
+
+def test_fixed_prefill_validation(lib):
+    f = lib.gdn_chunk_prefill_fixed_workspace
+    # the varlen workspace for B sequences of T tokens plus the index arrays
+    assert f(4, 100, 2, 4, 128, 128, 64, 1) > lib.gdn_chunk_prefill_workspace(400, 4, 2, 4, 128, 128, 64, 1)
+    assert f(4, 100, 2, 4, 128, 128, 48, 1) == 0
+    assert f(-1, 100, 2, 4, 128, 128, 64, 1) == 0
+
+    def fx(state=A + 5 * BIG, y=A + 8 * BIG, ws=A + 9 * BIG, B=4, T=100, Hk=2, Hv=4, Dk=128, Dv=128,
+           chunk=64, act=1, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = f(B, T, Hk, Hv, Dk, Dv, chunk, 1)
+        return lib.gdn_chunk_prefill_fixed(_p(A), _p(A + BIG), _p(A + 2 * BIG), _p(A + 3 * BIG),
+                                           _p(A + 4 * BIG), _p(state), B, T, Hk, Hv, Dk, Dv, chunk,
+                                           ctypes.c_float(0.0), 1, _p(y), act, _p(ws), ws_bytes, None)
+    assert fx(B=-1) == SHAPE
+    assert fx(Hk=3) == SHAPE
+    assert fx(act=5) == DTYPE
+    assert fx(B=0, ws=0) == OK
+    assert fx(T=0, ws=0) == OK
+    assert fx(ws=0) == NULL
+    assert fx(chunk=48, ws_bytes=1 << 30) == UNSUP
+    assert fx(Dk=512, ws_bytes=1 << 30) == UNSUP
+    assert fx(ws_bytes=1024) == WORKSPACE
+    assert fx(ws=A + 9 * BIG + 8) == ALIGN
+    main = lib.gdn_chunk_prefill_workspace(400, 4, 2, 4, 128, 128, 64, 1)
+    assert fx(ws=A + 5 * BIG - main) == ALIAS        # index arrays at the start of the state
+    assert fx(y=A + 5 * BIG + 64) == ALIAS           # y inside the state (varlen check)

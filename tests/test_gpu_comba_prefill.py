@@ -63,6 +63,7 @@ CASES = [
     ([100, 3], 1, 128, 96, 64),       # 32-column workgroups
     ([300, 129, 64], 2, 128, 128, 8),
     ([65, 31], 2, 64, 128, 64),
+    ([90, 40, 1], 2, 256, 128, 64),   # K = 256: runs 32-token chunks
 ]
 
 

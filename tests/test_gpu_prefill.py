@@ -104,6 +104,9 @@ CASES = [
     ([37, 100, 5], 2, 4, 128, 128, 32, "bf16"),    # 32-row tiles, eight waves
     ([90, 20], 1, 2, 64, 128, 64, "bf16"),         # Dk = 64 with eight waves
     ([77, 64], 1, 1, 32, 128, 16, "bf16"),         # Dk = 32, chunk 16, eight waves
+    ([100, 37, 1, 0], 1, 2, 256, 128, 64, "bf16"), # Dk = 256: runs 32-token chunks
+    ([70, 5, 33], 2, 4, 256, 64, 16, "bf16"),      # Dk = 256, four waves, chunk 16
+    ([65, 40], 1, 1, 256, 96, 32, "bf16"),         # Dk = 256, two waves
 ]
 
 
@@ -261,6 +264,7 @@ GATED_CASES = [
     ([70, 5], 1, 2, 128, 256, 64, "bf16"),     # two workgroups per head: separate norm kernel
     ([40, 9], 1, 2, 64, 64, 16, "bf16"),
     ([45, 16], 1, 1, 64, 32, 32, "f32"),
+    ([60, 7], 1, 2, 256, 128, 64, "bf16"),     # Dk = 256, fused norm
 ]
 
 
@@ -297,3 +301,44 @@ def test_gated_prefill_parity(lengths, Hk, Hv, Dk, Dv, chunk, act):
         assert maxrel(yv, y_ref) <= 1e-3
     else:
         assert relF(yv, y_ref) <= 2e-2
+
+
+FIXED_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, chunk, act
+    (3, 100, 2, 4, 128, 128, 64, "bf16"),
+    (2, 1, 1, 2, 64, 64, 32, "bf16"),
+    (4, 77, 1, 3, 256, 128, 64, "bf16"),
+    (2, 50, 1, 2, 64, 32, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,chunk,act", FIXED_CASES)
+def test_fixed_length_prefill(B, T, Hk, Hv, Dk, Dv, chunk, act):
+    """gdn_chunk_prefill_fixed on [B, T, H, D] inputs and a [B, Hv, Dv, Dk]
+    state equals the oracle with cu_seqlens = {0, T, ..., BT} and
+    cache_indices = {0..B-1}, and is bitwise the varlen call on the same data."""
+    rng = np.random.default_rng(B * 1000 + T + Dk + chunk)
+    state0 = _warm_pool(rng, B, Hk, Hv, Dk, Dv, steps=4)
+    inp = synth.prefill_inputs(rng, [T] * B, Hk, Hv, Dk, Dv, pool_size=B, act=act)
+    inp["cache_indices"] = np.arange(B, dtype=np.int64)
+    d = DT[act]
+    g, beta = gdn.gdn_prefill_gates(to_dev(inp["a"], d, DEV), to_dev(inp["b"], d, DEV),
+                                    to_dev(inp["A_log"], torch.float32, DEV),
+                                    to_dev(inp["dt_bias"], torch.float32, DEV))
+    q, k, v = (to_dev(inp[n], d, DEV) for n in ("q", "k", "v"))
+    state = to_dev(state0, torch.float32, DEV)
+    y = gdn.gdn_chunk_prefill_fixed(q.view(B, T, Hk, Dk), k.view(B, T, Hk, Dk), v.view(B, T, Hv, Dv),
+                                    g.view(B, T, Hv), beta.view(B, T, Hv), state, chunk=chunk)
+    torch.cuda.synchronize()
+    P_ref, y_ref = _run_oracle(inp, state0)
+    assert maxrel(to_np(state), P_ref) <= 1e-3
+    if act == "f32":
+        assert maxrel(to_np(y).reshape(B * T, Hv, Dv), y_ref) <= 1e-3
+    else:
+        assert relF(to_np(y).reshape(B * T, Hv, Dv), y_ref) <= 2e-2
+    pool = to_dev(state0, torch.float32, DEV)
+    y2 = gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, to_dev(inp["cache_indices"], torch.int64, DEV),
+                               to_dev(inp["cu_seqlens"], torch.int64, DEV), chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, state)
+    assert torch.equal(y2.view(B, T, Hv, Dv), y)
