@@ -82,12 +82,12 @@ def _timed(fn, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def bench_decode(steps, warmup, device):
+def bench_decode(steps, warmup, device, B=None, Dk=None):
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
     c = synth.DECODE_B256
-    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    B, Hk, Hv, Dk, Dv = B or c["B"], c["Hk"], c["Hv"], Dk or c["Dk"], c["Dv"]
     rng = np.random.default_rng(0)
     toks = []
     for _ in range(16):
@@ -206,12 +206,12 @@ def prefill_min_bytes(T, n_seq, Hk, Hv, Dk, Dv, act_bytes=2):
     return T * per_token + n_seq * 2 * Hv * Dv * Dk * 4
 
 
-def bench_prefill(steps, warmup, device):
+def bench_prefill(steps, warmup, device, Dk=None):
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
     c = synth.PREFILL_VARLEN
-    Hk, Hv, Dk, Dv, P, C = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"], c["chunk"]
+    Hk, Hv, Dk, Dv, P, C = c["Hk"], c["Hv"], Dk or c["Dk"], c["Dv"], c["pool"], c["chunk"]
     rng = np.random.default_rng(0)
     lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
     inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
@@ -240,9 +240,10 @@ def bench_prefill(steps, warmup, device):
         gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y, workspace=ws)
 
     sec = _timed(step, steps, warmup)
+    C = min(C, 32) if Dk == 256 else C  # the chunk Dk = 256 runs
     flops = prefill_flops_per_token(Hv, Dk, Dv, C) * T
     return dict(sec=sec, tokens=T, flops=flops, lengths=[int(x) for x in lengths],
-                issued=prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C),
+                issued=prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C) if C == 64 else None,
                 min_bytes=prefill_min_bytes(T, len(lengths), Hk, Hv, Dk, Dv),
                 shape=dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, chunk=C, pool=P))
 
@@ -447,6 +448,8 @@ def main():
     com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
     cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device)
+    pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256)
+    dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
     copy_gbps = bench_copy(device)
@@ -508,6 +511,15 @@ def main():
                                                                  / BF16_PEAK_TFLOPS, 4),
                           "min_bytes": cpre["min_bytes"],
                           "hbm_frac_of_peak": round(cpre["min_bytes"] / cpre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+        "dk256": {"workload": "key head size 256 (value 128): gdn_chunk_prefill at the varlen token mix "
+                              "(Hk=16 Hv=48, 32-token chunks) and gdn_decode_step at B=128 (the same "
+                              "1.6 GB of state per step as the headline)",
+                  "prefill_us_per_call": round(pre256["sec"] * 1e6, 2),
+                  "prefill_tokens_per_s": round(pre256["tokens"] / pre256["sec"], 1),
+                  "prefill_canonical_TFLOPs": round(pre256["flops"] / pre256["sec"] / 1e12, 2),
+                  "decode_GBps": round(dec256["state_bytes"] / dec256["sec"] / 1e9, 2),
+                  "decode_frac_of_hbm_peak": round(dec256["state_bytes"] / dec256["sec"] / 1e9
+                                                   / HBM_PEAK_GBPS, 4)},
         "layer": {"workload": "prologue gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per "
                               "slot) and epilogue gdn_gated_rmsnorm around the varlen prefill; conv "
                               "also as a decode step of 256 sequences",
