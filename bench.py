@@ -112,9 +112,11 @@ def bench_decode(steps, warmup, device, B=None, Dk=None):
                 shape=dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv))
 
 
-def bench_window(steps, warmup, device, T):
+def bench_window(steps, warmup, device, T, chunked=False):
     """Decode windows of T tokens per sequence at the B=256 decode batch,
-    committing all T (functional ping-pong, like the decode step)."""
+    committing all T: gdn_decode_window (functional ping-pong, like the
+    decode step) or, chunked, the same recurrence as gdn_chunk_prefill_fixed
+    with no norm and scale 1 (in place, chunk = min(T, 64))."""
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
@@ -129,11 +131,20 @@ def bench_window(steps, warmup, device, T):
     bufs = [torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=device),
             torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=device)]
     y = torch.empty((B, T, Hv, Dv), dtype=torch.bfloat16, device=device)
+    chunk = min(max(T, 8), 64)
+    ws = torch.empty(gdn.gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk) if chunked else 1,
+                     dtype=torch.uint8, device=device)
+    for w in wins:
+        w["beta32"] = w["beta"].float().contiguous()
 
     def step(i):
         w = wins[i % 4]
-        gdn.gdn_decode_window(bufs[i % 2], bufs[(i + 1) % 2], w["q"], w["k"], w["v"], w["g"], w["beta"],
-                              y=y)
+        if chunked:
+            gdn.gdn_chunk_prefill_fixed(w["q"], w["k"], w["v"], w["g"], w["beta32"], bufs[0], chunk=chunk,
+                                        scale=1.0, l2norm=False, y=y, workspace=ws)
+        else:
+            gdn.gdn_decode_window(bufs[i % 2], bufs[(i + 1) % 2], w["q"], w["k"], w["v"], w["g"], w["beta"],
+                                  y=y)
 
     for i in range(4):
         step(i)
@@ -452,6 +463,7 @@ def main():
     dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
+    cwins = {T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
     copy_gbps = bench_copy(device)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
@@ -482,7 +494,13 @@ def main():
                           **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
                                        "tokens_per_s": round(w["tokens"] / w["sec"], 1),
                                        "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
-                             for T, w in wins.items()}},
+                             for T, w in wins.items()},
+                          "chunked": {"workload": "the same committed windows as gdn_chunk_prefill_fixed "
+                                                  "(no norm, scale 1, chunk min(T, 64)), in place",
+                                      **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
+                                                   "tokens_per_s": round(w["tokens"] / w["sec"], 1),
+                                                   "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
+                                         for T, w in cwins.items()}}},
         "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
                   "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
                   "us_per_step": round(com["sec"] * 1e6, 2),

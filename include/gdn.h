@@ -91,6 +91,9 @@ int gdn_decode_step(const float* state_in, float* state_out, const void* q,
  *               state_in; every token's y is written in all cases.
  * Requirements: 1 <= T <= 8 and the gdn_decode_step sizes; q, k,
  * state_in, state_out 16-byte aligned.
+ * A committed window (commit == T) is also gdn_chunk_prefill_fixed with
+ * flags 0 and scale 1 on the same layouts (in place on the state, with a
+ * workspace); from T = 4 on that MFMA path is the faster of the two.
  */
 int gdn_decode_window(const float* state_in, float* state_out, const void* q,
                       const void* k, const void* v, const float* g,

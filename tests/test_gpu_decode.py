@@ -255,3 +255,24 @@ def test_decode_window_matches_single_steps_and_runs_in_place():
     assert maxrel(to_np(s_io), to_np(S)) <= 1e-6
     assert maxrel(to_np(y_win), to_np(y_steps)) <= 1e-2  # bf16 outputs of near-identical fp32 values
     assert relF(to_np(y_win), to_np(y_steps)) <= 1e-3
+
+
+def test_committed_window_equals_the_fixed_length_prefill():
+    """A committed 8-token window is gdn_chunk_prefill_fixed with no norm and
+    scale 1 on the same [B, T, H, D] layouts (the faster route for T >= 4)."""
+    rng = np.random.default_rng(32)
+    B, T, Hk, Hv, Dk, Dv = 6, 8, 2, 6, 128, 128
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    w = _window_tokens(rng, B, T, Hk, Hv, Dk, Dv, "bf16")
+    dw = {n: to_dev(x, torch.float32 if n == "g" else torch.bfloat16, DEV) for n, x in w.items()}
+    s_win = to_dev(S0, torch.float32, DEV)
+    _, y_win = gdn.gdn_decode_window(s_win, s_win, dw["q"], dw["k"], dw["v"], dw["g"], dw["beta"])
+    s_fix = to_dev(S0, torch.float32, DEV)
+    y_fix = gdn.gdn_chunk_prefill_fixed(dw["q"], dw["k"], dw["v"], dw["g"], dw["beta"].float().contiguous(),
+                                        s_fix, chunk=8, scale=1.0, l2norm=False)
+    torch.cuda.synchronize()
+    S_ref, y_ref = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"])
+    assert maxrel(to_np(s_win), S_ref) <= 1e-5
+    assert maxrel(to_np(s_fix), S_ref) <= 1e-3
+    assert relF(to_np(y_fix), y_ref) <= 2e-2
+    assert relF(to_np(y_fix), to_np(y_win)) <= 2e-2
