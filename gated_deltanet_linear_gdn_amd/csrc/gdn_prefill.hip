@@ -932,15 +932,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   // t = kg*16 + l16 takes row t's sums of squares from row block kg
   f32x4 gk[NPAIR], gq[NPAIR];
   float mk = 0.f, mq = 0.f;
+  // the Q (and Comba's P) fragments of row block I + 1 are in flight while
+  // the Gram blocks of row block I run
+  bf16x8v qn[KB], pn[KB];
+  auto load_qp = [&](int I) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      qn[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + row_off(I) + kb * 32));
+      if constexpr (COMBA)
+        pn[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(pr + row_off(I) + kb * 32));
+    }
+  };
+  load_qp(0);
 #pragma unroll
   for (int I = 0; I < MT; ++I) {
     bf16x8v qf[KB], lf[KB];  // lf: the left factor of the A Gram blocks (k, or Comba's p)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      qf[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + row_off(I) + kb * 32));
-      lf[kb] = COMBA ? __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(pr + row_off(I) + kb * 32))
-                     : kf[I][kb];
+      qf[kb] = qn[kb];
+      lf[kb] = COMBA ? pn[kb] : kf[I][kb];
     }
+    if (I + 1 < MT) load_qp(I + 1);
     if constexpr (!COMBA) {
       const float sk = sumsq(kf[I]), sq = sumsq(qf);
       mk = kg == I ? sk : mk;
