@@ -144,3 +144,19 @@ def test_comba_prefill_workload_sampled():
         assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, s
         assert relF(ov[idx][:, hs], o_ref) <= 2e-2, s
     _check_untouched(pool, pool0, inp)
+
+
+def test_comba_many_short_sequences():
+    """2,500 sequences of 0..6 tokens over a pool of 2,505 slots."""
+    rng = np.random.default_rng(78)
+    N, H, K, V = 2500, 2, 32, 32
+    lengths = rng.integers(0, 7, size=N)
+    P = N + 5
+    pool0 = (0.3 * rng.standard_normal((P, H, K, V))).astype(np.float32)
+    inp = synth.comba_prefill_inputs(rng, lengths, H, K, V, P)
+    pool, o = _run_gpu(inp, pool0, 16)
+    P_ref, o_ref = oracle.comba_prefill(*(inp[n] for n in NAMES), pool0, inp["cache_indices"],
+                                        inp["cu_seqlens"])
+    assert maxrel(to_np(pool), P_ref) <= 1e-3
+    assert relF(to_np(o), o_ref) <= 2e-2
+    _check_untouched(pool, pool0, inp)

@@ -342,3 +342,18 @@ def test_fixed_length_prefill(B, T, Hk, Hv, Dk, Dv, chunk, act):
     torch.cuda.synchronize()
     assert torch.equal(pool, state)
     assert torch.equal(y2.view(B, T, Hv, Dv), y)
+
+
+def test_many_short_sequences():
+    """2,500 sequences of 0..6 tokens (more sequences than the chunk-map scan
+    has threads, so each thread scans a range): every sequence and slot
+    matches the oracle, empty sequences leave their slots untouched."""
+    rng = np.random.default_rng(77)
+    N, Hk, Hv, Dk, Dv = 2500, 1, 2, 32, 32
+    lengths = rng.integers(0, 7, size=N)
+    P = N + 5
+    pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P, act="bf16")
+    pool, y = _run_gpu(inp, pool0, 8, "bf16")
+    P_ref, y_ref = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
