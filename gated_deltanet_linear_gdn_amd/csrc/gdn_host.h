@@ -21,6 +21,22 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
+// A buffer as (address, bytes).
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True when a buffer that is only read shares a byte with one that is
+// written (kernels read inputs while other workgroups write outputs).
+template <int NI, int NO>
+inline bool inputs_overlap_outputs(const Span (&in)[NI], const Span (&out)[NO]) {
+  for (int i = 0; i < NI; ++i)
+    for (int o = 0; o < NO; ++o)
+      if (overlaps(in[i].p, in[i].n, out[o].p, out[o].n)) return true;
+  return false;
+}
+
 inline bool pow2_head(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 // The gated RMS norm epilogue (gdn_layer.hip), also used by the prefill

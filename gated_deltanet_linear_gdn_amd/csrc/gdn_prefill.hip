@@ -1808,6 +1808,14 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
     return GDN_ERR_ALIAS;
   if (epi && (overlaps(epi->z, y_bytes, state_pool, pool_bytes) || overlaps(epi->z, y_bytes, workspace, L.total)))
     return GDN_ERR_ALIAS;
+  {
+    const size_t qk_bytes = static_cast<size_t>(T_tot) * Hk * Dk * act_bytes(act);
+    const size_t v_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
+    const size_t gb_bytes = static_cast<size_t>(T_tot) * Hv * sizeof(float);
+    const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {g, gb_bytes}, {beta, gb_bytes}};
+    const Span out[] = {{y, y_bytes}, {state_pool, pool_bytes}, {workspace, L.total}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
   if (check_only) return GDN_OK;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(Dk));
   const int l2 = (flags & GDN_QK_L2NORM) ? 1 : 0;
@@ -1922,6 +1930,14 @@ extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, 
   if (overlaps(o, o_bytes, state_pool, pool_bytes) || overlaps(workspace, L.total, state_pool, pool_bytes) ||
       overlaps(workspace, L.total, o, o_bytes))
     return GDN_ERR_ALIAS;
+  {
+    const size_t qk_bytes = static_cast<size_t>(T_tot) * H * K * sizeof(bf16);
+    const size_t tb = static_cast<size_t>(T_tot) * H;
+    const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {p, qk_bytes}, {v, o_bytes},
+                       {beta, tb * sizeof(bf16)}, {g, tb * sizeof(float)}};
+    const Span out[] = {{o, o_bytes}, {state_pool, pool_bytes}, {workspace, L.total}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(K));
   const CombaArgs a{static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                     static_cast<const bf16*>(p), static_cast<const bf16*>(beta), g, state_pool, pool_size,
@@ -1978,8 +1994,15 @@ extern "C" int gdn_chunk_prefill_fixed(const void* q, const void* k, const void*
   // the index arrays must not overlap the state or y (the varlen call checks the rest)
   const size_t state_bytes = static_cast<size_t>(B) * Hv * Dv * Dk * sizeof(float);
   const size_t y_bytes = static_cast<size_t>(B) * T * Hv * Dv * act_bytes(act);
-  if (overlaps(cu, total - main, state, state_bytes) || overlaps(cu, total - main, y, y_bytes))
-    return GDN_ERR_ALIAS;
+  const size_t qk_bytes = static_cast<size_t>(B) * T * Hk * Dk * act_bytes(act);
+  const size_t gb_bytes = static_cast<size_t>(B) * T * Hv * sizeof(float);
+  {
+    const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, y_bytes}, {g, gb_bytes}, {beta, gb_bytes}};
+    const Span out[] = {{cu, total - main}};
+    if (overlaps(cu, total - main, state, state_bytes) || overlaps(cu, total - main, y, y_bytes) ||
+        inputs_overlap_outputs(in, out))
+      return GDN_ERR_ALIAS;
+  }
   // everything the varlen call checks, before the index kernel touches the device
   const int rc = chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk,
                                Dv, chunk, scale, flags, y, act, workspace, main, nullptr, stream, true);

@@ -193,7 +193,9 @@ size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
  * operand tiles of that width do not fit in LDS); Dv a multiple of 32,
  * <= 256; Hv % Hk == 0; q, k, v, state_pool 16-byte aligned; 64 tokens of q/k
  * (64 * Hk * Dk elements) and of v (64 * Hv * Dv) each under 1 GiB, else
- * GDN_ERR_UNSUPPORTED.  N_s == 0 is a no-op.
+ * GDN_ERR_UNSUPPORTED.  y, state_pool and the workspace overlap neither
+ * each other nor any input (q, k, v, g, beta), else GDN_ERR_ALIAS.
+ * N_s == 0 is a no-op.
  * On an in-kernel failure the referenced slots are unspecified (the update
  * is in place): callers that need to retry keep a copy of those slots.
  */
@@ -356,6 +358,8 @@ size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
  * 128, 256} (256 runs chunks of at most 32 tokens); V a multiple of 32,
  * <= 256; q, k, p, v, state_pool 16-byte aligned;
  * 64 tokens of q (64 * H * K elements) and of v each under 1 GiB.
+ * o, state_pool and the workspace overlap neither each other nor any input
+ * (q, k, p, v, beta, g), else GDN_ERR_ALIAS.
  * N_s == 0 is a no-op.  On an in-kernel failure the referenced slots are
  * unspecified (the update is in place).
  */

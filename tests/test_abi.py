@@ -157,6 +157,9 @@ def test_prefill_validation(lib):
     assert prefill(lib, Hv=65536, Hk=65536, Dv=256) == UNSUP  # 64 tokens of v span >= 1 GiB
     assert prefill(lib, ws_bytes=1024) == WORKSPACE
     assert prefill(lib, y=A + 5 * BIG + 64) == ALIAS      # y inside the pool
+    assert prefill(lib, y=A + 2 * BIG + 64) == ALIAS      # y over v (an input)
+    assert prefill(lib, ws=A + 4 * BIG) == ALIAS          # workspace over beta
+    assert prefill(lib, q=A + 5 * BIG) == ALIAS           # an input inside the pool
     assert prefill(lib, N_s=0, q=0, cu=0) == OK           # nothing to do
 
 
@@ -267,6 +270,8 @@ def test_comba_prefill_validation(lib):
     assert cp(ws_bytes=1024) == WORKSPACE
     assert cp(o=A + 6 * BIG + 64) == ALIAS                # o inside the pool
     assert cp(ws=A + 9 * BIG + 64) == ALIAS               # workspace inside o
+    assert cp(o=A + 3 * BIG) == ALIAS                     # o over p (an input)
+    assert cp(beta=A + 10 * BIG) == ALIAS                 # an input inside the workspace
     assert cp(N_s=0, q=0, p=0) == OK
 
 
@@ -297,3 +302,4 @@ def test_fixed_prefill_validation(lib):
     main = lib.gdn_chunk_prefill_workspace(400, 4, 2, 4, 128, 128, 64, 1)
     assert fx(ws=A + 5 * BIG - main) == ALIAS        # index arrays at the start of the state
     assert fx(y=A + 5 * BIG + 64) == ALIAS           # y inside the state (varlen check)
+    assert fx(ws=A + 4 * BIG - main) == ALIAS        # index arrays over beta
