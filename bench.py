@@ -45,7 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 DECODE_TRAFFIC = {
     "bytes": 1659866752,
     "sources_sha256": {
-        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "eafb02eea5c0cb385cfd5bbf8ab512580fb1905b6664beb12d0fc5dc177f5f8e",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "25b04ae7d2607b0d94a506e00236447ea0e3f49adc7a7795234d012e75e0a6ef",
         "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "dba007333ce8708713001b4524a494916ff0b0e7a70406cf145e1271f616b6d5",
     },
 }

@@ -156,6 +156,13 @@ extern "C" int comba_decode_step(const float* state, float* state_new, const voi
   const size_t o_bytes = static_cast<size_t>(B) * H * V * act_bytes(act);
   if (overlaps(o, o_bytes, state_new, state_bytes) || overlaps(o, o_bytes, state, state_bytes))
     return GDN_ERR_ALIAS;
+  {
+    const size_t qk = static_cast<size_t>(B) * H * K * act_bytes(act);
+    const size_t bh = static_cast<size_t>(B) * H;
+    const Span in[] = {{q, qk}, {k, qk}, {p, qk}, {v, o_bytes}, {beta, bh * act_bytes(act)}, {g, bh * sizeof(float)}};
+    const Span out[] = {{o, o_bytes}, {state_new, state_bytes}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(K));
   const long slices = static_cast<long>(B) * H;
   if (act == GDN_BF16)

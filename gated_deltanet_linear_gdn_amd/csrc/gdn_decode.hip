@@ -343,6 +343,13 @@ extern "C" int gdn_decode_window(const float* state_in, float* state_out, const 
   const size_t y_bytes = static_cast<size_t>(B) * T * Hv * Dv * act_bytes(act);
   if (overlaps(y, y_bytes, state_in, state_bytes) || (state_out && overlaps(y, y_bytes, state_out, state_bytes)))
     return GDN_ERR_ALIAS;
+  {
+    const size_t qk = static_cast<size_t>(B) * T * Hk * Dk * act_bytes(act);
+    const size_t tv = static_cast<size_t>(B) * T * Hv;
+    const Span in[] = {{q, qk}, {k, qk}, {v, y_bytes}, {g, tv * sizeof(float)}, {beta, tv * act_bytes(act)}};
+    const Span out[] = {{y, y_bytes}, {state_out, commit > 0 ? state_bytes : 0}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
   if (act == GDN_BF16)
     return launch_window_dk<bf16>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, T, commit, stream);
   return launch_window_dk<float>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, T, commit, stream);
@@ -366,6 +373,13 @@ extern "C" int gdn_decode_step(const float* state_in, float* state_out, const vo
   const size_t y_bytes = static_cast<size_t>(B) * Hv * Dv * act_bytes(act);
   if (overlaps(y, y_bytes, state_out, state_bytes) || overlaps(y, y_bytes, state_in, state_bytes))
     return GDN_ERR_ALIAS;
+  {
+    const size_t qk = static_cast<size_t>(B) * Hk * Dk * act_bytes(act);
+    const size_t bv = static_cast<size_t>(B) * Hv;
+    const Span in[] = {{q, qk}, {k, qk}, {v, y_bytes}, {g, bv * sizeof(float)}, {beta, bv * act_bytes(act)}};
+    const Span out[] = {{y, y_bytes}, {state_out, state_bytes}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
   if (act == GDN_BF16)
     return launch<bf16>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, stream);
   return launch<float>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dk, Dv, stream);

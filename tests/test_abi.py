@@ -74,6 +74,9 @@ def test_decode_validation(lib):
     # partial overlap of the two states, and y inside the state
     assert decode(lib, state_out=A + 4096) == ALIAS
     assert decode(lib, y=A + 64) == ALIAS
+    # an input under an output: y over v, q inside the new state
+    assert decode(lib, y=A + 4 * BIG + 32) == ALIAS
+    assert decode(lib, q=A + BIG + 1024) == ALIAS
     # B == 0 is a no-op that touches nothing, even with null pointers
     assert decode(lib, B=0, q=0, k=0) == OK
 
@@ -94,6 +97,7 @@ def test_comba_validation(lib):
     assert comba(lib, p=0) == NULL
     assert comba(lib, o=A + 8 * BIG + 2) == ALIGN
     assert comba(lib, state_new=A + 16) == ALIAS
+    assert comba(lib, o=A + 5 * BIG) == ALIAS                     # o over p
     assert comba(lib, H=0, q=0) == OK
 
 
@@ -241,6 +245,8 @@ def test_decode_window_validation(lib):
     assert win(q=A + 2 * BIG + 4) == ALIGN
     assert win(sout=A + 64) == ALIAS             # partial overlap with state_in
     assert win(y=A + 16) == ALIAS
+    assert win(y=A + 3 * BIG) == ALIAS           # y over k
+    assert win(g=A + BIG + 256) == ALIAS         # g inside the committed state
 
 
 def test_comba_prefill_validation(lib):
