@@ -69,7 +69,8 @@ enum gdn_status {
  * g         [B, Hv] float32 (log-space gate).   beta [B, Hv] act.
  * Requirements: Hk >= 1, Hv % Hk == 0, Dk in {32, 64, 128, 256},
  * Dv a multiple of 32 in [32, 256], B >= 0 (B == 0 is a no-op);
- * state_in, state_out, q and k 16-byte aligned.
+ * state_in, state_out, q and k 16-byte aligned.  y overlaps neither state;
+ * no input (q, k, v, g, beta) overlaps y or state_out (GDN_ERR_ALIAS).
  */
 int gdn_decode_step(const float* state_in, float* state_out, const void* q,
                     const void* k, const void* v, const float* g,
@@ -90,7 +91,8 @@ int gdn_decode_step(const float* state_in, float* state_out, const void* q,
  *               window (state_out not written, may be NULL); may equal
  *               state_in; every token's y is written in all cases.
  * Requirements: 1 <= T <= 8 and the gdn_decode_step sizes; q, k,
- * state_in, state_out 16-byte aligned.
+ * state_in, state_out 16-byte aligned; the aliasing rules of
+ * gdn_decode_step (state_out counts as written only when commit > 0).
  * A committed window (commit == T) is also gdn_chunk_prefill_fixed with
  * flags 0 and scale 1 on the same layouts (in place on the state, with a
  * workspace); from T = 4 on that MFMA path is the faster of the two.
@@ -116,7 +118,9 @@ int gdn_decode_window(const float* state_in, float* state_out, const void* q,
  * g         [B, H] float32 (log-decay, <= 0 in practice).
  * scale     query scale; a value <= 0 selects K^-1/2.
  * Requirements: K and V in {32, 64, 128, 256}, not both 256; B, H >= 0;
- * state, state_new, q, k, p, v and o 16-byte aligned.
+ * state, state_new, q, k, p, v and o 16-byte aligned.  o overlaps neither
+ * state; no input (q, k, p, v, beta, g) overlaps o or state_new
+ * (GDN_ERR_ALIAS).
  */
 int comba_decode_step(const float* state, float* state_new, const void* q,
                       const void* k, const void* v, const void* p,
