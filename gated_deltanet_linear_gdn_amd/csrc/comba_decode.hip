@@ -24,13 +24,39 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int K, int V, typename T>
-__global__ __launch_bounds__(kThreads) void comba_decode_kernel(
+// N consecutive activations (a thread's rows of p, q or k) -> fp32: 16-byte
+// vector loads when the run is a whole number of them (the run then starts
+// 16-byte aligned: the slice and row offsets are multiples of it), else
+// element by element.
+template <typename T, int N>
+__device__ __forceinline__ void load_run(const T* src, float (&out)[N]) {
+  if constexpr ((N * sizeof(T)) % 16 == 0) {
+    constexpr int PER = 16 / sizeof(T);
+#pragma unroll
+    for (int c = 0; c < N / PER; ++c) {
+      const uint4 w = reinterpret_cast<const uint4*>(src)[c];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        if constexpr (sizeof(T) == 2)
+          out[c * PER + e] = (e & 1) ? __uint_as_float(u[e >> 1] & 0xffff0000u) : __uint_as_float(u[e >> 1] << 16);
+        else
+          out[c * PER + e] = __uint_as_float(u[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) out[n] = Act<T>::load(src + n);
+  }
+}
+
+template <int K, int V, typename T, int NT>
+__global__ __launch_bounds__(NT) void comba_decode_kernel(
     const float* state, float* state_new, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ p, const T* __restrict__ beta,
     const float* __restrict__ g, T* __restrict__ o, float scale) {
   constexpr int LPR = V / 4;             // lanes per row
-  constexpr int RG = kThreads / LPR;     // row groups
+  constexpr int RG = NT / LPR;           // row groups
   constexpr int RPT = K / RG;            // rows per thread (consecutive)
   static_assert(K % RG == 0 && RPT >= 1, "shape");
 
@@ -51,12 +77,11 @@ __global__ __launch_bounds__(kThreads) void comba_decode_kernel(
 
   const size_t koff = static_cast<size_t>(slice) * K + r0;
   float pr[RPT], qr[RPT], kr[RPT];
+  load_run<T, RPT>(p + koff, pr);
+  load_run<T, RPT>(q + koff, qr);
+  load_run<T, RPT>(k + koff, kr);
 #pragma unroll
-  for (int n = 0; n < RPT; ++n) {
-    pr[n] = Act<T>::load(p + koff + n);
-    qr[n] = scale * Act<T>::load(q + koff + n);
-    kr[n] = Act<T>::load(k + koff + n);
-  }
+  for (int n = 0; n < RPT; ++n) qr[n] *= scale;
   const f32x4 vv = Act<T>::load4(v + static_cast<size_t>(slice) * V + c4 * 4);
   const float gate = expf(g[slice]);
   const float bt = Act<T>::load(beta + slice);
@@ -95,9 +120,10 @@ int launch_kv(const float* state, float* state_new, const void* q, const void* k
               const void* v, const void* p, const void* beta, const float* g, void* o,
               long slices, float scale, hipStream_t stream) {
   if (slices > 0x7fffffffL) return GDN_ERR_SHAPE;
+  constexpr int NT = (V / 4) * K < kThreads ? (V / 4) * K : kThreads;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((comba_decode_kernel<K, V, T>), dim3(static_cast<unsigned>(slices)),
-                     dim3(kThreads), 0, stream, state, state_new, static_cast<const T*>(q),
+  hipLaunchKernelGGL((comba_decode_kernel<K, V, T, NT>), dim3(static_cast<unsigned>(slices)),
+                     dim3(NT), 0, stream, state, state_new, static_cast<const T*>(q),
                      static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<const T*>(p), static_cast<const T*>(beta), g,
                      static_cast<T*>(o), scale);
