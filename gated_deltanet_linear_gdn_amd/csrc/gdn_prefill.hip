@@ -187,7 +187,12 @@ template <> struct Raw<float> {
 };
 
 // ----------------------------------------------------------------------------
-// 1. chunk map: scs[s] = sum_{s' < s} ceil(L_s' / C), scs[N_s] = total.
+// 1. chunk map: scs[s] = sum_{s' < s} ceil(L_s' / C), scs[N_s] = total, and
+// after it (scs + N_s + 1) the order in which the chunk loop takes the
+// sequences: longest first, by the bit length of the chunk count (so a long
+// sequence never waits for a whole round of short ones to finish before its
+// chain starts; the order within a bit length is arbitrary, and no result
+// depends on it).
 
 __device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_tot, int64_t& b0,
                                            int64_t& len) {
@@ -230,13 +235,35 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
     __syncthreads();
   }
   int run = part[tid] - local;  // exclusive prefix of this thread's range
+  __shared__ int bucket[33];       // sequences per bit length of the chunk count (0..32)
+  if (tid < 33) bucket[tid] = 0;
+  __syncthreads();
   for (int s = s0; s < s0 + per && s < N_s; ++s) {
     scs[s] = run;
     int64_t b0, len;
     seq_bounds(cu, s, T_tot, b0, len);
-    run += static_cast<int>((len + C - 1) / C);
+    const int n = static_cast<int>((len + C - 1) / C);
+    run += n;
+    atomicAdd(&bucket[32 - __clz(n)], 1);
   }
   if (tid == 1023) scs[N_s] = part[1023];
+  __syncthreads();
+  if (tid == 0) {  // first rank of each bit length, longest first
+    int r = 0;
+    for (int b = 32; b >= 0; --b) {
+      const int cnt = bucket[b];
+      bucket[b] = r;
+      r += cnt;
+    }
+  }
+  __syncthreads();
+  int* ord = scs + N_s + 1;
+  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+    int64_t b0, len;
+    seq_bounds(cu, s, T_tot, b0, len);
+    const int n = static_cast<int>((len + C - 1) / C);
+    ord[atomicAdd(&bucket[32 - __clz(n)], 1)] = s;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -447,8 +474,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
   __shared__ float sGC;
 
   const int nvb = Dv / BV;
-  const int s = blockIdx.x / (Hv * nvb);
-  const int rem = blockIdx.x - s * (Hv * nvb);
+  const int pos = blockIdx.x / (Hv * nvb);
+  const int s = scs[N_s + 1 + pos];  // longest sequences first
+  const int rem = blockIdx.x - pos * (Hv * nvb);
   const int hv = rem / nvb;
   const int vb = rem - hv * nvb;
   const int64_t slot = cache_indices[s];
@@ -1181,8 +1209,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sPr[COMBA ? Tiles::Qcopy::ELEMS : 8];
 
   const int nvb = Dv / BV;
-  const int s = blockIdx.x / (Hv * nvb);
-  const int rem = blockIdx.x - s * (Hv * nvb);
+  const int pos = blockIdx.x / (Hv * nvb);
+  const int s = scs[N_s + 1 + pos];  // longest sequences first
+  const int rem = blockIdx.x - pos * (Hv * nvb);
   const int hv = rem / nvb;
   const int vb = rem - hv * nvb;
   const int64_t slot = cache_indices[s];
@@ -1569,7 +1598,7 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const size_t tile = up(mats * per * sizeof(bf16));
   Layout L;
   size_t off = 0;
-  L.scs = off; off += up(sizeof(int) * (static_cast<size_t>(N_s) + 1));
+  L.scs = off; off += up(sizeof(int) * (2 * static_cast<size_t>(N_s) + 1));  // chunk map + order
   L.th = off; off += tile;
   L.tl = off; off += tile;
   L.ph = off; off += tile;
