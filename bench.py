@@ -43,7 +43,7 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # read for a 2 GiB device copy), valid for the kernel built from these
 # sources only: after any change to them the figure is reported as null.
 DECODE_TRAFFIC = {
-    "bytes": 1659866752,
+    "bytes": 1659865280,
     "sources_sha256": {
         "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "25b04ae7d2607b0d94a506e00236447ea0e3f49adc7a7795234d012e75e0a6ef",
         "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "dba007333ce8708713001b4524a494916ff0b0e7a70406cf145e1271f616b6d5",
@@ -82,7 +82,10 @@ def _timed(fn, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def bench_decode(steps, warmup, device, B=None, Dk=None):
+def bench_decode(steps, warmup, device, B=None, Dk=None, inplace=True):
+    """gdn_decode_step at the B=256 decode batch: the state updated in place
+    (state_out == state_in, as a serving loop keeps its state cache), or
+    functionally between two buffers (ping-pong)."""
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
@@ -94,14 +97,16 @@ def bench_decode(steps, warmup, device, B=None, Dk=None):
         t = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
         toks.append({n: _dev(a, torch.float32 if n == "g" else torch.bfloat16, device)
                      for n, a in t.items()})
-    bufs = [torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=device),
-            torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=device)]
+    bufs = [torch.zeros((B, Hv, Dv, Dk), dtype=torch.float32, device=device)]
+    if not inplace:
+        bufs.append(torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=device))
     y = torch.empty((B, Hv, Dv), dtype=torch.bfloat16, device=device)
 
     def step(i):
         t = toks[i % 16]
-        gdn.gdn_decode_step(bufs[i % 2], bufs[(i + 1) % 2], t["q"], t["k"], t["v"], t["g"],
-                            t["beta"], y)
+        src = bufs[0] if inplace else bufs[i % 2]
+        dst = bufs[0] if inplace else bufs[(i + 1) % 2]
+        gdn.gdn_decode_step(src, dst, t["q"], t["k"], t["v"], t["g"], t["beta"], y)
 
     for i in range(synth.WARMUP_STEPS):      # realistic state magnitudes, untimed
         step(i)
@@ -455,6 +460,7 @@ def main():
     import torch
     device = torch.device("cuda:0")
     dec = bench_decode(args.steps, args.warmup, device)
+    dec_pp = bench_decode(max(10, args.steps // 2), args.warmup, device, inplace=False)
     com = bench_comba(args.steps, args.warmup, device)
     com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
@@ -481,12 +487,13 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "gdn_decode_step, large decode batch: B=256 Hk=16 Hv=48 Dk=Dv=128, "
-                               "bf16 q/k/v/beta, fp32 g and state (0.8 GB), functional ping-pong",
+                               "bf16 q/k/v/beta, fp32 g and state (0.8 GB), state updated in place",
                    **dec["shape"], "state_bytes_per_step": dec["state_bytes"],
                    "activation_bytes_per_step": dec["act_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": _decode_traffic()},
+        "decode_pingpong_GBps": round(dec_pp["state_bytes"] / dec_pp["sec"] / 1e9, 2),
         "copy_GBps": round(copy_gbps, 1),
         "decode_frac_of_copy": round(gbps / copy_gbps, 4),
         "decode_window": {"workload": "gdn_decode_window at the B=256 decode batch, all T tokens committed",
