@@ -160,3 +160,21 @@ def test_comba_many_short_sequences():
     assert maxrel(to_np(pool), P_ref) <= 1e-3
     assert relF(to_np(o), o_ref) <= 2e-2
     _check_untouched(pool, pool0, inp)
+
+
+def test_comba_prefill_long_memory():
+    """Slowly decaying heads (log-gates of about -1e-3 per token) over 1,900
+    tokens: the state carries information across all 30 chunks, so every
+    chunk's state-side product must keep fp32-grade accuracy."""
+    rng = np.random.default_rng(79)
+    H, K, V, P = 2, 128, 128, 3
+    pool0 = _warm_pool(rng, P, H, K, V)
+    inp = synth.comba_prefill_inputs(rng, [700, 1200], H, K, V, P)
+    inp["g"] = (-1e-3 * rng.random(inp["g"].shape)).astype(np.float32)
+    assert inp["g"].sum(axis=0).min() > -2.0          # the memory really is long
+    pool, o = _run_gpu(inp, pool0, 64)
+    P_ref, o_ref = oracle.comba_prefill(*(inp[n] for n in NAMES), pool0, inp["cache_indices"],
+                                        inp["cu_seqlens"])
+    assert maxrel(to_np(pool), P_ref) <= 1e-3
+    assert relF(to_np(o), o_ref) <= 2e-2
+    _check_untouched(pool, pool0, inp)

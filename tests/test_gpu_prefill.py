@@ -137,6 +137,21 @@ def test_prefill_long_memory():
     _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
 
 
+def test_prefill_long_memory_dk256():
+    """The long-memory case at Dk = 256 (32-token chunks: 60 chunk steps over
+    the longer sequence), where the state-side products span twice the width."""
+    rng = np.random.default_rng(6)
+    Hk, Hv, Dk, Dv = 1, 2, 256, 128
+    pool0 = _warm_pool(rng, 3, Hk, Hv, Dk, Dv, steps=4)
+    inp = synth.prefill_inputs(rng, [700, 1200], Hk, Hv, Dk, Dv, pool_size=3)
+    inp["A_log"] = np.full(Hv, -7.0, dtype=np.float32)
+    g, _ = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    assert g.sum(axis=0).max() > -2.0
+    pool, y = _run_gpu(inp, pool0, 64, "bf16")
+    P_ref, y_ref = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
+
+
 def test_prefill_without_l2norm_and_explicit_scale():
     rng = np.random.default_rng(21)
     Hk, Hv, Dk, Dv = 1, 2, 64, 64
