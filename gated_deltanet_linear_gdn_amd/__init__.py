@@ -108,8 +108,10 @@ def gdn_status_string(status: int) -> str:
 # ------------------------------------------------------------------ helpers
 
 
-def _stream() -> ctypes.c_void_p:
-    return _vp(torch.cuda.current_stream().cuda_stream)
+def _stream(device) -> ctypes.c_void_p:
+    """The current stream of the tensors' device (the library launches on it,
+    with that device current: see _call)."""
+    return _vp(torch.cuda.current_stream(device).cuda_stream)
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
@@ -135,8 +137,11 @@ def _act_of(t: torch.Tensor) -> int:
     return _ACT[t.dtype]
 
 
-def _call(fn: str, *args) -> None:
-    rc = getattr(load_library(), fn)(*args)
+def _call(fn: str, device, *args) -> None:
+    """Call entry point fn with `device` current (its kernels launch on the
+    current HIP device)."""
+    with torch.cuda.device(device):
+        rc = getattr(load_library(), fn)(*args)
     if rc != 0:
         raise GdnError(fn, rc)
 
@@ -167,8 +172,8 @@ def gdn_decode_step(state_in, state_out, q, k, v, g, beta, y=None):
     _check("g", g, (B, Hv), torch.float32, dev)
     _check("beta", beta, (B, Hv), act, dev)
     _check("y", y, (B, Hv, Dv), act, dev)
-    _call("gdn_decode_step", _ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
-          _ptr(g), _ptr(beta), _ptr(y), B, Hk, Hv, Dk, Dv, _act_of(q), _stream())
+    _call("gdn_decode_step", dev, _ptr(state_in), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
+          _ptr(g), _ptr(beta), _ptr(y), B, Hk, Hv, Dk, Dv, _act_of(q), _stream(dev))
     return state_out, y
 
 
@@ -197,8 +202,8 @@ def gdn_decode_window(state_in, state_out, q, k, v, g, beta, commit=None, y=None
     _check("beta", beta, (B, T, Hv), act, dev)
     _check("y", y, (B, T, Hv, Dv), act, dev)
     out_ptr = _ptr(state_out) if state_out is not None else ctypes.c_void_p(0)
-    _call("gdn_decode_window", _ptr(state_in), out_ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-          _ptr(y), B, T, Hk, Hv, Dk, Dv, commit, _act_of(q), _stream())
+    _call("gdn_decode_window", dev, _ptr(state_in), out_ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+          _ptr(y), B, T, Hk, Hv, Dk, Dv, commit, _act_of(q), _stream(dev))
     return state_out, y
 
 
@@ -226,8 +231,8 @@ def comba_decode_step(state, state_new, q, k, v, p, beta, g, o=None, scale=None)
     sc = 0.0 if scale is None else float(scale)
     if scale is not None and not sc > 0.0:
         raise ValueError("scale must be positive (None selects K^-1/2)")
-    _call("comba_decode_step", _ptr(state), _ptr(state_new), _ptr(q), _ptr(k), _ptr(v), _ptr(p),
-          _ptr(beta), _ptr(g), _ptr(o), B, H, K, V, sc, _act_of(q), _stream())
+    _call("comba_decode_step", dev, _ptr(state), _ptr(state_new), _ptr(q), _ptr(k), _ptr(v), _ptr(p),
+          _ptr(beta), _ptr(g), _ptr(o), B, H, K, V, sc, _act_of(q), _stream(dev))
     return state_new, o
 
 
@@ -246,8 +251,8 @@ def gdn_prefill_gates(a, b, A_log, dt_bias, g=None, beta=None):
     _check("dt_bias", dt_bias, (Hv,), torch.float32, dev)
     _check("g", g, (T, Hv), torch.float32, dev)
     _check("beta", beta, (T, Hv), torch.float32, dev)
-    _call("gdn_prefill_gates", _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
-          T, Hv, _act_of(a), _stream())
+    _call("gdn_prefill_gates", dev, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
+          T, Hv, _act_of(a), _stream(dev))
     return g, beta
 
 
@@ -298,18 +303,18 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     sc = 0.0 if scale is None else float(scale)
     flags = GDN_QK_L2NORM if l2norm else 0
     if z is None and gamma is None:
-        _call("gdn_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+        _call("gdn_chunk_prefill", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
               _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
-              flags, _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(), _stream())
+              flags, _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(), _stream(dev))
         return y
     if z is None or gamma is None:
         raise ValueError("the gated output needs both z and gamma")
     _check("z", z, (T, Hv, Dv), act, dev)
     _check("gamma", gamma, (Dv,), torch.float32, dev)
-    _call("gdn_chunk_prefill_gated", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+    _call("gdn_chunk_prefill_gated", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags,
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
-          _stream())
+          _stream(dev))
     return y
 
 
@@ -344,9 +349,9 @@ def gdn_chunk_prefill_fixed(q, k, v, g, beta, state, chunk=64, scale=None, l2nor
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
     sc = 0.0 if scale is None else float(scale)
-    _call("gdn_chunk_prefill_fixed", _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T,
+    _call("gdn_chunk_prefill_fixed", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T,
           Hk, Hv, Dk, Dv, int(chunk), sc, GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q),
-          _ptr(workspace), workspace.numel(), _stream())
+          _ptr(workspace), workspace.numel(), _stream(dev))
     return y
 
 
@@ -384,9 +389,9 @@ def comba_chunk_prefill(q, k, v, p, beta, g, state_pool, cache_indices, cu_seqle
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
     sc = 0.0 if scale is None else float(scale)
-    _call("comba_chunk_prefill", _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(beta), _ptr(g), _ptr(state_pool),
+    _call("comba_chunk_prefill", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(p), _ptr(beta), _ptr(g), _ptr(state_pool),
           P, _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, H, K, V, int(chunk), sc, _ptr(o),
-          _act_of(q), _ptr(workspace), workspace.numel(), _stream())
+          _act_of(q), _ptr(workspace), workspace.numel(), _stream(dev))
     return o
 
 
@@ -412,9 +417,9 @@ def gdn_conv_silu(qkv, conv_w, conv_state, cache_indices, cu_seqlens, Hk, Hv, Dk
     _check("q", q, (T, Hk, Dk), dt, dev)
     _check("k", k, (T, Hk, Dk), dt, dev)
     _check("v", v, (T, Hv, Dv), dt, dev)
-    _call("gdn_conv_silu", _ptr(qkv), _ptr(conv_w), _ptr(conv_state), conv_state.shape[0],
+    _call("gdn_conv_silu", dev, _ptr(qkv), _ptr(conv_w), _ptr(conv_state), conv_state.shape[0],
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v),
-          _act_of(qkv), _stream())
+          _act_of(qkv), _stream(dev))
     return q, k, v
 
 
@@ -428,8 +433,8 @@ def gdn_gated_rmsnorm(o, z, gamma, eps=1e-6, y=None):
     _check("z", z, (T, Hv, Dv), dt, dev)
     _check("gamma", gamma, (Dv,), torch.float32, dev)
     _check("y", y, (T, Hv, Dv), dt, dev)
-    _call("gdn_gated_rmsnorm", _ptr(o), _ptr(z), _ptr(gamma), float(eps), _ptr(y), T, Hv, Dv,
-          _act_of(o), _stream())
+    _call("gdn_gated_rmsnorm", dev, _ptr(o), _ptr(z), _ptr(gamma), float(eps), _ptr(y), T, Hv, Dv,
+          _act_of(o), _stream(dev))
     return y
 
 
@@ -437,5 +442,7 @@ def gdn_validate_varlen(cu_seqlens, cache_indices, T_tot, pool_size) -> int:
     """Check the prefill contract of device ``cu_seqlens``/``cache_indices``
     (synchronises the current stream).  Returns 0 or a negative status."""
     N_s = cache_indices.shape[0]
-    return int(load_library().gdn_validate_varlen(_ptr(cu_seqlens), _ptr(cache_indices), N_s,
-                                                  int(T_tot), int(pool_size), _stream()))
+    dev = cu_seqlens.device
+    with torch.cuda.device(dev):
+        return int(load_library().gdn_validate_varlen(_ptr(cu_seqlens), _ptr(cache_indices), N_s,
+                                                      int(T_tot), int(pool_size), _stream(dev)))
