@@ -215,13 +215,14 @@ __global__ __launch_bounds__(256) void gdn_fixed_index_kernel(int64_t* __restric
 
 __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
                                                              int N_s, int64_t T_tot, int C,
-                                                             int* __restrict__ scs) {
+                                                             int* __restrict__ scs, int wg_per_seq,
+                                                             int num_cu, int allow_split) {
   __shared__ int part[1024];
   const int tid = threadIdx.x;
-  const int per = (N_s + 1023) / 1024;
-  const int s0 = tid * per;
+  const int per_t = (N_s + 1023) / 1024;  // sequences (positions) per thread
+  const int s0 = tid * per_t;
   int local = 0;
-  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+  for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
     int64_t b0, len;
     seq_bounds(cu, s, T_tot, b0, len);
     local += static_cast<int>((len + C - 1) / C);
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
   __shared__ int bucket[33];       // sequences per bit length of the chunk count (0..32)
   if (tid < 33) bucket[tid] = 0;
   __syncthreads();
-  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+  for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
     scs[s] = run;
     int64_t b0, len;
     seq_bounds(cu, s, T_tot, b0, len);
@@ -258,12 +259,59 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
   }
   __syncthreads();
   int* ord = scs + N_s + 1;
-  for (int s = s0; s < s0 + per && s < N_s; ++s) {
+  for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
     int64_t b0, len;
     seq_bounds(cu, s, T_tot, b0, len);
     const int n = static_cast<int>((len + C - 1) / C);
     ord[atomicAdd(&bucket[32 - __clz(n)], 1)] = s;
   }
+  __syncthreads();
+  // wgp[r]: chunk-loop workgroups before position r of that order.  The
+  // first sequences of the order get two per (value head, column block) --
+  // each computing half of the columns with half of its waves, a shorter
+  // step -- as far as CUs would otherwise sit idle (splitting on a full
+  // machine measured slower: the halves then compete with whole workgroups),
+  // and only if that shortens the batch: the longest sequence left whole
+  // must be clearly shorter than the longest split one.
+  int* wgp = ord + N_s;
+  __shared__ int split_n;
+  if (tid == 0) {
+    const int64_t idle = static_cast<int64_t>(num_cu) - static_cast<int64_t>(N_s) * wg_per_seq;
+    int kk = allow_split && idle > 0 ? static_cast<int>(min(idle / wg_per_seq, static_cast<int64_t>(N_s))) : 0;
+    if (kk > 0 && kk < N_s) {
+      int64_t b0, l0, l1;
+      seq_bounds(cu, ord[0], T_tot, b0, l0);
+      seq_bounds(cu, ord[kk], T_tot, b0, l1);
+      if (20 * ((l1 + C - 1) / C) > 17 * ((l0 + C - 1) / C)) kk = 0;
+    }
+    split_n = kk;
+  }
+  __syncthreads();
+  const int room = split_n;  // positions that split
+  int loc = 0;
+  for (int r = s0; r < s0 + per_t && r < N_s; ++r) {
+    int64_t b0, len;
+    seq_bounds(cu, ord[r], T_tot, b0, len);
+    const bool sp = r < room && len > 0;
+    loc += sp ? 2 * wg_per_seq : wg_per_seq;
+  }
+  part[tid] = loc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int wrun = part[tid] - loc;
+  for (int r = s0; r < s0 + per_t && r < N_s; ++r) {
+    wgp[r] = wrun;
+    int64_t b0, len;
+    seq_bounds(cu, ord[r], T_tot, b0, len);
+    const bool sp = r < room && len > 0;
+    wrun += sp ? 2 * wg_per_seq : wg_per_seq;
+  }
+  if (tid == 1023) wgp[N_s] = part[1023];
 }
 
 // ----------------------------------------------------------------------------
@@ -1184,7 +1232,7 @@ struct StreamTiles {
   };
 };
 
-template <int DK, int CT, int NW, int CW, bool GATED = false, bool COMBA = false>
+template <int DK, int CT, int NW, int CW, bool GATED = false, bool COMBA = false, bool HALVES = false>
 __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
     const bf16* __restrict__ v,
@@ -1209,11 +1257,41 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   __shared__ __attribute__((aligned(16))) bf16 sPr[COMBA ? Tiles::Qcopy::ELEMS : 8];
 
   const int nvb = Dv / BV;
-  const int pos = blockIdx.x / (Hv * nvb);
-  const int s = scs[N_s + 1 + pos];  // longest sequences first
-  const int rem = blockIdx.x - pos * (Hv * nvb);
-  const int hv = rem / nvb;
-  const int vb = rem - hv * nvb;
+  // workgroup -> (position in the longest-first order, value head, column
+  // block, half).  HALVES (launched when CUs would otherwise sit idle): wgp
+  // (after the order) counts the workgroups before each position, and a
+  // split sequence has two per (head, block), each computing BV/2 columns on
+  // waves 0..NW/2-1 (half 0 or 1; -1: not split).
+  constexpr bool SPLIT = HALVES && NW == 8 && CW == 1 && !GATED;
+  const int* ord = scs + N_s + 1;
+  const int* wgp = ord + N_s;
+  const int bid = blockIdx.x;
+  int pos, local;
+  if constexpr (SPLIT) {
+    if (bid >= wgp[N_s]) return;
+    int lo = 0, hi = N_s;  // largest position r with wgp[r] <= bid (wgp strictly increases)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (wgp[mid] <= bid) lo = mid; else hi = mid;
+    }
+    pos = lo;
+    local = bid - wgp[pos];
+  } else {
+    pos = bid / (Hv * nvb);
+    local = bid - pos * (Hv * nvb);
+  }
+  const int s = ord[pos];
+  int hv, vb, half = -1;
+  if (SPLIT && wgp[pos + 1] - wgp[pos] == 2 * Hv * nvb) {
+    hv = local / (2 * nvb);
+    const int r2 = local - hv * 2 * nvb;
+    vb = r2 >> 1;
+    half = r2 & 1;
+  } else {
+    hv = local / nvb;
+    vb = local - hv * nvb;
+  }
+  const int hoff = half < 0 ? 0 : half * (BV / 2);  // first column of this half in the block
   const int64_t slot = cache_indices[s];
   if (slot < 0 || slot >= pool_size) return;
   int64_t b0, len;
@@ -1226,8 +1304,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   const int hk = hv / (Hv / Hk);
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave w owns value columns (w*CW + t)*16 + l16 of the block, t < CW
+  // wave w owns value columns (w*CW + t)*16 + l16 of the block (of the half),
+  // t < CW; in a half only waves 0..NW/2-1 compute, the others take their
+  // share of the copies, barriers and y stores
   auto dvl = [&](int t) __attribute__((always_inline)) { return (w * CW + t) * 16 + l16; };
+  const bool act = !SPLIT || half < 0 || w < NW / 2;
 
   const uint32_t kstride = static_cast<uint32_t>(Hk) * DK * 2;  // bytes between tokens
   const uint32_t vstride = static_cast<uint32_t>(Hv) * Dv * 2;
@@ -1265,11 +1346,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     return make_rsrc(base + matix(ci) * NTB * 256, rows(ci) > 0 ? NTB * 512 : 0u);
   };
   auto vy_off = [&](int ci) __attribute__((always_inline)) -> size_t {
-    return (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV;
+    return (static_cast<size_t>(tok0(ci)) * Hv + hv) * Dv + vb * BV + hoff;
   };
+  // (a half's range ends at its own columns: copies of the rest of a row
+  // read the next row's first columns, or zero past the last row)
   auto vy_bytes = [&](int ci) __attribute__((always_inline)) -> uint32_t {
     const int n = rows(ci);
-    return n > 0 ? (n - 1) * vstride + BV * 2 : 0u;
+    return n > 0 ? (n - 1) * vstride + (half < 0 ? BV : BV / 2) * 2 : 0u;
   };
   // The copies of chunk ci's set are a per-wave list of single 1 KiB copies
   // (K, the record, T hi, T lo, Q, P); a step issues them one at a time
@@ -1297,7 +1380,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   // S[t][m][r] is the state at key index m*16 + kg*4 + r, value column dvl(t)
   float* Sp = pool + (static_cast<size_t>(slot) * Hv + hv) * Dv * DK +
-              (COMBA ? static_cast<size_t>(vb * BV) : static_cast<size_t>(vb * BV) * DK);
+              (COMBA ? static_cast<size_t>(vb * BV + hoff) : static_cast<size_t>(vb * BV + hoff) * DK);
   auto s_at = [&](int t, int m, int r) __attribute__((always_inline)) -> float* {
     return COMBA ? Sp + static_cast<size_t>(m * 16 + kg * 4 + r) * Dv + dvl(t)
                  : Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4 + r;
@@ -1307,7 +1390,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   for (int t = 0; t < CW; ++t)
 #pragma unroll
     for (int m = 0; m < DT; ++m) {
-      if constexpr (COMBA) {
+      if (!act) {
+        S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if constexpr (COMBA) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[t][m][r] = *s_at(t, m, r);
       } else {
@@ -1365,6 +1450,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   auto store_y_one = [&](__amdgpu_buffer_rsrc_t yr, int it) __attribute__((always_inline)) {
     const int pc = w * PIECES + it * 64 + lane;
     const int row = pc / SPR, col = (pc - row * SPR) * 8;
+    if (half >= 0 && col >= BV / 2) return;  // a half stores its own columns only
     u32x4 d = *reinterpret_cast<const u32x4*>(sY + row * YP + col);
     if constexpr (GATED) {
       float o8[8], ss = 0.f;
@@ -1400,6 +1486,31 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
 
   // Every operand fragment read from LDS feeds the CW column tiles of the
   // wave; the tiles' MFMA chains are independent and interleave.
+  // a waiting wave of a half: the same copies, y stores and barriers as a
+  // step, no products
+  auto idle_step = [&](int ci, Set& nx) __attribute__((always_inline)) {
+    const Rsrc rn = set_rsrc(ci + 1);
+    {
+#pragma unroll
+      for (int n = 0; n < NJOBS; ++n) copy_job(rn, nx, n);
+      lds_handover();
+      const i32x4 rv = v_rsrc(ci + 1);
+#pragma unroll
+      for (int j = 0; j < Tiles_::Vcopy::PER; ++j) cV.issue_one(rv, sV, w, j);
+      if constexpr (COMBA) {
+        const i32x4 rp = kq_rsrc(pr, ci + 1);
+#pragma unroll
+        for (int j = 0; j < Tiles_::Qcopy::PER; ++j) cPr.issue_one(rp, sPr, w, j);
+      }
+      if (ci > 0) {
+        const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci - 1), vy_bytes(ci - 1));
+#pragma unroll
+        for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
+      }
+      handover<0>();
+    }
+  };
+
   auto step = [&](int ci, const Set& c, Set& nx) __attribute__((always_inline)) {
     const float* F = reinterpret_cast<const float*>(c.F);
     const Rsrc rn = set_rsrc(ci + 1);
@@ -1545,9 +1656,16 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     if constexpr (COMBA) cPr.issue(kq_rsrc(pr, 0), sPr, w);
   }
   handover<0>();
-  for (int ci = 0; ci < nch; ci += 2) {
-    step(ci, setA, setB);
-    if (ci + 1 < nch) step(ci + 1, setB, setA);
+  if (act) {
+    for (int ci = 0; ci < nch; ci += 2) {
+      step(ci, setA, setB);
+      if (ci + 1 < nch) step(ci + 1, setB, setA);
+    }
+  } else {
+    for (int ci = 0; ci < nch; ci += 2) {
+      idle_step(ci, setB);
+      if (ci + 1 < nch) idle_step(ci + 1, setA);
+    }
   }
   // (every copy has landed: each step ends waiting for all of them)
   lds_handover();
@@ -1561,6 +1679,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
   }
 
+  if (!act) return;
 #pragma unroll
   for (int t = 0; t < CW; ++t)
 #pragma unroll
@@ -1590,6 +1709,19 @@ struct Layout {
   size_t scs, th, tl, ph, pl, fac, total;
 };
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails): the chunk map's test for "every sequence split still fits".
+inline int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
 inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
@@ -1598,7 +1730,7 @@ inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const size_t tile = up(mats * per * sizeof(bf16));
   Layout L;
   size_t off = 0;
-  L.scs = off; off += up(sizeof(int) * (2 * static_cast<size_t>(N_s) + 1));  // chunk map + order
+  L.scs = off; off += up(sizeof(int) * (3 * static_cast<size_t>(N_s) + 2));  // chunk map, order, workgroup prefix
   L.th = off; off += tile;
   L.tl = off; off += tile;
   L.ph = off; off += tile;
@@ -1628,10 +1760,16 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   float* fac = reinterpret_cast<float*>(ws + L.fac);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
-  const size_t main_blocks = static_cast<size_t>(N_s) * Hv * (Dv / (16 * NW * CW));
+  const int per_seq = Hv * (Dv / (16 * NW * CW));  // chunk-loop workgroups per sequence, unsplit
+  // when CUs would sit idle, the longest sequences run as two half-width
+  // workgroups each (bf16, eight waves, no fused norm)
+  const bool split = std::is_same<T, bf16>::value && NW == 8 && CW == 1 && !(epi && Dv == 128) &&
+                     static_cast<int64_t>(N_s) * per_seq < cu_count();
+  const size_t main_blocks = static_cast<size_t>(N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs);
+  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs, per_seq,
+                     cu_count(), split ? 1 : 0);
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
@@ -1648,12 +1786,20 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
         return launch_status();
       }
     }
-    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
-                       dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu,
-                       scs, N_s, T_tot, Hk, Hv, Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, fac,
-                       static_cast<bf16*>(y), static_cast<const bf16*>(nullptr),
-                       static_cast<const float*>(nullptr), 0.0f);
+    if (split)
+      hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW, false, false, true>),
+                         dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream,
+                         static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
+                         static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv, chunk,
+                         static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
+                         static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+    else
+      hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
+                         dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                         static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu,
+                         scs, N_s, T_tot, Hk, Hv, Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, fac,
+                         static_cast<bf16*>(y), static_cast<const bf16*>(nullptr),
+                         static_cast<const float*>(nullptr), 0.0f);
   } else {
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
@@ -1760,17 +1906,28 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   float* fac = reinterpret_cast<float*>(ws + L.fac);
   const size_t maxc = static_cast<size_t>(a.T_tot / a.chunk) + static_cast<size_t>(a.N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(a.H);
-  const size_t main_blocks = static_cast<size_t>(a.N_s) * a.H * (a.V / (16 * NW));
+  const int per_seq = a.H * (a.V / (16 * NW));
+  // when CUs would sit idle, the longest sequences run as two half-width workgroups
+  const bool split = NW == 8 && static_cast<int64_t>(a.N_s) * per_seq < cu_count();
+  const size_t main_blocks = static_cast<size_t>(a.N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.N_s, a.T_tot, a.chunk, scs);
+  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.N_s, a.T_tot, a.chunk, scs,
+                     per_seq, cu_count(), split ? 1 : 0);
   hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
                      Th, Tl, Ph, fac);
-  hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true>), dim3(static_cast<unsigned>(main_blocks)),
-                     dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool, a.pool_size, a.ci, a.cu, scs, a.N_s,
-                     a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, a.o,
-                     static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+  if (split)
+    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true, true>),
+                       dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,
+                       a.pool_size, a.ci, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc),
+                       Th, Tl, Ph, fac, a.o, static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr),
+                       0.0f);
+  else
+    hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true>), dim3(static_cast<unsigned>(main_blocks)),
+                       dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool, a.pool_size, a.ci, a.cu, scs, a.N_s,
+                       a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, a.o,
+                       static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
   return launch_status();
 }
 

@@ -372,3 +372,28 @@ def test_many_short_sequences():
     pool, y = _run_gpu(inp, pool0, 8, "bf16")
     P_ref, y_ref = _run_oracle(inp, pool0)
     _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
+
+
+def test_split_of_the_longest_sequence_only():
+    """Four sequences at 48 value heads (192 chunk-loop workgroups): idle CUs
+    leave room to run only the longest as two half-width workgroups per head;
+    the others stay whole.  Checked on sampled heads of every sequence."""
+    rng = np.random.default_rng(81)
+    lengths, Hk, Hv, Dk, Dv, P = [1000, 130, 70, 40], 16, 48, 128, 128, 6
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    pool, y = _run_gpu(inp, pool0, 64, "bf16")
+    yv = to_np(y)
+    assert not np.isnan(yv).any()
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    cu = inp["cu_seqlens"]
+    for s in range(len(lengths)):
+        idx = np.arange(cu[s], cu[s + 1])
+        slot = int(inp["cache_indices"][s])
+        for hk in (0, 15):
+            hs = np.arange(hk * 3, hk * 3 + 3)
+            P_ref, y_ref = oracle.gdn_prefill(
+                inp["q"][idx][:, [hk]], inp["k"][idx][:, [hk]], inp["v"][idx][:, hs],
+                g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0], [0, len(idx)])
+            assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, (s, hk)
+            assert relF(yv[idx][:, hs], y_ref) <= 2e-2, (s, hk)
