@@ -222,14 +222,15 @@ def prefill_min_bytes(T, n_seq, Hk, Hv, Dk, Dv, act_bytes=2):
     return T * per_token + n_seq * 2 * Hv * Dv * Dk * 4
 
 
-def bench_prefill(steps, warmup, device, Dk=None):
+def bench_prefill(steps, warmup, device, Dk=None, lengths=None):
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
     c = synth.PREFILL_VARLEN
     Hk, Hv, Dk, Dv, P, C = c["Hk"], c["Hv"], Dk or c["Dk"], c["Dv"], c["pool"], c["chunk"]
     rng = np.random.default_rng(0)
-    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    drawn = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    lengths = drawn if lengths is None else np.asarray(lengths, dtype=np.int64)
     inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
     T = int(inp["cu_seqlens"][-1])
     bf = torch.bfloat16
@@ -466,6 +467,7 @@ def main():
     pre = bench_prefill(max(5, args.steps // 20), 3, device)
     cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device)
     pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256)
+    pre1 = bench_prefill(max(5, args.steps // 20), 3, device, lengths=[4096])
     dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
@@ -525,6 +527,10 @@ def main():
                     "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
                     "min_bytes": pre["min_bytes"],
                     "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
+        "prefill_single": {"workload": "gdn_prefill_gates + gdn_chunk_prefill of one 4,096-token sequence "
+                                       "(the workload's longest length), Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64",
+                           "us_per_call": round(pre1["sec"] * 1e6, 2),
+                           "tokens_per_s": round(pre1["tokens"] / pre1["sec"], 1)},
         "comba_prefill": {"workload": "comba_chunk_prefill, the same 8 sequences, H=32 K=V=128, bf16, "
                                       "chunk 64, pool 16",
                           "tokens": cpre["tokens"],
