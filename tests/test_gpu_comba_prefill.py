@@ -178,3 +178,18 @@ def test_comba_prefill_long_memory():
     assert maxrel(to_np(pool), P_ref) <= 1e-3
     assert relF(to_np(o), o_ref) <= 2e-2
     _check_untouched(pool, pool0, inp)
+
+
+def test_comba_batch_of_empty_sequences_leaves_the_pool_untouched():
+    """Two sequences of zero tokens (T_tot = 0): the pool is bitwise unchanged."""
+    rng = np.random.default_rng(92)
+    H, K, V, P = 2, 128, 128, 4
+    pool0 = (0.3 * rng.standard_normal((P, H, K, V))).astype(np.float32)
+    pool = to_dev(pool0, torch.float32, DEV)
+    e = lambda *s, dt=BF: torch.empty(s, dtype=dt, device=DEV)
+    ci = torch.tensor([3, 1], dtype=torch.int64, device=DEV)
+    cu = torch.zeros(3, dtype=torch.int64, device=DEV)
+    gdn.comba_chunk_prefill(e(0, H, K), e(0, H, K), e(0, H, V), e(0, H, K), e(0, H), e(0, H, dt=torch.float32),
+                            pool, ci, cu, chunk=64, o=e(0, H, V))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(pool).astype(np.float32), pool0)

@@ -397,3 +397,22 @@ def test_split_of_the_longest_sequence_only():
                 g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0], [0, len(idx)])
             assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, (s, hk)
             assert relF(yv[idx][:, hs], y_ref) <= 2e-2, (s, hk)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_batch_of_empty_sequences_leaves_the_pool_untouched(act):
+    """Three sequences of zero tokens (T_tot = 0): every launch runs and finds
+    no chunk; the pool, gated path included, is bitwise unchanged."""
+    d = DT[act]
+    rng = np.random.default_rng(91)
+    Hk, Hv, Dk, Dv, P = 2, 4, 128, 128, 5
+    pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
+    pool = to_dev(pool0, torch.float32, DEV)
+    ci = torch.tensor([2, 0, 4], dtype=torch.int64, device=DEV)
+    cu = torch.zeros(4, dtype=torch.int64, device=DEV)
+    e = lambda *s, dt=d: torch.empty(s, dtype=dt, device=DEV)
+    y = e(0, Hv, Dv)
+    gdn.gdn_chunk_prefill(e(0, Hk, Dk), e(0, Hk, Dk), e(0, Hv, Dv), e(0, Hv, dt=torch.float32),
+                          e(0, Hv, dt=torch.float32), pool, ci, cu, chunk=64, y=y)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(pool).astype(np.float32), pool0)
