@@ -925,10 +925,12 @@ __device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
 // chunk loop: transposed as bf16 hi/lo, and P transposed as bf16 (each
 // lane's four accumulator rows are then one 8-byte store), blocks on and
 // below the diagonal only, in the compact upper-triangular form of the
-// transposes (tri_block).  One wave
-// needs no barriers; the LDS footprint (19 KB) and a register budget of 256
-// (two waves per SIMD, requested from the compiler) let eight waves share a
-// CU and hide each other's latency.
+// transposes (tri_block).  The lanes of the one wave hand each other data
+// through LDS (norms and gates, A, the diagonal inverses): a __syncthreads()
+// at each hand-off waits for no other wave but keeps the compiler from
+// serving a lane's read from what that lane itself stored earlier.  The LDS
+// footprint (19 KB) and a register budget of 256 (two waves per SIMD,
+// requested from the compiler) let eight waves share a CU.
 //
 // COMBA: the Comba forward (read key p, write key k; KBench
 // `comba_decode_step` spec run over every token).  Its chunk form is the
@@ -1079,6 +1081,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
       sG[lane] = G;
       sB[lane] = bt;
     }
+    __syncthreads();  // norms and gates -> every lane
 
     // ---- A (LDS, fp32) and P (global, bf16, transposed) from the Gram blocks
     bf16* th = Th + mat * NPAIR * 256;
@@ -1107,6 +1110,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
         *reinterpret_cast<s16x4*>(ph + tri_block<CT>(J, I) * 256 + l16 * 16 + kg * 4) = pv;
       }
 
+    __syncthreads();  // A -> the solving lanes
+
     // ---- diagonal blocks: lane (b, cc) solves column cc of (I + A_bb)^-1
     {
       const int b = lane >> 4, cc = l16;
@@ -1132,6 +1137,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
         for (int i = 0; i < 16; ++i) sD[b][i * 20 + cc] = x[i];
       }
     }
+
+    __syncthreads();  // D -> every lane
 
     // ---- block columns of T; stored as T diag(beta) (column jb*16 + l16 of
     // this lane scaled by its beta)
@@ -1166,6 +1173,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
         Tc[i][jb] = -mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
         put_T(i, jb, Tc[i][jb]);
       }
+    __syncthreads();  // this head's reads of A, D and the gates before the next head's writes
   }
 }
 
