@@ -1240,7 +1240,8 @@ struct StreamTiles {
   };
 };
 
-template <int DK, int CT, int NW, int CW, bool GATED = false, bool COMBA = false, bool HALVES = false>
+template <int DK, int CT, int NW, int CW, bool GATED = false, bool COMBA = false, bool HALVES = false,
+          bool SINGLE = false>
 __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
     const bf16* __restrict__ v,
@@ -1256,7 +1257,16 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
   // Two distinct sets (not an indexed pair): reads of one never depend on
   // copies into the other.
-  __shared__ Set setA, setB;
+  // SINGLE (every sequence is one chunk long): no chunk ci+1 to copy ahead,
+  // so one operand set and none of the copies the double-buffered loop
+  // issues for the (empty) next chunk
+  static_assert(!SINGLE || (!GATED && !COMBA && !HALVES), "single-set variant: plain GDN only");
+  __shared__ Set setA;
+  __shared__ std::conditional_t<SINGLE, char, Set> setB_mem;
+  Set& setB = [&]() -> Set& {
+    if constexpr (SINGLE) return setA;
+    else return setB_mem;
+  }();
   __shared__ __attribute__((aligned(16))) bf16 sV[Tiles::Vcopy::ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 sY[CT * YP];
   // the gated epilogue's z tile and Comba's read-key tile (8 elements when unused)
@@ -1308,7 +1318,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
   const int cbase = scs[s];
   const int nch_all = static_cast<int>((len + C - 1) / C);
   const int nch = cbase + nch_all > maxc ? (maxc > cbase ? maxc - cbase : 0) : nch_all;
-  if (nch <= 0) return;
+  if (nch <= 0 || (SINGLE && nch != 1)) return;
   const int hk = hv / (Hv / Hk);
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1551,11 +1561,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           Y[t][mt] = mma(aq, Sh[t], Y[t][mt]);
           X[t][mt] = mma(a, Sl[t], X[t][mt]);
         }
-        copy_job(rn, nx, kb * MT + mt);  // chunk ci+1's set, one copy per product group
+        if constexpr (!SINGLE) copy_job(rn, nx, kb * MT + mt);  // chunk ci+1's set, one copy per product group
       }
     }
+    if constexpr (!SINGLE) {
 #pragma unroll
-    for (int n = KB * MT; n < NJOBS; ++n) copy_job(rn, nx, n);
+      for (int n = KB * MT; n < NJOBS; ++n) copy_job(rn, nx, n);
+    }
     f32x4 R[CW][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -1597,11 +1609,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           D[t][mt] = mma(tl, Rh[t][cb], D[t][mt]);
         }
       }
-      cV.issue_one(rv, sV, w, mt);  // chunk ci+1's V
+      if constexpr (!SINGLE) cV.issue_one(rv, sV, w, mt);  // chunk ci+1's V
       if constexpr (COMBA) cPr.issue_one(rp, sPr, w, mt);
     }
+    if constexpr (!SINGLE) {
 #pragma unroll
-    for (int j = MT; j < Tiles_::Vcopy::PER; ++j) cV.issue_one(rv, sV, w, j);
+      for (int j = MT; j < Tiles_::Vcopy::PER; ++j) cV.issue_one(rv, sV, w, j);
+    }
     if constexpr (COMBA) {
 #pragma unroll
       for (int j = MT; j < Tiles_::Qcopy::PER; ++j) cPr.issue_one(rp, sPr, w, j);
@@ -1664,7 +1678,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     if constexpr (COMBA) cPr.issue(kq_rsrc(pr, 0), sPr, w);
   }
   handover<0>();
-  if (act) {
+  if constexpr (SINGLE) {
+    step(0, setA, setB);
+  } else if (act) {
     for (int ci = 0; ci < nch; ci += 2) {
       step(ci, setA, setB);
       if (ci + 1 < nch) step(ci + 1, setB, setA);
@@ -1759,7 +1775,7 @@ template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
-               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
+               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream, bool one_chunk) {
   int* scs = reinterpret_cast<int*>(ws + L.scs);
   bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
   bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
@@ -1791,6 +1807,19 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                            static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
                            chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
                            static_cast<const bf16*>(epi->z), epi->gamma, epi->eps);
+        return launch_status();
+      }
+    }
+    // every sequence one chunk long (the host knows it for fixed-length
+    // batches): the single-set variant, more workgroups per CU
+    if constexpr (CT == 32 && NW == 8 && CW == 1) {
+      if (one_chunk && !split) {
+        hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW, false, false, false, true>),
+                           dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream,
+                           static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
+                           static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv, chunk,
+                           static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
+                           static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
         return launch_status();
       }
     }
@@ -1829,7 +1858,8 @@ template <typename T, int DK, int CT>
 int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
+                bool one_chunk) {
   // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
   // workgroup so each chunk operand is fetched once per 128 columns.  fp32
   // activations: the register-fragment kernel, 64 (four waves, up to 512
@@ -1837,29 +1867,30 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
       return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                         chunk, scale, l2norm, y, ws, L, epi, stream);
+                                         chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream);
+                                    chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
   return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
 }
 
 template <typename T, int DK>
 int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
+                bool one_chunk) {
   if constexpr (DK == 256) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
   } else {
     if (CT == 32)
       return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream);
+                                    chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
     return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
   }
 }
 
@@ -1868,14 +1899,14 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
                 const float* g, const float* beta, float* pool, int64_t pool_size,
                 const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
                 int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
-                const Epilogue* epi, hipStream_t stream) {
+                const Epilogue* epi, hipStream_t stream, bool one_chunk) {
   switch (Dk) {
-    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
-    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
-    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
     case 256:  // bf16 activations only (the fp32 kernels would spill at this width)
       if constexpr (std::is_same<T, bf16>::value)
-        return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream);
+        return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
       else
         return GDN_ERR_UNSUPPORTED;
   }
@@ -1975,7 +2006,7 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
                   const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
                   int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
                   size_t workspace_bytes, const Epilogue* epi, hipStream_t stream,
-                  bool check_only = false) {
+                  bool check_only = false, int64_t max_len = 0) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
@@ -2015,11 +2046,14 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
   const int l2 = (flags & GDN_QK_L2NORM) ? 1 : 0;
   const int CT = chunk_tile(chunk);
   char* ws = static_cast<char*>(workspace);
+  // max_len > 0: no sequence is longer (the caller knows it); then whether
+  // every sequence fits one chunk
+  const bool one_chunk = max_len > 0 && max_len <= chunk;
   if (act == GDN_BF16)
     return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream);
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, one_chunk);
   return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream);
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, one_chunk);
 }
 
 }  // namespace
@@ -2206,5 +2240,5 @@ extern "C" int gdn_chunk_prefill_fixed(const void* q, const void* k, const void*
                      stream, cu, ci, B, T);
   if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
   return chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk, Dv,
-                       chunk, scale, flags, y, act, workspace, main, nullptr, stream);
+                       chunk, scale, flags, y, act, workspace, main, nullptr, stream, false, T);
 }

@@ -324,6 +324,11 @@ FIXED_CASES = [
     (2, 1, 1, 2, 64, 64, 32, "bf16"),
     (4, 77, 1, 3, 256, 128, 64, "bf16"),
     (2, 50, 1, 2, 64, 32, 16, "f32"),
+    # one chunk per sequence and at least one workgroup per CU: the
+    # single-operand-set chunk loop (bitwise the varlen call all the same)
+    (64, 5, 2, 4, 128, 128, 8, "bf16"),
+    (64, 16, 1, 4, 256, 128, 16, "bf16"),
+    (64, 32, 2, 4, 64, 128, 32, "bf16"),
 ]
 
 
