@@ -329,6 +329,7 @@ FIXED_CASES = [
     (64, 5, 2, 4, 128, 128, 8, "bf16"),
     (64, 16, 1, 4, 256, 128, 16, "bf16"),
     (64, 32, 2, 4, 64, 128, 32, "bf16"),
+    (64, 7, 1, 4, 32, 128, 8, "bf16"),
 ]
 
 
