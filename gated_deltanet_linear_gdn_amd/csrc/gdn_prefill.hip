@@ -213,13 +213,14 @@ __global__ __launch_bounds__(256) void gdn_fixed_index_kernel(int64_t* __restric
   if (i < B) ci[i] = i;
 }
 
-__global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
+template <int NT>
+__global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
                                                              int N_s, int64_t T_tot, int C,
                                                              int* __restrict__ scs, int wg_per_seq,
                                                              int num_cu, int allow_split) {
-  __shared__ int part[1024];
+  __shared__ int part[NT];
   const int tid = threadIdx.x;
-  const int per_t = (N_s + 1023) / 1024;  // sequences (positions) per thread
+  const int per_t = (N_s + NT - 1) / NT;  // sequences (positions) per thread
   const int s0 = tid * per_t;
   int local = 0;
   for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
   }
   part[tid] = local;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
+  for (int off = 1; off < NT; off <<= 1) {  // inclusive scan
     const int v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
     run += n;
     atomicAdd(&bucket[32 - __clz(n)], 1);
   }
-  if (tid == 1023) scs[N_s] = part[1023];
+  if (tid == NT - 1) scs[N_s] = part[NT - 1];
   __syncthreads();
   if (tid == 0) {  // first rank of each bit length, longest first
     int r = 0;
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
   }
   part[tid] = loc;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
+  for (int off = 1; off < NT; off <<= 1) {
     const int v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(1024) void gdn_chunk_map_kernel(const int64_t* __re
     const bool sp = r < room && len > 0;
     wrun += sp ? 2 * wg_per_seq : wg_per_seq;
   }
-  if (tid == 1023) wgp[N_s] = part[1023];
+  if (tid == NT - 1) wgp[N_s] = part[NT - 1];
 }
 
 // ----------------------------------------------------------------------------
@@ -1746,6 +1747,19 @@ inline int cu_count() {
   return n;
 }
 
+// The chunk map on one workgroup: a single wave while every thread has at
+// most four sequences to scan (its barriers are then nearly free), else
+// 1,024 threads.
+inline void chunk_map(const int64_t* cu, int N_s, int64_t T_tot, int chunk, int* scs, int per_seq,
+                      bool split, hipStream_t stream) {
+  if (N_s <= 256)
+    hipLaunchKernelGGL(gdn_chunk_map_kernel<64>, dim3(1), dim3(64), 0, stream, cu, N_s, T_tot, chunk, scs,
+                       per_seq, cu_count(), split ? 1 : 0);
+  else
+    hipLaunchKernelGGL(gdn_chunk_map_kernel<1024>, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs,
+                       per_seq, cu_count(), split ? 1 : 0);
+}
+
 inline Layout layout(int64_t T_tot, int N_s, int Hv, int chunk, bool bf16_act) {
   const int CT = chunk_tile(chunk);
   const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
@@ -1792,8 +1806,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   const size_t main_blocks = static_cast<size_t>(N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, cu, N_s, T_tot, chunk, scs, per_seq,
-                     cu_count(), split ? 1 : 0);
+  chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
                        stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
@@ -1951,8 +1964,7 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   const size_t main_blocks = static_cast<size_t>(a.N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(gdn_chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu, a.N_s, a.T_tot, a.chunk, scs,
-                     per_seq, cu_count(), split ? 1 : 0);
+  chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
   hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
                      Th, Tl, Ph, fac);

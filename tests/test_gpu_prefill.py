@@ -380,6 +380,22 @@ def test_many_short_sequences():
     _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
 
 
+def test_a_few_hundred_sequences():
+    """200 sequences of 0..40 tokens: the one-wave chunk map with several
+    sequences per thread, mixed one- and multi-chunk sequences, and more
+    chunk-loop workgroups than CUs.  Every sequence and slot matches the
+    oracle."""
+    rng = np.random.default_rng(83)
+    N, Hk, Hv, Dk, Dv = 200, 1, 2, 64, 128
+    lengths = rng.integers(0, 41, size=N)
+    P = N + 3
+    pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P, act="bf16")
+    pool, y = _run_gpu(inp, pool0, 16, "bf16")
+    P_ref, y_ref = _run_oracle(inp, pool0)
+    _check(pool, y, P_ref, y_ref, pool0, inp, "bf16")
+
+
 def test_split_of_the_longest_sequence_only():
     """Four sequences at 48 value heads (192 chunk-loop workgroups): idle CUs
     leave room to run only the longest as two half-width workgroups per head;
