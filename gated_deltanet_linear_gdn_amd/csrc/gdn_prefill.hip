@@ -1747,12 +1747,12 @@ inline int cu_count() {
   return n;
 }
 
-// The chunk map on one workgroup: a single wave while every thread has at
-// most four sequences to scan (its barriers are then nearly free), else
-// 1,024 threads.
+// The chunk map on one workgroup: a single wave for up to 64 sequences (one
+// per lane; its barriers are then nearly free), else 1,024 threads (a wave
+// scanning several sequences per lane measured slower than that).
 inline void chunk_map(const int64_t* cu, int N_s, int64_t T_tot, int chunk, int* scs, int per_seq,
                       bool split, hipStream_t stream) {
-  if (N_s <= 256)
+  if (N_s <= 64)
     hipLaunchKernelGGL(gdn_chunk_map_kernel<64>, dim3(1), dim3(64), 0, stream, cu, N_s, T_tot, chunk, scs,
                        per_seq, cu_count(), split ? 1 : 0);
   else

@@ -381,10 +381,9 @@ def test_many_short_sequences():
 
 
 def test_a_few_hundred_sequences():
-    """200 sequences of 0..40 tokens: the one-wave chunk map with several
-    sequences per thread, mixed one- and multi-chunk sequences, and more
-    chunk-loop workgroups than CUs.  Every sequence and slot matches the
-    oracle."""
+    """200 sequences of 0..40 tokens: mixed one- and multi-chunk sequences
+    and more chunk-loop workgroups than CUs.  Every sequence and slot
+    matches the oracle."""
     rng = np.random.default_rng(83)
     N, Hk, Hv, Dk, Dv = 200, 1, 2, 64, 128
     lengths = rng.integers(0, 41, size=N)
