@@ -316,6 +316,9 @@ size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv,
  *               bytes, 16-byte aligned; its contents are scratch (the call
  *               writes the index arrays into its end before the kernels run).
  * Requirements: those of gdn_chunk_prefill.  B == 0 or T == 0 is a no-op.
+ * When T fits one chunk (after the Dk = 256 cap) the call knows every
+ * sequence is a single chunk and runs a chunk loop without next-chunk
+ * prefetch (same results, bit for bit; faster for decode windows).
  */
 int gdn_chunk_prefill_fixed(const void* q, const void* k, const void* v,
                             const float* g, const float* beta, float* state,
