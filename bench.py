@@ -397,54 +397,145 @@ def bench_comba_hbm(steps, warmup, device, B=896, H=16, K=128, V=128):
 
 
 def bench_copy(device, nbytes=2 << 30, reps=20):
+    """A 2 GiB device-to-device copy, timed two ways: torch's own copy, and
+    the library's one-load, one-store stream copy (gdn_stream_copy, the
+    decode step's access pattern).  Returns GB/s over read + write bytes for
+    each."""
     import torch
+    import gated_deltanet_linear_gdn_amd as gdn
     n = nbytes // 4
     a = torch.ones(n, dtype=torch.float32, device=device)
     b = torch.empty_like(a)
-    sec = _timed(lambda i: b.copy_(a), reps, 3)
-    return 2 * nbytes / sec / 1e9
+    torch_sec = _timed(lambda i: b.copy_(a), reps, 3)
+    own_sec = _timed(lambda i: gdn.gdn_stream_copy(a, b), reps, 3)
+    assert torch.equal(a, b)
+    return 2 * nbytes / torch_sec / 1e9, 2 * nbytes / own_sec / 1e9
 
 
-def cpu_baseline(budget_s=10.0):
-    """The fp64 oracle on the decode workload's shape, on this host's cores:
-    whole B=256 decode steps repeated until `budget_s` elapses."""
-    import concurrent.futures as cf
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
     import platform
+    return platform.processor() or platform.machine()
+
+
+def _run_units(fn, units, threads):
+    """fn(unit) for every unit, the units split statically over `threads`
+    threads (ctypes releases the GIL inside the oracle).  Returns seconds."""
+    import concurrent.futures as cf
+    parts = [units[i::threads] for i in range(threads)]
+    parts = [p for p in parts if p]
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        list(ex.map(lambda ps: [fn(u) for u in ps], parts))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(budget_s=8.0):
+    """The fp64 oracle (plain C, one token at a time) on this host's cores,
+    beside the GPU figures of the same run: the B=256 decode step (the
+    headline, GB/s over the same state bytes), the Comba step at B=128
+    H=32 K=V=128 (GB/s over the KBench byte count) and the varlen prefill
+    (tokens/s over the same 8 sequences x 48 heads).  Independent (sequence,
+    head) units are split statically over N threads; each unit runs
+    sequentially.  N-thread and 1-thread times are both reported."""
     import oracle
     from gated_deltanet_linear_gdn_amd import synth
-    c = synth.DECODE_B256
-    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = max(1, min(cores, 64))
+    legs = {}
+
+    # decode: whole B=256 steps, batch entries split over the threads
+    c = synth.DECODE_B256
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
     rng = np.random.default_rng(1)
     S = np.zeros((B, Hv, Dv, Dk), dtype=np.float64)
     tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
-    parts = [p for p in np.array_split(np.arange(B), threads) if p.size]
-    sls = [slice(int(p[0]), int(p[-1]) + 1) for p in parts]
 
-    def run(sl):
-        oracle.gdn_step(S[sl], tok["q"][sl], tok["k"][sl], tok["v"][sl], tok["g"][sl],
-                        tok["beta"][sl], inplace=True)
+    def dec(b):
+        sl = slice(b, b + 1)
+        oracle.gdn_step(S[sl], tok["q"][sl], tok["k"][sl], tok["v"][sl], tok["g"][sl], tok["beta"][sl],
+                        inplace=True)
 
-    n = 0
-    with cf.ThreadPoolExecutor(max_workers=len(sls)) as ex:
-        list(ex.map(run, sls))          # first touch of the pages, untimed
-        t0 = time.perf_counter()
-        while True:
-            list(ex.map(run, sls))
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or n >= 5000:
-                break
+    _run_units(dec, list(range(B)), threads)          # first touch of the pages, untimed
+    n, el = 0, 0.0
+    while el < budget_s and n < 5000:
+        el += _run_units(dec, list(range(B)), threads)
+        n += 1
+    one = _run_units(dec, list(range(B // 8)), 1) * 8  # 1 thread: an eighth of a step, scaled
     state_bytes = 2 * B * Hv * Dv * Dk * 4
-    return dict(value=round(state_bytes * n / el / 1e9, 4), unit="GB/s", cores=len(sls),
-                kind="oracle",
-                sample=(f"{n} fp64 oracle decode steps of the whole B=256 Hk=16 Hv=48 Dk=Dv=128 "
-                        f"batch in {el:.1f} s on {len(sls)} threads "
-                        f"({platform.processor() or platform.machine()})"))
+    legs["decode"] = dict(workload="gdn_decode_step B=256 Hk=16 Hv=48 Dk=Dv=128", steps=n,
+                          s_per_step=round(el / n, 4), s_per_step_1thread=round(one, 4),
+                          GBps=round(state_bytes * n / el / 1e9, 3),
+                          GBps_1thread=round(state_bytes / one / 1e9, 3))
+    del S
+
+    # Comba: whole B=128 H=32 steps
+    c = synth.COMBA_B128
+    B, H, K, V = c["B"], c["H"], c["K"], c["V"]
+    S = np.zeros((B, H, K, V), dtype=np.float64)
+    tok = synth.comba_token(rng, B, H, K, V)
+
+    def com(b):
+        sl = slice(b, b + 1)
+        oracle.comba_step(S[sl], tok["q"][sl], tok["k"][sl], tok["v"][sl], tok["p"][sl], tok["beta"][sl],
+                          tok["g"][sl], inplace=True)
+
+    _run_units(com, list(range(B)), threads)
+    n, el = 0, 0.0
+    while el < budget_s / 4 and n < 5000:
+        el += _run_units(com, list(range(B)), threads)
+        n += 1
+    one = _run_units(com, list(range(B // 8)), 1) * 8
+    canonical = 2 * B * H * K * V * 4 + B * H * (6 * K + 4 * V + 6)
+    legs["comba"] = dict(workload="comba_decode_step B=128 H=32 K=V=128", steps=n,
+                         s_per_step=round(el / n, 4), s_per_step_1thread=round(one, 4),
+                         GBps=round(canonical * n / el / 1e9, 3), GBps_1thread=round(canonical / one / 1e9, 3))
+    del S
+
+    # varlen prefill: every (sequence, value head) unit of the 8-sequence batch
+    c = synth.PREFILL_VARLEN
+    Hk, Hv, Dk, Dv, P = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"]
+    rng = np.random.default_rng(0)
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    cu, G = inp["cu_seqlens"], Hv // Hk
+    pool = np.zeros((P, Hv, Dv, Dk))
+
+    def pre(u):
+        s, hv = u
+        idx = slice(int(cu[s]), int(cu[s + 1]))
+        hk, h = hv // G, slice(hv, hv + 1)
+        slot = int(inp["cache_indices"][s])
+        oracle.gdn_prefill(inp["q"][idx, hk:hk + 1], inp["k"][idx, hk:hk + 1], inp["v"][idx, h], g[idx, h],
+                           beta[idx, h], pool[slot:slot + 1, h], [0], [0, int(cu[s + 1] - cu[s])])
+
+    units = sorted(((s, hv) for s in range(len(lengths)) for hv in range(Hv)),
+                   key=lambda u: -int(lengths[u[0]]))
+    T = int(cu[-1])
+    el = _run_units(pre, units, threads)
+    one_units = [(s, 0) for s in range(len(lengths))]   # 1 thread: head 0 of every sequence, scaled
+    one = _run_units(pre, one_units, 1) * Hv
+    legs["prefill"] = dict(workload="gdn_chunk_prefill (token by token): 8 sequences of U[512,4096] tokens, "
+                                    "Hk=16 Hv=48 Dk=Dv=128", tokens=T, s_per_call=round(el, 3),
+                           s_per_call_1thread=round(one, 3), tokens_per_s=round(T / el, 1),
+                           tokens_per_s_1thread=round(T / one, 1))
+    d = legs["decode"]
+    return dict(value=d["GBps"], unit="GB/s", cores=threads, kind="oracle", cpu=_cpu_model(),
+                sample=(f"{d['steps']} fp64 oracle decode steps of the whole B=256 Hk=16 Hv=48 Dk=Dv=128 batch "
+                        f"on {threads} threads ({d['s_per_step']} s per step; 1 thread: "
+                        f"{d['s_per_step_1thread']} s per step from an eighth of the batch); Comba and "
+                        f"prefill legs below"),
+                legs=legs)
 
 
 def main():
@@ -474,7 +565,7 @@ def main():
     lay = bench_layer(max(5, args.steps // 50), 3, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
     cwins = {T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
-    copy_gbps = bench_copy(device)
+    copy_gbps, own_copy_gbps = bench_copy(device)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
     out = {
@@ -496,9 +587,17 @@ def main():
                    "activation_bytes_per_step": dec["act_bytes"]},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": _decode_traffic()},
+                     "traffic": _decode_traffic(),
+                     "traffic_source": ("stored figure from two earlier rocprofv3 --pmc runs (FETCH_SIZE x 2 + "
+                                        "WRITE_SIZE x 1) of this kernel, reported only while its sources hash "
+                                        "to the values recorded with it; not read in this run")},
         "decode_inplace_GBps": round(dec_ip["state_bytes"] / dec_ip["sec"] / 1e9, 2),
         "torch_copy_GBps": round(copy_gbps, 1),
+        "stream_copy": {"workload": "gdn_stream_copy of 2 GiB: one 16-byte non-temporal load and store per "
+                                    "thread, the decode step's access pattern (GB/s over read + write bytes)",
+                        "GBps": round(own_copy_gbps, 1),
+                        "frac_of_hbm_peak": round(own_copy_gbps / HBM_PEAK_GBPS, 4),
+                        "decode_frac_of_copy": round(gbps / own_copy_gbps, 4)},
         "decode_window": {"workload": "gdn_decode_window at the B=256 decode batch, all T tokens committed",
                           "tokens_per_s_single_step": round(dec["shape"]["B"] / dec["sec"], 1),
                           **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),

@@ -25,7 +25,7 @@ __all__ = [
     "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
     "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
-    "comba_chunk_prefill_workspace", "comba_chunk_prefill",
+    "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +97,8 @@ def load_library():
     lib.comba_chunk_prefill.restype = _i
     lib.comba_chunk_prefill.argtypes = ([_vp] * 7 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4
                                         + [_f, _vp, _i, _vp, ctypes.c_size_t, _vp])
+    lib.gdn_stream_copy.restype = _i
+    lib.gdn_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
     return lib
 
@@ -446,3 +448,15 @@ def gdn_validate_varlen(cu_seqlens, cache_indices, T_tot, pool_size) -> int:
     with torch.cuda.device(dev):
         return int(load_library().gdn_validate_varlen(_ptr(cu_seqlens), _ptr(cache_indices), N_s,
                                                       int(T_tot), int(pool_size), _stream(dev)))
+
+
+def gdn_stream_copy(src, dst):
+    """Measurement helper: copy the bytes of ``src`` into ``dst`` (same
+    shape and dtype, contiguous, on one device) with the library's stream
+    copy kernel.  Returns dst."""
+    _check("dst", dst, tuple(src.shape), src.dtype, src.device)
+    if not src.is_contiguous():
+        raise ValueError("src: must be contiguous")
+    dev = src.device
+    _call("gdn_stream_copy", dev, _ptr(src), _ptr(dst), src.numel() * src.element_size(), _stream(dev))
+    return dst

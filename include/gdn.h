@@ -378,6 +378,19 @@ int comba_chunk_prefill(const void* q, const void* k, const void* v,
                         float scale, void* o, gdn_dtype act, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * gdn_stream_copy - measurement helper: copies `bytes` bytes from src to dst
+ * with one 16-byte non-temporal load and one 16-byte non-temporal store per
+ * thread, the access pattern of the decode step's state stream.  Source:
+ * KBench `comba_decode_step` page, perf_md (a bandwidth-bound step is judged
+ * against a large stream copy measured on the same machine).  Its rate over
+ * 2 * bytes is the measured ceiling the streaming kernels are compared with.
+ * src, dst: device memory, 16-byte aligned, not overlapping (GDN_ERR_ALIAS).
+ * bytes: a multiple of 16 (else GDN_ERR_SHAPE); 0 is a no-op; at most
+ * 2^31 - 1 workgroups of 4 KiB (GDN_ERR_UNSUPPORTED beyond).
+ */
+int gdn_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 /* Human-readable name of a gdn_status value (static string, never NULL). */
 const char* gdn_status_string(int status);
 

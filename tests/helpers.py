@@ -25,6 +25,34 @@ def relF(x, ref) -> float:
     return float(np.linalg.norm((x - ref).ravel())) / (den if den > 0 else 1.0)
 
 
+def rowrel(x, ref, floor=1e-3) -> float:
+    """Largest error of one output row (the last axis): over every row,
+    max |x - ref| in the row / max |ref| in the row.  Rows whose largest
+    element is below `floor` times the tensor's largest are measured against
+    that floor, so a row that is nearly zero in the reference does not turn
+    fp32 rounding into a large ratio."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0
+    n = ref.shape[-1]
+    err = np.max(np.abs(x - ref).reshape(-1, n), axis=1)
+    scale = np.max(np.abs(ref).reshape(-1, n), axis=1)
+    top = float(np.max(scale))
+    den = np.maximum(scale, floor * top if top > 0 else 1.0)
+    return float(np.max(err / den))
+
+
+def check_bf16_out(x, ref, what="output"):
+    """A bf16 output against the fp64 oracle, element by element: relative
+    Frobenius error <= 2e-2, max |error| <= 1e-2 of the largest reference
+    value, and in every row max |error| <= 1e-2 of that row's largest value
+    (rounding to bf16 alone gives at most 2^-9 ~ 2e-3 of an element)."""
+    e = (relF(x, ref), maxrel(x, ref), rowrel(x, ref))
+    assert e[0] <= 2e-2 and e[1] <= 1e-2 and e[2] <= 1e-2, f"{what}: relF {e[0]:.3g}, maxrel {e[1]:.3g}, rowrel {e[2]:.3g}"
+    return e
+
+
 def to_dev(x, dtype, device):
     """numpy float32/int64 -> torch tensor on device.  float32 values that are
     bf16-representable convert exactly (round-to-nearest-even)."""

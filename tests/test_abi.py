@@ -309,3 +309,14 @@ def test_fixed_prefill_validation(lib):
     assert fx(ws=A + 5 * BIG - main) == ALIAS        # index arrays at the start of the state
     assert fx(y=A + 5 * BIG + 64) == ALIAS           # y inside the state (varlen check)
     assert fx(ws=A + 4 * BIG - main) == ALIAS        # index arrays over beta
+
+
+def test_stream_copy_validation(lib):
+    cp = lambda src=A, dst=A + BIG, n=4096: lib.gdn_stream_copy(_p(src), _p(dst), n, None)
+    assert cp(n=0, src=0, dst=0) == OK          # nothing to copy: no pointer is used
+    assert cp(src=0) == NULL
+    assert cp(dst=0) == NULL
+    assert cp(src=A + 8) == ALIGN
+    assert cp(n=4100) == SHAPE
+    assert cp(dst=A + 2048) == ALIAS
+    assert cp(dst=A + (1 << 44), n=(1 << 31) * 4096) == UNSUP  # more workgroups than one launch holds

@@ -11,7 +11,7 @@ import torch
 import oracle
 import gated_deltanet_linear_gdn_amd as gdn
 from gated_deltanet_linear_gdn_amd import synth
-from tests.helpers import maxrel, relF, to_dev, to_np, oracle_comba_batched
+from tests.helpers import check_bf16_out, maxrel, relF, to_dev, to_np, oracle_comba_batched
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -51,9 +51,11 @@ def test_comba_parity(B, H, K, V, act):
     Sn, o = _comba(to_dev(S, torch.float32, DEV), _dev_tok(tok, act))
     S_ref, o_ref = oracle.comba_step(S, tok["q"], tok["k"], tok["v"], tok["p"], tok["beta"], tok["g"])
     assert maxrel(to_np(Sn), S_ref) <= 1e-5
-    assert relF(to_np(Sn), S_ref) <= 2e-2 and relF(to_np(o), o_ref) <= 2e-2
+    assert relF(to_np(Sn), S_ref) <= 2e-2
     if act == "f32":
         assert maxrel(to_np(o), o_ref) <= 1e-5
+    else:
+        check_bf16_out(to_np(o), o_ref, "o")
 
 
 def test_comba_explicit_scale_and_in_place():
@@ -68,24 +70,34 @@ def test_comba_explicit_scale_and_in_place():
     assert torch.equal(Sa, Sb) and torch.equal(oa, ob)
     S_ref, o_ref = oracle.comba_step(S, tok["q"], tok["k"], tok["v"], tok["p"], tok["beta"], tok["g"],
                                      scale=0.25)
-    assert maxrel(to_np(Sa), S_ref) <= 1e-5 and relF(to_np(oa), o_ref) <= 2e-2
+    assert maxrel(to_np(Sa), S_ref) <= 1e-5
+    check_bf16_out(to_np(oa), o_ref, "o")
 
 
 def test_comba_batch_b128():
-    """Comba decode batch B=128, H=32, K=V=128, warmed 16 steps (sampled)."""
+    """Comba decode batch B=128, H=32, K=V=128, warmed 16 steps (16 warmed
+    sequences tiled over the batch): step 1 on the whole state and output,
+    then two more steps on 6 sampled sequences."""
     c = synth.COMBA_B128
     rng = np.random.default_rng(0)
     B, H, K, V = c["B"], c["H"], c["K"], c["V"]
     W = _warm(rng, 16, H, K, V)
     S = np.tile(W, (B // 16, 1, 1, 1))
-    tok = synth.comba_token(rng, B, H, K, V)
-    Sn, o = _comba(to_dev(S, torch.float32, DEV), _dev_tok(tok, "bf16"))
     sample = np.array([0, 5, 17, 64, 99, 127])
-    sub = {n: a[sample] for n, a in tok.items()}
-    S_ref, o_ref = oracle_comba_batched(S[sample].astype(np.float64), sub)
-    got = Sn[torch.from_numpy(sample).to(DEV)]
-    assert maxrel(to_np(got), S_ref) <= 1e-5
-    assert relF(to_np(o)[sample], o_ref) <= 2e-2
+    S_dev = to_dev(S, torch.float32, DEV)
+    S_ref = S.astype(np.float64)
+    for step in range(3):
+        tok = synth.comba_token(rng, B, H, K, V)
+        S_dev, o = _comba(S_dev, _dev_tok(tok, "bf16"))
+        if step == 0:
+            S_ref, o_ref = oracle_comba_batched(S_ref, tok)
+            assert maxrel(to_np(S_dev), S_ref) <= 1e-5
+            check_bf16_out(to_np(o), o_ref, "o")
+            S_ref = S_ref[sample].copy()
+            continue
+        S_ref, o_ref = oracle_comba_batched(S_ref, {n: a[sample] for n, a in tok.items()})
+        assert maxrel(to_np(S_dev[torch.from_numpy(sample).to(DEV)]), S_ref) <= 1e-5, step
+        check_bf16_out(to_np(o)[sample], o_ref, f"o at step {step}")
 
 
 def test_comba_reads_with_p_not_k():

@@ -10,7 +10,7 @@ import torch
 import oracle
 import gated_deltanet_linear_gdn_amd as gdn
 from gated_deltanet_linear_gdn_amd import synth
-from tests.helpers import maxrel, relF, to_dev, to_np, oracle_decode_batched
+from tests.helpers import check_bf16_out, maxrel, relF, to_dev, to_np, oracle_decode_batched
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -31,8 +31,7 @@ def _check_y(y_gpu, y_ref, act):
     if act == "f32":
         assert maxrel(y_gpu, y_ref) <= 1e-5
     else:
-        assert relF(y_gpu, y_ref) <= 2e-2
-        assert maxrel(y_gpu, y_ref) <= 1e-2
+        check_bf16_out(y_gpu, y_ref, "y")
 
 
 def test_tiny_fp32_from_zero_then_steps():
@@ -142,11 +141,12 @@ def test_decode_batch_b64_full_tensor():
         _check_y(to_np(y), y_ref, "bf16")
 
 
-def test_decode_batch_b256_sampled():
+def test_decode_batch_b256():
     """Large decode batch B=256 (0.8 GB state) in the benchmark's launch
-    configuration (functional ping-pong); the oracle follows 8 sampled
-    sequences through 4 steps.  The warmed state is 16 oracle-warmed
-    sequences tiled over the batch."""
+    configuration (functional ping-pong).  Step 1 is checked on the whole
+    state and output; the oracle then follows 8 sampled sequences through
+    3 more steps.  The warmed state is 16 oracle-warmed sequences tiled over
+    the batch."""
     c = synth.DECODE_B256
     rng = np.random.default_rng(0)
     B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
@@ -154,12 +154,20 @@ def test_decode_batch_b256_sampled():
     S = np.tile(W, (B // 16, 1, 1, 1))
     bufs = [to_dev(S, torch.float32, DEV), torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=DEV)]
     sample = np.array([0, 1, 37, 100, 128, 201, 254, 255])
-    S_ref = S[sample].astype(np.float64)
+    S_full = S.astype(np.float64)
+    del S
     for step in range(4):
         tok = synth.decode_token(rng, B, Hk, Hv, Dk, Dv)
         t = _dev_token(tok, "bf16")
         _, y = gdn.gdn_decode_step(bufs[step % 2], bufs[(step + 1) % 2], t["q"], t["k"], t["v"],
                                    t["g"], t["beta"])
+        if step == 0:
+            S_full, y_ref = oracle_decode_batched(S_full, tok)
+            assert maxrel(to_np(bufs[1]), S_full) <= 1e-5
+            _check_y(to_np(y), y_ref, "bf16")
+            S_ref = S_full[sample].copy()
+            del S_full
+            continue
         sub = {n: a[sample] for n, a in tok.items()}
         S_ref, y_ref = oracle_decode_batched(S_ref, sub)
         got = bufs[(step + 1) % 2][torch.from_numpy(sample).to(DEV)]
@@ -189,7 +197,7 @@ def test_batch_beyond_one_launch_grid():
     torch.cuda.synchronize()
     Sw, yw_ref = oracle.gdn_window(S0[sample], *(w[n][sample] for n in ("q", "k", "v", "g", "beta")))
     assert maxrel(to_np(s_io[idx]), Sw) <= 1e-5
-    assert relF(to_np(yw)[sample], yw_ref) <= 2e-2
+    check_bf16_out(to_np(yw)[sample], yw_ref, "window y")
 
 
 # ------------------------------------------------------------ decode windows
@@ -230,7 +238,7 @@ def test_decode_window_parity(B, T, Hk, Hv, Dk, Dv, commit, act):
     if act == "f32":
         assert maxrel(yv, y_ref) <= 1e-5
     else:
-        assert relF(yv, y_ref) <= 2e-2
+        check_bf16_out(yv, y_ref, "window y")
     assert np.array_equal(to_np(s_in).astype(np.float32), S0)  # state_in untouched
 
 
@@ -274,5 +282,5 @@ def test_committed_window_equals_the_fixed_length_prefill():
     S_ref, y_ref = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"])
     assert maxrel(to_np(s_win), S_ref) <= 1e-5
     assert maxrel(to_np(s_fix), S_ref) <= 1e-3
-    assert relF(to_np(y_fix), y_ref) <= 2e-2
-    assert relF(to_np(y_fix), to_np(y_win)) <= 2e-2
+    check_bf16_out(to_np(y_fix), y_ref, "fixed-length y")
+    check_bf16_out(to_np(y_win), y_ref, "window y")
