@@ -66,10 +66,25 @@ def _dev(x, dtype, device):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype)
 
 
+SETTLE_S = 0.1   # untimed running before each leg's warmup steps
+
+
 def _timed(fn, steps, warmup):
-    """Run fn(i) warmup times untimed, then `steps` times between HIP events
-    recorded on the current stream.  Returns seconds per step."""
+    """Run fn(i) untimed for about SETTLE_S seconds, then warmup times
+    untimed, then `steps` times between HIP events recorded on the current
+    stream (the stream the library launches on).  Returns seconds per step.
+
+    The settle phase is there because a GPU that has been idle (host-side
+    input generation between legs) runs its first few dozen launches slower:
+    measured on MI355X, decode steps 10-35 after an idle second take
+    260-268 us against 251-255 us once settled."""
     import torch
+    t0 = time.perf_counter()
+    fn(0)
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5)
+    for i in range(min(2000, int(SETTLE_S / one) + 1)):
+        fn(i)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()

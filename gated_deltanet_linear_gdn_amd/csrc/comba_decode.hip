@@ -11,8 +11,8 @@
 // V floats is V/4 lanes x float4, the 256/(V/4) row groups each own K/RG
 // consecutive rows.  One pass computes, per lane, partial column sums of
 // p_i S[i,:] and (scale q_i) S[i,:] over its rows (and the scalar
-// sum_i scale q_i k_i); the row groups combine them through LDS behind one
-// barrier.  Then u = beta (v - a Sp), o = a Sq + (scale q . k) u (the exact
+// sum_i scale q_i k_i); the row groups of a wave combine them with cross-lane
+// adds, the waves through LDS behind one barrier.  Then u = beta (v - a Sp), o = a Sq + (scale q . k) u (the exact
 // identity for the readout from the updated state), and every lane writes
 // its rows a S + k_i u once.  The state crosses HBM exactly twice.
 
@@ -58,11 +58,12 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
   constexpr int LPR = V / 4;             // lanes per row
   constexpr int RG = NT / LPR;           // row groups
   constexpr int RPT = K / RG;            // rows per thread (consecutive)
-  static_assert(K % RG == 0 && RPT >= 1, "shape");
+  static_assert(K % RG == 0 && RPT >= 1 && NT % 64 == 0 && LPR <= 64, "shape");
 
-  __shared__ f32x4 red_p[RG][LPR];
-  __shared__ f32x4 red_q[RG][LPR];
-  __shared__ float red_kq[RG];
+  constexpr int WAVES = NT / 64;
+  __shared__ f32x4 red_p[WAVES][LPR];
+  __shared__ f32x4 red_q[WAVES][LPR];
+  __shared__ float red_kq[WAVES];
 
   const int slice = blockIdx.x;
   const int tid = threadIdx.x;
@@ -94,18 +95,36 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
     sq += qr[n] * s[n];
     kq += qr[n] * kr[n];
   }
-  red_p[rg][c4] = sp;
-  red_q[rg][c4] = sq;
-  if (c4 == 0) red_kq[rg] = kq;
+  // Row groups of one wave first: its lanes that hold the same columns
+  // differ only in the lane bits from LPR up (cross-lane adds, no LDS), then
+  // one partial per wave through LDS behind the single barrier.
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1) {
+    sp.x += __shfl_xor(sp.x, m);
+    sp.y += __shfl_xor(sp.y, m);
+    sp.z += __shfl_xor(sp.z, m);
+    sp.w += __shfl_xor(sp.w, m);
+    sq.x += __shfl_xor(sq.x, m);
+    sq.y += __shfl_xor(sq.y, m);
+    sq.z += __shfl_xor(sq.z, m);
+    sq.w += __shfl_xor(sq.w, m);
+    kq += __shfl_xor(kq, m);
+  }
+  const int wave = tid / 64, lane = tid % 64;
+  if (lane < LPR) {
+    red_p[wave][lane] = sp;
+    red_q[wave][lane] = sq;
+  }
+  if (lane == 0) red_kq[wave] = kq;
   __syncthreads();
   sp = red_p[0][c4];
   sq = red_q[0][c4];
   kq = red_kq[0];
 #pragma unroll
-  for (int r = 1; r < RG; ++r) {
-    sp += red_p[r][c4];
-    sq += red_q[r][c4];
-    kq += red_kq[r];
+  for (int w = 1; w < WAVES; ++w) {
+    sp += red_p[w][c4];
+    sq += red_q[w][c4];
+    kq += red_kq[w];
   }
 
   const f32x4 u = bt * (vv - gate * sp);

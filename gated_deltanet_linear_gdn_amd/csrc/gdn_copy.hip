@@ -12,7 +12,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kCopyThreads = 256;
+constexpr int kCopyThreads = 128;
 
 __global__ __launch_bounds__(kCopyThreads) void gdn_copy_kernel(const float* __restrict__ src,
                                                                 float* __restrict__ dst,

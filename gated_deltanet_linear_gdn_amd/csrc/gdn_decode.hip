@@ -46,6 +46,25 @@ unsigned hk_reciprocal(int G) {
   return G == 1 ? 0u : static_cast<unsigned>(((1ull << 32) + G - 1) / static_cast<unsigned>(G));
 }
 
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ f32x4 f() const {
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+};
+template <> struct Raw4<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ f32x4 f() const { return w; }
+};
+
+// One activation element as stored, converted on use.
+__device__ __forceinline__ float to_f32(bf16 h) { return bf16_to_f32(h); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
 template <int DK, int NV, bool FULL, typename T>
 __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const float* state_in, float* state_out, const T* __restrict__ q,
@@ -78,22 +97,31 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
   // their stores are skipped.
   auto rowc = [&](int n) { return FULL ? row0 + n * RPS : min(row0 + n * RPS, Dv - 1); };
 
-  // Loads complete in issue order, so the small activation loads go first
-  // (their first use then does not wait for the state rows), then the NV
-  // state rows.  The barrier keeps the scheduler from sinking any load below
-  // the first wait.
-  const f32x4 kk = Act<T>::load4(k + qk_off);
-  const f32x4 qq = Act<T>::load4(q + qk_off);
+  // Every load is issued before the first wait: the small activation loads
+  // first (loads complete in issue order, so their first use does not wait
+  // for the state rows), kept as stored, then the NV state rows.  Converting
+  // bf16 activations right after their loads would make the compiler wait
+  // for them before issuing the state loads: two memory round trips per
+  // workgroup instead of one.  The barriers keep the scheduler from moving
+  // any conversion (and its wait) between the loads.
+  Raw4<T> kr, qr;
+  kr.load(k + qk_off);
+  qr.load(q + qk_off);
   const float graw = g[slice];
-  const float bt = Act<T>::load(beta + slice);
-  float vv[NV];
+  const T btr = beta[slice];
+  T vr[NV];
 #pragma unroll
-  for (int n = 0; n < NV; ++n) vv[n] = Act<T>::load(v + static_cast<size_t>(slice) * Dv + rowc(n));
+  for (int n = 0; n < NV; ++n) vr[n] = v[static_cast<size_t>(slice) * Dv + rowc(n)];
   __builtin_amdgcn_sched_barrier(0);
   f32x4 s[NV];
 #pragma unroll
   for (int n = 0; n < NV; ++n) s[n] = load_stream(sin + static_cast<size_t>(rowc(n)) * DK);
   __builtin_amdgcn_sched_barrier(0);
+  const f32x4 kk = kr.f(), qq = qr.f();
+  const float bt = to_f32(btr);
+  float vv[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) vv[n] = to_f32(vr[n]);
   const float gate = expf(graw);
   const float kq = group_sum<LPR>(dot4(kk, qq));
 
@@ -166,21 +194,6 @@ int launch(const float* state_in, float* state_out, const void* q, const void* k
 // after the first `commit` tokens is kept in registers and stored at the
 // end (commit 0: a verify window, no state write).  The state crosses HBM
 // once per window instead of once per token.
-
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16> {
-  uint2 w;
-  __device__ __forceinline__ void load(const bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ f32x4 f() const {
-    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-  }
-};
-template <> struct Raw4<float> {
-  f32x4 w;
-  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
-  __device__ __forceinline__ f32x4 f() const { return w; }
-};
 
 template <int DK, int NV, bool FULL, typename T, int NT>
 __global__ __launch_bounds__(kThreads) void gdn_window_kernel(

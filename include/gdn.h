@@ -387,7 +387,7 @@ int comba_chunk_prefill(const void* q, const void* k, const void* v,
  * 2 * bytes is the measured ceiling the streaming kernels are compared with.
  * src, dst: device memory, 16-byte aligned, not overlapping (GDN_ERR_ALIAS).
  * bytes: a multiple of 16 (else GDN_ERR_SHAPE); 0 is a no-op; at most
- * 2^31 - 1 workgroups of 4 KiB (GDN_ERR_UNSUPPORTED beyond).
+ * 2^31 - 1 workgroups of 2 KiB (GDN_ERR_UNSUPPORTED beyond).
  */
 int gdn_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
