@@ -25,7 +25,7 @@ __all__ = [
     "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
     "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
-    "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy",
+    "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy", "gdn_chunk_prefill_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +97,9 @@ def load_library():
     lib.comba_chunk_prefill.restype = _i
     lib.comba_chunk_prefill.argtypes = ([_vp] * 7 + [_i64, _vp, _vp, _i, _i64] + [_i] * 4
                                         + [_f, _vp, _i, _vp, ctypes.c_size_t, _vp])
+    lib.gdn_chunk_prefill_noalloc.restype = _i
+    lib.gdn_chunk_prefill_noalloc.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
+                                              + [_f, ctypes.c_uint, _vp, _i, _vp])
     lib.gdn_stream_copy.restype = _i
     lib.gdn_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -317,6 +320,36 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags,
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
           _stream(dev))
+    return y
+
+
+def gdn_chunk_prefill_noalloc(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, y, chunk=64,
+                              scale=None, l2norm=True):
+    """``gdn_chunk_prefill`` with the library's static device workspace
+    instead of a caller one (see ``gdn_chunk_prefill_noalloc`` in
+    include/gdn.h): nothing is allocated, so y must be given.  Same
+    arguments otherwise; calls that overlap in time on one GPU race.
+    Returns y."""
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    P = state_pool.shape[0]
+    N_s = cache_indices.shape[0]
+    dev = q.device
+    act = q.dtype
+    _check("q", q, (T, Hk, Dk), act, dev)
+    _check("k", k, (T, Hk, Dk), act, dev)
+    _check("v", v, (T, Hv, Dv), act, dev)
+    _check("g", g, (T, Hv), torch.float32, dev)
+    _check("beta", beta, (T, Hv), torch.float32, dev)
+    _check("state_pool", state_pool, (P, Hv, Dv, Dk), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    _check("y", y, (T, Hv, Dv), act, dev)
+    sc = 0.0 if scale is None else float(scale)
+    flags = GDN_QK_L2NORM if l2norm else 0
+    _call("gdn_chunk_prefill_noalloc", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+          _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags, _ptr(y),
+          _act_of(q), _stream(dev))
     return y
 
 

@@ -39,6 +39,7 @@
 //     fp32 activations: gdn_prefill_kernel (section 3), register fragments
 //     from global memory, hi/lo on both sides of every product.
 
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -2012,13 +2013,15 @@ extern "C" size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, in
 namespace gdn {
 namespace {
 
-// Every host-side check, then (unless check_only) the launches.
+// Every host-side check, then (unless check_only) the launches.  With
+// no_ws_checks (a check-only pass for the library's own scratch) the checks
+// of the workspace pointer, size and overlaps are left out.
 int chunk_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   float* state_pool, int64_t pool_size, const int64_t* cache_indices,
                   const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
                   int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
                   size_t workspace_bytes, const Epilogue* epi, hipStream_t stream,
-                  bool check_only = false, int64_t max_len = 0) {
+                  bool check_only = false, int64_t max_len = 0, bool no_ws_checks = false) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
@@ -2028,29 +2031,31 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
     return GDN_ERR_UNSUPPORTED;
   chunk = effective_chunk(Dk, chunk);
   if (N_s == 0) return GDN_OK;
-  if (!cache_indices || !cu_seqlens || !state_pool || !workspace) return GDN_ERR_NULL;
+  if (!cache_indices || !cu_seqlens || !state_pool || (!workspace && !no_ws_checks)) return GDN_ERR_NULL;
   if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_pool) || !aligned16(workspace))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_pool) ||
+      (!aligned16(workspace) && !no_ws_checks))
     return GDN_ERR_ALIGN;
   // per-chunk copy offsets are 32-bit: 64 token rows of q/k/v must span < 1 GiB
   if (static_cast<uint64_t>(Hk) * Dk * 2 * 64 >= (1ull << 30) ||
       static_cast<uint64_t>(Hv) * Dv * 2 * 64 >= (1ull << 30))
     return GDN_ERR_UNSUPPORTED;
   const Layout L = layout(T_tot, N_s, Hv, chunk, act == GDN_BF16);
-  if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < L.total && !no_ws_checks) return GDN_ERR_WORKSPACE;
+  const size_t ws_bytes = no_ws_checks ? 0 : L.total;  // an empty span overlaps nothing
   const size_t pool_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
   const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
-  if (overlaps(y, y_bytes, state_pool, pool_bytes) || overlaps(workspace, L.total, state_pool, pool_bytes) ||
-      overlaps(workspace, L.total, y, y_bytes))
+  if (overlaps(y, y_bytes, state_pool, pool_bytes) || overlaps(workspace, ws_bytes, state_pool, pool_bytes) ||
+      overlaps(workspace, ws_bytes, y, y_bytes))
     return GDN_ERR_ALIAS;
-  if (epi && (overlaps(epi->z, y_bytes, state_pool, pool_bytes) || overlaps(epi->z, y_bytes, workspace, L.total)))
+  if (epi && (overlaps(epi->z, y_bytes, state_pool, pool_bytes) || overlaps(epi->z, y_bytes, workspace, ws_bytes)))
     return GDN_ERR_ALIAS;
   {
     const size_t qk_bytes = static_cast<size_t>(T_tot) * Hk * Dk * act_bytes(act);
     const size_t v_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
     const size_t gb_bytes = static_cast<size_t>(T_tot) * Hv * sizeof(float);
     const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {g, gb_bytes}, {beta, gb_bytes}};
-    const Span out[] = {{y, y_bytes}, {state_pool, pool_bytes}, {workspace, L.total}};
+    const Span out[] = {{y, y_bytes}, {state_pool, pool_bytes}, {workspace, ws_bytes}};
     if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
   }
   if (check_only) return GDN_OK;
@@ -2253,4 +2258,74 @@ extern "C" int gdn_chunk_prefill_fixed(const void* q, const void* k, const void*
   if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
   return chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk, Dv,
                        chunk, scale, flags, y, act, workspace, main, nullptr, stream, false, T);
+}
+
+// ------------------------------------------------- allocation-free prefill
+//
+// gdn_chunk_prefill_noalloc: the same call with the workspace in a static
+// device array of this library instead of caller memory, for callers that
+// cannot allocate (code under graph capture, tight serving loops).  Every
+// GPU the library runs on holds its own copy of the array until the process
+// ends.  Nothing in the workspace needs to start at zero: the chunk-map
+// kernel writes every index the later kernels read, and the WY pass writes
+// every plane and factor record the chunk loop reads.
+
+namespace gdn {
+namespace {
+
+constexpr size_t kScratchBytes = size_t{128} << 20;
+constexpr int kScratchDevices = 64;
+
+std::mutex scratch_mutex;
+void* scratch_address[kScratchDevices];
+
+}  // namespace
+}  // namespace gdn
+
+static __device__ __align__(256) unsigned char scratch[gdn::kScratchBytes];
+
+namespace gdn {
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there and kept.  The array's name in host code stands for a host-side
+// shadow, never for device memory: only this address reaches a kernel.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return GDN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_address[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return GDN_ERR_DEVICE;
+    }
+    scratch_address[dev] = p;
+  }
+  *out = scratch_address[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                         const float* beta, float* state_pool, int64_t pool_size,
+                                         const int64_t* cache_indices, const int64_t* cu_seqlens, int N_s,
+                                         int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk,
+                                         float scale, unsigned flags, void* y, gdn_dtype act,
+                                         hipStream_t stream) {
+  using namespace gdn;
+  // every check of the caller's arguments first, before any HIP call
+  const int pre = chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot,
+                                Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, nullptr, 0, nullptr, stream, true, 0,
+                                true);
+  if (pre != GDN_OK || N_s == 0) return pre;
+  const size_t need = gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act);
+  if (need == 0 || need > kScratchBytes) return GDN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_on_current_device(&ws);
+  if (st != GDN_OK) return st;
+  return chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot, Hk, Hv,
+                       Dk, Dv, chunk, scale, flags, y, act, ws, kScratchBytes, nullptr, stream);
 }

@@ -379,6 +379,32 @@ int comba_chunk_prefill(const void* q, const void* k, const void* v,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill_noalloc - gdn_chunk_prefill without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace lives in a static 128 MiB device array of the library (one per
+ * GPU, held until the process ends); the call allocates nothing and calls
+ * no allocating routine.  Arguments, results and requirements: those of
+ * gdn_chunk_prefill, minus workspace and workspace_bytes.
+ * Limit: gdn_chunk_prefill_workspace() for these sizes must be at most
+ * 134,217,728 bytes (e.g. about 8,000 tokens at 48 value heads, chunk 64,
+ * bf16), else GDN_ERR_WORKSPACE and nothing is launched.
+ * Every call on one GPU uses that GPU's one array: calls that can overlap in
+ * time on the same GPU (different streams, or host threads without ordering)
+ * race and give unspecified results; calls ordered on one stream are safe.
+ * The first call on each device looks the array's address up (no device
+ * memory is touched); GDN_ERR_DEVICE if that fails.
+ */
+int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              float* state_pool, int64_t pool_size,
+                              const int64_t* cache_indices,
+                              const int64_t* cu_seqlens, int N_s,
+                              int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
+                              int chunk, float scale, unsigned flags, void* y,
+                              gdn_dtype act, hipStream_t stream);
+
+/*
  * gdn_stream_copy - measurement helper: copies `bytes` bytes from src to dst
  * with one 16-byte non-temporal load and one 16-byte non-temporal store per
  * thread, the access pattern of the decode step's state stream.  Source:

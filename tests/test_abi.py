@@ -320,3 +320,28 @@ def test_stream_copy_validation(lib):
     assert cp(n=4100) == SHAPE
     assert cp(dst=A + 2048) == ALIAS
     assert cp(dst=A + (1 << 44), n=(1 << 31) * 4096) == UNSUP  # more workgroups than one launch holds
+
+
+def prefill_noalloc(lib, q=A, k=A + BIG, v=A + 2 * BIG, g=A + 3 * BIG, beta=A + 4 * BIG, pool=A + 5 * BIG,
+                    P=4, ci=A + 6 * BIG, cu=A + 7 * BIG, N_s=2, T=100, Hk=2, Hv=4, Dk=128, Dv=128, chunk=64,
+                    flags=1, y=A + 8 * BIG, act=1):
+    return lib.gdn_chunk_prefill_noalloc(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(pool), P, _p(ci), _p(cu),
+                                         N_s, T, Hk, Hv, Dk, Dv, chunk, ctypes.c_float(0.0), flags, _p(y), act,
+                                         None)
+
+
+def test_prefill_noalloc_validation(lib):
+    """The caller's arguments are checked, and a call whose workspace would
+    exceed the library's 128 MiB scratch is refused, before any HIP call."""
+    assert prefill_noalloc(lib, N_s=-1) == SHAPE
+    assert prefill_noalloc(lib, act=9) == DTYPE
+    assert prefill_noalloc(lib, Dk=512) == UNSUP
+    assert prefill_noalloc(lib, q=0) == NULL
+    assert prefill_noalloc(lib, cu=0) == NULL
+    assert prefill_noalloc(lib, pool=A + 5 * BIG + 8) == ALIGN
+    assert prefill_noalloc(lib, y=A + 5 * BIG + 64) == ALIAS
+    assert prefill_noalloc(lib, N_s=0, q=0, cu=0) == OK
+    big = dict(T=20000, N_s=8, Hk=16, Hv=48)
+    assert lib.gdn_chunk_prefill_workspace(20000, 8, 16, 48, 128, 128, 64, 1) > 128 << 20
+    assert prefill_noalloc(lib, **big) == WORKSPACE
+    assert lib.gdn_chunk_prefill_workspace(8000, 8, 16, 48, 128, 128, 64, 1) <= 128 << 20
