@@ -385,6 +385,63 @@ def bench_layer(steps, warmup, device):
                 plain_sec=plain_sec, fused_sec=fused_sec)
 
 
+def bench_conv_decode(steps, warmup, device):
+    """gdn_conv_decode_step at the B=256 decode batch (conv + SiLU of the
+    10,240 raw channels with the history in place, q/k norm, gates and the
+    decode step: a q/k prologue kernel and the decode kernel with the value
+    channels' conv; states ping-pong between two buffers), and the same
+    token through separate kernels: gdn_conv_silu (one token per sequence),
+    gdn_prefill_gates and gdn_decode_step (which has no q/k norm, so the
+    separate chain does slightly less work)."""
+    import torch
+    import gated_deltanet_linear_gdn_amd as gdn
+    from gated_deltanet_linear_gdn_amd import synth
+    c = synth.DECODE_B256
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    rng = np.random.default_rng(0)
+    bf, f32 = torch.bfloat16, torch.float32
+    toks = []
+    for _ in range(4):
+        d = synth.layer_decode_inputs(rng, B, Hk, Hv, Dk, Dv)
+        toks.append({n: _dev(x, f32 if n in ("conv_w", "conv_state", "A_log", "dt_bias") else bf, device)
+                     for n, x in d.items()})
+    w, A_log, dtb = toks[0]["conv_w"], toks[0]["A_log"], toks[0]["dt_bias"]
+    S = [torch.zeros((B, Hv, Dv, Dk), dtype=f32, device=device), torch.empty((B, Hv, Dv, Dk), dtype=f32, device=device)]
+    H = toks[0]["conv_state"].clone()
+    y = torch.empty((B, Hv, Dv), dtype=bf, device=device)
+    ws = torch.empty(gdn.gdn_conv_decode_workspace(B, Hk, Hv, Dk, Dv), dtype=torch.uint8, device=device)
+
+    def fused(i):
+        t = toks[i % 4]
+        gdn.gdn_conv_decode_step(S[i % 2], S[(i + 1) % 2], t["qkv"], w, H, t["a"], t["b"], A_log, dtb, Hk, y=y,
+                                 workspace=ws)
+
+    for i in range(synth.WARMUP_STEPS):
+        fused(i)
+    fused_sec = _timed(fused, steps, warmup)
+    ci = torch.arange(B, dtype=torch.int64, device=device)
+    cu = torch.arange(B + 1, dtype=torch.int64, device=device)
+    q = torch.empty((B, Hk, Dk), dtype=bf, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty((B, Hv, Dv), dtype=bf, device=device)
+    g = torch.empty((B, Hv), dtype=f32, device=device)
+    beta = torch.empty((B, Hv), dtype=f32, device=device)
+    beta_act = torch.full((B, Hv), 0.5, dtype=bf, device=device)
+
+    def separate(i):
+        t = toks[i % 4]
+        gdn.gdn_conv_silu(t["qkv"], w, H, ci, cu, Hk, Hv, Dk, Dv, q, k, v)
+        gdn.gdn_prefill_gates(t["a"], t["b"], A_log, dtb, g, beta)
+        gdn.gdn_decode_step(S[i % 2], S[(i + 1) % 2], q, k, v, g, beta_act, y)
+
+    sep_sec = _timed(separate, steps, warmup)
+    C = 2 * Hk * Dk + Hv * Dv
+    state_bytes = 2 * B * Hv * Dv * Dk * 4
+    hist_bytes = 2 * B * C * 3 * 4
+    return dict(fused_sec=fused_sec, sep_sec=sep_sec, state_bytes=state_bytes,
+                bytes=state_bytes + hist_bytes + B * C * 2 + C * 16 + B * Hv * (2 * 2 + Dv * 2))
+
+
 def bench_comba_hbm(steps, warmup, device, B=896, H=16, K=128, V=128):
     """Comba at one of the KBench measure shapes (0.94 GB state per copy,
     well beyond the 256 MB MALL)."""
@@ -578,6 +635,7 @@ def main():
     pre1 = bench_prefill(max(5, args.steps // 20), 3, device, lengths=[4096])
     dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256)
     lay = bench_layer(max(5, args.steps // 50), 3, device)
+    cdec = bench_conv_decode(max(10, args.steps // 5), 5, device)
     wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
     cwins = {T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
     copy_gbps, own_copy_gbps = bench_copy(device)
@@ -632,6 +690,15 @@ def main():
                   "measure_shape_B896_H16": {"GBps": round(com_hbm, 2),
                                              "us_per_step": round(com_hbm_sec * 1e6, 2),
                                              "frac_of_hbm_peak": round(com_hbm / HBM_PEAK_GBPS, 4)}},
+        "conv_decode": {"workload": "gdn_conv_decode_step at B=256 Hk=16 Hv=48 Dk=Dv=128 bf16: conv + SiLU of "
+                                    "10,240 raw channels (history in place), q/k norm, gates and the decode "
+                                    "step (q/k prologue kernel + decode kernel with the value conv); states "
+                                    "ping-pong",
+                        "us_per_step": round(cdec["fused_sec"] * 1e6, 2),
+                        "GBps": round(cdec["bytes"] / cdec["fused_sec"] / 1e9, 1),
+                        "state_GBps": round(cdec["state_bytes"] / cdec["fused_sec"] / 1e9, 1),
+                        "separate_kernels_us_per_step": round(cdec["sep_sec"] * 1e6, 2),
+                        "bytes_per_step": cdec["bytes"]},
         "prefill": {"workload": "gdn_prefill_gates + gdn_chunk_prefill, 8 sequences of U[512,4096] "
                                 "tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64, pool 16",
                     "tokens": pre["tokens"], "lengths": pre["lengths"],

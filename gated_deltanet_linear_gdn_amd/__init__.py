@@ -26,6 +26,7 @@ __all__ = [
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
     "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
     "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy", "gdn_chunk_prefill_noalloc",
+    "gdn_conv_decode_step", "gdn_conv_decode_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +101,10 @@ def load_library():
     lib.gdn_chunk_prefill_noalloc.restype = _i
     lib.gdn_chunk_prefill_noalloc.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
                                               + [_f, ctypes.c_uint, _vp, _i, _vp])
+    lib.gdn_conv_decode_workspace.restype = ctypes.c_size_t
+    lib.gdn_conv_decode_workspace.argtypes = [_i] * 5
+    lib.gdn_conv_decode_step.restype = _i
+    lib.gdn_conv_decode_step.argtypes = [_vp] * 10 + [_i] * 5 + [_f, ctypes.c_uint, _i, _vp, ctypes.c_size_t, _vp]
     lib.gdn_stream_copy.restype = _i
     lib.gdn_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -321,6 +326,53 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
           _stream(dev))
     return y
+
+
+def gdn_conv_decode_workspace(B, Hk, Hv, Dk, Dv) -> int:
+    """Bytes of workspace ``gdn_conv_decode_step`` needs."""
+    return int(load_library().gdn_conv_decode_workspace(B, Hk, Hv, Dk, Dv))
+
+
+def gdn_conv_decode_step(state_in, state_out, qkv, conv_w, conv_state, a, b, A_log, dt_bias, Hk, y=None,
+                         scale=None, l2norm=True, workspace=None):
+    """One decode token of the layer front (see ``gdn_conv_decode_step`` in
+    include/gdn.h): conv + SiLU of the raw q/k/v channels with the history
+    ``conv_state`` updated in place, q/k L2 norm and scale, gates from raw
+    a, b, and the decode step.
+
+    state_in [B,Hv,Dv,Dk] f32; state_out same shape, None (allocated) or
+    state_in itself; qkv [B, 2*Hk*Dk + Hv*Dv] act; conv_w [C,4] f32;
+    conv_state [B,C,3] f32; a, b [B,Hv] act; A_log, dt_bias [Hv] f32;
+    y [B,Hv,Dv] or None; workspace: a uint8 device tensor of at least
+    ``gdn_conv_decode_workspace`` bytes, or None.  Returns (state_out, y)."""
+    B, Hv, Dv, Dk = state_in.shape
+    dev, act = qkv.device, qkv.dtype
+    C = 2 * Hk * Dk + Hv * Dv
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    if y is None:
+        y = torch.empty((B, Hv, Dv), dtype=act, device=dev)
+    _check("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    _check("qkv", qkv, (B, C), act, dev)
+    _check("conv_w", conv_w, (C, 4), torch.float32, dev)
+    _check("conv_state", conv_state, (B, C, 3), torch.float32, dev)
+    _check("a", a, (B, Hv), act, dev)
+    _check("b", b, (B, Hv), act, dev)
+    _check("A_log", A_log, (Hv,), torch.float32, dev)
+    _check("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check("y", y, (B, Hv, Dv), act, dev)
+    need = gdn_conv_decode_workspace(B, Hk, Hv, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    flags = GDN_QK_L2NORM if l2norm else 0
+    _call("gdn_conv_decode_step", dev, _ptr(state_in), _ptr(state_out), _ptr(qkv), _ptr(conv_w), _ptr(conv_state),
+          _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(y), B, Hk, Hv, Dk, Dv, sc, flags, _act_of(qkv),
+          _ptr(workspace), workspace.numel(), _stream(dev))
+    return state_out, y
 
 
 def gdn_chunk_prefill_noalloc(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, y, chunk=64,

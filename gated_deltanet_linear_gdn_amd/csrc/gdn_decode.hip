@@ -28,158 +28,20 @@
 // * In-place (state_out == state_in) is safe: each element is read and then
 //   written by the same lane.
 
-#include "gdn_device.h"
-#include "gdn_host.h"
+#include "gdn_decode_core.h"
 
 namespace gdn {
 namespace {
-
-constexpr int kThreads = 128;
-constexpr int kRowsPerLane = 2;
-// grid z holds at most this many sequences: larger batches launch in slices
-constexpr int kMaxGridZ = 65535;
-
-// ceil(2^32 / G) for the kernels' multiply-high hk = hv / G; 0 for G == 1,
-// whose reciprocal does not fit 32 bits.  Exact for every hv < 2^16: the
-// reciprocal's rounding error m*G - 2^32 is below G <= 2^16.
-unsigned hk_reciprocal(int G) {
-  return G == 1 ? 0u : static_cast<unsigned>(((1ull << 32) + G - 1) / static_cast<unsigned>(G));
-}
-
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16> {
-  uint2 w;
-  __device__ __forceinline__ void load(const bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ f32x4 f() const {
-    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-  }
-};
-template <> struct Raw4<float> {
-  f32x4 w;
-  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
-  __device__ __forceinline__ f32x4 f() const { return w; }
-};
-
-// One activation element as stored, converted on use.
-__device__ __forceinline__ float to_f32(bf16 h) { return bf16_to_f32(h); }
-__device__ __forceinline__ float to_f32(float x) { return x; }
-
-template <int DK, int NV, bool FULL, typename T>
-__global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
-    const float* state_in, float* state_out, const T* __restrict__ q,
-    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
-    const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
-    unsigned hk_mul) {
-  constexpr int LPR = DK / 4;            // lanes per row
-  constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
-  constexpr int ROWS = RPS * NV;         // rows per workgroup
-
-  // grid (part, hv, b): the same dispatch order as slice-major with parts
-  // innermost, and no integer division on the way in (hk = hv / (Hv/Hk) as a
-  // multiply-high by hk_mul, the host's hk_reciprocal(Hv/Hk)).
-  const int part = blockIdx.x;
-  const int hv = blockIdx.y;
-  const int b = blockIdx.z;
-  const int slice = b * Hv + hv;  // n = b * Hv + hv
-  const int hk = hk_mul ? static_cast<int>(__umulhi(static_cast<unsigned>(hv), hk_mul)) : hv;
-  const int tid = threadIdx.x;
-  const int c4 = tid % LPR;                        // float4 column within the row
-  const int row0 = part * ROWS + tid / LPR;
-
-  const size_t qk_off = (static_cast<size_t>(b) * Hk + hk) * DK + c4 * 4;
-  const size_t slice_off = static_cast<size_t>(slice) * Dv * DK;
-  const float* sin = state_in + slice_off + c4 * 4;
-  float* sout = state_out + slice_off + c4 * 4;
-  // FULL: every row this workgroup covers exists (Dv % ROWS == 0) and the
-  // body is branch-free.  Otherwise rows past Dv load the last row again
-  // (a branch around a load makes it wait for the previous one) and only
-  // their stores are skipped.
-  auto rowc = [&](int n) { return FULL ? row0 + n * RPS : min(row0 + n * RPS, Dv - 1); };
-
-  // Every load is issued before the first wait: the small activation loads
-  // first (loads complete in issue order, so their first use does not wait
-  // for the state rows), kept as stored, then the NV state rows.  Converting
-  // bf16 activations right after their loads would make the compiler wait
-  // for them before issuing the state loads: two memory round trips per
-  // workgroup instead of one.  The barriers keep the scheduler from moving
-  // any conversion (and its wait) between the loads.
-  Raw4<T> kr, qr;
-  kr.load(k + qk_off);
-  qr.load(q + qk_off);
-  const float graw = g[slice];
-  const T btr = beta[slice];
-  T vr[NV];
-#pragma unroll
-  for (int n = 0; n < NV; ++n) vr[n] = v[static_cast<size_t>(slice) * Dv + rowc(n)];
-  __builtin_amdgcn_sched_barrier(0);
-  f32x4 s[NV];
-#pragma unroll
-  for (int n = 0; n < NV; ++n) s[n] = load_stream(sin + static_cast<size_t>(rowc(n)) * DK);
-  __builtin_amdgcn_sched_barrier(0);
-  const f32x4 kk = kr.f(), qq = qr.f();
-  const float bt = to_f32(btr);
-  float vv[NV];
-#pragma unroll
-  for (int n = 0; n < NV; ++n) vv[n] = to_f32(vr[n]);
-  const float gate = expf(graw);
-  const float kq = group_sum<LPR>(dot4(kk, qq));
-
-#pragma unroll
-  for (int n = 0; n < NV; ++n) {
-    const int row = row0 + n * RPS;
-    const float sk = group_sum<LPR>(dot4(s[n], kk));
-    const float sq = group_sum<LPR>(dot4(s[n], qq));
-    const float d = bt * (vv[n] - gate * sk);
-    const f32x4 sn = gate * s[n] + d * kk;
-    if (FULL || row < Dv) {
-      store_stream(sout + static_cast<size_t>(row) * DK, sn);
-      if (c4 == 0) Act<T>::store(y + static_cast<size_t>(slice) * Dv + row, gate * sq + d * kq);
-    }
-  }
-}
-
-template <int DK, typename T>
-int launch_dk(const float* state_in, float* state_out, const void* q, const void* k,
-              const void* v, const float* g, const void* beta, void* y, int B, int Hk,
-              int Hv, int Dv, hipStream_t stream) {
-  constexpr int NV = kRowsPerLane;
-  constexpr int ROWS = kThreads / (DK / 4) * NV;
-  const int parts = (Dv + ROWS - 1) / ROWS;
-  if (Hv > 65535) return GDN_ERR_SHAPE;  // grid y
-  const unsigned hk_mul = hk_reciprocal(Hv / Hk);
-  const T* qa = static_cast<const T*>(q);
-  const T* ka = static_cast<const T*>(k);
-  const T* va = static_cast<const T*>(v);
-  const T* ba = static_cast<const T*>(beta);
-  T* ya = static_cast<T*>(y);
-  (void)hipGetLastError();
-  for (int b0 = 0; b0 < B; b0 += kMaxGridZ) {
-    const int nb = std::min(B - b0, kMaxGridZ);
-    const size_t sv = static_cast<size_t>(b0) * Hv;  // value-head slices before this one
-    const size_t sk = static_cast<size_t>(b0) * Hk * DK;
-    const dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(Hv), static_cast<unsigned>(nb));
-    if (Dv % ROWS == 0)
-      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, true, T>), grid, dim3(kThreads), 0, stream,
-                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + sk, ka + sk,
-                         va + sv * Dv, g + sv, ba + sv, ya + sv * Dv, Hk, Hv, Dv, hk_mul);
-    else
-      hipLaunchKernelGGL((gdn_decode_kernel<DK, NV, false, T>), grid, dim3(kThreads), 0, stream,
-                         state_in + sv * Dv * DK, state_out + sv * Dv * DK, qa + sk, ka + sk,
-                         va + sv * Dv, g + sv, ba + sv, ya + sv * Dv, Hk, Hv, Dv, hk_mul);
-  }
-  return launch_status();
-}
 
 template <typename T>
 int launch(const float* state_in, float* state_out, const void* q, const void* k,
            const void* v, const float* g, const void* beta, void* y, int B, int Hk, int Hv,
            int Dk, int Dv, hipStream_t stream) {
   switch (Dk) {
-    case 32: return launch_dk<32, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
-    case 64: return launch_dk<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
-    case 128: return launch_dk<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
-    case 256: return launch_dk<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 32: return launch_decode_dk<32, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 64: return launch_decode_dk<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 128: return launch_decode_dk<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 256: return launch_decode_dk<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }

@@ -61,6 +61,28 @@ template <> struct Act<bf16> {
   }
 };
 
+// One activation element as stored, converted to fp32 on use.
+__device__ __forceinline__ float to_f32(bf16 h) { return bf16_to_f32(h); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Four consecutive activations as stored (one 8- or 16-byte load), converted
+// on use: keeping a load's result unconverted lets later loads issue before
+// the compiler's wait for it.
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  uint2 w;
+  __device__ __forceinline__ void load(const bf16* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ f32x4 f() const {
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+};
+template <> struct Raw4<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ f32x4 f() const { return w; }
+};
+
 // ------------------------------------------------------- streaming state I/O
 
 __device__ __forceinline__ f32x4 load_stream(const float* p) {

@@ -37,6 +37,13 @@ inline bool inputs_overlap_outputs(const Span (&in)[NI], const Span (&out)[NO]) 
   return false;
 }
 
+// ceil(2^32 / G) for the decode kernels' multiply-high hk = hv / G; 0 for
+// G == 1, whose reciprocal does not fit 32 bits.  Exact for every hv < 2^16:
+// the reciprocal's rounding error m*G - 2^32 is below G <= 2^16.
+inline unsigned hk_reciprocal(int G) {
+  return G == 1 ? 0u : static_cast<unsigned>(((1ull << 32) + G - 1) / static_cast<unsigned>(G));
+}
+
 inline bool pow2_head(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 // The gated RMS norm epilogue (gdn_layer.hip), also used by the prefill

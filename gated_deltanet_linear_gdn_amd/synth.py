@@ -134,6 +134,24 @@ def layer_inputs(rng, T, Hk, Hv, Dk, Dv, pool_size, act="bf16"):
     return dict(qkv=qkv, conv_w=conv_w, conv_state=conv_state, z=z, gamma=gamma)
 
 
+def layer_decode_inputs(rng, B, Hk, Hv, Dk, Dv, act="bf16"):
+    """One decode token of the layer front for B sequences: qkv [B, C] ~
+    N(0,1) (C = 2*Hk*Dk + Hv*Dv raw channels, before the conv); conv weights
+    [C, 4] ~ N(0, 0.5^2) and conv history [B, C, 3] ~ N(0,1) (fp32); raw
+    gates a, b [B, Hv] ~ N(0,1) (activation dtype); A_log [Hv] ~ U(0, 2.7)
+    and dt_bias [Hv] ~ N(0, 0.5^2) (fp32): the layer recipe above with the
+    prefill's gate recipe."""
+    C = 2 * Hk * Dk + Hv * Dv
+    qkv = _act(rng.standard_normal((B, C), dtype=np.float32), act)
+    conv_w = (0.5 * rng.standard_normal((C, 4), dtype=np.float32)).astype(np.float32)
+    conv_state = rng.standard_normal((B, C, 3), dtype=np.float32)
+    a = _act(rng.standard_normal((B, Hv), dtype=np.float32), act)
+    b = _act(rng.standard_normal((B, Hv), dtype=np.float32), act)
+    A_log = rng.uniform(0.0, 2.7, size=Hv).astype(np.float32)
+    dt_bias = (0.5 * rng.standard_normal(Hv, dtype=np.float32)).astype(np.float32)
+    return dict(qkv=qkv, conv_w=conv_w, conv_state=conv_state, a=a, b=b, A_log=A_log, dt_bias=dt_bias)
+
+
 # Workload shapes (seed 0 for each).
 TINY = dict(B=2, Hk=2, Hv=4, Dk=32, Dv=32, act="f32", prefill_len=16, chunk=8)
 DECODE_B64 = dict(B=64, Hk=16, Hv=48, Dk=128, Dv=128, act="bf16")

@@ -379,6 +379,57 @@ int comba_chunk_prefill(const void* q, const void* k, const void* v,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_conv_decode_workspace - bytes of device workspace gdn_conv_decode_step
+ * needs: B * (2*Hk*Dk + Hv*Dv + 2*Hv) floats (the convolved, normalised
+ * q, k, v and the gates of the token, fp32); 0 for invalid sizes.
+ */
+size_t gdn_conv_decode_workspace(int B, int Hk, int Hv, int Dk, int Dv);
+
+/*
+ * gdn_conv_decode_step - one decode token of the layer front: the 4-tap
+ * causal conv + SiLU of the token's q, k and v channels with the history
+ * updated in place (gdn_conv_silu), the L2 norm of q and k with the query
+ * scale and the gates from raw a, b (gdn_prefill_gates), then the gated
+ * delta-rule step (gdn_decode_step).  Two kernels: a prologue writes the
+ * token's convolved, normalised q, k, v and its gates to the workspace in
+ * fp32 (never rounded to the activation dtype), the decode kernel reads them.
+ * Source: regolith `gdn.metal`, header comment and the conv/SiLU block of
+ * its kernel (conv, SiLU, norms and gates ahead of the recurrence);
+ * metaltile-std `gated_delta.rs`, "Recurrence per step".  For sequence b:
+ *     x'_c = SiLU(h[c][0] w[c][0] + h[c][1] w[c][1] + h[c][2] w[c][2] + x_c w[c][3])
+ *            over the C = 2*Hk*Dk + Hv*Dv channels [q heads | k heads | v heads],
+ *            after which conv_state[b][c] = (h[c][1], h[c][2], x_c)
+ *     k^ = k' / sqrt(|k'|^2 + 1e-6),  q^ = scale q' / sqrt(|q'|^2 + 1e-6)
+ *            (with GDN_QK_L2NORM; without it k^ = k', q^ = scale q')
+ *     g = -exp(A_log[hv]) softplus(a + dt_bias[hv]),  beta = sigmoid(b)
+ *     then for every value head hv (key head hv / (Hv/Hk)) the decode step
+ *     on state slice (b, hv) with (q^, k^, v', g, beta), y its readout.
+ *
+ * state_in, state_out  [B, Hv, Dv, Dk] float32; state_out may equal state_in.
+ * qkv          [B, C] act, this token's raw channels (before the conv).
+ * conv_w       [C, 4] float32 (tap 3 weighs the current token).
+ * conv_state   [B, C, 3] float32, the history (oldest first), read and
+ *              updated in place.
+ * a, b         [B, Hv] act (raw gate inputs).   A_log, dt_bias [Hv] float32.
+ * y            [B, Hv, Dv] act, written.
+ * scale        query scale; <= 0 selects Dk^-1/2.  flags: 0 or GDN_QK_L2NORM.
+ * workspace    device memory of at least gdn_conv_decode_workspace() bytes,
+ *              16-byte aligned; scratch.  Two kernels run on `stream`.
+ * Requirements: those of gdn_decode_step (Dk in {32, 64, 128, 256}, Dv a
+ * multiple of 32 up to 256, Hv % Hk == 0); state_in, state_out, conv_w and
+ * the workspace 16-byte aligned, conv_state 4-byte aligned; y, state_out,
+ * conv_state and the workspace overlap no input and each other
+ * (GDN_ERR_ALIAS).  B == 0 is a no-op.
+ */
+int gdn_conv_decode_step(const float* state_in, float* state_out,
+                         const void* qkv, const float* conv_w,
+                         float* conv_state, const void* a, const void* b,
+                         const float* A_log, const float* dt_bias, void* y,
+                         int B, int Hk, int Hv, int Dk, int Dv, float scale,
+                         unsigned flags, gdn_dtype act, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * gdn_chunk_prefill_noalloc - gdn_chunk_prefill without a caller workspace,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  The

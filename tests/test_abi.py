@@ -345,3 +345,37 @@ def test_prefill_noalloc_validation(lib):
     assert lib.gdn_chunk_prefill_workspace(20000, 8, 16, 48, 128, 128, 64, 1) > 128 << 20
     assert prefill_noalloc(lib, **big) == WORKSPACE
     assert lib.gdn_chunk_prefill_workspace(8000, 8, 16, 48, 128, 128, 64, 1) <= 128 << 20
+
+
+def conv_decode(lib, s_in=A, s_out=A + BIG, x=A + 2 * BIG, w=A + 3 * BIG, hist=A + 4 * BIG, a=A + 6 * BIG,
+                b=A + 7 * BIG, alog=A + 8 * BIG, dtb=A + 9 * BIG, y=A + 10 * BIG, B=2, Hk=2, Hv=4, Dk=128,
+                Dv=128, flags=1, act=1, ws=A + 11 * BIG, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.gdn_conv_decode_workspace(B, Hk, Hv, Dk, Dv)
+    return lib.gdn_conv_decode_step(_p(s_in), _p(s_out), _p(x), _p(w), _p(hist), _p(a), _p(b), _p(alog),
+                                    _p(dtb), _p(y), B, Hk, Hv, Dk, Dv, ctypes.c_float(0.0), flags, act, _p(ws),
+                                    ws_bytes, None)
+
+
+def test_conv_decode_validation(lib):
+    assert lib.gdn_conv_decode_workspace(256, 16, 48, 128, 128) == 256 * (2 * 16 * 128 + 48 * 128 + 96) * 4
+    assert lib.gdn_conv_decode_workspace(-1, 16, 48, 128, 128) == 0
+    assert conv_decode(lib, B=-1) == SHAPE
+    assert conv_decode(lib, Hk=3) == SHAPE
+    assert conv_decode(lib, act=5) == DTYPE
+    assert conv_decode(lib, Dk=96) == UNSUP
+    assert conv_decode(lib, Dv=48) == UNSUP
+    assert conv_decode(lib, flags=4) == UNSUP
+    assert conv_decode(lib, B=0, x=0) == OK               # nothing to do
+    assert conv_decode(lib, x=0) == NULL
+    assert conv_decode(lib, hist=0) == NULL
+    assert conv_decode(lib, ws=0) == NULL
+    assert conv_decode(lib, s_in=A + 8) == ALIGN
+    assert conv_decode(lib, w=A + 3 * BIG + 4) == ALIGN
+    assert conv_decode(lib, hist=A + 4 * BIG + 2) == ALIGN
+    assert conv_decode(lib, ws=A + 11 * BIG + 8) == ALIGN
+    assert conv_decode(lib, ws_bytes=100) == WORKSPACE
+    assert conv_decode(lib, s_out=A + 64) == ALIAS        # partial overlap of the states
+    assert conv_decode(lib, y=A + 2 * BIG) == ALIAS       # y over the raw channels
+    assert conv_decode(lib, hist=A + BIG + 128) == ALIAS  # history inside the new state
+    assert conv_decode(lib, ws=A + 4 * BIG + 64) == ALIAS # workspace over the history
