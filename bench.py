@@ -610,12 +610,17 @@ def cpu_baseline(budget_s=8.0):
                 legs=legs)
 
 
+LEGS = ("inplace", "comba", "prefill", "comba_prefill", "dk256", "layer", "conv_decode", "windows", "copy")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma-separated legs to run beside the headline decode "
+                    "(for profiling runs): " + ", ".join(LEGS))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode and prefill kernels shard by "
@@ -626,19 +631,25 @@ def main():
     import torch
     device = torch.device("cuda:0")
     dec = bench_decode(args.steps, args.warmup, device)
-    dec_ip = bench_decode(max(10, args.steps // 2), args.warmup, device, inplace=True)
-    com = bench_comba(args.steps, args.warmup, device)
-    com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device)
-    pre = bench_prefill(max(5, args.steps // 20), 3, device)
-    cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device)
-    pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256)
-    pre1 = bench_prefill(max(5, args.steps // 20), 3, device, lengths=[4096])
-    dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256)
-    lay = bench_layer(max(5, args.steps // 50), 3, device)
-    cdec = bench_conv_decode(max(10, args.steps // 5), 5, device)
-    wins = {T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
-    cwins = {T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
-    copy_gbps, own_copy_gbps = bench_copy(device)
+    only = set(args.only.split(",")) if args.only else None
+    want = lambda leg: only is None or leg in only
+    if only and not only <= set(LEGS):
+        sys.exit(f"--only: unknown legs {sorted(only - set(LEGS))}; known: {', '.join(LEGS)}")
+    dec_ip = bench_decode(max(10, args.steps // 2), args.warmup, device, inplace=True) if want("inplace") else None
+    com = bench_comba(args.steps, args.warmup, device) if want("comba") else None
+    com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device) if want("comba") else (None, None)
+    pre = bench_prefill(max(5, args.steps // 20), 3, device) if want("prefill") else None
+    cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device) if want("comba_prefill") else None
+    pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256) if want("dk256") else None
+    pre1 = bench_prefill(max(5, args.steps // 20), 3, device, lengths=[4096]) if want("prefill") else None
+    dec256 = bench_decode(max(10, args.steps // 5), 5, device, B=128, Dk=256) if want("dk256") else None
+    lay = bench_layer(max(5, args.steps // 50), 3, device) if want("layer") else None
+    cdec = bench_conv_decode(max(10, args.steps // 5), 5, device) if want("conv_decode") else None
+    wins = ({T: bench_window(max(10, args.steps // 5), 5, device, T) for T in (2, 4, 8)}
+            if want("windows") else None)
+    cwins = ({T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
+             if want("windows") else None)
+    copy_gbps, own_copy_gbps = bench_copy(device) if want("copy") else (None, None)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
     out = {
@@ -664,89 +675,100 @@ def main():
                      "traffic_source": ("stored figure from two earlier rocprofv3 --pmc runs (FETCH_SIZE x 2 + "
                                         "WRITE_SIZE x 1) of this kernel, reported only while its sources hash "
                                         "to the values recorded with it; not read in this run")},
-        "decode_inplace_GBps": round(dec_ip["state_bytes"] / dec_ip["sec"] / 1e9, 2),
-        "torch_copy_GBps": round(copy_gbps, 1),
-        "stream_copy": {"workload": "gdn_stream_copy of 2 GiB: one 16-byte non-temporal load and store per "
-                                    "thread, the decode step's access pattern (GB/s over read + write bytes)",
-                        "GBps": round(own_copy_gbps, 1),
-                        "frac_of_hbm_peak": round(own_copy_gbps / HBM_PEAK_GBPS, 4),
-                        "decode_frac_of_copy": round(gbps / own_copy_gbps, 4)},
-        "decode_window": {"workload": "gdn_decode_window at the B=256 decode batch, all T tokens committed",
-                          "tokens_per_s_single_step": round(dec["shape"]["B"] / dec["sec"], 1),
-                          **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
-                                       "tokens_per_s": round(w["tokens"] / w["sec"], 1),
-                                       "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
-                             for T, w in wins.items()},
-                          "chunked": {"workload": "the same committed windows as gdn_chunk_prefill_fixed "
-                                                  "(no norm, scale 1, chunk min(T, 64)), in place",
-                                      **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
-                                                   "tokens_per_s": round(w["tokens"] / w["sec"], 1),
-                                                   "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
-                                         for T, w in cwins.items()}}},
-        "comba": {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
-                  "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
-                  "us_per_step": round(com["sec"] * 1e6, 2),
-                  "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4),
-                  "measure_shape_B896_H16": {"GBps": round(com_hbm, 2),
-                                             "us_per_step": round(com_hbm_sec * 1e6, 2),
-                                             "frac_of_hbm_peak": round(com_hbm / HBM_PEAK_GBPS, 4)}},
-        "conv_decode": {"workload": "gdn_conv_decode_step at B=256 Hk=16 Hv=48 Dk=Dv=128 bf16: conv + SiLU of "
-                                    "10,240 raw channels (history in place), q/k norm, gates and the decode "
-                                    "step (q/k prologue kernel + decode kernel with the value conv); states "
-                                    "ping-pong",
-                        "us_per_step": round(cdec["fused_sec"] * 1e6, 2),
-                        "GBps": round(cdec["bytes"] / cdec["fused_sec"] / 1e9, 1),
-                        "state_GBps": round(cdec["state_bytes"] / cdec["fused_sec"] / 1e9, 1),
-                        "separate_kernels_us_per_step": round(cdec["sep_sec"] * 1e6, 2),
-                        "bytes_per_step": cdec["bytes"]},
-        "prefill": {"workload": "gdn_prefill_gates + gdn_chunk_prefill, 8 sequences of U[512,4096] "
-                                "tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64, pool 16",
-                    "tokens": pre["tokens"], "lengths": pre["lengths"],
-                    "us_per_call": round(pre["sec"] * 1e6, 2),
-                    "tokens_per_s": round(pre["tokens"] / pre["sec"], 1),
-                    "canonical_TFLOPs": round(pre["flops"] / pre["sec"] / 1e12, 2),
-                    "mfma_frac_of_bf16_peak": round(pre["flops"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "min_bytes": pre["min_bytes"],
-                    "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
-        "prefill_single": {"workload": "gdn_prefill_gates + gdn_chunk_prefill of one 4,096-token sequence "
-                                       "(the workload's longest length), Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64",
-                           "us_per_call": round(pre1["sec"] * 1e6, 2),
-                           "tokens_per_s": round(pre1["tokens"] / pre1["sec"], 1)},
-        "comba_prefill": {"workload": "comba_chunk_prefill, the same 8 sequences, H=32 K=V=128, bf16, "
-                                      "chunk 64, pool 16",
-                          "tokens": cpre["tokens"],
-                          "us_per_call": round(cpre["sec"] * 1e6, 2),
-                          "tokens_per_s": round(cpre["tokens"] / cpre["sec"], 1),
-                          "canonical_TFLOPs": round(cpre["flops"] / cpre["sec"] / 1e12, 2),
-                          "mfma_frac_of_bf16_peak": round(cpre["flops"] / cpre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
-                          "issued_mfma_frac_of_bf16_peak": round(cpre["issued"] / cpre["sec"] / 1e12
-                                                                 / BF16_PEAK_TFLOPS, 4),
-                          "min_bytes": cpre["min_bytes"],
-                          "hbm_frac_of_peak": round(cpre["min_bytes"] / cpre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)},
-        "dk256": {"workload": "key head size 256 (value 128): gdn_chunk_prefill at the varlen token mix "
-                              "(Hk=16 Hv=48, 32-token chunks) and gdn_decode_step at B=128 (the same "
-                              "1.6 GB of state per step as the headline)",
-                  "prefill_us_per_call": round(pre256["sec"] * 1e6, 2),
-                  "prefill_tokens_per_s": round(pre256["tokens"] / pre256["sec"], 1),
-                  "prefill_canonical_TFLOPs": round(pre256["flops"] / pre256["sec"] / 1e12, 2),
-                  "decode_GBps": round(dec256["state_bytes"] / dec256["sec"] / 1e9, 2),
-                  "decode_frac_of_hbm_peak": round(dec256["state_bytes"] / dec256["sec"] / 1e9
-                                                   / HBM_PEAK_GBPS, 4)},
-        "layer": {"workload": "prologue gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per "
-                              "slot) and epilogue gdn_gated_rmsnorm around the varlen prefill; conv "
-                              "also as a decode step of 256 sequences",
-                  "conv_us": round(lay["conv_sec"] * 1e6, 2),
-                  "conv_GBps": round(lay["conv_bytes"] / lay["conv_sec"] / 1e9, 1),
-                  "conv_decode_B256_us": round(lay["convd_sec"] * 1e6, 2),
-                  "conv_decode_B256_GBps": round(lay["convd_bytes"] / lay["convd_sec"] / 1e9, 1),
-                  "norm_us": round(lay["norm_sec"] * 1e6, 2),
-                  "norm_GBps": round(lay["norm_bytes"] / lay["norm_sec"] / 1e9, 1),
-                  "prefill_us": round(lay["plain_sec"] * 1e6, 2),
-                  "prefill_gated_fused_us": round(lay["fused_sec"] * 1e6, 2),
-                  "prefill_then_norm_us": round((lay["plain_sec"] + lay["norm_sec"]) * 1e6, 2)},
     }
-    if not args.no_cpu_baseline:
+    if want("inplace"):
+        out["decode_inplace_GBps"] = round(dec_ip["state_bytes"] / dec_ip["sec"] / 1e9, 2)
+    if want("copy"):
+        out["torch_copy_GBps"] = round(copy_gbps, 1)
+    if want("copy"):
+        out["stream_copy"] = {"workload": "gdn_stream_copy of 2 GiB: one 16-byte non-temporal load and store per "
+                                         "thread, the decode step's access pattern (GB/s over read + write bytes)",
+                             "GBps": round(own_copy_gbps, 1),
+                             "frac_of_hbm_peak": round(own_copy_gbps / HBM_PEAK_GBPS, 4),
+                             "decode_frac_of_copy": round(gbps / own_copy_gbps, 4)}
+    if want("windows"):
+        out["decode_window"] = {"workload": "gdn_decode_window at the B=256 decode batch, all T tokens committed",
+                               "tokens_per_s_single_step": round(dec["shape"]["B"] / dec["sec"], 1),
+                               **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
+                                            "tokens_per_s": round(w["tokens"] / w["sec"], 1),
+                                            "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
+                                  for T, w in wins.items()},
+                               "chunked": {"workload": "the same committed windows as gdn_chunk_prefill_fixed "
+                                                       "(no norm, scale 1, chunk min(T, 64)), in place",
+                                           **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
+                                                        "tokens_per_s": round(w["tokens"] / w["sec"], 1),
+                                                        "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
+                                              for T, w in cwins.items()}}}
+    if want("comba"):
+        out["comba"] = {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
+                       "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
+                       "us_per_step": round(com["sec"] * 1e6, 2),
+                       "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4),
+                       "measure_shape_B896_H16": {"GBps": round(com_hbm, 2),
+                                                  "us_per_step": round(com_hbm_sec * 1e6, 2),
+                                                  "frac_of_hbm_peak": round(com_hbm / HBM_PEAK_GBPS, 4)}}
+    if want("conv_decode"):
+        out["conv_decode"] = {"workload": "gdn_conv_decode_step at B=256 Hk=16 Hv=48 Dk=Dv=128 bf16: conv + SiLU of "
+                                         "10,240 raw channels (history in place), q/k norm and gates in a prologue "
+                                         "kernel (fp32 results to a workspace), then the decode kernel; states "
+                                         "ping-pong",
+                             "us_per_step": round(cdec["fused_sec"] * 1e6, 2),
+                             "GBps": round(cdec["bytes"] / cdec["fused_sec"] / 1e9, 1),
+                             "state_GBps": round(cdec["state_bytes"] / cdec["fused_sec"] / 1e9, 1),
+                             "separate_kernels_us_per_step": round(cdec["sep_sec"] * 1e6, 2),
+                             "bytes_per_step": cdec["bytes"]}
+    if want("prefill"):
+        out["prefill"] = {"workload": "gdn_prefill_gates + gdn_chunk_prefill, 8 sequences of U[512,4096] "
+                                     "tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64, pool 16",
+                         "tokens": pre["tokens"], "lengths": pre["lengths"],
+                         "us_per_call": round(pre["sec"] * 1e6, 2),
+                         "tokens_per_s": round(pre["tokens"] / pre["sec"], 1),
+                         "canonical_TFLOPs": round(pre["flops"] / pre["sec"] / 1e12, 2),
+                         "mfma_frac_of_bf16_peak": round(pre["flops"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "issued_mfma_frac_of_bf16_peak": round(pre["issued"] / pre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "min_bytes": pre["min_bytes"],
+                         "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)}
+    if want("prefill"):
+        out["prefill_single"] = {"workload": "gdn_prefill_gates + gdn_chunk_prefill of one 4,096-token sequence "
+                                            "(the workload's longest length), Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64",
+                                "us_per_call": round(pre1["sec"] * 1e6, 2),
+                                "tokens_per_s": round(pre1["tokens"] / pre1["sec"], 1)}
+    if want("comba_prefill"):
+        out["comba_prefill"] = {"workload": "comba_chunk_prefill, the same 8 sequences, H=32 K=V=128, bf16, "
+                                           "chunk 64, pool 16",
+                               "tokens": cpre["tokens"],
+                               "us_per_call": round(cpre["sec"] * 1e6, 2),
+                               "tokens_per_s": round(cpre["tokens"] / cpre["sec"], 1),
+                               "canonical_TFLOPs": round(cpre["flops"] / cpre["sec"] / 1e12, 2),
+                               "mfma_frac_of_bf16_peak": round(cpre["flops"] / cpre["sec"] / 1e12 / BF16_PEAK_TFLOPS, 4),
+                               "issued_mfma_frac_of_bf16_peak": round(cpre["issued"] / cpre["sec"] / 1e12
+                                                                      / BF16_PEAK_TFLOPS, 4),
+                               "min_bytes": cpre["min_bytes"],
+                               "hbm_frac_of_peak": round(cpre["min_bytes"] / cpre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)}
+    if want("dk256"):
+        out["dk256"] = {"workload": "key head size 256 (value 128): gdn_chunk_prefill at the varlen token mix "
+                                   "(Hk=16 Hv=48, 32-token chunks) and gdn_decode_step at B=128 (the same "
+                                   "1.6 GB of state per step as the headline)",
+                       "prefill_us_per_call": round(pre256["sec"] * 1e6, 2),
+                       "prefill_tokens_per_s": round(pre256["tokens"] / pre256["sec"], 1),
+                       "prefill_canonical_TFLOPs": round(pre256["flops"] / pre256["sec"] / 1e12, 2),
+                       "decode_GBps": round(dec256["state_bytes"] / dec256["sec"] / 1e9, 2),
+                       "decode_frac_of_hbm_peak": round(dec256["state_bytes"] / dec256["sec"] / 1e9
+                                                        / HBM_PEAK_GBPS, 4)}
+    if want("layer"):
+        out["layer"] = {"workload": "prologue gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per "
+                                   "slot) and epilogue gdn_gated_rmsnorm around the varlen prefill; conv "
+                                   "also as a decode step of 256 sequences",
+                       "conv_us": round(lay["conv_sec"] * 1e6, 2),
+                       "conv_GBps": round(lay["conv_bytes"] / lay["conv_sec"] / 1e9, 1),
+                       "conv_decode_B256_us": round(lay["convd_sec"] * 1e6, 2),
+                       "conv_decode_B256_GBps": round(lay["convd_bytes"] / lay["convd_sec"] / 1e9, 1),
+                       "norm_us": round(lay["norm_sec"] * 1e6, 2),
+                       "norm_GBps": round(lay["norm_bytes"] / lay["norm_sec"] / 1e9, 1),
+                       "prefill_us": round(lay["plain_sec"] * 1e6, 2),
+                       "prefill_gated_fused_us": round(lay["fused_sec"] * 1e6, 2),
+                       "prefill_then_norm_us": round((lay["plain_sec"] + lay["norm_sec"]) * 1e6, 2)}
+    if not args.no_cpu_baseline and only is None:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
