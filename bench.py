@@ -44,10 +44,11 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # read for a 2 GiB device copy), valid for the kernel built from these
 # sources only: after any change to them the figure is reported as null.
 DECODE_TRAFFIC = {
-    "bytes": 1659865376,
+    "bytes": 1659865600,
     "sources_sha256": {
-        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "25b04ae7d2607b0d94a506e00236447ea0e3f49adc7a7795234d012e75e0a6ef",
-        "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "dba007333ce8708713001b4524a494916ff0b0e7a70406cf145e1271f616b6d5",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "f704cae4ab6a92e0ff345244d61af3ab45b6588c87226fd01dc873f8e839384f",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_decode_core.h": "8cb7542853a02ad7e4dc7b66eab6f2a50524fa225381d0f7d748ae92b662559a",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "a8a63df092593d9aa44ffbc973e351c288ef2e9d6679183e042cbb07333183b6",
     },
 }
 
