@@ -55,7 +55,8 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
     const float* state, float* state_new, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ p, const T* __restrict__ beta,
     const float* __restrict__ g, T* __restrict__ o, float scale) {
-  constexpr int LPR = V / 4;             // lanes per row
+  constexpr int ACT = V / 4;             // float4 columns of a row
+  constexpr int LPR = row_lanes(ACT);    // lanes per row (ACT rounded up to a power of two)
   constexpr int RG = NT / LPR;           // row groups
   constexpr int RPT = K / RG;            // rows per thread (consecutive)
   static_assert(K % RG == 0 && RPT >= 1 && NT % 64 == 0 && LPR <= 64, "shape");
@@ -70,8 +71,12 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
   const int c4 = tid % LPR;
   const int rg = tid / LPR;
   const int r0 = rg * RPT;
+  // Lanes past the row's ACT columns (V not a power of two) load the last
+  // column again, add nothing to the sums and store nothing.
+  const bool live = ACT == LPR || c4 < ACT;
+  const int cc = ACT == LPR ? c4 : min(c4, ACT - 1);
 
-  const size_t soff = static_cast<size_t>(slice) * K * V + static_cast<size_t>(r0) * V + c4 * 4;
+  const size_t soff = static_cast<size_t>(slice) * K * V + static_cast<size_t>(r0) * V + cc * 4;
   f32x4 s[RPT];
 #pragma unroll
   for (int n = 0; n < RPT; ++n) s[n] = load_stream(state + soff + static_cast<size_t>(n) * V);
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
   load_run<T, RPT>(k + koff, kr);
 #pragma unroll
   for (int n = 0; n < RPT; ++n) qr[n] *= scale;
-  const f32x4 vv = Act<T>::load4(v + static_cast<size_t>(slice) * V + c4 * 4);
+  const f32x4 vv = Act<T>::load4(v + static_cast<size_t>(slice) * V + cc * 4);
   const float gate = expf(g[slice]);
   const float bt = Act<T>::load(beta + slice);
 
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
     sq += qr[n] * s[n];
     kq += qr[n] * kr[n];
   }
+  if (!live) sp = sq = f32x4{0.f, 0.f, 0.f, 0.f};
   // Row groups of one wave first: its lanes that hold the same columns
   // differ only in the lane bits from LPR up (cross-lane adds, no LDS), then
   // one partial per wave through LDS behind the single barrier.
@@ -128,10 +134,12 @@ __global__ __launch_bounds__(NT) void comba_decode_kernel(
   }
 
   const f32x4 u = bt * (vv - gate * sp);
-  if (rg == 0) Act<T>::store4(o + static_cast<size_t>(slice) * V + c4 * 4, gate * sq + kq * u);
+  if (rg == 0 && live) Act<T>::store4(o + static_cast<size_t>(slice) * V + cc * 4, gate * sq + kq * u);
+  if (live) {
 #pragma unroll
-  for (int n = 0; n < RPT; ++n)
-    store_stream(state_new + soff + static_cast<size_t>(n) * V, gate * s[n] + kr[n] * u);
+    for (int n = 0; n < RPT; ++n)
+      store_stream(state_new + soff + static_cast<size_t>(n) * V, gate * s[n] + kr[n] * u);
+  }
 }
 
 template <int K, int V, typename T>
@@ -139,7 +147,7 @@ int launch_kv(const float* state, float* state_new, const void* q, const void* k
               const void* v, const void* p, const void* beta, const float* g, void* o,
               long slices, float scale, hipStream_t stream) {
   if (slices > 0x7fffffffL) return GDN_ERR_SHAPE;
-  constexpr int NT = (V / 4) * K < kThreads ? (V / 4) * K : kThreads;
+  constexpr int NT = row_lanes(V / 4) * K < kThreads ? row_lanes(V / 4) * K : kThreads;
   (void)hipGetLastError();
   hipLaunchKernelGGL((comba_decode_kernel<K, V, T, NT>), dim3(static_cast<unsigned>(slices)),
                      dim3(NT), 0, stream, state, state_new, static_cast<const T*>(q),
@@ -153,13 +161,22 @@ template <int K, typename T>
 int launch_k(const float* state, float* state_new, const void* q, const void* k,
              const void* v, const void* p, const void* beta, const float* g, void* o,
              long slices, int V, float scale, hipStream_t stream) {
+  // at most 32 rows (128 state registers) per thread: K * row_lanes(V / 4) <= 8192
   switch (V) {
     case 32: return launch_kv<K, 32, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
     case 64: return launch_kv<K, 64, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+    case 96: return launch_kv<K, 96, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
     case 128: return launch_kv<K, 128, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+    case 160:
+    case 192:
+    case 224:
     case 256:
-      if constexpr (K <= 128)
+      if constexpr (K <= 128) {
+        if (V == 160) return launch_kv<K, 160, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+        if (V == 192) return launch_kv<K, 192, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+        if (V == 224) return launch_kv<K, 224, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
         return launch_kv<K, 256, T>(state, state_new, q, k, v, p, beta, g, o, slices, scale, stream);
+      }
       break;
   }
   return GDN_ERR_UNSUPPORTED;
@@ -174,6 +191,10 @@ int launch(const float* state, float* state_new, const void* q, const void* k, c
     case 64: return launch_k<64, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
     case 128: return launch_k<128, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
     case 256: return launch_k<256, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 96: return launch_k<96, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 160: return launch_k<160, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 192: return launch_k<192, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
+    case 224: return launch_k<224, T>(state, state_new, q, k, v, p, beta, g, o, slices, V, scale, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -189,7 +210,7 @@ extern "C" int comba_decode_step(const float* state, float* state_new, const voi
   using namespace gdn;
   if (B < 0 || H < 0 || K <= 0 || V <= 0) return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!pow2_head(K) || !pow2_head(V) || (K == 256 && V == 256)) return GDN_ERR_UNSUPPORTED;
+  if (!valid_head(K) || !valid_head(V) || K * row_lanes(V / 4) > 8192) return GDN_ERR_UNSUPPORTED;
   if (B == 0 || H == 0) return GDN_OK;
   if (!state || !state_new || !q || !k || !v || !p || !beta || !g || !o) return GDN_ERR_NULL;
   if (!aligned16(state) || !aligned16(state_new) || !aligned16(q) || !aligned16(k) ||

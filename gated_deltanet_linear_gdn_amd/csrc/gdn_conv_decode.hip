@@ -199,6 +199,18 @@ int launch_layer(const float* state_in, float* state_out, const void* qkv, const
     case 256:
       return launch_layer_dk<256, T>(state_in, state_out, qkv, conv_w, conv_state, ws, a, bg, A_log, dt_bias, y,
                                      B, Hk, Hv, Dv, scale, l2, stream);
+    case 96:
+      return launch_layer_dk<96, T>(state_in, state_out, qkv, conv_w, conv_state, ws, a, bg, A_log, dt_bias, y,
+                                     B, Hk, Hv, Dv, scale, l2, stream);
+    case 160:
+      return launch_layer_dk<160, T>(state_in, state_out, qkv, conv_w, conv_state, ws, a, bg, A_log, dt_bias, y,
+                                     B, Hk, Hv, Dv, scale, l2, stream);
+    case 192:
+      return launch_layer_dk<192, T>(state_in, state_out, qkv, conv_w, conv_state, ws, a, bg, A_log, dt_bias, y,
+                                     B, Hk, Hv, Dv, scale, l2, stream);
+    case 224:
+      return launch_layer_dk<224, T>(state_in, state_out, qkv, conv_w, conv_state, ws, a, bg, A_log, dt_bias, y,
+                                     B, Hk, Hv, Dv, scale, l2, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -220,7 +232,7 @@ extern "C" int gdn_conv_decode_step(const float* state_in, float* state_out, con
   using namespace gdn;
   if (B < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!pow2_head(Dk) || Dv % 32 != 0 || Dv > 256 || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
+  if (!valid_head(Dk) || Dv % 32 != 0 || Dv > 256 || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
     return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   if (!state_in || !state_out || !qkv || !conv_w || !conv_state || !a || !b || !A_log || !dt_bias || !y ||

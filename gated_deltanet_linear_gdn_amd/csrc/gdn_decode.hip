@@ -42,6 +42,10 @@ int launch(const float* state_in, float* state_out, const void* q, const void* k
     case 64: return launch_decode_dk<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
     case 128: return launch_decode_dk<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
     case 256: return launch_decode_dk<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 96: return launch_decode_dk<96, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 160: return launch_decode_dk<160, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 192: return launch_decode_dk<192, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
+    case 224: return launch_decode_dk<224, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -63,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const T* __restrict__ beta, T* __restrict__ y, int Hk, int Hv, int Dv,
     unsigned hk_mul, int Tn, int commit) {
-  constexpr int LPR = DK / 4;            // lanes per row
+  constexpr int ACT = DK / 4;            // float4 columns of a row
+  constexpr int LPR = row_lanes(ACT);    // lanes per row
   constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
   constexpr int ROWS = RPS * NV;         // rows per workgroup
 
@@ -77,10 +82,13 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
   const int c4 = tid % LPR;
   const int row0 = part * ROWS + tid / LPR;
   auto rowc = [&](int n) { return FULL ? row0 + n * RPS : min(row0 + n * RPS, Dv - 1); };
+  // idle lanes past the row's columns, as in the single-step kernel
+  const bool live = ACT == LPR || c4 < ACT;
+  const int cc = ACT == LPR ? c4 : min(c4, ACT - 1);
 
   const size_t slice_off = static_cast<size_t>(slice) * Dv * DK;
-  const float* sin = state_in + slice_off + c4 * 4;
-  float* sout = state_out + slice_off + c4 * 4;
+  const float* sin = state_in + slice_off + cc * 4;
+  float* sout = state_out + slice_off + cc * 4;
 
   // every token's activations first (token t of sequence b is row b*Tn + t)
   Raw4<T> kr[NT], qr[NT];
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
   for (int t = 0; t < NT; ++t) {
     if (t < Tn) {
       const size_t bt_ = static_cast<size_t>(b) * Tn + t;
-      const size_t qk_off = (bt_ * Hk + hk) * DK + c4 * 4;
+      const size_t qk_off = (bt_ * Hk + hk) * DK + cc * 4;
       kr[t].load(k + qk_off);
       qr[t].load(q + qk_off);
       graw[t] = g[bt_ * Hv + hv];
@@ -109,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (t < Tn) {
-      const f32x4 kk = kr[t].f(), qq = qr[t].f();
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 kk = live ? kr[t].f() : zero4, qq = live ? qr[t].f() : zero4;
       const float gate = expf(graw[t]);
       const float kq = group_sum<LPR>(dot4(kk, qq));
       const size_t yrow = ((static_cast<size_t>(b) * Tn + t) * Hv + hv) * Dv;
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void gdn_window_kernel(
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
       const int row = row0 + n * RPS;
-      if (FULL || row < Dv) store_stream(sout + static_cast<size_t>(row) * DK, kept[n]);
+      if ((FULL || row < Dv) && live) store_stream(sout + static_cast<size_t>(row) * DK, kept[n]);
     }
   }
 }
@@ -142,7 +151,7 @@ int launch_window_nt(const float* state_in, float* state_out, const void* q, con
                      const float* g, const void* beta, void* y, int B, int Hk, int Hv, int Dv, int Tn,
                      int commit, hipStream_t stream) {
   constexpr int NV = kRowsPerLane;
-  constexpr int ROWS = kThreads / (DK / 4) * NV;
+  constexpr int ROWS = kThreads / row_lanes(DK / 4) * NV;
   const int parts = (Dv + ROWS - 1) / ROWS;
   if (Hv > 65535) return GDN_ERR_SHAPE;  // grid y
   const unsigned hk_mul = hk_reciprocal(Hv / Hk);
@@ -191,6 +200,10 @@ int launch_window_dk(const float* state_in, float* state_out, const void* q, con
     case 64: return launch_window<64, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
     case 128: return launch_window<128, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
     case 256: return launch_window<256, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 96: return launch_window<96, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 160: return launch_window<160, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 192: return launch_window<192, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
+    case 224: return launch_window<224, T>(state_in, state_out, q, k, v, g, beta, y, B, Hk, Hv, Dv, Tn, commit, stream);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -207,7 +220,7 @@ extern "C" int gdn_decode_window(const float* state_in, float* state_out, const 
       commit > T)
     return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!pow2_head(Dk) || Dv % 32 != 0 || Dv > 256 || T > 8) return GDN_ERR_UNSUPPORTED;
+  if (!valid_head(Dk) || Dv % 32 != 0 || Dv > 256 || T > 8) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   if (!state_in || !q || !k || !v || !g || !beta || !y || (commit > 0 && !state_out)) return GDN_ERR_NULL;
   if (!aligned16(state_in) || (state_out && !aligned16(state_out)) || !aligned16(q) || !aligned16(k))
@@ -237,7 +250,7 @@ extern "C" int gdn_decode_step(const float* state_in, float* state_out, const vo
   using namespace gdn;
   if (B < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!pow2_head(Dk) || Dv % 32 != 0 || Dv > 256) return GDN_ERR_UNSUPPORTED;
+  if (!valid_head(Dk) || Dv % 32 != 0 || Dv > 256) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   if (!state_in || !state_out || !q || !k || !v || !g || !beta || !y) return GDN_ERR_NULL;
   if (!aligned16(state_in) || !aligned16(state_out) || !aligned16(q) || !aligned16(k))

@@ -23,7 +23,8 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const T* __restrict__ beta, TY* __restrict__ y, int Hk, int Hv, int Dv,
     unsigned hk_mul) {
-  constexpr int LPR = DK / 4;            // lanes per row
+  constexpr int ACT = DK / 4;            // float4 columns of a row
+  constexpr int LPR = row_lanes(ACT);    // lanes per row (ACT rounded up to a power of two)
   constexpr int RPS = kThreads / LPR;    // rows per register slot, whole workgroup
   constexpr int ROWS = RPS * NV;         // rows per workgroup
 
@@ -38,11 +39,15 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
   const int tid = threadIdx.x;
   const int c4 = tid % LPR;                        // float4 column within the row
   const int row0 = part * ROWS + tid / LPR;
+  // Lanes past the row's ACT columns (only when Dk is not a power of two)
+  // load the last column again, count as zero in the sums, store nothing.
+  const bool live = ACT == LPR || c4 < ACT;
+  const int cc = ACT == LPR ? c4 : min(c4, ACT - 1);
 
-  const size_t qk_off = (static_cast<size_t>(b) * Hk + hk) * DK + c4 * 4;
+  const size_t qk_off = (static_cast<size_t>(b) * Hk + hk) * DK + cc * 4;
   const size_t slice_off = static_cast<size_t>(slice) * Dv * DK;
-  const float* sin = state_in + slice_off + c4 * 4;
-  float* sout = state_out + slice_off + c4 * 4;
+  const float* sin = state_in + slice_off + cc * 4;
+  float* sout = state_out + slice_off + cc * 4;
   // FULL: every row this workgroup covers exists (Dv % ROWS == 0) and the
   // body is branch-free.  Otherwise rows past Dv load the last row again
   // (a branch around a load makes it wait for the previous one) and only
@@ -69,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
 #pragma unroll
   for (int n = 0; n < NV; ++n) s[n] = load_stream(sin + static_cast<size_t>(rowc(n)) * DK);
   __builtin_amdgcn_sched_barrier(0);
-  const f32x4 kk = kr.f(), qq = qr.f();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 kk = live ? kr.f() : zero4, qq = live ? qr.f() : zero4;
   const float bt = to_f32(btr);
   float vv[NV];
 #pragma unroll
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const float sq = group_sum<LPR>(dot4(s[n], qq));
     const float d = bt * (vv[n] - gate * sk);
     const f32x4 sn = gate * s[n] + d * kk;
-    if (FULL || row < Dv) {
+    if ((FULL || row < Dv) && live) {
       store_stream(sout + static_cast<size_t>(row) * DK, sn);
       if (c4 == 0) Act<TY>::store(y + static_cast<size_t>(slice) * Dv + row, gate * sq + d * kq);
     }
@@ -96,7 +102,7 @@ int launch_decode_dk(const float* state_in, float* state_out, const void* q, con
                      const void* v, const float* g, const void* beta, void* y, int B, int Hk,
                      int Hv, int Dv, hipStream_t stream) {
   constexpr int NV = kRowsPerLane;
-  constexpr int ROWS = kThreads / (DK / 4) * NV;
+  constexpr int ROWS = kThreads / row_lanes(DK / 4) * NV;
   const int parts = (Dv + ROWS - 1) / ROWS;
   if (Hv > 65535) return GDN_ERR_SHAPE;  // grid y
   const unsigned hk_mul = hk_reciprocal(Hv / Hk);

@@ -83,6 +83,11 @@ template <> struct Raw4<float> {
   __device__ __forceinline__ f32x4 f() const { return w; }
 };
 
+// Lanes given to one row of n float4 columns: n rounded up to a power of two
+// (a lane group of group_sum).  Head sizes that are multiples of 32 but not
+// powers of two (96, 160, 192, 224) leave the lanes past n idle.
+constexpr int row_lanes(int n) { return n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64; }
+
 // ------------------------------------------------------- streaming state I/O
 
 __device__ __forceinline__ f32x4 load_stream(const float* p) {

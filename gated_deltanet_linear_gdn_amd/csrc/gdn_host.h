@@ -46,6 +46,9 @@ inline unsigned hk_reciprocal(int G) {
 
 inline bool pow2_head(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
+// Head sizes of the streaming kernels: a multiple of 32 up to 256.
+inline bool valid_head(int d) { return d >= 32 && d <= 256 && d % 32 == 0; }
+
 // The gated RMS norm epilogue (gdn_layer.hip), also used by the prefill
 // when a value head spans several chunk-loop workgroups.
 int gated_rmsnorm_launch(const void* o, const void* z, const float* gamma, float eps, long rows,

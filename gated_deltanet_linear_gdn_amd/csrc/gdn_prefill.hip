@@ -1896,7 +1896,7 @@ int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, con
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
                 bool one_chunk) {
-  if constexpr (DK == 256) {  // 32-row tiles only (effective_chunk)
+  if constexpr (DK > 128) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
                                   chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
   } else {
@@ -1918,21 +1918,27 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
     case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
     case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
     case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-    case 256:  // bf16 activations only (the fp32 kernels would spill at this width)
-      if constexpr (std::is_same<T, bf16>::value)
-        return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-      else
-        return GDN_ERR_UNSUPPORTED;
+    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+  }
+  // wider heads: bf16 activations only (the fp32 kernels would spill at these widths)
+  if constexpr (std::is_same<T, bf16>::value) {
+    switch (Dk) {
+      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+    }
   }
   return GDN_ERR_UNSUPPORTED;
 }
 
 inline bool valid_chunk(int chunk) { return chunk == 8 || chunk == 16 || chunk == 32 || chunk == 64; }
 
-// Dk = 256 runs chunks of at most 32 tokens: two 64-row K and Q tiles of
-// that width (plus their double buffers) do not fit in a CU's LDS, 32-row
-// ones do.  The chunk size changes results only through rounding.
-inline int effective_chunk(int Dk, int chunk) { return Dk == 256 && chunk > 32 ? 32 : chunk; }
+// Key heads wider than 128 run chunks of at most 32 tokens: two 64-row K
+// and Q tiles of that width (plus their double buffers) do not fit in a
+// CU's LDS, 32-row ones do.  The chunk size changes results only through
+// rounding.
+inline int effective_chunk(int Dk, int chunk) { return Dk > 128 && chunk > 32 ? 32 : chunk; }
 
 // The Comba forward (bf16 activations): the WY pass on P K^T Gram blocks and
 // the chunk loop reading with p, over a [K, V] state pool; one key head per
@@ -1992,7 +1998,7 @@ int comba_dispatch_nw(const CombaArgs& a, char* ws, const Layout& L, hipStream_t
 
 template <int DK>
 int comba_dispatch_ct(int CT, const CombaArgs& a, char* ws, const Layout& L, hipStream_t stream) {
-  if constexpr (DK == 256)  // 32-row tiles only (effective_chunk)
+  if constexpr (DK > 128)  // 32-row tiles only (effective_chunk)
     return comba_dispatch_nw<DK, 32>(a, ws, L, stream);
   else
     return CT == 32 ? comba_dispatch_nw<DK, 32>(a, ws, L, stream) : comba_dispatch_nw<DK, 64>(a, ws, L, stream);
@@ -2026,7 +2032,7 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (!(Dk == 32 || Dk == 64 || Dk == 128 || (Dk == 256 && act == GDN_BF16)) || Dv % 32 != 0 ||
+  if (!(valid_head(Dk) && (Dk <= 128 || act == GDN_BF16)) || Dv % 32 != 0 ||
       Dv > 256 || !valid_chunk(chunk) || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
     return GDN_ERR_UNSUPPORTED;
   chunk = effective_chunk(Dk, chunk);
@@ -2155,7 +2161,7 @@ extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, 
   using namespace gdn;
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || H <= 0 || K <= 0 || V <= 0) return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
-  if (act != GDN_BF16 || !(K == 32 || K == 64 || K == 128 || K == 256) || V % 32 != 0 || V > 256 ||
+  if (act != GDN_BF16 || !valid_head(K) || V % 32 != 0 || V > 256 ||
       !valid_chunk(chunk))
     return GDN_ERR_UNSUPPORTED;
   chunk = effective_chunk(K, chunk);
@@ -2192,7 +2198,11 @@ extern "C" int comba_chunk_prefill(const void* q, const void* k, const void* v, 
   switch (K) {
     case 32: return comba_dispatch_ct<32>(CT, a, ws, L, stream);
     case 64: return comba_dispatch_ct<64>(CT, a, ws, L, stream);
+    case 96: return comba_dispatch_ct<96>(CT, a, ws, L, stream);
     case 128: return comba_dispatch_ct<128>(CT, a, ws, L, stream);
+    case 160: return comba_dispatch_ct<160>(CT, a, ws, L, stream);
+    case 192: return comba_dispatch_ct<192>(CT, a, ws, L, stream);
+    case 224: return comba_dispatch_ct<224>(CT, a, ws, L, stream);
     default: return comba_dispatch_ct<256>(CT, a, ws, L, stream);
   }
 }

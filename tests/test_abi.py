@@ -64,7 +64,8 @@ def test_decode_validation(lib):
     assert decode(lib, Hk=3, Hv=4) == SHAPE
     assert decode(lib, Hk=0) == SHAPE
     assert decode(lib, act=7) == DTYPE
-    assert decode(lib, Dk=96) == UNSUP
+    assert decode(lib, Dk=80) == UNSUP                  # head sizes: multiples of 32 up to 256
+    assert decode(lib, Dk=288) == UNSUP
     assert decode(lib, Dv=48) == UNSUP
     assert decode(lib, Dv=288) == UNSUP
     assert decode(lib, q=0) == NULL
@@ -92,8 +93,9 @@ def test_comba_validation(lib):
     assert comba(lib, B=-1) == SHAPE
     assert comba(lib, K=0) == SHAPE
     assert comba(lib, act=2) == DTYPE
-    assert comba(lib, K=96) == UNSUP
-    assert comba(lib, K=256, V=256) == UNSUP
+    assert comba(lib, K=80) == UNSUP
+    assert comba(lib, K=256, V=256) == UNSUP            # at most 32 rows of state per thread
+    assert comba(lib, K=160, V=160) == UNSUP
     assert comba(lib, p=0) == NULL
     assert comba(lib, o=A + 8 * BIG + 2) == ALIGN
     assert comba(lib, state_new=A + 16) == ALIAS
@@ -139,8 +141,10 @@ def test_prefill_workspace_size(lib):
     assert f(100, 2, 2, 4, 128, 128, 64, 7) == 0                 # unknown dtype
     # bf16 builds T and P on chip: no per-chunk matrices in the workspace
     assert f(1000, 2, 2, 4, 128, 128, 64, 1) < f(1000, 2, 2, 4, 128, 128, 64, 0)
-    # Dk = 256 runs 32-token chunks whatever chunk asks for
+    # Dk > 128 runs 32-token chunks whatever chunk asks for
     assert f(1000, 2, 2, 4, 256, 128, 64, 1) == f(1000, 2, 2, 4, 128, 128, 32, 1)
+    assert f(1000, 2, 2, 4, 160, 128, 64, 1) == f(1000, 2, 2, 4, 128, 128, 32, 1)
+    assert f(1000, 2, 2, 4, 96, 128, 64, 1) == f(1000, 2, 2, 4, 128, 128, 64, 1)
     assert f(1000, 2, 2, 4, 256, 128, 16, 1) == f(1000, 2, 2, 4, 128, 128, 16, 1)
 
 
@@ -149,7 +153,9 @@ def test_prefill_validation(lib):
     assert prefill(lib, Hk=3) == SHAPE
     assert prefill(lib, act=9) == DTYPE
     assert prefill(lib, Dk=512) == UNSUP
-    assert prefill(lib, Dk=256, act=0) == UNSUP            # Dk = 256 with bf16 activations only
+    assert prefill(lib, Dk=256, act=0) == UNSUP            # Dk > 128 with bf16 activations only
+    assert prefill(lib, Dk=160, act=0) == UNSUP
+    assert prefill(lib, Dk=80) == UNSUP                    # a multiple of 32 up to 256
     assert prefill(lib, Dv=40) == UNSUP
     assert prefill(lib, chunk=128) == UNSUP
     assert prefill(lib, flags=2) == UNSUP
@@ -363,7 +369,7 @@ def test_conv_decode_validation(lib):
     assert conv_decode(lib, B=-1) == SHAPE
     assert conv_decode(lib, Hk=3) == SHAPE
     assert conv_decode(lib, act=5) == DTYPE
-    assert conv_decode(lib, Dk=96) == UNSUP
+    assert conv_decode(lib, Dk=80) == UNSUP
     assert conv_decode(lib, Dv=48) == UNSUP
     assert conv_decode(lib, flags=4) == UNSUP
     assert conv_decode(lib, B=0, x=0) == OK               # nothing to do

@@ -39,7 +39,9 @@ def _warm(rng, B, H, K, V, steps=synth.WARMUP_STEPS):
 
 # the KBench spec's correctness shapes (B, H, K, V) plus the other supported sizes
 SHAPES = [(8, 4, 128, 128), (16, 2, 64, 128), (4, 8, 128, 64), (32, 4, 64, 64),
-          (3, 2, 32, 32), (2, 3, 256, 128), (2, 2, 32, 256), (2, 1, 256, 32)]
+          (3, 2, 32, 32), (2, 3, 256, 128), (2, 2, 32, 256), (2, 1, 256, 32),
+          # multiples of 32 that are not powers of two
+          (4, 2, 96, 128), (2, 2, 128, 96), (3, 2, 192, 64), (2, 2, 64, 224), (2, 1, 224, 128)]
 
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])

@@ -64,6 +64,8 @@ CASES = [
     ([300, 129, 64], 2, 128, 128, 8),
     ([65, 31], 2, 64, 128, 64),
     ([90, 40, 1], 2, 256, 128, 64),   # K = 256: runs 32-token chunks
+    ([100, 3], 2, 96, 128, 64),       # K = 96
+    ([70, 35], 1, 192, 64, 32),       # K = 192: 32-token chunks
 ]
 
 

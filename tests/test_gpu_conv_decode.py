@@ -72,6 +72,8 @@ SHAPES = [
     (2, 3, 3, 256, 64),    # two q and two k channels per thread
     (5, 4, 8, 128, 32),
     (2, 1, 48, 32, 32),    # 48 value heads read one key head
+    (2, 2, 4, 96, 64),     # head sizes that are not powers of two
+    (2, 1, 2, 192, 128),
 ]
 
 

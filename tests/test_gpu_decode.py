@@ -60,6 +60,12 @@ SHAPES = [
     (5, 4, 8, 128, 32),
     (2, 1, 48, 32, 32),    # 48 value heads read one key head
     (1, 6, 48, 64, 64),    # groups of 8
+    # head sizes that are multiples of 32 but not powers of two (lanes past
+    # the row's columns idle)
+    (2, 2, 4, 96, 64),
+    (2, 1, 2, 160, 96),
+    (1, 2, 4, 192, 128),
+    (2, 1, 3, 224, 160),
 ]
 
 
@@ -210,6 +216,8 @@ WINDOW_CASES = [
     (2, 4, 2, 4, 128, 128, 0, "bf16"),       # verify: no state write
     (1, 8, 1, 2, 128, 160, 5, "f32"),        # Dv not a multiple of a workgroup's rows
     (2, 8, 1, 1, 256, 64, 8, "bf16"),
+    (2, 3, 1, 2, 96, 64, 2, "bf16"),
+    (1, 4, 1, 2, 224, 96, 4, "f32"),
 ]
 
 

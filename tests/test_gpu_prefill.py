@@ -107,6 +107,12 @@ CASES = [
     ([100, 37, 1, 0], 1, 2, 256, 128, 64, "bf16"), # Dk = 256: runs 32-token chunks
     ([70, 5, 33], 2, 4, 256, 64, 16, "bf16"),      # Dk = 256, four waves, chunk 16
     ([65, 40], 1, 1, 256, 96, 32, "bf16"),         # Dk = 256, two waves
+    # key heads that are multiples of 32 but not powers of two
+    ([100, 37, 0, 5], 2, 4, 96, 128, 64, "bf16"),  # Dk = 96, 64-token chunks
+    ([70, 9], 1, 2, 96, 64, 16, "f32"),
+    ([90, 33, 1], 1, 2, 160, 128, 64, "bf16"),     # Dk = 160: runs 32-token chunks
+    ([64, 41], 2, 2, 192, 96, 32, "bf16"),
+    ([77, 12], 1, 3, 224, 128, 64, "bf16"),
 ]
 
 
