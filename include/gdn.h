@@ -67,7 +67,7 @@ enum gdn_status {
  *           (in-place update); any other overlap is GDN_ERR_ALIAS.
  * q, k      [B, Hk, Dk] act.     v, y [B, Hv, Dv] act.
  * g         [B, Hv] float32 (log-space gate).   beta [B, Hv] act.
- * Requirements: Hk >= 1, Hv % Hk == 0, Dk in {32, 64, 128, 256},
+ * Requirements: Hk >= 1, Hv % Hk == 0, Dk a multiple of 32 in [32, 256],
  * Dv a multiple of 32 in [32, 256], B >= 0 (B == 0 is a no-op);
  * state_in, state_out, q and k 16-byte aligned.  y overlaps neither state;
  * no input (q, k, v, g, beta) overlaps y or state_out (GDN_ERR_ALIAS).
@@ -117,7 +117,9 @@ int gdn_decode_window(const float* state_in, float* state_out, const void* q,
  * q, k, p   [B, H, K] act.   v, o [B, H, V] act.   beta [B, H] act.
  * g         [B, H] float32 (log-decay, <= 0 in practice).
  * scale     query scale; a value <= 0 selects K^-1/2.
- * Requirements: K and V in {32, 64, 128, 256}, not both 256; B, H >= 0;
+ * Requirements: K and V multiples of 32 in [32, 256] with at most 32 state
+ * rows per thread: K * L <= 8192, L = V/4 rounded up to a power of two
+ * (every K with V <= 128; K <= 128 with V > 128); B, H >= 0;
  * state, state_new, q, k, p, v and o 16-byte aligned.  o overlaps neither
  * state; no input (q, k, p, v, beta, g) overlaps o or state_new
  * (GDN_ERR_ALIAS).
@@ -152,7 +154,7 @@ int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
  * gdn_chunk_prefill_workspace - bytes of device workspace gdn_chunk_prefill
  * needs for these sizes and activation dtype (0 for invalid arguments).  It
  * depends only on T_tot, N_s, Hv, chunk, act and (through the chunk of at
- * most 32 tokens that Dk = 256 runs) Dk; the other sizes are accepted for a
+ * most 32 tokens that Dk > 128 runs) Dk; the other sizes are accepted for a
  * stable signature.
  */
 size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
@@ -192,9 +194,10 @@ size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
  * flags         0 or GDN_QK_L2NORM.
  * workspace     device memory of at least gdn_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
- * Requirements: Dk in {32, 64, 128, 256} (256 with bf16 activations only;
- * it runs chunks of at most 32 tokens whatever `chunk` asks for: two 64-row
- * operand tiles of that width do not fit in LDS); Dv a multiple of 32,
+ * Requirements: Dk a multiple of 32 up to 256 (above 128 with bf16
+ * activations only, and in chunks of at most 32 tokens whatever `chunk`
+ * asks for: two 64-row operand tiles of that width do not fit in LDS); Dv a
+ * multiple of 32,
  * <= 256; Hv % Hk == 0; q, k, v, state_pool 16-byte aligned; 64 tokens of q/k
  * (64 * Hk * Dk elements) and of v (64 * Hv * Dv) each under 1 GiB, else
  * GDN_ERR_UNSUPPORTED.  y, state_pool and the workspace overlap neither
@@ -316,7 +319,7 @@ size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv,
  *               bytes, 16-byte aligned; its contents are scratch (the call
  *               writes the index arrays into its end before the kernels run).
  * Requirements: those of gdn_chunk_prefill.  B == 0 or T == 0 is a no-op.
- * When T fits one chunk (after the Dk = 256 cap) the call knows every
+ * When T fits one chunk (after the Dk > 128 cap) the call knows every
  * sequence is a single chunk and runs a chunk loop without next-chunk
  * prefetch (same results, bit for bit; faster for decode windows).
  */
@@ -330,7 +333,7 @@ int gdn_chunk_prefill_fixed(const void* q, const void* k, const void* v,
 /*
  * comba_chunk_prefill_workspace - bytes of device workspace
  * comba_chunk_prefill needs (0 for invalid arguments or act != GDN_BF16).
- * Depends only on T_tot, N_s, H, chunk and (K = 256 runs chunks of at most
+ * Depends only on T_tot, N_s, H, chunk and (K > 128 runs chunks of at most
  * 32 tokens) K.
  */
 size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
@@ -361,8 +364,8 @@ size_t comba_chunk_prefill_workspace(int64_t T_tot, int N_s, int H, int K,
  * chunk         8, 16, 32 or 64 tokens.   scale: <= 0 selects K^-1/2.
  * workspace     device memory of at least comba_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
- * Requirements: act == GDN_BF16 (else GDN_ERR_UNSUPPORTED); K in {32, 64,
- * 128, 256} (256 runs chunks of at most 32 tokens); V a multiple of 32,
+ * Requirements: act == GDN_BF16 (else GDN_ERR_UNSUPPORTED); K a multiple of
+ * 32 up to 256 (above 128 in chunks of at most 32 tokens); V a multiple of 32,
  * <= 256; q, k, p, v, state_pool 16-byte aligned;
  * 64 tokens of q (64 * H * K elements) and of v each under 1 GiB.
  * o, state_pool and the workspace overlap neither each other nor any input
@@ -415,7 +418,7 @@ size_t gdn_conv_decode_workspace(int B, int Hk, int Hv, int Dk, int Dv);
  * scale        query scale; <= 0 selects Dk^-1/2.  flags: 0 or GDN_QK_L2NORM.
  * workspace    device memory of at least gdn_conv_decode_workspace() bytes,
  *              16-byte aligned; scratch.  Two kernels run on `stream`.
- * Requirements: those of gdn_decode_step (Dk in {32, 64, 128, 256}, Dv a
+ * Requirements: those of gdn_decode_step (Dk a multiple of 32 up to 256, Dv a
  * multiple of 32 up to 256, Hv % Hk == 0); state_in, state_out, conv_w and
  * the workspace 16-byte aligned, conv_state 4-byte aligned; y, state_out,
  * conv_state and the workspace overlap no input and each other
