@@ -221,7 +221,7 @@ def prefill_flops_per_token(Hv, Dk, Dv, C):
 def prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C):
     """FLOPs the bf16 prefill kernels actually issue as MFMAs, hi/lo extra
     products included.  Chunk loop, per (chunk, value head) and per wave of 16
-    value columns: X = K S (hi + lo) and Y = Q S (hi) take 3 (C/16)(Dk/32)
+    value columns: X = K S and Y = Q S (S as hi + lo) take 4 (C/16)(Dk/32)
     16x16x32 products; Delta = (T diag beta) R takes 3 per lower 32-row block
     pair; P Delta one per pair; the state update 2 (Dk/16)(C/32).  WY pass, per
     (chunk, key head): the Gram blocks K K^T and Q K^T (2 (Dk/32) per lower
@@ -230,7 +230,7 @@ def prefill_issued_flops(lengths, Hk, Hv, Dk, Dv, C):
     assert C == 64
     MT, KB, DT, CKB = C // 16, Dk // 32, Dk // 16, C // 32
     pairs = sum(mt // 2 + 1 for mt in range(MT))
-    per_wave = 3 * MT * KB + 3 * pairs + pairs + 2 * DT * CKB
+    per_wave = 4 * MT * KB + 3 * pairs + pairs + 2 * DT * CKB
     chunks = sum(-(-int(L) // C) for L in lengths)
     loop = chunks * Hv * (Dv // 16) * per_wave * 16 * 16 * 32 * 2
     npair = MT * (MT + 1) // 2

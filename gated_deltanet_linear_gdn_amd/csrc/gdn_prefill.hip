@@ -192,8 +192,9 @@ template <> struct Raw<float> {
 // after it (scs + N_s + 1) the order in which the chunk loop takes the
 // sequences: longest first, by the bit length of the chunk count (so a long
 // sequence never waits for a whole round of short ones to finish before its
-// chain starts; the order within a bit length is arbitrary, and no result
-// depends on it).
+// chain starts), with the longest sequence itself first (the split test
+// below compares against it); the order within a bit length is otherwise
+// arbitrary, and no result depends on it.
 
 __device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_tot, int64_t& b0,
                                            int64_t& len) {
@@ -239,7 +240,9 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   }
   int run = part[tid] - local;  // exclusive prefix of this thread's range
   __shared__ int bucket[33];       // sequences per bit length of the chunk count (0..32)
+  __shared__ unsigned long long top_key;  // the longest sequence (ties: the first)
   if (tid < 33) bucket[tid] = 0;
+  if (tid == 0) top_key = 0ull;
   __syncthreads();
   for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
     scs[s] = run;
@@ -248,9 +251,12 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
     const int n = static_cast<int>((len + C - 1) / C);
     run += n;
     atomicAdd(&bucket[32 - __clz(n)], 1);
+    atomicMax(&top_key, (static_cast<unsigned long long>(n) << 32) | (0xffffffffu - static_cast<unsigned>(s)));
   }
   if (tid == NT - 1) scs[N_s] = part[NT - 1];
   __syncthreads();
+  const int top_s = static_cast<int>(0xffffffffu - static_cast<unsigned>(top_key & 0xffffffffull));
+  const int top_n = static_cast<int>(top_key >> 32);
   if (tid == 0) {  // first rank of each bit length, longest first
     int r = 0;
     for (int b = 32; b >= 0; --b) {
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
       bucket[b] = r;
       r += cnt;
     }
+    bucket[32 - __clz(top_n)] = 1;  // its first rank (0) goes to the longest sequence itself
   }
   __syncthreads();
   int* ord = scs + N_s + 1;
@@ -265,16 +272,16 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
     int64_t b0, len;
     seq_bounds(cu, s, T_tot, b0, len);
     const int n = static_cast<int>((len + C - 1) / C);
-    ord[atomicAdd(&bucket[32 - __clz(n)], 1)] = s;
+    ord[s == top_s ? 0 : atomicAdd(&bucket[32 - __clz(n)], 1)] = s;
   }
   __syncthreads();
   // wgp[r]: chunk-loop workgroups before position r of that order.  The
   // first sequences of the order get two per (value head, column block) --
   // each computing half of the columns with half of its waves, a shorter
-  // step -- as far as CUs would otherwise sit idle (splitting on a full
-  // machine measured slower: the halves then compete with whole workgroups),
-  // and only if that shortens the batch: the longest sequence left whole
-  // must be clearly shorter than the longest split one.
+  // step -- as far as CUs would otherwise sit idle (on a full machine the
+  // half-capable kernel is not launched: its whole workgroups run a little
+  // slower), and only if that shortens the batch: the longest sequence left
+  // whole must be clearly shorter than the longest split one.
   int* wgp = ord + N_s;
   __shared__ int split_n;
   if (tid == 0) {
@@ -1188,7 +1195,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
 // ci+1 when step ci starts; V is copied right after the phase that reads it.
 // Per step (products that do not depend on each other share a phase, so
 // their MFMA chains interleave):
-//   A: X = K S (S as hi + lo), Y = Q S (hi);  R = V - (gamma/|k|) X
+//   A: X = K S and Y = Q S (S as hi + lo);  R = V - (gamma/|k|) X
 //      -- barrier, copy V (ci+1)
 //   B: Delta = (T diag(beta)) R                 (lower triangular)
 //   C: O = (gamma scale/|q|) Y + P Delta;  S <- gamma_C S + K^T diag(exp(G_C - G)/|k|) Delta
@@ -1538,7 +1545,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       if (ci > 0) z_load(ci - 1);
     }
 
-    // ---- A: X = K S (S as hi + lo), Y = Q S (hi), R, and O's first term
+    // ---- A: X = K S and Y = Q S (S as hi + lo: a row of y whose state-side
+    // term nearly cancels the in-chunk term would otherwise carry 2^-9 of
+    // that term as error), R, and O's first term
     f32x4 X[CW][MT], Y[CW][MT];
 #pragma unroll
     for (int t = 0; t < CW; ++t)
@@ -1562,6 +1571,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
           X[t][mt] = mma(a, Sh[t], X[t][mt]);
           Y[t][mt] = mma(aq, Sh[t], Y[t][mt]);
           X[t][mt] = mma(a, Sl[t], X[t][mt]);
+          Y[t][mt] = mma(aq, Sl[t], Y[t][mt]);
         }
         if constexpr (!SINGLE) copy_job(rn, nx, kb * MT + mt);  // chunk ci+1's set, one copy per product group
       }

@@ -29,8 +29,9 @@ def test_prefill_issued_flops_single_chunk():
     f = bench.prefill_issued_flops([64], 1, 1, 128, 128, 64)
     mfma32 = 16 * 16 * 32 * 2   # one 16x16x32 product
     mfma16 = 16 * 16 * 16 * 2   # one 16x16x16 product
-    # chunk loop: 8 waves x (48 phase A + 18 phase B + 6 P Delta + 32 update)
-    loop = 8 * 104 * mfma32
+    # chunk loop: 8 waves x (64 phase A: X and Y with S as hi + lo; 18 phase
+    # B + 6 P Delta + 32 update)
+    loop = 8 * 120 * mfma32
     # WY: 10 lower 16x16 blocks x 4 k-steps x (K K^T, Q K^T); 16 steps of the
     # blocked inverse x 3 hi/lo products
     wy = 10 * 4 * 2 * mfma32 + 16 * 3 * mfma16

@@ -426,6 +426,41 @@ def test_split_of_the_longest_sequence_only():
             check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
 
 
+@pytest.mark.parametrize("lengths", [
+    [1250, 130, 1980, 70],             # CUs to spare: the longest splits
+    [1100, 1200, 128, 1000, 100, 90],  # a full machine: none splits
+])
+def test_split_choice(lengths):
+    """At 48 value heads.  Four sequences (192 chunk-loop workgroups, room
+    for one split): the longest (31 chunks) is the third of the batch and
+    shares the bit length of its chunk count with the first (20 chunks); it
+    must be the one that runs as two half-width workgroups per head (the
+    first, split instead, would leave the longest whole and the split
+    refused).  Six sequences (288 workgroups, more than the CUs): all stay
+    whole; the 1000-token sequence has a row of y where the state-side and
+    in-chunk terms nearly cancel.  Checked on sampled heads of every
+    sequence."""
+    rng = np.random.default_rng(85)
+    Hk, Hv, Dk, Dv, P = 16, 48, 128, 128, 8
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    pool, y = _run_gpu(inp, pool0, 64, "bf16")
+    yv = to_np(y)
+    assert not np.isnan(yv).any()
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    cu = inp["cu_seqlens"]
+    for s in range(len(lengths)):
+        idx = np.arange(cu[s], cu[s + 1])
+        slot = int(inp["cache_indices"][s])
+        hk = (0, 15)[s % 2]
+        hs = np.arange(hk * 3, hk * 3 + 3)
+        P_ref, y_ref = oracle.gdn_prefill(
+            inp["q"][idx][:, [hk]], inp["k"][idx][:, [hk]], inp["v"][idx][:, hs],
+            g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0], [0, len(idx)])
+        assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, (s, hk)
+        check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
+
+
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_batch_of_empty_sequences_leaves_the_pool_untouched(act):
     """Three sequences of zero tokens (T_tot = 0): every launch runs and finds
