@@ -10,8 +10,8 @@
  *
  * Sources (the four pages this project is built from):
  *  - metaltile-std `gated_delta.rs` (docs.rs), module doc, "Recurrence per step"
- *    and "Layouts": decay, key read, delta, rank-1 write, readout; state
- *    [B,Hv,Dv,Dk] with Dk fastest; q,k [B,Hk,Dk]; head sharing hk = hv/(Hv/Hk).
+ *    and "Layouts": the gated delta rule for one token; state [B,Hv,Dv,Dk]
+ *    with Dk fastest; q,k [B,Hk,Dk]; head sharing hk = hv/(Hv/Hk).
  *  - KBench `comba_decode_step` spec, spec_md and contract_md: the Comba step
  *    with a separate read key p and a query scale; state [B,H,K,V], V fastest.
  *  - pymllm `gdn_chunkwise` docs, `gdn_extend_chunkwise` parameters: packed
@@ -32,35 +32,40 @@
 #include <string.h>
 
 /*
- * One gated delta-rule step on one value head, in the order the metaltile
- * page's "Recurrence per step" gives it.  S is that head's state, stored
- * value-major: S[j*Dk + i] with j the value index (Dv) and i the key index
- * (Dk).  `gate_log` is the log-space decay; the gate is exp(gate_log).
- *   1. decay:      S <- exp(g) S
- *   2. key read:   kv[j] = sum_i S[j,i] k[i]
- *   3. delta:      d[j]  = beta (v[j] - kv[j])
- *   4. write:      S[j,i] <- S[j,i] + d[j] k[i]
- *   5. readout:    y[j]  = sum_i S[j,i] q[i]   (updated state, no scale)
- * kv and d are scratch arrays of length Dv.
+ * One gated delta-rule step on one value head (metaltile-std `gated_delta.rs`,
+ * module documentation, "Recurrence per step").  S is the head's Dv x Dk
+ * state matrix, stored row by row (S[j*Dk + i]: value index j, key index i),
+ * so that the readout is y = S q.  With a = exp(g) (g the log-space gate) the
+ * step is the matrix update
+ *     S' = a S (I - beta k k^T) + beta v k^T,
+ * which multiplies out to a rank-one correction of the decayed state:
+ *     S' = a S + e k^T,   e = beta (v - a S k),
+ * and the output reads the new state:
+ *     y = S' q = a (S q) + (k . q) e.
+ * Both products with the old state (S k and S q) are formed first, then the
+ * state is overwritten.  Sk and Sq are scratch vectors of length Dv.
  */
 static void gdn_head_step(double* S, const double* q, const double* k,
-                          const double* v, double gate_log, double beta,
-                          double* y, int Dk, int Dv, double* kv, double* d) {
-  const double alpha = exp(gate_log);
-  for (int j = 0; j < Dv; ++j)
-    for (int i = 0; i < Dk; ++i) S[(size_t)j * Dk + i] *= alpha;
+                          const double* v, double g, double beta, double* y,
+                          int Dk, int Dv, double* Sk, double* Sq) {
+  const double a = exp(g);
+  double kq = 0.0;
+  for (int i = 0; i < Dk; ++i) kq += k[i] * q[i];
   for (int j = 0; j < Dv; ++j) {
-    double acc = 0.0;
-    for (int i = 0; i < Dk; ++i) acc += S[(size_t)j * Dk + i] * k[i];
-    kv[j] = acc;
+    const double* row = S + (size_t)j * Dk;
+    double rk = 0.0, rq = 0.0;
+    for (int i = 0; i < Dk; ++i) {
+      rk += row[i] * k[i];
+      rq += row[i] * q[i];
+    }
+    Sk[j] = rk;
+    Sq[j] = rq;
   }
-  for (int j = 0; j < Dv; ++j) d[j] = beta * (v[j] - kv[j]);
-  for (int j = 0; j < Dv; ++j)
-    for (int i = 0; i < Dk; ++i) S[(size_t)j * Dk + i] += d[j] * k[i];
   for (int j = 0; j < Dv; ++j) {
-    double acc = 0.0;
-    for (int i = 0; i < Dk; ++i) acc += S[(size_t)j * Dk + i] * q[i];
-    y[j] = acc;
+    double* row = S + (size_t)j * Dk;
+    const double e = beta * (v[j] - a * Sk[j]);
+    for (int i = 0; i < Dk; ++i) row[i] = a * row[i] + e * k[i];
+    y[j] = a * Sq[j] + kq * e;
   }
 }
 
@@ -75,9 +80,9 @@ int oracle_gdn_step(double* state, const double* q, const double* k,
                     const double* v, const double* g, const double* beta,
                     double* y, int B, int Hk, int Hv, int Dk, int Dv) {
   if (B < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0) return -1;
-  double* kv = (double*)malloc(sizeof(double) * (size_t)Dv * 2);
-  if (!kv) return -1;
-  double* d = kv + Dv;
+  double* Sk = (double*)malloc(sizeof(double) * (size_t)Dv * 2);
+  if (!Sk) return -1;
+  double* Sq = Sk + Dv;
   const int group = Hv / Hk;
   for (int b = 0; b < B; ++b) {
     for (int hv = 0; hv < Hv; ++hv) {
@@ -85,10 +90,10 @@ int oracle_gdn_step(double* state, const double* q, const double* k,
       const size_t n = (size_t)b * Hv + hv;
       const size_t qk = ((size_t)b * Hk + hk) * Dk;
       gdn_head_step(state + n * Dv * Dk, q + qk, k + qk, v + n * Dv, g[n],
-                    beta[n], y + n * Dv, Dk, Dv, kv, d);
+                    beta[n], y + n * Dv, Dk, Dv, Sk, Sq);
     }
   }
-  free(kv);
+  free(Sk);
   return 0;
 }
 
@@ -131,9 +136,9 @@ int oracle_gdn_prefill(const double* q, const double* k, const double* v,
   }
   double* work = (double*)malloc(sizeof(double) * ((size_t)Dv * 2 + (size_t)Dk * 2));
   if (!work) return -1;
-  double* kv = work;
-  double* d = kv + Dv;
-  double* kn = d + Dv;
+  double* Sk = work;
+  double* Sq = Sk + Dv;
+  double* kn = Sq + Dv;
   double* qn = kn + Dk;
   const int group = Hv / Hk;
   for (int s = 0; s < N_s; ++s) {
@@ -154,7 +159,7 @@ int oracle_gdn_prefill(const double* q, const double* k, const double* v,
         for (int i = 0; i < Dk; ++i) qn[i] *= scale;
         const size_t th = (size_t)t * Hv + hv;
         gdn_head_step(S, qn, kn, v + th * Dv, g[th], beta[th], y + th * Dv, Dk,
-                      Dv, kv, d);
+                      Dv, Sk, Sq);
       }
     }
   }
@@ -163,13 +168,15 @@ int oracle_gdn_prefill(const double* q, const double* k, const double* v,
 }
 
 /*
- * One Comba step for a dense batch (KBench `comba_decode_step` spec_md,
- * elementwise form), state [B,H,K,V] with V fastest, updated in place:
- *   S[i,j] <- exp(g) S[i,j]
- *   u[j]    = beta (v[j] - sum_i p[i] S[i,j])     (read with p)
- *   S[i,j] <- S[i,j] + k[i] u[j]                   (write with k)
- *   o[j]    = sum_i (scale q[i]) S[i,j]            (updated state)
- * q,k,p [B,H,K]; v,o [B,H,V]; beta, g [B,H].
+ * One Comba step for a dense batch (KBench `comba_decode_step` specification
+ * and contract).  Per (batch, head), S is the K x V state matrix stored row
+ * by row (S[i*V + j]: key index i, value index j), read through its own key
+ * p and written through k.  With a = exp(g) the matrix update is
+ *     S' = a (I - beta k p^T) S + beta k v^T  =  a S + k u^T,
+ *     u  = beta (v - a S^T p),
+ * and the output reads the new state with the scaled query qs = scale q:
+ *     o = S'^T qs = a (S^T qs) + (k . qs) u.
+ * q, k, p [B,H,K]; v, o [B,H,V]; beta, g [B,H]; state [B,H,K,V], in place.
  * Returns 0, or -1 on an invalid shape.
  */
 int oracle_comba_step(double* state, const double* q, const double* k,
@@ -177,34 +184,42 @@ int oracle_comba_step(double* state, const double* q, const double* k,
                       const double* g, double scale, double* o, int B, int H,
                       int K, int V) {
   if (B < 0 || H <= 0 || K <= 0 || V <= 0) return -1;
-  double* u = (double*)malloc(sizeof(double) * (size_t)V);
-  if (!u) return -1;
+  double* col = (double*)malloc(sizeof(double) * (size_t)V * 2);
+  if (!col) return -1;
+  double* Stp = col;      /* S^T p  */
+  double* Stq = col + V;  /* S^T qs */
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < H; ++h) {
       const size_t n = (size_t)b * H + h;
       double* S = state + n * (size_t)K * V;
-      const double* qn = q + n * K;
-      const double* kn = k + n * K;
-      const double* pn = p + n * K;
-      const double* vn = v + n * V;
-      const double alpha = exp(g[n]);
-      for (int i = 0; i < K; ++i)
-        for (int j = 0; j < V; ++j) S[(size_t)i * V + j] *= alpha;
-      for (int j = 0; j < V; ++j) {
-        double acc = 0.0;
-        for (int i = 0; i < K; ++i) acc += pn[i] * S[(size_t)i * V + j];
-        u[j] = beta[n] * (vn[j] - acc);
+      const double* qh = q + n * K;
+      const double* kh = k + n * K;
+      const double* ph = p + n * K;
+      const double* vh = v + n * V;
+      const double a = exp(g[n]);
+      double kq = 0.0;
+      for (int i = 0; i < K; ++i) kq += kh[i] * (scale * qh[i]);
+      for (int j = 0; j < V; ++j) Stp[j] = Stq[j] = 0.0;
+      for (int i = 0; i < K; ++i) {
+        const double* row = S + (size_t)i * V;
+        const double pi = ph[i], qi = scale * qh[i];
+        for (int j = 0; j < V; ++j) {
+          Stp[j] += pi * row[j];
+          Stq[j] += qi * row[j];
+        }
       }
-      for (int i = 0; i < K; ++i)
-        for (int j = 0; j < V; ++j) S[(size_t)i * V + j] += kn[i] * u[j];
       for (int j = 0; j < V; ++j) {
-        double acc = 0.0;
-        for (int i = 0; i < K; ++i) acc += (scale * qn[i]) * S[(size_t)i * V + j];
-        o[n * V + j] = acc;
+        const double u = beta[n] * (vh[j] - a * Stp[j]);
+        Stp[j] = u;  /* from here on: u */
+        o[n * V + j] = a * Stq[j] + kq * u;
+      }
+      for (int i = 0; i < K; ++i) {
+        double* row = S + (size_t)i * V;
+        for (int j = 0; j < V; ++j) row[j] = a * row[j] + kh[i] * Stp[j];
       }
     }
   }
-  free(u);
+  free(col);
   return 0;
 }
 
