@@ -286,6 +286,8 @@ GATED_CASES = [
     ([40, 9], 1, 2, 64, 64, 16, "bf16"),
     ([45, 16], 1, 1, 64, 32, 32, "f32"),
     ([60, 7], 1, 2, 256, 128, 64, "bf16"),     # Dk = 256, fused norm
+    # more chunk-loop workgroups than CUs (288), with the fused norm
+    ([150, 60, 40, 100, 30, 20], 16, 48, 128, 128, 64, "bf16"),
 ]
 
 
