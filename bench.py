@@ -451,8 +451,8 @@ def bench_conv_decode(steps, warmup, device):
 
 
 def bench_comba_hbm(steps, warmup, device, B=896, H=16, K=128, V=128):
-    """Comba at one of the KBench measure shapes (0.94 GB state per copy,
-    well beyond the 256 MB MALL)."""
+    """Comba at one of the KBench measure shapes (0.47-0.94 GB of state per
+    copy, beyond the 256 MB MALL)."""
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
@@ -645,7 +645,12 @@ def main():
         sys.exit(f"--only: unknown legs {sorted(only - set(LEGS))}; known: {', '.join(LEGS)}")
     dec_ip = bench_decode(max(10, args.steps // 2), args.warmup, device, inplace=True) if want("inplace") else None
     com = bench_comba(args.steps, args.warmup, device) if want("comba") else None
-    com_hbm, com_hbm_sec = bench_comba_hbm(max(10, args.steps // 5), 5, device) if want("comba") else (None, None)
+    com_shapes = {}
+    if want("comba"):
+        from gated_deltanet_linear_gdn_amd import synth as _synth
+        for (B_, H_, K_, V_) in _synth.COMBA_MEASURE_SHAPES:
+            com_shapes[f"B{B_}_H{H_}_K{K_}_V{V_}"] = bench_comba_hbm(max(10, args.steps // 5), 5, device,
+                                                                     B_, H_, K_, V_)
     pre = bench_prefill(max(5, args.steps // 20), 3, device) if want("prefill") else None
     cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device) if want("comba_prefill") else None
     pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256) if want("dk256") else None
@@ -712,9 +717,9 @@ def main():
                        "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),
                        "us_per_step": round(com["sec"] * 1e6, 2),
                        "frac_of_hbm_peak": round(com["bytes"] / com["sec"] / 1e9 / HBM_PEAK_GBPS, 4),
-                       "measure_shape_B896_H16": {"GBps": round(com_hbm, 2),
-                                                  "us_per_step": round(com_hbm_sec * 1e6, 2),
-                                                  "frac_of_hbm_peak": round(com_hbm / HBM_PEAK_GBPS, 4)}}
+                       "measure_shapes": {name: {"GBps": round(gbps, 2), "us_per_step": round(sec * 1e6, 2),
+                                                 "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+                                          for name, (gbps, sec) in com_shapes.items()}}
     if want("conv_decode"):
         out["conv_decode"] = {"workload": "gdn_conv_decode_step at B=256 Hk=16 Hv=48 Dk=Dv=128 bf16: conv + SiLU of "
                                          "10,240 raw channels (history in place), q/k norm and gates in a prologue "

@@ -159,6 +159,9 @@ DECODE_B256 = dict(B=256, Hk=16, Hv=48, Dk=128, Dv=128, act="bf16")
 PREFILL_VARLEN = dict(n_seq=8, len_lo=512, len_hi=4096, Hk=16, Hv=48, Dk=128, Dv=128,
                       pool=16, chunk=64, act="bf16")
 COMBA_B128 = dict(B=128, H=32, K=128, V=128, act="bf16")
+# The Comba decode measure shapes (B, H, K, V) the KBench comba_decode_step
+# page lists for its throughput figures (states of 0.47-0.94 GB per copy).
+COMBA_MEASURE_SHAPES = ((896, 16, 128, 128), (448, 32, 128, 128), (1792, 8, 128, 128), (1280, 16, 64, 128))
 COMBA_PREFILL_VARLEN = dict(n_seq=8, len_lo=512, len_hi=4096, H=32, K=128, V=128, pool=16,
                             chunk=64, act="bf16")
 WARMUP_STEPS = 16

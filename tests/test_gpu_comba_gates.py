@@ -102,6 +102,27 @@ def test_comba_batch_b128():
         check_bf16_out(to_np(o)[sample], o_ref, f"o at step {step}")
 
 
+@pytest.mark.parametrize("shape", synth.COMBA_MEASURE_SHAPES)
+def test_comba_measure_shapes_sampled(shape):
+    """The KBench measure shapes the bench times (K = 64 among them), from
+    warmed states: two steps on the whole batch, the oracle following 4
+    sampled sequences."""
+    B, H, K, V = shape
+    rng = np.random.default_rng(B + K)
+    W = _warm(rng, 16, H, K, V, steps=4)
+    S = np.tile(W, (B // 16, 1, 1, 1))
+    sample = np.array([0, 7, B // 2 + 3, B - 1])
+    idx = torch.from_numpy(sample).to(DEV)
+    S_dev = to_dev(S, torch.float32, DEV)
+    S_ref = S[sample].astype(np.float64)
+    for step in range(2):
+        tok = synth.comba_token(rng, B, H, K, V)
+        S_dev, o = _comba(S_dev, _dev_tok(tok, "bf16"))
+        S_ref, o_ref = oracle_comba_batched(S_ref, {n: a[sample] for n, a in tok.items()})
+        assert maxrel(to_np(S_dev[idx]), S_ref) <= 1e-5, step
+        check_bf16_out(to_np(o)[sample], o_ref, f"o at step {step}")
+
+
 def test_comba_reads_with_p_not_k():
     """Negative control: the GPU result is far from an oracle that reads with k."""
     rng = np.random.default_rng(6)
