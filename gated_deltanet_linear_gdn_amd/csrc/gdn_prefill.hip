@@ -897,8 +897,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(short x) {
   return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16);
 }
 
-// Two 16x16x16 products accumulate as C += A B with A, B fp32 fragments
-// split into bf16 hi + lo (the lo x lo term is below fp32 rounding).
+// 16x16x16 products of fp32 fragments split into bf16 hi + lo, three per
+// product (the lo x lo term is below fp32 rounding).
 // A: row l16, k = kg*4 + e;  B and C: column l16, k/row = kg*4 + e.
 __device__ __forceinline__ void split4(f32x4 x, s16x4& h, s16x4& l) {
   uint32_t h0, l0, h1, l1;
@@ -907,10 +907,20 @@ __device__ __forceinline__ void split4(f32x4 x, s16x4& h, s16x4& l) {
   h = __builtin_bit_cast(s16x4, u32x2{h0, h1});
   l = __builtin_bit_cast(s16x4, u32x2{l0, l1});
 }
-__device__ __forceinline__ f32x4 mm3(f32x4 a, f32x4 b, f32x4 c) {
-  s16x4 ah, al, bh, bl;
+// C += A B with the right operand already split (bh, bl).
+__device__ __forceinline__ f32x4 mm3_rb(f32x4 a, s16x4 bh, s16x4 bl, f32x4 c) {
+  s16x4 ah, al;
   split4(a, ah, al);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+  return c;
+}
+// A B with the left operand already split (ah, al), from a zero accumulator.
+__device__ __forceinline__ f32x4 mm3_la(s16x4 ah, s16x4 al, f32x4 b) {
+  s16x4 bh, bl;
   split4(b, bh, bl);
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
   c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
@@ -1079,15 +1089,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
       const float up = __shfl_up(G, off);
       if (lane >= off) G += up;
     }
-    const float GC = __shfl(G, CT - 1);
+    // the prefix in base 2 (G log2 e), so that each decay below is one exp2
+    const float G2 = G * 1.44269504088896341f;
+    const float GC2 = __shfl(G2, CT - 1);
     if (lane < CT) {
-      const float gam = __expf(G);
+      const float gam = __builtin_amdgcn_exp2f(G2);
       float* r = fac + mat * FSTR;
       r[lane] = gam * rk;
       r[CT + lane] = gam * rq;
-      r[2 * CT + lane] = __expf(GC - G) * rk;
-      if (lane < 4) r[3 * CT + lane] = lane == 0 ? __expf(GC) : 0.f;
-      sG[lane] = G;
+      r[2 * CT + lane] = __builtin_amdgcn_exp2f(GC2 - G2) * rk;
+      if (lane < 4) r[3 * CT + lane] = lane == 0 ? __builtin_amdgcn_exp2f(GC2) : 0.f;
+      sG[lane] = G2;
       sB[lane] = bt;
     }
     __syncthreads();  // norms and gates -> every lane
@@ -1096,28 +1108,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     bf16* th = Th + mat * NPAIR * 256;
     bf16* tl = Tl + mat * NPAIR * 256;
     bf16* ph = Ph + mat * NPAIR * 256;
+    // A_ij = beta_i/|k_i| (k_i . k_j)/|k_j| e^(G_i - G_j) below the diagonal;
+    // P_ij = scale/|q_i| (q_i . k_j)/|k_j| e^(G_i - G_j) on and below it
 #pragma unroll
-    for (int I = 0; I < MT; ++I)
+    for (int I = 0; I < MT; ++I) {
+      const f32x4 Gi = *reinterpret_cast<const f32x4*>(sG + I * 16 + kg * 4);
+      const f32x4 rki = *reinterpret_cast<const f32x4*>(sRK + I * 16 + kg * 4);
+      const f32x4 rqi = *reinterpret_cast<const f32x4*>(sRQ + I * 16 + kg * 4);
+      const f32x4 bki = *reinterpret_cast<const f32x4*>(sB + I * 16 + kg * 4) * rki;
 #pragma unroll
       for (int J = 0; J <= I; ++J) {
         const int pidx = I * (I + 1) / 2 + J;
         const int jj = J * 16 + l16;
         const float Gj = sG[jj], rkj = sRK[jj];
-        const f32x4 Gi = *reinterpret_cast<const f32x4*>(sG + I * 16 + kg * 4);
-        const f32x4 rki = *reinterpret_cast<const f32x4*>(sRK + I * 16 + kg * 4);
-        const f32x4 rqi = *reinterpret_cast<const f32x4*>(sRQ + I * 16 + kg * 4);
-        const f32x4 bi = *reinterpret_cast<const f32x4*>(sB + I * 16 + kg * 4);
         s16x4 pv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ii = I * 16 + kg * 4 + r;
-          const float dec = jj <= ii ? __expf(Gi[r] - Gj) : 0.f;
-          sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bi[r] * dec * rki[r] * rkj * gk[pidx][r] : 0.f;
-          pv[r] = __builtin_bit_cast(short, (__bf16)(dec * rqi[r] * rkj * gq[pidx][r]));
+          const float t = jj <= ii ? __builtin_amdgcn_exp2f(Gi[r] - Gj) * rkj : 0.f;  // decay / |k_j|
+          sA[pidx][(kg * 4 + r) * 20 + l16] = jj < ii ? bki[r] * t * gk[pidx][r] : 0.f;
+          pv[r] = __builtin_bit_cast(short, (__bf16)(rqi[r] * t * gq[pidx][r]));
         }
         // P^T row jj, columns I*16 + kg*4 .. +3: block (J, I), row l16
         *reinterpret_cast<s16x4*>(ph + tri_block<CT>(J, I) * 256 + l16 * 16 + kg * 4) = pv;
       }
+    }
 
     __syncthreads();  // A -> the solving lanes
 
@@ -1149,26 +1164,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
 
     __syncthreads();  // D -> every lane
 
-    // ---- block columns of T; stored as T diag(beta) (column jb*16 + l16 of
-    // this lane scaled by its beta)
-    float bcol[MT];
-#pragma unroll
-    for (int jb = 0; jb < MT; ++jb) bcol[jb] = sB[jb * 16 + l16];
+    // ---- block columns of T diag(beta), the form the chunk loop reads.  The
+    // block recurrence T_i,jb = -D_i sum_kk A_i,kk T_kk,jb is linear in each
+    // block column, so scaling the diagonal blocks D_jb by the column's beta
+    // scales the whole column; each block's hi/lo split, made once for its
+    // store, is then also its operand in the later products of the column.
+    s16x4 Th_[MT][MT], Tl_[MT][MT];  // accumulator layout: column l16, rows kg*4 .. +3
     auto put_T = [&](int i, int jb, f32x4 t) __attribute__((always_inline)) {
-      s16x4 h, l;
-      split4(t * bcol[jb], h, l);
+      split4(t, Th_[i][jb], Tl_[i][jb]);
       const int off = tri_block<CT>(jb, i) * 256 + l16 * 16 + kg * 4;  // T^T row jb*16 + l16
-      *reinterpret_cast<s16x4*>(th + off) = h;
-      *reinterpret_cast<s16x4*>(tl + off) = l;
+      *reinterpret_cast<s16x4*>(th + off) = Th_[i][jb];
+      *reinterpret_cast<s16x4*>(tl + off) = Tl_[i][jb];
     };
-    f32x4 Tc[MT][MT];
 #pragma unroll
     for (int jb = 0; jb < MT; ++jb) {
-      // D_jb in accumulator layout: column l16, rows kg*4 .. +3
+      // D_jb diag(beta) in accumulator layout
+      const float bc = sB[jb * 16 + l16];
+      f32x4 t;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Tc[jb][jb][r] = sD[jb][(kg * 4 + r) * 20 + l16];
-      put_T(jb, jb, Tc[jb][jb]);
+      for (int r = 0; r < 4; ++r) t[r] = sD[jb][(kg * 4 + r) * 20 + l16] * bc;
+      put_T(jb, jb, t);
     }
+    // D_i as the left operand (row l16, k = kg*4 + e), split once per block
+    s16x4 Dh_[MT], Dl_[MT];
+#pragma unroll
+    for (int i = 1; i < MT; ++i) split4(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), Dh_[i], Dl_[i]);
     // level by level (i - jb = 1, 2, ...) so the columns' chains interleave
 #pragma unroll
     for (int d = 1; d < MT; ++d)
@@ -1178,9 +1198,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
         f32x4 M = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = jb; kk < i; ++kk)
-          M = mm3(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16 * 20 + kg * 4]), Tc[kk][jb], M);
-        Tc[i][jb] = -mm3(*reinterpret_cast<const f32x4*>(&sD[i][l16 * 20 + kg * 4]), M, f32x4{0.f, 0.f, 0.f, 0.f});
-        put_T(i, jb, Tc[i][jb]);
+          M = mm3_rb(*reinterpret_cast<const f32x4*>(&sA[i * (i + 1) / 2 + kk][l16 * 20 + kg * 4]), Th_[kk][jb],
+                     Tl_[kk][jb], M);
+        put_T(i, jb, -mm3_la(Dh_[i], Dl_[i], M));
       }
     __syncthreads();  // this head's reads of A, D and the gates before the next head's writes
   }
