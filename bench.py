@@ -142,11 +142,12 @@ def bench_decode(steps, warmup, device, B=None, Dk=None, inplace=False):
                 shape=dict(B=B, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv))
 
 
-def bench_window(steps, warmup, device, T, chunked=False):
+def bench_window(steps, warmup, device, T, chunked=False, verify=False):
     """Decode windows of T tokens per sequence at the B=256 decode batch,
-    committing all T: gdn_decode_window (functional ping-pong, like the
-    decode step) or, chunked, the same recurrence as gdn_chunk_prefill_fixed
-    with no norm and scale 1 (in place, chunk = min(T, 64))."""
+    committing all T (or, verify, none: every y, the state only read):
+    gdn_decode_window (functional ping-pong, like the decode step) or,
+    chunked, the same recurrence as gdn_chunk_prefill_fixed with no norm and
+    scale 1 (in place, chunk = min(T, 64); GDN_KEEP_STATE to verify)."""
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
@@ -171,15 +172,15 @@ def bench_window(steps, warmup, device, T, chunked=False):
         w = wins[i % 4]
         if chunked:
             gdn.gdn_chunk_prefill_fixed(w["q"], w["k"], w["v"], w["g"], w["beta32"], bufs[0], chunk=chunk,
-                                        scale=1.0, l2norm=False, y=y, workspace=ws)
+                                        scale=1.0, l2norm=False, y=y, workspace=ws, keep_state=verify)
         else:
             gdn.gdn_decode_window(bufs[i % 2], bufs[(i + 1) % 2], w["q"], w["k"], w["v"], w["g"], w["beta"],
-                                  y=y)
+                                  y=y, commit=0 if verify else T)
 
     for i in range(4):
         step(i)
     sec = _timed(step, steps, warmup)
-    return dict(sec=sec, tokens=B * T, state_bytes=2 * B * Hv * Dv * Dk * 4)
+    return dict(sec=sec, tokens=B * T, state_bytes=(1 if verify else 2) * B * Hv * Dv * Dk * 4)
 
 
 def bench_comba(steps, warmup, device):
@@ -662,6 +663,9 @@ def main():
             if want("windows") else None)
     cwins = ({T: bench_window(max(10, args.steps // 5), 5, device, T, chunked=True) for T in (4, 8, 16, 64)}
              if want("windows") else None)
+    vwins = ({(T, ch): bench_window(max(10, args.steps // 5), 5, device, T, chunked=ch, verify=True)
+              for T in (4, 8, 16) for ch in (False, True) if ch or T <= 8}
+             if want("windows") else None)
     copy_gbps, own_copy_gbps = bench_copy(device) if want("copy") else (None, None)
 
     gbps = dec["state_bytes"] / dec["sec"] / 1e9
@@ -711,7 +715,15 @@ def main():
                                            **{f"T{T}": {"us_per_window": round(w["sec"] * 1e6, 2),
                                                         "tokens_per_s": round(w["tokens"] / w["sec"], 1),
                                                         "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
-                                              for T, w in cwins.items()}}}
+                                              for T, w in cwins.items()}},
+                               "verify": {"workload": "verify windows (every y, nothing committed, the state only "
+                                                      "read): gdn_decode_window with commit 0, and chunked as "
+                                                      "gdn_chunk_prefill_fixed with GDN_KEEP_STATE",
+                                          **{f"{'chunked_' if ch else ''}T{T}": {
+                                              "us_per_window": round(w["sec"] * 1e6, 2),
+                                              "tokens_per_s": round(w["tokens"] / w["sec"], 1),
+                                              "state_GBps": round(w["state_bytes"] / w["sec"] / 1e9, 1)}
+                                             for (T, ch), w in vwins.items()}}}
     if want("comba"):
         out["comba"] = {"workload": "comba_decode_step B=128 H=32 K=V=128 bf16, fp32 state",
                        "GBps": round(com["bytes"] / com["sec"] / 1e9, 2),

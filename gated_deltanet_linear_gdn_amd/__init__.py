@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "GdnError", "library_path", "load_library",
     "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
-    "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM",
+    "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM", "GDN_KEEP_STATE",
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
     "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
     "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy", "gdn_chunk_prefill_noalloc",
@@ -267,6 +267,7 @@ def gdn_prefill_gates(a, b, A_log, dt_bias, g=None, beta=None):
 
 
 GDN_QK_L2NORM = 1
+GDN_KEEP_STATE = 2
 
 
 def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64, dtype=None) -> int:
@@ -277,7 +278,8 @@ def gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64, dtype=None
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, chunk=64,
-                      scale=None, l2norm=True, y=None, workspace=None, z=None, gamma=None, eps=1e-6):
+                      scale=None, l2norm=True, y=None, workspace=None, z=None, gamma=None, eps=1e-6,
+                      keep_state=False):
     """Varlen chunkwise prefill, ``state_pool`` updated in place (see
     ``gdn_chunk_prefill`` in include/gdn.h).
 
@@ -287,7 +289,8 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     ``gdn_validate_varlen``); y [T,Hv,Dv] or None; workspace: a uint8 device
     tensor of at least ``gdn_chunk_prefill_workspace`` bytes, or None.
     With z [T,Hv,Dv] and gamma [Dv] f32 given, y is the gated RMS norm of the
-    output (``gdn_chunk_prefill_gated``).  Returns y."""
+    output (``gdn_chunk_prefill_gated``).  keep_state: the pool is only read
+    (GDN_KEEP_STATE, a verify window).  Returns y."""
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     P = state_pool.shape[0]
@@ -311,7 +314,7 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
     if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
     sc = 0.0 if scale is None else float(scale)
-    flags = GDN_QK_L2NORM if l2norm else 0
+    flags = (GDN_QK_L2NORM if l2norm else 0) | (GDN_KEEP_STATE if keep_state else 0)
     if z is None and gamma is None:
         _call("gdn_chunk_prefill", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
               _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
@@ -376,7 +379,7 @@ def gdn_conv_decode_step(state_in, state_out, qkv, conv_w, conv_state, a, b, A_l
 
 
 def gdn_chunk_prefill_noalloc(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, y, chunk=64,
-                              scale=None, l2norm=True):
+                              scale=None, l2norm=True, keep_state=False):
     """``gdn_chunk_prefill`` with the library's static device workspace
     instead of a caller one (see ``gdn_chunk_prefill_noalloc`` in
     include/gdn.h): nothing is allocated, so y must be given.  Same
@@ -398,7 +401,7 @@ def gdn_chunk_prefill_noalloc(q, k, v, g, beta, state_pool, cache_indices, cu_se
     _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
     _check("y", y, (T, Hv, Dv), act, dev)
     sc = 0.0 if scale is None else float(scale)
-    flags = GDN_QK_L2NORM if l2norm else 0
+    flags = (GDN_QK_L2NORM if l2norm else 0) | (GDN_KEEP_STATE if keep_state else 0)
     _call("gdn_chunk_prefill_noalloc", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags, _ptr(y),
           _act_of(q), _stream(dev))
@@ -413,11 +416,12 @@ def gdn_chunk_prefill_fixed_workspace(B, T, Hk, Hv, Dk, Dv, chunk=64, dtype=None
 
 
 def gdn_chunk_prefill_fixed(q, k, v, g, beta, state, chunk=64, scale=None, l2norm=True, y=None,
-                            workspace=None):
+                            workspace=None, keep_state=False):
     """Chunkwise prefill of a fixed-length batch, ``state`` updated in place
     (see ``gdn_chunk_prefill_fixed`` in include/gdn.h).  q, k [B,T,Hk,Dk];
     v [B,T,Hv,Dv]; g, beta [B,T,Hv] f32; state [B,Hv,Dv,Dk] f32; y [B,T,Hv,Dv]
-    or None.  Returns y."""
+    or None.  keep_state: ``state`` is only read (GDN_KEEP_STATE; with no
+    norm and scale 1 this is a verify window of T tokens).  Returns y."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dev, act = q.device, q.dtype
@@ -437,7 +441,8 @@ def gdn_chunk_prefill_fixed(q, k, v, g, beta, state, chunk=64, scale=None, l2nor
         raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
     sc = 0.0 if scale is None else float(scale)
     _call("gdn_chunk_prefill_fixed", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), B, T,
-          Hk, Hv, Dk, Dv, int(chunk), sc, GDN_QK_L2NORM if l2norm else 0, _ptr(y), _act_of(q),
+          Hk, Hv, Dk, Dv, int(chunk), sc, (GDN_QK_L2NORM if l2norm else 0) | (GDN_KEEP_STATE if keep_state else 0),
+          _ptr(y), _act_of(q),
           _ptr(workspace), workspace.numel(), _stream(dev))
     return y
 

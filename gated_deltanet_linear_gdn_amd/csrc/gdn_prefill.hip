@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
     const int64_t* __restrict__ cache_indices, const int64_t* __restrict__ cu,
     const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk, int Hv, int Dv, int C, int maxc,
     const bf16* __restrict__ Th, const bf16* __restrict__ Tl, const bf16* __restrict__ Ph,
-    const bf16* __restrict__ Pl, const float* __restrict__ fac, T* __restrict__ y) {
+    const bf16* __restrict__ Pl, const float* __restrict__ fac, T* __restrict__ y, int keep) {
   constexpr bool PRECISE = std::is_same<T, float>::value;
   constexpr int BV = 16 * NW, NT = 64 * NW;
   constexpr int MT = CT / 16, CKB = CT / 32, DT = DK / 16, KB = DK / 32;
@@ -745,7 +745,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_kernel(
   }
 
 #pragma unroll
-  for (int m = 0; m < DT; ++m) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];
+  for (int m = 0; m < DT; ++m)
+    if (!keep) *reinterpret_cast<f32x4*>(Sp + m * 16 + kg * 4) = S[m];  // keep: the slot is read only
 }
 
 // ----------------------------------------------------------------------------
@@ -1278,7 +1279,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const int64_t* __restrict__ cu, const int* __restrict__ scs, int N_s, int64_t T_tot, int Hk,
     int Hv, int Dv, int C, int maxc, const bf16* __restrict__ Th, const bf16* __restrict__ Tl,
     const bf16* __restrict__ Ph, const float* __restrict__ fac, bf16* __restrict__ y,
-    const bf16* __restrict__ z, const float* __restrict__ gamma, float eps) {
+    const bf16* __restrict__ z, const float* __restrict__ gamma, float eps, int keep) {
   using Tiles = StreamTiles<DK, CT, NW, CW>;
   using Set = typename Tiles::Set;
   constexpr int BV = Tiles::BV, KP = Tiles::KP, QP = Tiles::QP, VP = Tiles::VP, YP = Tiles::YP,
@@ -1735,7 +1736,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
   }
 
-  if (!act) return;
+  if (!act || keep) return;  // keep: the slot is read only
 #pragma unroll
   for (int t = 0; t < CW; ++t)
 #pragma unroll
@@ -1777,6 +1778,10 @@ inline int cu_count() {
   if (dev >= 0 && dev < 64) cache[dev] = n;
   return n;
 }
+
+// Options of one prefill call, passed down to the launches.
+constexpr unsigned kOneChunk = 1u;   // every sequence is one chunk long (the host knows it)
+constexpr unsigned kKeepState = 2u;  // the state slots are read, never written
 
 // The chunk map on one workgroup: a single wave for up to 64 sequences (one
 // per lane; its barriers are then nearly free), else 1,024 threads (a wave
@@ -1820,7 +1825,9 @@ template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
-               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream, bool one_chunk) {
+               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream, unsigned opts) {
+  const bool one_chunk = (opts & kOneChunk) != 0;
+  const int keep = (opts & kKeepState) ? 1 : 0;
   int* scs = reinterpret_cast<int*>(ws + L.scs);
   bf16* Th = reinterpret_cast<bf16*>(ws + L.th);
   bf16* Tl = reinterpret_cast<bf16*>(ws + L.tl);
@@ -1850,7 +1857,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                            dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                            static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv,
                            chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
-                           static_cast<const bf16*>(epi->z), epi->gamma, epi->eps);
+                           static_cast<const bf16*>(epi->z), epi->gamma, epi->eps, keep);
         return launch_status();
       }
     }
@@ -1863,7 +1870,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                            static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
                            static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv, chunk,
                            static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
-                           static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+                           static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f, keep);
         return launch_status();
       }
     }
@@ -1873,14 +1880,14 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
                          static_cast<const bf16*>(v), pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv, Dv, chunk,
                          static_cast<int>(maxc), Th, Tl, Ph, fac, static_cast<bf16*>(y),
-                         static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+                         static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f, keep);
     else
       hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, CW>), dim3(static_cast<unsigned>(main_blocks)),
                          dim3(64 * NW), 0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                          static_cast<const bf16*>(nullptr), static_cast<const bf16*>(v), pool, pool_size, ci, cu,
                          scs, N_s, T_tot, Hk, Hv, Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, fac,
                          static_cast<bf16*>(y), static_cast<const bf16*>(nullptr),
-                         static_cast<const float*>(nullptr), 0.0f);
+                         static_cast<const float*>(nullptr), 0.0f, keep);
   } else {
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
@@ -1888,7 +1895,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
     hipLaunchKernelGGL((gdn_prefill_kernel<T, DK, CT, NW>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), beta, pool, pool_size, ci, cu, scs, N_s, T_tot, Hk, Hv,
-                       Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, fac, static_cast<T*>(y));
+                       Dv, chunk, static_cast<int>(maxc), Th, Tl, Ph, Pl, fac, static_cast<T*>(y), keep ? 1 : 0);
   }
   if (launch_status() != GDN_OK) return GDN_ERR_LAUNCH;
   // otherwise the separate norm kernel, in place on y
@@ -1903,7 +1910,7 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
-                bool one_chunk) {
+                unsigned opts) {
   // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
   // workgroup so each chunk operand is fetched once per 128 columns.  fp32
   // activations: the register-fragment kernel, 64 (four waves, up to 512
@@ -1911,13 +1918,13 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
       return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                         chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                         chunk, scale, l2norm, y, ws, L, epi, stream, opts);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                    chunk, scale, l2norm, y, ws, L, epi, stream, opts);
   return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
 }
 
 template <typename T, int DK>
@@ -1925,16 +1932,16 @@ int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, con
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
-                bool one_chunk) {
+                unsigned opts) {
   if constexpr (DK > 128) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
   } else {
     if (CT == 32)
       return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                    chunk, scale, l2norm, y, ws, L, epi, stream, opts);
     return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
   }
 }
 
@@ -1943,20 +1950,20 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
                 const float* g, const float* beta, float* pool, int64_t pool_size,
                 const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
                 int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
-                const Epilogue* epi, hipStream_t stream, bool one_chunk) {
+                const Epilogue* epi, hipStream_t stream, unsigned opts) {
   switch (Dk) {
-    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
   }
   // wider heads: bf16 activations only (the fp32 kernels would spill at these widths)
   if constexpr (std::is_same<T, bf16>::value) {
     switch (Dk) {
-      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
-      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, one_chunk);
+      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
     }
   }
   return GDN_ERR_UNSUPPORTED;
@@ -2010,12 +2017,12 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
                        dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,
                        a.pool_size, a.ci, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc),
                        Th, Tl, Ph, fac, a.o, static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr),
-                       0.0f);
+                       0.0f, 0);
   else
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true>), dim3(static_cast<unsigned>(main_blocks)),
                        dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool, a.pool_size, a.ci, a.cu, scs, a.N_s,
                        a.T_tot, a.H, a.H, a.V, a.chunk, static_cast<int>(maxc), Th, Tl, Ph, fac, a.o,
-                       static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f);
+                       static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr), 0.0f, 0);
   return launch_status();
 }
 
@@ -2063,7 +2070,7 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
     return GDN_ERR_SHAPE;
   if (!is_act(act)) return GDN_ERR_DTYPE;
   if (!(valid_head(Dk) && (Dk <= 128 || act == GDN_BF16)) || Dv % 32 != 0 ||
-      Dv > 256 || !valid_chunk(chunk) || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM)) != 0)
+      Dv > 256 || !valid_chunk(chunk) || (flags & ~static_cast<unsigned>(GDN_QK_L2NORM | GDN_KEEP_STATE)) != 0)
     return GDN_ERR_UNSUPPORTED;
   chunk = effective_chunk(Dk, chunk);
   if (N_s == 0) return GDN_OK;
@@ -2102,11 +2109,12 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
   // max_len > 0: no sequence is longer (the caller knows it); then whether
   // every sequence fits one chunk
   const bool one_chunk = max_len > 0 && max_len <= chunk;
+  const unsigned opts = (one_chunk ? kOneChunk : 0u) | ((flags & GDN_KEEP_STATE) ? kKeepState : 0u);
   if (act == GDN_BF16)
     return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, one_chunk);
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, opts);
   return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, one_chunk);
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, opts);
 }
 
 }  // namespace

@@ -95,7 +95,8 @@ int gdn_decode_step(const float* state_in, float* state_out, const void* q,
  * gdn_decode_step (state_out counts as written only when commit > 0).
  * A committed window (commit == T) is also gdn_chunk_prefill_fixed with
  * flags 0 and scale 1 on the same layouts (in place on the state, with a
- * workspace); from T = 4 on that MFMA path is the faster of the two.
+ * workspace), and a verify window (commit == 0) the same call with flags
+ * GDN_KEEP_STATE; from T = 4 on that MFMA path is the faster of the two.
  */
 int gdn_decode_window(const float* state_in, float* state_out, const void* q,
                       const void* k, const void* v, const float* g,
@@ -150,6 +151,12 @@ int gdn_prefill_gates(const void* a, const void* b, const float* A_log,
  * and the regolith kernel normalises both. */
 #define GDN_QK_L2NORM 1u
 
+/* gdn_chunk_prefill flag: the state slots are read but never written, and
+ * every y is still produced - a verify window of speculative decoding (the
+ * regolith `gdn.metal` commit rule with nothing committed), run on the
+ * chunked path. */
+#define GDN_KEEP_STATE 2u
+
 /*
  * gdn_chunk_prefill_workspace - bytes of device workspace gdn_chunk_prefill
  * needs for these sizes and activation dtype (0 for invalid arguments).  It
@@ -191,7 +198,8 @@ size_t gdn_chunk_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
  *               gdn_validate_varlen checks the contract.
  * y             [T_tot, Hv, Dv] act, written.
  * chunk         8, 16, 32 or 64 tokens.     scale: <= 0 selects Dk^-1/2.
- * flags         0 or GDN_QK_L2NORM.
+ * flags         0, or GDN_QK_L2NORM and/or GDN_KEEP_STATE (then state_pool is
+ *               only read).
  * workspace     device memory of at least gdn_chunk_prefill_workspace()
  *               bytes, 16-byte aligned; its contents are scratch.
  * Requirements: Dk a multiple of 32 up to 256 (above 128 with bf16
@@ -313,7 +321,7 @@ size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv,
  * q, k          [B, T, Hk, Dk] act.     v, y [B, T, Hv, Dv] act (y written).
  * g, beta       [B, T, Hv] float32.
  * state         [B, Hv, Dv, Dk] float32 (the gdn_decode_step layout), read
- *               and written in place.
+ *               and written in place (only read with GDN_KEEP_STATE).
  * chunk, scale, flags: as for gdn_chunk_prefill.
  * workspace     device memory of at least gdn_chunk_prefill_fixed_workspace()
  *               bytes, 16-byte aligned; its contents are scratch (the call

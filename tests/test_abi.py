@@ -158,7 +158,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, Dk=80) == UNSUP                    # a multiple of 32 up to 256
     assert prefill(lib, Dv=40) == UNSUP
     assert prefill(lib, chunk=128) == UNSUP
-    assert prefill(lib, flags=2) == UNSUP
+    assert prefill(lib, flags=4) == UNSUP                 # no such flag
+    assert prefill(lib, flags=3, ws=0) == NULL            # GDN_QK_L2NORM | GDN_KEEP_STATE pass the flag check
     assert prefill(lib, ws=0) == NULL
     assert prefill(lib, cu=0) == NULL
     assert prefill(lib, q=0) == NULL

@@ -292,3 +292,37 @@ def test_committed_window_equals_the_fixed_length_prefill():
     assert maxrel(to_np(s_fix), S_ref) <= 1e-3
     check_bf16_out(to_np(y_fix), y_ref, "fixed-length y")
     check_bf16_out(to_np(y_win), y_ref, "window y")
+
+
+@pytest.mark.parametrize("B,T,chunk,act", [
+    (6, 8, 8, "bf16"),     # 36 chunk-loop workgroups: the half-width kernel
+    (6, 16, 8, "bf16"),    # two chunks per sequence
+    (48, 8, 8, "bf16"),    # 288 workgroups, more than the CUs
+    (4, 16, 16, "f32"),    # fp32 activations: the register-fragment kernel
+])
+def test_verify_window_on_the_chunked_path(B, T, chunk, act):
+    """A verify window (nothing committed) is gdn_chunk_prefill_fixed with
+    GDN_KEEP_STATE, no norm and scale 1: y as the oracle's verify window, the
+    state bit for bit unchanged, and y bit for bit the y of the same call
+    without the flag (which does commit)."""
+    rng = np.random.default_rng(B * 10 + T + chunk)
+    Hk, Hv, Dk, Dv = 2, 6, 128, 128
+    S0 = (0.3 * rng.standard_normal((B, Hv, Dv, Dk))).astype(np.float32)
+    w = _window_tokens(rng, B, T, Hk, Hv, Dk, Dv, act)
+    d = DT[act]
+    dw = {n: to_dev(x, torch.float32 if n == "g" else d, DEV) for n, x in w.items()}
+    beta32 = dw["beta"].float().contiguous()
+    s_keep = to_dev(S0, torch.float32, DEV)
+    y_keep = gdn.gdn_chunk_prefill_fixed(dw["q"], dw["k"], dw["v"], dw["g"], beta32, s_keep, chunk=chunk,
+                                         scale=1.0, l2norm=False, keep_state=True)
+    s_commit = to_dev(S0, torch.float32, DEV)
+    y_commit = gdn.gdn_chunk_prefill_fixed(dw["q"], dw["k"], dw["v"], dw["g"], beta32, s_commit, chunk=chunk,
+                                           scale=1.0, l2norm=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(s_keep).astype(np.float32), S0)
+    assert torch.equal(y_keep, y_commit)
+    _, y_ref = oracle.gdn_window(S0, w["q"], w["k"], w["v"], w["g"], w["beta"], commit=0)
+    if act == "f32":
+        assert maxrel(to_np(y_keep), y_ref) <= 1e-3
+    else:
+        check_bf16_out(to_np(y_keep), y_ref, "verify window y")

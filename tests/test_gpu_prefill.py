@@ -463,6 +463,45 @@ def test_split_choice(lengths):
         check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
 
 
+@pytest.mark.parametrize("route", ["plain", "gated", "noalloc"])
+def test_keep_state_reads_the_pool_only(route):
+    """GDN_KEEP_STATE: the pool is bit for bit unchanged and y is bit for
+    bit the y of the same call without the flag (plain varlen call on the
+    half-width kernel, the fused gated norm, the allocation-free entry)."""
+    rng = np.random.default_rng(90)
+    lengths, Hk, Hv, Dk, Dv, P = [100, 37, 0, 5], 2, 4, 128, 128, 6
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv, steps=2)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    bf = torch.bfloat16
+    a, b = to_dev(inp["a"], bf, DEV), to_dev(inp["b"], bf, DEV)
+    g, beta = gdn.gdn_prefill_gates(a, b, to_dev(inp["A_log"], torch.float32, DEV),
+                                    to_dev(inp["dt_bias"], torch.float32, DEV))
+    q, k, v = (to_dev(inp[n], bf, DEV) for n in ("q", "k", "v"))
+    ci = to_dev(inp["cache_indices"], torch.int64, DEV)
+    cu = to_dev(inp["cu_seqlens"], torch.int64, DEV)
+    T = q.shape[0]
+    extra = {}
+    if route == "gated":
+        extra = dict(z=to_dev(rng.standard_normal((T, Hv, Dv)).astype(np.float32), bf, DEV),
+                     gamma=to_dev(rng.uniform(0.5, 1.5, Dv).astype(np.float32), torch.float32, DEV))
+
+    def run(keep):
+        pool = to_dev(pool0, torch.float32, DEV)
+        if route == "noalloc":
+            y = torch.empty((T, Hv, Dv), dtype=bf, device=DEV)
+            gdn.gdn_chunk_prefill_noalloc(q, k, v, g, beta, pool, ci, cu, y, chunk=64, keep_state=keep)
+        else:
+            y = gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=64, keep_state=keep, **extra)
+        torch.cuda.synchronize()
+        return pool, y
+
+    pool_k, y_k = run(True)
+    pool_c, y_c = run(False)
+    assert np.array_equal(to_np(pool_k).astype(np.float32), pool0)
+    assert torch.equal(y_k, y_c)
+    assert not np.array_equal(to_np(pool_c).astype(np.float32), pool0)  # the call without it commits
+
+
 @pytest.mark.parametrize("act", ["bf16", "f32"])
 def test_batch_of_empty_sequences_leaves_the_pool_untouched(act):
     """Three sequences of zero tokens (T_tot = 0): every launch runs and finds
