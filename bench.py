@@ -248,7 +248,10 @@ def prefill_min_bytes(T, n_seq, Hk, Hv, Dk, Dv, act_bytes=2):
     return T * per_token + n_seq * 2 * Hv * Dv * Dk * 4
 
 
-def bench_prefill(steps, warmup, device, Dk=None, lengths=None):
+def bench_prefill(steps, warmup, device, Dk=None, lengths=None, raw=True):
+    """The varlen prefill from raw gate inputs: gdn_chunk_prefill_raw (the
+    gates formed inside the WY pass), or with raw=False gdn_prefill_gates
+    then gdn_chunk_prefill."""
     import torch
     import gated_deltanet_linear_gdn_amd as gdn
     from gated_deltanet_linear_gdn_amd import synth
@@ -275,12 +278,15 @@ def bench_prefill(steps, warmup, device, Dk=None, lengths=None):
     g = torch.empty((T, Hv), dtype=torch.float32, device=device)
     beta = torch.empty_like(g)
     y = torch.empty((T, Hv, Dv), dtype=bf, device=device)
-    ws = torch.empty(gdn.gdn_chunk_prefill_workspace(T, len(lengths), Hk, Hv, Dk, Dv, C),
-                     dtype=torch.uint8, device=device)
+    wsf = gdn.gdn_chunk_prefill_raw_workspace if raw else gdn.gdn_chunk_prefill_workspace
+    ws = torch.empty(wsf(T, len(lengths), Hk, Hv, Dk, Dv, C), dtype=torch.uint8, device=device)
 
     def step(i):
-        gdn.gdn_prefill_gates(a, b, A_log, dt_bias, g, beta)
-        gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y, workspace=ws)
+        if raw:
+            gdn.gdn_chunk_prefill_raw(q, k, v, a, b, A_log, dt_bias, pool, ci, cu, chunk=C, y=y, workspace=ws)
+        else:
+            gdn.gdn_prefill_gates(a, b, A_log, dt_bias, g, beta)
+            gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y, workspace=ws)
 
     sec = _timed(step, steps, warmup)
     C = min(C, 32) if Dk == 256 else C  # the chunk Dk = 256 runs
@@ -653,6 +659,7 @@ def main():
             com_shapes[f"B{B_}_H{H_}_K{K_}_V{V_}"] = bench_comba_hbm(max(10, args.steps // 5), 5, device,
                                                                      B_, H_, K_, V_)
     pre = bench_prefill(max(5, args.steps // 20), 3, device) if want("prefill") else None
+    pre_two = bench_prefill(max(5, args.steps // 20), 3, device, raw=False) if want("prefill") else None
     cpre = bench_comba_prefill(max(5, args.steps // 20), 3, device) if want("comba_prefill") else None
     pre256 = bench_prefill(max(5, args.steps // 20), 3, device, Dk=256) if want("dk256") else None
     pre1 = bench_prefill(max(5, args.steps // 20), 3, device, lengths=[4096]) if want("prefill") else None
@@ -743,8 +750,10 @@ def main():
                              "separate_kernels_us_per_step": round(cdec["sep_sec"] * 1e6, 2),
                              "bytes_per_step": cdec["bytes"]}
     if want("prefill"):
-        out["prefill"] = {"workload": "gdn_prefill_gates + gdn_chunk_prefill, 8 sequences of U[512,4096] "
-                                     "tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64, pool 16",
+        out["prefill"] = {"workload": "gdn_chunk_prefill_raw (gates from raw a, b, A_log, dt_bias formed inside "
+                                     "the WY pass), 8 sequences of U[512,4096] tokens, Hk=16 Hv=48 Dk=Dv=128, bf16, "
+                                     "chunk 64, pool 16",
+                         "two_calls_us_per_call": round(pre_two["sec"] * 1e6, 2),
                          "tokens": pre["tokens"], "lengths": pre["lengths"],
                          "us_per_call": round(pre["sec"] * 1e6, 2),
                          "tokens_per_s": round(pre["tokens"] / pre["sec"], 1),
@@ -754,7 +763,7 @@ def main():
                          "min_bytes": pre["min_bytes"],
                          "hbm_frac_of_peak": round(pre["min_bytes"] / pre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)}
     if want("prefill"):
-        out["prefill_single"] = {"workload": "gdn_prefill_gates + gdn_chunk_prefill of one 4,096-token sequence "
+        out["prefill_single"] = {"workload": "gdn_chunk_prefill_raw of one 4,096-token sequence "
                                             "(the workload's longest length), Hk=16 Hv=48 Dk=Dv=128, bf16, chunk 64",
                                 "us_per_call": round(pre1["sec"] * 1e6, 2),
                                 "tokens_per_s": round(pre1["tokens"] / pre1["sec"], 1)}
@@ -771,7 +780,7 @@ def main():
                                "min_bytes": cpre["min_bytes"],
                                "hbm_frac_of_peak": round(cpre["min_bytes"] / cpre["sec"] / 1e9 / HBM_PEAK_GBPS, 4)}
     if want("dk256"):
-        out["dk256"] = {"workload": "key head size 256 (value 128): gdn_chunk_prefill at the varlen token mix "
+        out["dk256"] = {"workload": "key head size 256 (value 128): gdn_chunk_prefill_raw at the varlen token mix "
                                    "(Hk=16 Hv=48, 32-token chunks) and gdn_decode_step at B=128 (the same "
                                    "1.6 GB of state per step as the headline)",
                        "prefill_us_per_call": round(pre256["sec"] * 1e6, 2),

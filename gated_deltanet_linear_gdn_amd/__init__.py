@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "GdnError", "library_path", "load_library",
     "gdn_decode_step", "comba_decode_step", "gdn_prefill_gates", "gdn_status_string",
-    "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_validate_varlen", "GDN_QK_L2NORM", "GDN_KEEP_STATE",
+    "gdn_chunk_prefill_workspace", "gdn_chunk_prefill", "gdn_chunk_prefill_raw_workspace", "gdn_chunk_prefill_raw", "gdn_validate_varlen", "GDN_QK_L2NORM", "GDN_KEEP_STATE",
     "gdn_decode_window", "gdn_conv_silu", "gdn_gated_rmsnorm",
     "gdn_chunk_prefill_fixed_workspace", "gdn_chunk_prefill_fixed",
     "comba_chunk_prefill_workspace", "comba_chunk_prefill", "gdn_stream_copy", "gdn_chunk_prefill_noalloc",
@@ -79,6 +79,11 @@ def load_library():
     lib.gdn_chunk_prefill.restype = _i
     lib.gdn_chunk_prefill.argtypes = ([_vp] * 6 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
                                       + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
+    lib.gdn_chunk_prefill_raw_workspace.restype = ctypes.c_size_t
+    lib.gdn_chunk_prefill_raw_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i, _i]
+    lib.gdn_chunk_prefill_raw.restype = _i
+    lib.gdn_chunk_prefill_raw.argtypes = ([_vp] * 8 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
+                                          + [_f, ctypes.c_uint, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.gdn_validate_varlen.restype = _i
     lib.gdn_validate_varlen.argtypes = [_vp, _vp, _i, _i64, _i64, _vp]
     lib.gdn_chunk_prefill_gated.restype = _i
@@ -328,6 +333,50 @@ def gdn_chunk_prefill(q, k, v, g, beta, state_pool, cache_indices, cu_seqlens, c
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc, flags,
           _ptr(z), _ptr(gamma), float(eps), _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(),
           _stream(dev))
+    return y
+
+
+def gdn_chunk_prefill_raw_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64, dtype=None) -> int:
+    """Bytes of workspace ``gdn_chunk_prefill_raw`` needs (torch.bfloat16
+    activations by default)."""
+    act = 0 if dtype == torch.float32 else 1
+    return int(load_library().gdn_chunk_prefill_raw_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act))
+
+
+def gdn_chunk_prefill_raw(q, k, v, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens, chunk=64,
+                          scale=None, l2norm=True, y=None, workspace=None, keep_state=False):
+    """``gdn_prefill_gates`` and ``gdn_chunk_prefill`` in one call from the
+    raw gate inputs (see ``gdn_chunk_prefill_raw`` in include/gdn.h): a, b
+    [T,Hv] act, A_log, dt_bias [Hv] f32; the rest as ``gdn_chunk_prefill``.
+    Returns y."""
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    P = state_pool.shape[0]
+    N_s = cache_indices.shape[0]
+    dev, act = q.device, q.dtype
+    if y is None:
+        y = torch.empty((T, Hv, Dv), dtype=act, device=dev)
+    _check("q", q, (T, Hk, Dk), act, dev)
+    _check("k", k, (T, Hk, Dk), act, dev)
+    _check("v", v, (T, Hv, Dv), act, dev)
+    _check("a", a, (T, Hv), act, dev)
+    _check("b", b, (T, Hv), act, dev)
+    _check("A_log", A_log, (Hv,), torch.float32, dev)
+    _check("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check("state_pool", state_pool, (P, Hv, Dv, Dk), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    _check("y", y, (T, Hv, Dv), act, dev)
+    need = gdn_chunk_prefill_raw_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk, act)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    flags = (GDN_QK_L2NORM if l2norm else 0) | (GDN_KEEP_STATE if keep_state else 0)
+    _call("gdn_chunk_prefill_raw", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+          _ptr(state_pool), P, _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, int(chunk), sc,
+          flags, _ptr(y), _act_of(q), _ptr(workspace), workspace.numel(), _stream(dev))
     return y
 
 

@@ -122,9 +122,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_prologue_kernel(
   for (int j = tid; j < G; j += kThreads) {
     const int hv = hk * G + j;
     const size_t n = static_cast<size_t>(b) * Hv + hv;
-    const float xa = to_f32(a[n]) + dt_bias[hv];
-    out.g[n] = -expf(A_log[hv]) * (fmaxf(xa, 0.0f) + log1pf(expf(-fabsf(xa))));
-    out.beta[n] = 1.0f / (1.0f + expf(-to_f32(bg[n])));
+    gates_of(to_f32(a[n]) + dt_bias[hv], A_log[hv], to_f32(bg[n]), out.g[n], out.beta[n]);
   }
   float fq = scale, fk = 1.0f;
   if (l2) {

@@ -24,6 +24,20 @@ __device__ __forceinline__ bf16 f32_to_bf16(float f) {
   return static_cast<bf16>(u >> 16);
 }
 
+// ------------------------------------------------------------------ gates
+
+// The gates of one (token, value head) from its raw inputs (pymllm
+// `gdn_extend_chunkwise` parameters; formulas of the regolith `gdn.metal`
+// header comment): xa = a + dt_bias[h], g = -exp(A_log[h]) softplus(xa)
+// (log-space) and beta = sigmoid(b).  softplus(x) is evaluated as
+// max(x, 0) + log1p(exp(-|x|)), the same function with no overflow and no
+// threshold.  Every kernel that forms gates calls this, so they agree bit
+// for bit.
+__device__ __forceinline__ void gates_of(float xa, float A_log, float braw, float& g, float& beta) {
+  g = -expf(A_log) * (fmaxf(xa, 0.0f) + log1pf(expf(-fabsf(xa))));
+  beta = 1.0f / (1.0f + expf(-braw));
+}
+
 // ---------------------------------------------------- activation loads/stores
 
 template <typename T> struct Act;

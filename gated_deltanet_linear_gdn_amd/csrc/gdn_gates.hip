@@ -4,9 +4,8 @@
 // A_log, dt_bias; formulas from the regolith `gdn.metal` header comment):
 //   g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (log-space)
 //   beta[t,h] = 1 / (1 + exp(-b[t,h]))
-// softplus(x) is evaluated as max(x, 0) + log1p(exp(-|x|)): the same function
-// with no overflow and no threshold.  Elementwise and HBM-bound (a few bytes
-// per token and head); one thread per element, grid-stride.
+// (gates_of in gdn_device.h).  Elementwise and HBM-bound (a few bytes per
+// token and head); one thread per element, grid-stride.
 
 #include "gdn_device.h"
 #include "gdn_host.h"
@@ -22,10 +21,7 @@ __global__ __launch_bounds__(256) void gdn_gates_kernel(
   const long stride = static_cast<long>(gridDim.x) * blockDim.x;
   for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     const int h = static_cast<int>(i % Hv);
-    const float x = Act<T>::load(a + i) + dt_bias[h];
-    const float sp = fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
-    g[i] = -expf(A_log[h]) * sp;
-    beta[i] = 1.0f / (1.0f + expf(-Act<T>::load(b + i)));
+    gates_of(Act<T>::load(a + i) + dt_bias[h], A_log[h], Act<T>::load(b + i), g[i], beta[i]);
   }
 }
 

@@ -196,6 +196,15 @@ template <> struct Raw<float> {
 // below compares against it); the order within a bit length is otherwise
 // arbitrary, and no result depends on it.
 
+// Raw gate inputs of a prefill whose gates are formed inside the WY pass
+// (gdn_chunk_prefill_raw); a, b in the bf16 activation dtype.
+struct RawGates {
+  const bf16* a;
+  const bf16* b;
+  const float* A_log;
+  const float* dt_bias;
+};
+
 __device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_tot, int64_t& b0,
                                            int64_t& len) {
   int64_t a = cu[s], b = cu[s + 1];
@@ -963,13 +972,17 @@ __device__ __forceinline__ f32x4 mm3_la(s16x4 ah, s16x4 al, f32x4 b) {
 __device__ __forceinline__ float ld_beta(const float* b, size_t i) { return b[i]; }
 __device__ __forceinline__ float ld_beta(const bf16* b, size_t i) { return bf16_to_f32(b[i]); }
 
-template <int DK, int CT, bool COMBA = false, typename BT = float>
+// RAW: the gates come from the raw inputs a, b [T, Hv] (bf16), A_log and
+// dt_bias [Hv] (gates_of), formed where the gate scan needs them, instead
+// of from g and beta.
+template <int DK, int CT, bool COMBA = false, typename BT = float, bool RAW = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gdn_wy_wave_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
     const float* __restrict__ g, const BT* __restrict__ beta, const int64_t* __restrict__ cu,
     const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
-    bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac) {
+    bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac, RawGates rg) {
+  static_assert(!RAW || !COMBA, "raw gates: GDN only");
   constexpr int MT = CT / 16, KB = DK / 32;
   constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 3 * CT + 4;
   __shared__ __attribute__((aligned(16))) float sG[CT], sRK[CT], sRQ[CT], sB[CT];
@@ -1001,7 +1014,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   // holds row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on
   // both sides of every Gram product); Q fragments follow one row block at a
   // time, as the Q K^T blocks of that row need them
-  float gl = g[tg], bl = ld_beta(beta, tg);
+  // gates of value head hk*HG + j for this lane's token
+  auto gates = [&](int j, float& gv, float& bv) __attribute__((always_inline)) {
+    if constexpr (RAW) {
+      const int h = hk * HG + j;
+      gates_of(bf16_to_f32(rg.a[tg + j]) + rg.dt_bias[h], rg.A_log[h], bf16_to_f32(rg.b[tg + j]), gv, bv);
+    } else {
+      gv = g[tg + j];
+      bv = ld_beta(beta, tg + j);
+    }
+  };
+  float gl, bl;
+  gates(0, gl, bl);
   auto row_off = [&](int I) __attribute__((always_inline)) {
     return (static_cast<size_t>(t0 + min(I * 16 + l16, n - 1)) * Hk + hk) * DK + kg * 8;
   };
@@ -1081,10 +1105,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     const size_t mat = static_cast<size_t>(c) * Hv + hv;
     float G = ok ? gl : 0.f;
     const float bt = ok ? bl : 0.f;
-    if (j + 1 < HG) {  // the next head's gates, in flight during this head
-      gl = g[tg + j + 1];
-      bl = ld_beta(beta, tg + j + 1);
-    }
+    if (j + 1 < HG) gates(j + 1, gl, bl);  // the next head's gates, in flight during this head
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float up = __shfl_up(G, off);
@@ -1825,7 +1846,7 @@ template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
-               char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream, unsigned opts) {
+               char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw, hipStream_t stream, unsigned opts) {
   const bool one_chunk = (opts & kOneChunk) != 0;
   const int keep = (opts & kKeepState) ? 1 : 0;
   int* scs = reinterpret_cast<int*>(ws + L.scs);
@@ -1846,10 +1867,16 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   (void)hipGetLastError();
   chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), dim3(static_cast<unsigned>(maxc * static_cast<size_t>(Hk))), dim3(64), 0,
-                       stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(nullptr), g, beta, cu, scs, N_s, T_tot, Hk, Hv, chunk, scale,
-                       l2norm, Th, Tl, Ph, fac);
+    const dim3 wy_grid(static_cast<unsigned>(maxc * static_cast<size_t>(Hk)));
+    if (raw)  // the gates formed inside the WY pass
+      hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, false, float, true>), wy_grid, dim3(64), 0, stream,
+                         static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
+                         static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), cu, scs, N_s, T_tot,
+                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, *raw);
+    else
+      hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), wy_grid, dim3(64), 0, stream, static_cast<const bf16*>(q),
+                         static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr), g, beta, cu, scs, N_s, T_tot,
+                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, RawGates{});
     // the epilogue is fused when one workgroup covers a whole 128-column head
     if constexpr (NW == 8 && CW == 1) {
       if (epi && Dv == 128) {
@@ -1889,6 +1916,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                          static_cast<bf16*>(y), static_cast<const bf16*>(nullptr),
                          static_cast<const float*>(nullptr), 0.0f, keep);
   } else {
+    if (raw) return GDN_ERR_UNSUPPORTED;  // fp32 activations take their gates from gdn_prefill_gates
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
                        T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
@@ -1909,8 +1937,8 @@ template <typename T, int DK, int CT>
 int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
-                unsigned opts) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw,
+                hipStream_t stream, unsigned opts) {
   // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
   // workgroup so each chunk operand is fetched once per 128 columns.  fp32
   // activations: the register-fragment kernel, 64 (four waves, up to 512
@@ -1918,30 +1946,30 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
       return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                         chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                         chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                    chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
   return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
 }
 
 template <typename T, int DK>
 int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, const float* g,
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
-                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, hipStream_t stream,
-                unsigned opts) {
+                int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw,
+                hipStream_t stream, unsigned opts) {
   if constexpr (DK > 128) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
   } else {
     if (CT == 32)
       return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                    chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                    chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
     return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
   }
 }
 
@@ -1950,20 +1978,20 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
                 const float* g, const float* beta, float* pool, int64_t pool_size,
                 const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
                 int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
-                const Epilogue* epi, hipStream_t stream, unsigned opts) {
+                const Epilogue* epi, const RawGates* raw, hipStream_t stream, unsigned opts) {
   switch (Dk) {
-    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
   }
   // wider heads: bf16 activations only (the fp32 kernels would spill at these widths)
   if constexpr (std::is_same<T, bf16>::value) {
     switch (Dk) {
-      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
-      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, stream, opts);
+      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
     }
   }
   return GDN_ERR_UNSUPPORTED;
@@ -2011,7 +2039,7 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
   hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
-                     Th, Tl, Ph, fac);
+                     Th, Tl, Ph, fac, RawGates{});
   if (split)
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true, true>),
                        dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,
@@ -2064,7 +2092,8 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
                   const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
                   int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
                   size_t workspace_bytes, const Epilogue* epi, hipStream_t stream,
-                  bool check_only = false, int64_t max_len = 0, bool no_ws_checks = false) {
+                  bool check_only = false, int64_t max_len = 0, bool no_ws_checks = false,
+                  const RawGates* raw = nullptr) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
@@ -2075,7 +2104,10 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
   chunk = effective_chunk(Dk, chunk);
   if (N_s == 0) return GDN_OK;
   if (!cache_indices || !cu_seqlens || !state_pool || (!workspace && !no_ws_checks)) return GDN_ERR_NULL;
-  if (T_tot > 0 && (!q || !k || !v || !g || !beta || !y)) return GDN_ERR_NULL;
+  if (T_tot > 0 && (!q || !k || !v || !y || (raw ? (!raw->a || !raw->b || !raw->A_log || !raw->dt_bias)
+                                                     : (!g || !beta))))
+    return GDN_ERR_NULL;
+  if (raw && act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_pool) ||
       (!aligned16(workspace) && !no_ws_checks))
     return GDN_ERR_ALIGN;
@@ -2097,9 +2129,17 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
     const size_t qk_bytes = static_cast<size_t>(T_tot) * Hk * Dk * act_bytes(act);
     const size_t v_bytes = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
     const size_t gb_bytes = static_cast<size_t>(T_tot) * Hv * sizeof(float);
-    const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {g, gb_bytes}, {beta, gb_bytes}};
     const Span out[] = {{y, y_bytes}, {state_pool, pool_bytes}, {workspace, ws_bytes}};
-    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+    if (raw) {
+      const size_t ab_bytes = static_cast<size_t>(T_tot) * Hv * act_bytes(act);
+      const size_t h_bytes = static_cast<size_t>(Hv) * sizeof(float);
+      const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {raw->a, ab_bytes}, {raw->b, ab_bytes},
+                         {raw->A_log, h_bytes}, {raw->dt_bias, h_bytes}};
+      if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+    } else {
+      const Span in[] = {{q, qk_bytes}, {k, qk_bytes}, {v, v_bytes}, {g, gb_bytes}, {beta, gb_bytes}};
+      if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+    }
   }
   if (check_only) return GDN_OK;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf(static_cast<float>(Dk));
@@ -2112,9 +2152,9 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
   const unsigned opts = (one_chunk ? kOneChunk : 0u) | ((flags & GDN_KEEP_STATE) ? kKeepState : 0u);
   if (act == GDN_BF16)
     return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, opts);
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, stream, opts);
   return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, stream, opts);
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, stream, opts);
 }
 
 }  // namespace
@@ -2129,6 +2169,65 @@ extern "C" int gdn_chunk_prefill(const void* q, const void* k, const void* v, co
   return gdn::chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s,
                             T_tot, Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, workspace_bytes,
                             nullptr, stream);
+}
+
+// ------------------------------------------------- prefill from raw gates
+//
+// gdn_chunk_prefill_raw: the gates from the raw inputs in the same call.
+// bf16 activations form them inside the WY pass (the only kernel that reads
+// them); fp32 activations run gdn_prefill_gates into the workspace's tail
+// first.  Either way the gates are those gdn_prefill_gates writes, bit for
+// bit (gates_of).
+
+extern "C" size_t gdn_chunk_prefill_raw_workspace(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int Dv,
+                                                  int chunk, gdn_dtype act) {
+  const size_t base = gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act);
+  if (base == 0 || act == GDN_BF16) return base;
+  return base + gdn::up(2 * static_cast<size_t>(T_tot) * static_cast<size_t>(Hv) * sizeof(float));
+}
+
+extern "C" int gdn_chunk_prefill_raw(const void* q, const void* k, const void* v, const void* a,
+                                     const void* b, const float* A_log, const float* dt_bias,
+                                     float* state_pool, int64_t pool_size, const int64_t* cache_indices,
+                                     const int64_t* cu_seqlens, int N_s, int64_t T_tot, int Hk, int Hv,
+                                     int Dk, int Dv, int chunk, float scale, unsigned flags, void* y,
+                                     gdn_dtype act, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  using namespace gdn;
+  if (act == GDN_BF16) {
+    const RawGates rg{static_cast<const bf16*>(a), static_cast<const bf16*>(b), A_log, dt_bias};
+    return chunk_prefill(q, k, v, nullptr, nullptr, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot,
+                         Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, workspace_bytes, nullptr, stream,
+                         false, 0, false, &rg);
+  }
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (N_s < 0 || T_tot < 0 || Hv <= 0) return GDN_ERR_SHAPE;
+  if (N_s == 0) return chunk_prefill(q, k, v, nullptr, nullptr, state_pool, pool_size, cache_indices, cu_seqlens,
+                                     N_s, T_tot, Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, workspace,
+                                     workspace_bytes, nullptr, stream);
+  const size_t base = gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act);
+  const size_t need = gdn_chunk_prefill_raw_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act);
+  if (!workspace) return GDN_ERR_NULL;
+  if (need == 0 || workspace_bytes < need) return base == 0 ? GDN_ERR_UNSUPPORTED : GDN_ERR_WORKSPACE;
+  if (T_tot > 0 && (!a || !b || !A_log || !dt_bias)) return GDN_ERR_NULL;
+  float* g = reinterpret_cast<float*>(static_cast<char*>(workspace) + base);
+  float* beta = g + static_cast<size_t>(T_tot) * Hv;
+  {  // the raw inputs must not overlap the gates' scratch or the outputs
+    const size_t ab = static_cast<size_t>(T_tot) * Hv * act_bytes(act), hb = static_cast<size_t>(Hv) * 4;
+    const size_t yb = static_cast<size_t>(T_tot) * Hv * Dv * act_bytes(act);
+    const size_t pb = static_cast<size_t>(pool_size < 0 ? 0 : pool_size) * Hv * Dv * Dk * sizeof(float);
+    const Span in[] = {{a, ab}, {b, ab}, {A_log, hb}, {dt_bias, hb}};
+    const Span out[] = {{workspace, need}, {y, yb}, {state_pool, pb}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+  }
+  // every other check before any launch
+  int rc = chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot, Hk, Hv,
+                         Dk, Dv, chunk, scale, flags, y, act, workspace, base, nullptr, stream, true);
+  if (rc != GDN_OK) return rc;
+  rc = gdn_prefill_gates(a, b, A_log, dt_bias, g, beta, T_tot, Hv, act, stream);
+  if (rc != GDN_OK) return rc;
+  return chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot, Hk, Hv, Dk,
+                       Dv, chunk, scale, flags, y, act, workspace, base, nullptr, stream);
 }
 
 extern "C" int gdn_chunk_prefill_gated(const void* q, const void* k, const void* v, const float* g,

@@ -223,6 +223,39 @@ int gdn_chunk_prefill(const void* q, const void* k, const void* v,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_chunk_prefill_raw_workspace - bytes of workspace gdn_chunk_prefill_raw
+ * needs: gdn_chunk_prefill_workspace(), plus 8 bytes per (token, value head)
+ * with fp32 activations (the gates' scratch).  0 for invalid arguments.
+ */
+size_t gdn_chunk_prefill_raw_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
+                                       int Dk, int Dv, int chunk, gdn_dtype act);
+
+/*
+ * gdn_chunk_prefill_raw - gdn_prefill_gates and gdn_chunk_prefill in one
+ * call, from the raw gate inputs the pymllm `gdn_extend_chunkwise`
+ * parameter list names (a, b, A_log, dt_bias; the formulas of
+ * gdn_prefill_gates).  With bf16 activations the gates are formed inside the
+ * prefill's WY pass, the one kernel that reads them, so no [T_tot, Hv] g
+ * and beta pass through memory; with fp32 activations gdn_prefill_gates
+ * writes them into the workspace's tail first.  Results equal those of the
+ * two calls bit for bit.
+ * a, b          [T_tot, Hv] act.   A_log, dt_bias [Hv] float32.
+ * Every other argument as for gdn_chunk_prefill (flags GDN_QK_L2NORM and/or
+ * GDN_KEEP_STATE); workspace: at least gdn_chunk_prefill_raw_workspace()
+ * bytes, 16-byte aligned, scratch.  a, b, A_log and dt_bias must not overlap
+ * y, the pool or the workspace (GDN_ERR_ALIAS); otherwise the errors of
+ * gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_raw(const void* q, const void* k, const void* v,
+                          const void* a, const void* b, const float* A_log,
+                          const float* dt_bias, float* state_pool,
+                          int64_t pool_size, const int64_t* cache_indices,
+                          const int64_t* cu_seqlens, int N_s, int64_t T_tot,
+                          int Hk, int Hv, int Dk, int Dv, int chunk, float scale,
+                          unsigned flags, void* y, gdn_dtype act, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * gdn_chunk_prefill_gated - gdn_chunk_prefill followed by the layer's gated
  * RMS norm of every output row (gdn_gated_rmsnorm below): y receives
  *     o_j / sqrt(mean_j(o_j^2) + eps) * gamma[j] * sigmoid(z_j)

@@ -128,6 +128,33 @@ def prefill(lib, q=A, k=A + BIG, v=A + 2 * BIG, g=A + 3 * BIG, beta=A + 4 * BIG,
                                  _p(ws), ws_bytes, None)
 
 
+def prefill_raw(lib, q=A, k=A + BIG, v=A + 2 * BIG, a=A + 3 * BIG, b=A + 4 * BIG, A_log=A + 10 * BIG,
+                dt_bias=A + 11 * BIG, pool=A + 5 * BIG, P=4, ci=A + 6 * BIG, cu=A + 7 * BIG, N_s=2, T=100, Hk=2,
+                Hv=4, Dk=128, Dv=128, chunk=64, flags=1, y=A + 8 * BIG, act=1, ws=A + 9 * BIG, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.gdn_chunk_prefill_raw_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk, act if act in (0, 1) else 1)
+    return lib.gdn_chunk_prefill_raw(_p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log), _p(dt_bias), _p(pool), P,
+                                     _p(ci), _p(cu), N_s, T, Hk, Hv, Dk, Dv, chunk, ctypes.c_float(0.0), flags,
+                                     _p(y), act, _p(ws), ws_bytes, None)
+
+
+def test_prefill_raw_validation(lib):
+    f = lib.gdn_chunk_prefill_raw_workspace
+    base = lib.gdn_chunk_prefill_workspace
+    assert f(100, 2, 2, 4, 128, 128, 64, 1) == base(100, 2, 2, 4, 128, 128, 64, 1)   # bf16: gates in the WY pass
+    assert f(100, 2, 2, 4, 128, 128, 64, 0) >= base(100, 2, 2, 4, 128, 128, 64, 0) + 100 * 4 * 8  # fp32: g, beta
+    assert f(100, 2, 2, 4, 128, 128, 48, 0) == 0
+    for act in (0, 1):
+        assert prefill_raw(lib, act=act, a=0) == NULL
+        assert prefill_raw(lib, act=act, dt_bias=0) == NULL
+        assert prefill_raw(lib, act=act, a=A + 8 * BIG + 64) == ALIAS      # a over y
+        assert prefill_raw(lib, act=act, b=A + 9 * BIG) == ALIAS           # b over the workspace
+        assert prefill_raw(lib, act=act, flags=4) == UNSUP
+        assert prefill_raw(lib, act=act, ws_bytes=1024) == WORKSPACE
+        assert prefill_raw(lib, act=act, N_s=0, q=0, a=0) == OK            # nothing to do
+    assert prefill_raw(lib, act=9) == DTYPE
+
+
 def test_prefill_workspace_size(lib):
     f = lib.gdn_chunk_prefill_workspace
     for act in (0, 1):

@@ -463,6 +463,37 @@ def test_split_choice(lengths):
         check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
 
 
+@pytest.mark.parametrize("case", ["small-bf16", "small-f32", "workload"])
+def test_raw_gates_equal_the_two_calls(case):
+    """gdn_chunk_prefill_raw (gates formed from a, b, A_log, dt_bias inside
+    the call: in the WY pass for bf16, by the gates kernel into the
+    workspace for fp32) equals gdn_prefill_gates + gdn_chunk_prefill bit for
+    bit, y and pool, on a ragged batch and on the varlen workload."""
+    rng = np.random.default_rng(95)
+    if case == "workload":
+        c = synth.PREFILL_VARLEN
+        Hk, Hv, Dk, Dv, P, act = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"], "bf16"
+        lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    else:
+        Hk, Hv, Dk, Dv, P, act = 2, 6, 64, 128, 7, case.split("-")[1]
+        lengths = [100, 37, 0, 5, 64]
+    pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P, act=act)
+    d = DT[act]
+    q, k, v, a, b = (to_dev(inp[n], d, DEV) for n in ("q", "k", "v", "a", "b"))
+    A_log, dtb = to_dev(inp["A_log"], torch.float32, DEV), to_dev(inp["dt_bias"], torch.float32, DEV)
+    ci = to_dev(inp["cache_indices"], torch.int64, DEV)
+    cu = to_dev(inp["cu_seqlens"], torch.int64, DEV)
+    pool_two = to_dev(pool0, torch.float32, DEV)
+    g, beta = gdn.gdn_prefill_gates(a, b, A_log, dtb)
+    y_two = gdn.gdn_chunk_prefill(q, k, v, g, beta, pool_two, ci, cu, chunk=64)
+    pool_raw = to_dev(pool0, torch.float32, DEV)
+    y_raw = gdn.gdn_chunk_prefill_raw(q, k, v, a, b, A_log, dtb, pool_raw, ci, cu, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(y_raw, y_two)
+    assert torch.equal(pool_raw, pool_two)
+
+
 @pytest.mark.parametrize("route", ["plain", "gated", "noalloc"])
 def test_keep_state_reads_the_pool_only(route):
     """GDN_KEEP_STATE: the pool is bit for bit unchanged and y is bit for
