@@ -229,15 +229,27 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
                                                              int N_s, int64_t T_tot, int C,
                                                              int* __restrict__ scs, int wg_per_seq,
                                                              int num_cu, int allow_split) {
+  // The first NC sequences' chunk counts and the first NC positions of the
+  // order stay in LDS after the pass that forms them (every later pass
+  // would otherwise wait on another round of global loads); beyond NC they
+  // are read again.
+  constexpr int NC = 4 * NT;
   __shared__ int part[NT];
+  __shared__ int ncache[NC], ocache[NC];
   const int tid = threadIdx.x;
+  auto nch_global = [&](int s) -> int {
+    int64_t b0, len;
+    seq_bounds(cu, s, T_tot, b0, len);
+    return static_cast<int>((len + C - 1) / C);
+  };
+  auto nch = [&](int s) -> int { return s < NC ? ncache[s] : nch_global(s); };
   const int per_t = (N_s + NT - 1) / NT;  // sequences (positions) per thread
   const int s0 = tid * per_t;
   int local = 0;
   for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
-    int64_t b0, len;
-    seq_bounds(cu, s, T_tot, b0, len);
-    local += static_cast<int>((len + C - 1) / C);
+    const int n = nch_global(s);
+    if (s < NC) ncache[s] = n;
+    local += n;
   }
   part[tid] = local;
   __syncthreads();
@@ -255,9 +267,7 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   __syncthreads();
   for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
     scs[s] = run;
-    int64_t b0, len;
-    seq_bounds(cu, s, T_tot, b0, len);
-    const int n = static_cast<int>((len + C - 1) / C);
+    const int n = nch(s);
     run += n;
     atomicAdd(&bucket[32 - __clz(n)], 1);
     atomicMax(&top_key, (static_cast<unsigned long long>(n) << 32) | (0xffffffffu - static_cast<unsigned>(s)));
@@ -278,12 +288,12 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   __syncthreads();
   int* ord = scs + N_s + 1;
   for (int s = s0; s < s0 + per_t && s < N_s; ++s) {
-    int64_t b0, len;
-    seq_bounds(cu, s, T_tot, b0, len);
-    const int n = static_cast<int>((len + C - 1) / C);
-    ord[s == top_s ? 0 : atomicAdd(&bucket[32 - __clz(n)], 1)] = s;
+    const int r = s == top_s ? 0 : atomicAdd(&bucket[32 - __clz(nch(s))], 1);
+    ord[r] = s;
+    if (r < NC) ocache[r] = s;
   }
   __syncthreads();
+  auto ord_at = [&](int r) -> int { return r < NC ? ocache[r] : ord[r]; };
   // wgp[r]: chunk-loop workgroups before position r of that order.  The
   // first sequences of the order get two per (value head, column block) --
   // each computing half of the columns with half of its waves, a shorter
@@ -296,21 +306,14 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   if (tid == 0) {
     const int64_t idle = static_cast<int64_t>(num_cu) - static_cast<int64_t>(N_s) * wg_per_seq;
     int kk = allow_split && idle > 0 ? static_cast<int>(min(idle / wg_per_seq, static_cast<int64_t>(N_s))) : 0;
-    if (kk > 0 && kk < N_s) {
-      int64_t b0, l0, l1;
-      seq_bounds(cu, ord[0], T_tot, b0, l0);
-      seq_bounds(cu, ord[kk], T_tot, b0, l1);
-      if (20 * ((l1 + C - 1) / C) > 17 * ((l0 + C - 1) / C)) kk = 0;
-    }
+    if (kk > 0 && kk < N_s && 20 * nch(ord_at(kk)) > 17 * nch(ord_at(0))) kk = 0;
     split_n = kk;
   }
   __syncthreads();
   const int room = split_n;  // positions that split
   int loc = 0;
   for (int r = s0; r < s0 + per_t && r < N_s; ++r) {
-    int64_t b0, len;
-    seq_bounds(cu, ord[r], T_tot, b0, len);
-    const bool sp = r < room && len > 0;
+    const bool sp = r < room && nch(ord_at(r)) > 0;
     loc += sp ? 2 * wg_per_seq : wg_per_seq;
   }
   part[tid] = loc;
@@ -324,9 +327,7 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   int wrun = part[tid] - loc;
   for (int r = s0; r < s0 + per_t && r < N_s; ++r) {
     wgp[r] = wrun;
-    int64_t b0, len;
-    seq_bounds(cu, ord[r], T_tot, b0, len);
-    const bool sp = r < room && len > 0;
+    const bool sp = r < room && nch(ord_at(r)) > 0;
     wrun += sp ? 2 * wg_per_seq : wg_per_seq;
   }
   if (tid == NT - 1) wgp[N_s] = part[NT - 1];

@@ -373,12 +373,15 @@ def test_fixed_length_prefill(B, T, Hk, Hv, Dk, Dv, chunk, act):
     assert torch.equal(y2.view(B, T, Hv, Dv), y)
 
 
-def test_many_short_sequences():
-    """2,500 sequences of 0..6 tokens (more sequences than the chunk-map scan
-    has threads, so each thread scans a range): every sequence and slot
-    matches the oracle, empty sequences leave their slots untouched."""
-    rng = np.random.default_rng(77)
-    N, Hk, Hv, Dk, Dv = 2500, 1, 2, 32, 32
+@pytest.mark.parametrize("N", [2500, 5000])
+def test_many_short_sequences(N):
+    """2,500 or 5,000 sequences of 0..6 tokens (more sequences than the
+    chunk-map scan has threads, so each thread scans a range; past 4,096 the
+    map reads counts and order back from memory instead of LDS): every
+    sequence and slot matches the oracle, empty sequences leave their slots
+    untouched."""
+    rng = np.random.default_rng(77 + N)
+    Hk, Hv, Dk, Dv = 1, 2, 32, 32
     lengths = rng.integers(0, 7, size=N)
     P = N + 5
     pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
