@@ -224,18 +224,32 @@ __global__ __launch_bounds__(256) void gdn_fixed_index_kernel(int64_t* __restric
   if (i < B) ci[i] = i;
 }
 
+// LDS of the chunk map for NT threads.  The first NC sequences' chunk
+// counts and the first NC positions of the order stay there after the pass
+// that forms them (every later pass would otherwise wait on another round
+// of global loads); beyond NC they are read again.
 template <int NT>
-__global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
-                                                             int N_s, int64_t T_tot, int C,
-                                                             int* __restrict__ scs, int wg_per_seq,
-                                                             int num_cu, int allow_split) {
-  // The first NC sequences' chunk counts and the first NC positions of the
-  // order stay in LDS after the pass that forms them (every later pass
-  // would otherwise wait on another round of global loads); beyond NC they
-  // are read again.
-  constexpr int NC = 4 * NT;
-  __shared__ int part[NT];
-  __shared__ int ncache[NC], ocache[NC];
+struct MapLds {
+  static constexpr int NC = 4 * NT;
+  int part[NT];
+  int ncache[NC], ocache[NC];
+  int bucket[33];  // sequences per bit length of the chunk count (0..32)
+  int split_n;
+  unsigned long long top_key;  // the longest sequence (ties: the first)
+};
+
+// The chunk map on NT threads of one workgroup (all of them call it).
+template <int NT>
+__device__ __forceinline__ void chunk_map_body(MapLds<NT>& m, const int64_t* __restrict__ cu, int N_s,
+                                               int64_t T_tot, int C, int* __restrict__ scs, int wg_per_seq,
+                                               int num_cu, int allow_split) {
+  constexpr int NC = MapLds<NT>::NC;
+  int* part = m.part;
+  int* ncache = m.ncache;
+  int* ocache = m.ocache;
+  int* bucket = m.bucket;
+  unsigned long long& top_key = m.top_key;
+  int& split_n = m.split_n;
   const int tid = threadIdx.x;
   auto nch_global = [&](int s) -> int {
     int64_t b0, len;
@@ -260,8 +274,6 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
     __syncthreads();
   }
   int run = part[tid] - local;  // exclusive prefix of this thread's range
-  __shared__ int bucket[33];       // sequences per bit length of the chunk count (0..32)
-  __shared__ unsigned long long top_key;  // the longest sequence (ties: the first)
   if (tid < 33) bucket[tid] = 0;
   if (tid == 0) top_key = 0ull;
   __syncthreads();
@@ -302,7 +314,6 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
   // slower), and only if that shortens the batch: the longest sequence left
   // whole must be clearly shorter than the longest split one.
   int* wgp = ord + N_s;
-  __shared__ int split_n;
   if (tid == 0) {
     const int64_t idle = static_cast<int64_t>(num_cu) - static_cast<int64_t>(N_s) * wg_per_seq;
     int kk = allow_split && idle > 0 ? static_cast<int>(min(idle / wg_per_seq, static_cast<int64_t>(N_s))) : 0;
@@ -331,6 +342,15 @@ __global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __rest
     wrun += sp ? 2 * wg_per_seq : wg_per_seq;
   }
   if (tid == NT - 1) wgp[N_s] = part[NT - 1];
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void gdn_chunk_map_kernel(const int64_t* __restrict__ cu,
+                                                             int N_s, int64_t T_tot, int C,
+                                                             int* __restrict__ scs, int wg_per_seq,
+                                                             int num_cu, int allow_split) {
+  __shared__ MapLds<NT> m;
+  chunk_map_body<NT>(m, cu, N_s, T_tot, C, scs, wg_per_seq, num_cu, allow_split);
 }
 
 // ----------------------------------------------------------------------------
@@ -982,7 +1002,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     const float* __restrict__ g, const BT* __restrict__ beta, const int64_t* __restrict__ cu,
     const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
-    bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac, RawGates rg) {
+    bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac, RawGates rg, int own_map,
+    int* __restrict__ map_out, int wg_per_seq, int num_cu, int allow_split) {
   static_assert(!RAW || !COMBA, "raw gates: GDN only");
   constexpr int MT = CT / 16, KB = DK / 32;
   constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 3 * CT + 4;
@@ -995,15 +1016,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
 
   const int c = blockIdx.x / Hk;
   const int hk = blockIdx.x - c * Hk;
-  if (c >= scs[N_s]) return;
-  int lo = 0, hi = N_s;  // largest s with scs[s] <= c
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (scs[mid] <= c) lo = mid; else hi = mid;
+  int lo = 0, cbase;  // the sequence holding chunk c and its first chunk
+  if (own_map) {
+    // This launch also makes the chunk map the chunk loop reads (its last
+    // workgroup, in the storage of sA); every other wave finds its chunk
+    // from cu_seqlens itself: N_s <= 64, a lane per sequence.
+    static_assert(sizeof(MapLds<64>) <= sizeof(sA), "the chunk map's LDS lives in sA");
+    if (blockIdx.x == gridDim.x - 1) {
+      chunk_map_body<64>(*reinterpret_cast<MapLds<64>*>(&sA[0][0]), cu, N_s, T_tot, C, map_out, wg_per_seq,
+                         num_cu, allow_split);
+      return;
+    }
+    const int ln = threadIdx.x;
+    int nl = 0;
+    if (ln < N_s) {
+      int64_t bx, lx;
+      seq_bounds(cu, ln, T_tot, bx, lx);
+      nl = static_cast<int>((lx + C - 1) / C);
+    }
+    int incl = nl;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off);
+      if (ln >= off) incl += u;
+    }
+    const int excl = incl - nl;
+    if (c >= __shfl(incl, 63)) return;
+    lo = 63 - __clzll(__ballot(ln < N_s && excl <= c));  // largest such s
+    cbase = __shfl(excl, lo);
+  } else {
+    if (c >= scs[N_s]) return;
+    int hi = N_s;  // largest s with scs[s] <= c
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (scs[mid] <= c) lo = mid; else hi = mid;
+    }
+    cbase = scs[lo];
   }
   int64_t b0, len;
   seq_bounds(cu, lo, T_tot, b0, len);
-  const int64_t j0 = static_cast<int64_t>(c - scs[lo]) * C;
+  const int64_t j0 = static_cast<int64_t>(c - cbase) * C;
   const int64_t t0 = b0 + j0;
   const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
   const int HG = Hv / Hk;
@@ -1866,18 +1918,22 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   const size_t main_blocks = static_cast<size_t>(N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
   if constexpr (std::is_same<T, bf16>::value) {
-    const dim3 wy_grid(static_cast<unsigned>(maxc * static_cast<size_t>(Hk)));
+    // up to 64 sequences: the WY launch makes the chunk map too (one more workgroup)
+    const int own = N_s <= 64 ? 1 : 0;
+    if (!own) chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
+    const dim3 wy_grid(static_cast<unsigned>(maxc * static_cast<size_t>(Hk) + own));
     if (raw)  // the gates formed inside the WY pass
       hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, false, float, true>), wy_grid, dim3(64), 0, stream,
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
                          static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), cu, scs, N_s, T_tot,
-                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, *raw);
+                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, *raw, own, scs, per_seq, cu_count(),
+                         split ? 1 : 0);
     else
       hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), wy_grid, dim3(64), 0, stream, static_cast<const bf16*>(q),
                          static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr), g, beta, cu, scs, N_s, T_tot,
-                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, RawGates{});
+                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq, cu_count(),
+                         split ? 1 : 0);
     // the epilogue is fused when one workgroup covers a whole 128-column head
     if constexpr (NW == 8 && CW == 1) {
       if (epi && Dv == 128) {
@@ -1918,6 +1974,7 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
                          static_cast<const float*>(nullptr), 0.0f, keep);
   } else {
     if (raw) return GDN_ERR_UNSUPPORTED;  // fp32 activations take their gates from gdn_prefill_gates
+    chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
     hipLaunchKernelGGL((gdn_wy_kernel<T, DK, CT>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                        stream, static_cast<const T*>(q), static_cast<const T*>(k), g, beta, cu, scs, N_s,
                        T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, Pl, fac);
@@ -2040,7 +2097,7 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
   hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
                      stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
-                     Th, Tl, Ph, fac, RawGates{});
+                     Th, Tl, Ph, fac, RawGates{}, 0, scs, per_seq, cu_count(), split ? 1 : 0);
   if (split)
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true, true>),
                        dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,

@@ -250,15 +250,22 @@ def test_decode_loop_matches_prefill():
 def test_varlen_prefill_workload_sampled():
     """Varlen prefill workload: 8 sequences of U[512, 4096] tokens, Hk=16,
     Hv=48, Dk=Dv=128, bf16, chunk 64, pool of 16 warmed slots, random
-    cache_indices.  The whole batch runs on the GPU; the oracle checks 3
-    sequences on 6 value heads (key heads 0 and 15)."""
+    cache_indices, run as the bench runs it (gdn_chunk_prefill_raw: the
+    gates from raw a, b inside the call).  The whole batch runs on the GPU;
+    the oracle checks 3 sequences on 6 value heads (key heads 0 and 15)."""
     c = synth.PREFILL_VARLEN
     rng = np.random.default_rng(0)
     Hk, Hv, Dk, Dv, P = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"]
     lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
     pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv)
     inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
-    pool, y = _run_gpu(inp, pool0, c["chunk"], "bf16")
+    bf = torch.bfloat16
+    pool = to_dev(pool0, torch.float32, DEV)
+    y = gdn.gdn_chunk_prefill_raw(*(to_dev(inp[n], bf, DEV) for n in ("q", "k", "v", "a", "b")),
+                                  to_dev(inp["A_log"], torch.float32, DEV), to_dev(inp["dt_bias"], torch.float32, DEV),
+                                  pool, to_dev(inp["cache_indices"], torch.int64, DEV),
+                                  to_dev(inp["cu_seqlens"], torch.int64, DEV), chunk=c["chunk"])
+    torch.cuda.synchronize()
     yv = to_np(y)
     assert not np.isnan(yv).any()
     g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
