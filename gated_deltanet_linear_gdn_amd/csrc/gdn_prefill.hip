@@ -2094,10 +2094,12 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   const size_t main_blocks = static_cast<size_t>(a.N_s) * per_seq * (split ? 2 : 1);
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
-  chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
-  hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks)), dim3(64), 0,
-                     stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
-                     Th, Tl, Ph, fac, RawGates{}, 0, scs, per_seq, cu_count(), split ? 1 : 0);
+  // up to 64 sequences: the WY launch makes the chunk map too (one more workgroup)
+  const int own = a.N_s <= 64 ? 1 : 0;
+  if (!own) chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
+  hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks + own)), dim3(64),
+                     0, stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
+                     Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq, cu_count(), split ? 1 : 0);
   if (split)
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true, true>),
                        dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,
