@@ -16,11 +16,14 @@
 // rescaled by the cumulative decay (no 1/gamma anywhere).
 //
 // Kernels (gfx950, wave64, v_mfma_f32_16x16x32_bf16 for the contractions):
-//  1. gdn_chunk_map_kernel: scan over cu_seqlens -> first chunk of each
-//     sequence (device side, no host sync).
+//  1. The chunk map: scan over cu_seqlens -> first chunk of each sequence
+//     and the order the chunk loop takes them in (device side, no host
+//     sync); gdn_chunk_map_kernel, or with bf16 activations and up to 64
+//     sequences one more workgroup of the WY launch.
 //  2. The WY pass, all chunks of all sequences in parallel (nothing here
 //     depends on the state): q/k row norms, G, the Gram blocks K K^T and
-//     Q K^T on MFMA, A and P, T = (I + A)^-1, and per-token factors.
+//     Q K^T on MFMA, A and P, T = (I + A)^-1, and per-token factors (the
+//     gates themselves too when they come raw: gdn_chunk_prefill_raw).
 //     bf16 activations: gdn_wy_wave_kernel (section 4), one wave per
 //     (chunk, key head), blocked inverse.  fp32 activations: gdn_wy_kernel
 //     (section 2), one wave per (chunk, value head), column-parallel forward
@@ -33,8 +36,8 @@
 //     identically on both sides so no data moves between lanes).  Raw q/k/v
 //     enter the MFMAs exactly; norms and decays scale fp32 accumulators;
 //     operands that carry the state (S, R, Delta, T, and the scaled Delta of
-//     the update) are split into bf16 hi + lo halves so the state keeps
-//     fp32-grade accuracy.  bf16 activations: gdn_prefill_stream_kernel
+//     the update) are split into bf16 hi + lo halves so the state and the
+//     output keep fp32-grade accuracy.  bf16 activations: gdn_prefill_stream_kernel
 //     (section 5), operands streamed through LDS by asynchronous copies.
 //     fp32 activations: gdn_prefill_kernel (section 3), register fragments
 //     from global memory, hi/lo on both sides of every product.
