@@ -473,6 +473,43 @@ def test_split_choice(lengths):
         check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
 
 
+@pytest.mark.parametrize("Dk,keep", [(256, False), (96, True), (128, True)])
+def test_raw_gates_wide_heads_and_keep_state(Dk, keep):
+    """gdn_chunk_prefill_raw on other paths: Dk = 256 (32-token chunks) and
+    Dk = 96, and with GDN_KEEP_STATE (the pool read only): y and the pool bit
+    for bit those of gdn_prefill_gates + gdn_chunk_prefill with the same
+    flags, y within the bf16 bounds of the oracle on one sequence."""
+    rng = np.random.default_rng(96 + Dk)
+    Hk, Hv, Dv, P = 2, 4, 64, 5
+    lengths = [70, 0, 33, 129]
+    pool0 = (0.3 * rng.standard_normal((P, Hv, Dv, Dk))).astype(np.float32)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    bf = torch.bfloat16
+    q, k, v, a, b = (to_dev(inp[n], bf, DEV) for n in ("q", "k", "v", "a", "b"))
+    A_log, dtb = to_dev(inp["A_log"], torch.float32, DEV), to_dev(inp["dt_bias"], torch.float32, DEV)
+    ci = to_dev(inp["cache_indices"], torch.int64, DEV)
+    cu = to_dev(inp["cu_seqlens"], torch.int64, DEV)
+    pool_two = to_dev(pool0, torch.float32, DEV)
+    g, beta = gdn.gdn_prefill_gates(a, b, A_log, dtb)
+    y_two = gdn.gdn_chunk_prefill(q, k, v, g, beta, pool_two, ci, cu, chunk=64, keep_state=keep)
+    pool_raw = to_dev(pool0, torch.float32, DEV)
+    y_raw = gdn.gdn_chunk_prefill_raw(q, k, v, a, b, A_log, dtb, pool_raw, ci, cu, chunk=64, keep_state=keep)
+    torch.cuda.synchronize()
+    assert torch.equal(y_raw, y_two)
+    assert torch.equal(pool_raw, pool_two)
+    if keep:
+        assert np.array_equal(to_np(pool_raw).astype(np.float32), pool0)
+    s = 3
+    idx = np.arange(inp["cu_seqlens"][s], inp["cu_seqlens"][s + 1])
+    slot = int(inp["cache_indices"][s])
+    g64, b64 = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    P_ref, y_ref = oracle.gdn_prefill(inp["q"][idx], inp["k"][idx], inp["v"][idx], g64[idx], b64[idx],
+                                      pool0[[slot]], [0], [0, len(idx)])
+    check_bf16_out(to_np(y_raw)[idx], y_ref, "raw y")
+    if not keep:
+        assert maxrel(to_np(pool_raw[slot]), P_ref[0]) <= 1e-3
+
+
 @pytest.mark.parametrize("case", ["small-bf16", "small-f32", "workload"])
 def test_raw_gates_equal_the_two_calls(case):
     """gdn_chunk_prefill_raw (gates formed from a, b, A_log, dt_bias inside
