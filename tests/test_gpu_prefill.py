@@ -285,6 +285,53 @@ def test_varlen_prefill_workload_sampled():
         assert np.array_equal(to_np(pool[slot]).astype(np.float32), pool0[slot])
 
 
+
+def test_one_sequence_of_65536_tokens_sampled():
+    """The longest chain the tests run: one sequence of 65,536 tokens (1,024
+    chunks, one after another) between two short ones, at the varlen
+    workload's heads (Hk=16, Hv=48, Dk=Dv=128, bf16, chunk 64), through
+    gdn_chunk_prefill_raw.  The oracle checks, on key head 9 (value heads
+    27..29), the long sequence's final state and every output row, and the
+    300-token sequence; and the one-token sequence on every head.  The unused
+    pool slot stays untouched."""
+    c = synth.PREFILL_VARLEN
+    rng = np.random.default_rng(65536)
+    Hk, Hv, Dk, Dv, P = c["Hk"], c["Hv"], c["Dk"], c["Dv"], 4
+    lengths = [300, 65536, 1]
+    pool0 = _warm_pool(rng, P, Hk, Hv, Dk, Dv)
+    inp = synth.prefill_inputs(rng, lengths, Hk, Hv, Dk, Dv, pool_size=P)
+    bf = torch.bfloat16
+    pool = to_dev(pool0, torch.float32, DEV)
+    y = gdn.gdn_chunk_prefill_raw(*(to_dev(inp[n], bf, DEV) for n in ("q", "k", "v", "a", "b")),
+                                  to_dev(inp["A_log"], torch.float32, DEV), to_dev(inp["dt_bias"], torch.float32, DEV),
+                                  pool, to_dev(inp["cache_indices"], torch.int64, DEV),
+                                  to_dev(inp["cu_seqlens"], torch.int64, DEV), chunk=c["chunk"])
+    torch.cuda.synchronize()
+    yv = to_np(y)
+    assert not np.isnan(yv).any()
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    cu = inp["cu_seqlens"]
+    hk = 9
+    hs = np.arange(hk * 3, hk * 3 + 3)
+    for s in (1, 0):
+        idx = np.arange(cu[s], cu[s + 1])
+        slot = int(inp["cache_indices"][s])
+        P_ref, y_ref = oracle.gdn_prefill(
+            inp["q"][idx][:, [hk]], inp["k"][idx][:, [hk]], inp["v"][idx][:, hs],
+            g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0], [0, len(idx)])
+        assert maxrel(to_np(pool[slot][hs]), P_ref[0]) <= 1e-3, s
+        check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}")
+    # the one-token sequence on every head
+    t = [int(cu[2])]
+    one = int(inp["cache_indices"][2])
+    P_ref, y_ref = oracle.gdn_prefill(inp["q"][t], inp["k"][t], inp["v"][t], g[t], beta[t], pool0[[one]], [0], [0, 1])
+    assert maxrel(to_np(pool[one]), P_ref[0]) <= 1e-3
+    check_bf16_out(yv[t], y_ref, "y of the one-token sequence")
+    unused = sorted(set(range(P)) - set(int(x) for x in inp["cache_indices"]))
+    assert len(unused) == 1
+    assert np.array_equal(to_np(pool[unused[0]]).astype(np.float32), pool0[unused[0]])
+
+
 GATED_CASES = [
     # lengths, Hk, Hv, Dk, Dv, chunk, act   (bf16 with Dv = 128: norm fused in the chunk loop)
     ([1, 64, 130, 0, 77], 2, 4, 128, 128, 64, "bf16"),
@@ -510,17 +557,22 @@ def test_raw_gates_wide_heads_and_keep_state(Dk, keep):
         assert maxrel(to_np(pool_raw[slot]), P_ref[0]) <= 1e-3
 
 
-@pytest.mark.parametrize("case", ["small-bf16", "small-f32", "workload"])
+@pytest.mark.parametrize("case", ["small-bf16", "small-f32", "workload", "many-bf16"])
 def test_raw_gates_equal_the_two_calls(case):
     """gdn_chunk_prefill_raw (gates formed from a, b, A_log, dt_bias inside
     the call: in the WY pass for bf16, by the gates kernel into the
     workspace for fp32) equals gdn_prefill_gates + gdn_chunk_prefill bit for
-    bit, y and pool, on a ragged batch and on the varlen workload."""
+    bit, y and pool, on a ragged batch, on the varlen workload, and on 300
+    sequences (more than the WY launch maps itself: the chunk map then runs
+    as a kernel of its own)."""
     rng = np.random.default_rng(95)
     if case == "workload":
         c = synth.PREFILL_VARLEN
         Hk, Hv, Dk, Dv, P, act = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"], "bf16"
         lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    elif case == "many-bf16":
+        Hk, Hv, Dk, Dv, P, act = 2, 4, 64, 64, 310, "bf16"
+        lengths = rng.integers(0, 150, size=300)
     else:
         Hk, Hv, Dk, Dv, P, act = 2, 6, 64, 128, 7, case.split("-")[1]
         lengths = [100, 37, 0, 5, 64]
