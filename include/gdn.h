@@ -503,8 +503,8 @@ int gdn_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
  * gdn_stream_copy - measurement helper: copies `bytes` bytes from src to dst
  * with one 16-byte non-temporal load and one 16-byte non-temporal store per
  * thread, the access pattern of the decode step's state stream.  Source:
- * KBench `comba_decode_step` page, perf_md (a bandwidth-bound step is judged
- * against a large stream copy measured on the same machine).  Its rate over
+ * KBench `comba_decode_step` page, perf_md (a bandwidth-bound step is
+ * compared with a large stream copy measured on the same machine).  Its rate over
  * 2 * bytes is the measured ceiling the streaming kernels are compared with.
  * src, dst: device memory, 16-byte aligned, not overlapping (GDN_ERR_ALIAS).
  * bytes: a multiple of 16 (else GDN_ERR_SHAPE); 0 is a no-op; at most
