@@ -645,17 +645,19 @@ def test_comba_prefill_one_hot_keys_closed_form():
     beta = np.array([[0.8], [0.6]])
     g = np.array([[-0.3], [-0.7]])
     a1, a2 = np.exp(g[0, 0]), np.exp(g[1, 0])
-    P, o = oracle.comba_prefill(q, k, v, p, beta, g, np.zeros((1, 1, K, V)), [0], [0, 2], scale=s)
     u1 = 0.8 * v[0, 0]
     row0 = a2 * u1
     u2 = 0.6 * (v[1, 0] - row0)
     ref = np.zeros((K, V))
     ref[0], ref[1] = row0, u2
-    np.testing.assert_allclose(P[0, 0], ref, rtol=1e-14, atol=1e-15)
-    np.testing.assert_allclose(o[0, 0], s * q[0, 0, 0] * u1, rtol=1e-14, atol=1e-15)
-    np.testing.assert_allclose(o[1, 0], s * (q[1, 0, 0] * row0 + q[1, 0, 1] * u2), rtol=1e-14, atol=1e-15)
+    # an explicit query scale, and the spec's default K^-1/2 when none is given
+    for arg, sc in ((s, s), (None, K ** -0.5)):
+        P, o = oracle.comba_prefill(q, k, v, p, beta, g, np.zeros((1, 1, K, V)), [0], [0, 2], scale=arg)
+        np.testing.assert_allclose(P[0, 0], ref, rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(o[0, 0], sc * q[0, 0, 0] * u1, rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(o[1, 0], sc * (q[1, 0, 0] * row0 + q[1, 0, 1] * u2), rtol=1e-14, atol=1e-15)
     Pswap, _ = oracle.comba_prefill(q, p, v, k, beta, g, np.zeros((1, 1, K, V)), [0], [0, 2], scale=s)
-    assert not np.allclose(Pswap, P)
+    assert not np.allclose(Pswap, ref)
 
 
 def test_comba_prefill_split_and_index_handling():
