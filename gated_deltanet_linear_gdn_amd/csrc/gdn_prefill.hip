@@ -227,6 +227,40 @@ __global__ __launch_bounds__(256) void gdn_fixed_index_kernel(int64_t* __restric
   if (i < B) ci[i] = i;
 }
 
+// A fixed-length batch with bf16 activations (gdn_chunk_prefill_fixed):
+// every sequence is T tokens long and owns the state slot of its index.
+// The WY launch then finds each chunk's sequence by division, and its last
+// workgroup writes cu_seqlens and cache_indices (for the chunk loop) and
+// the chunk map, so no index or map kernel runs ahead of it.
+struct FixedBatch {
+  int64_t T;     // tokens per sequence (0: a varlen batch)
+  int64_t* cu;   // [N_s + 1], written by the WY launch
+  int64_t* ci;   // [N_s], written by the WY launch
+};
+
+// The chunk map of a fixed-length batch, on the threads of one workgroup:
+// what chunk_map_body computes when every sequence has the same length
+// (the order is the identity, which is longest first; the sequences split
+// in halves all together or not at all, since none is longer than another).
+__device__ __forceinline__ void fixed_map_body(const FixedBatch& fb, int N_s, int C, int* __restrict__ scs,
+                                               int wg_per_seq, int num_cu, int allow_split) {
+  const int per = static_cast<int>((fb.T + C - 1) / C);
+  const int64_t idle = static_cast<int64_t>(num_cu) - static_cast<int64_t>(N_s) * wg_per_seq;
+  const bool all_split = allow_split && idle > 0 && idle / wg_per_seq >= N_s;
+  const int wg = all_split ? 2 * wg_per_seq : wg_per_seq;
+  int* ord = scs + N_s + 1;
+  int* wgp = ord + N_s;
+  for (int i = threadIdx.x; i <= N_s; i += blockDim.x) {
+    fb.cu[i] = static_cast<int64_t>(i) * fb.T;
+    scs[i] = i * per;
+    wgp[i] = i * wg;
+    if (i < N_s) {
+      fb.ci[i] = i;
+      ord[i] = i;
+    }
+  }
+}
+
 // LDS of the chunk map for NT threads.  The first NC sequences' chunk
 // counts and the first NC positions of the order stay there after the pass
 // that forms them (every later pass would otherwise wait on another round
@@ -1006,7 +1040,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     const int* __restrict__ scs,
     int N_s, int64_t T_tot, int Hk, int Hv, int C, float scale, int l2norm, bf16* __restrict__ Th,
     bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac, RawGates rg, int own_map,
-    int* __restrict__ map_out, int wg_per_seq, int num_cu, int allow_split) {
+    int* __restrict__ map_out, int wg_per_seq, int num_cu, int allow_split, FixedBatch fb) {
   static_assert(!RAW || !COMBA, "raw gates: GDN only");
   constexpr int MT = CT / 16, KB = DK / 32;
   constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 3 * CT + 4;
@@ -1023,13 +1057,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   if (own_map) {
     // This launch also makes the chunk map the chunk loop reads (its last
     // workgroup, in the storage of sA); every other wave finds its chunk
-    // from cu_seqlens itself: N_s <= 64, a lane per sequence.
+    // itself: by division in a fixed-length batch (whose cu_seqlens the last
+    // workgroup is still writing), else from cu_seqlens, N_s <= 64, a lane
+    // per sequence.
     static_assert(sizeof(MapLds<64>) <= sizeof(sA), "the chunk map's LDS lives in sA");
     if (blockIdx.x == gridDim.x - 1) {
-      chunk_map_body<64>(*reinterpret_cast<MapLds<64>*>(&sA[0][0]), cu, N_s, T_tot, C, map_out, wg_per_seq,
-                         num_cu, allow_split);
+      if (fb.T > 0)
+        fixed_map_body(fb, N_s, C, map_out, wg_per_seq, num_cu, allow_split);
+      else
+        chunk_map_body<64>(*reinterpret_cast<MapLds<64>*>(&sA[0][0]), cu, N_s, T_tot, C, map_out, wg_per_seq,
+                           num_cu, allow_split);
       return;
     }
+  }
+  if (own_map && fb.T > 0) {
+    const int per = static_cast<int>((fb.T + C - 1) / C);
+    lo = c / per;
+    if (lo >= N_s) return;
+    cbase = lo * per;
+  } else if (own_map) {
     const int ln = threadIdx.x;
     int nl = 0;
     if (ln < N_s) {
@@ -1057,7 +1103,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     cbase = scs[lo];
   }
   int64_t b0, len;
-  seq_bounds(cu, lo, T_tot, b0, len);
+  if (fb.T > 0) {
+    b0 = static_cast<int64_t>(lo) * fb.T;
+    len = fb.T;
+  } else {
+    seq_bounds(cu, lo, T_tot, b0, len);
+  }
   const int64_t j0 = static_cast<int64_t>(c - cbase) * C;
   const int64_t t0 = b0 + j0;
   const int n = static_cast<int>(len - j0 < C ? len - j0 : C);
@@ -1902,7 +1953,8 @@ template <typename T, int DK, int CT, int NW, int CW = 1>
 int launch_all(const void* q, const void* k, const void* v, const float* g, const float* beta,
                float* pool, int64_t pool_size, const int64_t* ci, const int64_t* cu, int N_s,
                int64_t T_tot, int Hk, int Hv, int Dv, int chunk, float scale, int l2norm, void* y,
-               char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw, hipStream_t stream, unsigned opts) {
+               char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw, const FixedBatch* fixb,
+               hipStream_t stream, unsigned opts) {
   const bool one_chunk = (opts & kOneChunk) != 0;
   const int keep = (opts & kKeepState) ? 1 : 0;
   int* scs = reinterpret_cast<int*>(ws + L.scs);
@@ -1922,21 +1974,25 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   if (wy_blocks > 0x7fffffffu || main_blocks > 0x7fffffffu) return GDN_ERR_SHAPE;
   (void)hipGetLastError();
   if constexpr (std::is_same<T, bf16>::value) {
-    // up to 64 sequences: the WY launch makes the chunk map too (one more workgroup)
-    const int own = N_s <= 64 ? 1 : 0;
+    // up to 64 sequences, or a fixed-length batch (whose cu_seqlens and
+    // cache_indices it writes as well): the WY launch makes the chunk map
+    // too (one more workgroup)
+    const int own = N_s <= 64 || fixb ? 1 : 0;
     if (!own) chunk_map(cu, N_s, T_tot, chunk, scs, per_seq, split, stream);
+    const FixedBatch fb = fixb ? *fixb : FixedBatch{0, nullptr, nullptr};
+    const int64_t* wy_cu = fixb ? nullptr : cu;  // not read in a fixed-length batch
     const dim3 wy_grid(static_cast<unsigned>(maxc * static_cast<size_t>(Hk) + own));
     if (raw)  // the gates formed inside the WY pass
       hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, false, float, true>), wy_grid, dim3(64), 0, stream,
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
-                         static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), cu, scs, N_s, T_tot,
-                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, *raw, own, scs, per_seq, cu_count(),
-                         split ? 1 : 0);
+                         static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), wy_cu, scs, N_s,
+                         T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, *raw, own, scs, per_seq, cu_count(),
+                         split ? 1 : 0, fb);
     else
       hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT>), wy_grid, dim3(64), 0, stream, static_cast<const bf16*>(q),
-                         static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr), g, beta, cu, scs, N_s, T_tot,
-                         Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq, cu_count(),
-                         split ? 1 : 0);
+                         static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr), g, beta, wy_cu, scs, N_s,
+                         T_tot, Hk, Hv, chunk, scale, l2norm, Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq,
+                         cu_count(), split ? 1 : 0, fb);
     // the epilogue is fused when one workgroup covers a whole 128-column head
     if constexpr (NW == 8 && CW == 1) {
       if (epi && Dv == 128) {
@@ -1999,7 +2055,7 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw,
-                hipStream_t stream, unsigned opts) {
+                const FixedBatch* fixb, hipStream_t stream, unsigned opts) {
   // bf16: the streamed LDS kernel, up to 128 value columns (eight waves) per
   // workgroup so each chunk operand is fetched once per 128 columns.  fp32
   // activations: the register-fragment kernel, 64 (four waves, up to 512
@@ -2007,13 +2063,13 @@ int dispatch_nw(int Dv, const void* q, const void* k, const void* v, const float
   if constexpr (std::is_same<T, bf16>::value) {
     if (Dv % 128 == 0)
       return launch_all<T, DK, CT, 8, 1>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                         chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                         chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
   }
   if (Dv % 64 == 0)
     return launch_all<T, DK, CT, 4>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                    chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                    chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
   return launch_all<T, DK, CT, 2>(q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, Dv,
-                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
 }
 
 template <typename T, int DK>
@@ -2021,16 +2077,16 @@ int dispatch_ct(int CT, int Dv, const void* q, const void* k, const void* v, con
                 const float* beta, float* pool, int64_t pool_size, const int64_t* ci,
                 const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv, int chunk, float scale,
                 int l2norm, void* y, char* ws, const Layout& L, const Epilogue* epi, const RawGates* raw,
-                hipStream_t stream, unsigned opts) {
+                const FixedBatch* fixb, hipStream_t stream, unsigned opts) {
   if constexpr (DK > 128) {  // 32-row tiles only (effective_chunk)
     return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
   } else {
     if (CT == 32)
       return dispatch_nw<T, DK, 32>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                    chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                    chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
     return dispatch_nw<T, DK, 64>(Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv,
-                                  chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+                                  chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
   }
 }
 
@@ -2039,20 +2095,21 @@ int dispatch_dk(int Dk, int CT, int Dv, const void* q, const void* k, const void
                 const float* g, const float* beta, float* pool, int64_t pool_size,
                 const int64_t* ci, const int64_t* cu, int N_s, int64_t T_tot, int Hk, int Hv,
                 int chunk, float scale, int l2norm, void* y, char* ws, const Layout& L,
-                const Epilogue* epi, const RawGates* raw, hipStream_t stream, unsigned opts) {
+                const Epilogue* epi, const RawGates* raw, const FixedBatch* fixb, hipStream_t stream,
+                unsigned opts) {
   switch (Dk) {
-    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+    case 32: return dispatch_ct<T, 32>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+    case 64: return dispatch_ct<T, 64>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+    case 128: return dispatch_ct<T, 128>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+    case 96: return dispatch_ct<T, 96>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
   }
   // wider heads: bf16 activations only (the fp32 kernels would spill at these widths)
   if constexpr (std::is_same<T, bf16>::value) {
     switch (Dk) {
-      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
-      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, stream, opts);
+      case 160: return dispatch_ct<T, 160>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+      case 192: return dispatch_ct<T, 192>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+      case 224: return dispatch_ct<T, 224>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
+      case 256: return dispatch_ct<T, 256>(CT, Dv, q, k, v, g, beta, pool, pool_size, ci, cu, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, y, ws, L, epi, raw, fixb, stream, opts);
     }
   }
   return GDN_ERR_UNSUPPORTED;
@@ -2102,7 +2159,8 @@ int comba_launch(const CombaArgs& a, char* ws, const Layout& L, hipStream_t stre
   if (!own) chunk_map(a.cu, a.N_s, a.T_tot, a.chunk, scs, per_seq, split, stream);
   hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, true, bf16>), dim3(static_cast<unsigned>(wy_blocks + own)), dim3(64),
                      0, stream, a.q, a.k, a.p, a.g, a.beta, a.cu, scs, a.N_s, a.T_tot, a.H, a.H, a.chunk, a.scale, 0,
-                     Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq, cu_count(), split ? 1 : 0);
+                     Th, Tl, Ph, fac, RawGates{}, own, scs, per_seq, cu_count(), split ? 1 : 0,
+                     FixedBatch{0, nullptr, nullptr});
   if (split)
     hipLaunchKernelGGL((gdn_prefill_stream_kernel<DK, CT, NW, 1, false, true, true>),
                        dim3(static_cast<unsigned>(main_blocks)), dim3(64 * NW), 0, stream, a.q, a.k, a.p, a.v, a.pool,
@@ -2156,7 +2214,7 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
                   int chunk, float scale, unsigned flags, void* y, gdn_dtype act, void* workspace,
                   size_t workspace_bytes, const Epilogue* epi, hipStream_t stream,
                   bool check_only = false, int64_t max_len = 0, bool no_ws_checks = false,
-                  const RawGates* raw = nullptr) {
+                  const RawGates* raw = nullptr, const FixedBatch* fixb = nullptr) {
   if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 ||
       Hv % Hk != 0)
     return GDN_ERR_SHAPE;
@@ -2215,9 +2273,9 @@ int chunk_prefill(const void* q, const void* k, const void* v, const float* g, c
   const unsigned opts = (one_chunk ? kOneChunk : 0u) | ((flags & GDN_KEEP_STATE) ? kKeepState : 0u);
   if (act == GDN_BF16)
     return dispatch_dk<bf16>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, stream, opts);
+                             cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, fixb, stream, opts);
   return dispatch_dk<float>(Dk, CT, Dv, q, k, v, g, beta, state_pool, pool_size, cache_indices,
-                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, stream, opts);
+                            cu_seqlens, N_s, T_tot, Hk, Hv, chunk, scale, l2, y, ws, L, epi, raw, fixb, stream, opts);
 }
 
 }  // namespace
@@ -2462,6 +2520,12 @@ extern "C" int gdn_chunk_prefill_fixed(const void* q, const void* k, const void*
   const int rc = chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk,
                                Dv, chunk, scale, flags, y, act, workspace, main, nullptr, stream, true);
   if (rc != GDN_OK) return rc;
+  if (act == GDN_BF16) {  // the WY launch writes the index arrays and the chunk map
+    const FixedBatch fb{T, cu, ci};
+    return chunk_prefill(q, k, v, g, beta, state, B, ci, cu, B, static_cast<int64_t>(B) * T, Hk, Hv, Dk, Dv,
+                         chunk, scale, flags, y, act, workspace, main, nullptr, stream, false, T, false, nullptr,
+                         &fb);
+  }
   (void)hipGetLastError();
   hipLaunchKernelGGL(gdn_fixed_index_kernel, dim3(static_cast<unsigned>((B + 1 + 255) / 256)), dim3(256), 0,
                      stream, cu, ci, B, T);

@@ -358,7 +358,9 @@ size_t gdn_chunk_prefill_fixed_workspace(int B, int64_t T, int Hk, int Hv,
  * chunk, scale, flags: as for gdn_chunk_prefill.
  * workspace     device memory of at least gdn_chunk_prefill_fixed_workspace()
  *               bytes, 16-byte aligned; its contents are scratch (the call
- *               writes the index arrays into its end before the kernels run).
+ *               writes the index arrays into its end: with bf16 activations
+ *               the first kernel does, which also finds each chunk's
+ *               sequence by division; with fp32 ones a small kernel first).
  * Requirements: those of gdn_chunk_prefill.  B == 0 or T == 0 is a no-op.
  * When T fits one chunk (after the Dk > 128 cap) the call knows every
  * sequence is a single chunk and runs a chunk loop without next-chunk

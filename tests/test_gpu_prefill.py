@@ -392,6 +392,11 @@ FIXED_CASES = [
     (64, 16, 1, 4, 256, 128, 16, "bf16"),
     (64, 32, 2, 4, 64, 128, 32, "bf16"),
     (64, 7, 1, 4, 32, 128, 8, "bf16"),
+    # more sequences than one wave maps (the varlen call runs a chunk-map
+    # kernel; the fixed-length call finds every chunk's sequence by division)
+    (100, 9, 2, 4, 64, 64, 8, "bf16"),
+    (96, 8, 1, 4, 128, 128, 8, "bf16"),
+    (300, 3, 1, 2, 256, 128, 16, "bf16"),
 ]
 
 
