@@ -1562,19 +1562,38 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
                  : Sp + static_cast<size_t>(dvl(t)) * DK + m * 16 + kg * 4 + r;
   };
   f32x4 S[CW][DT];
+  if (!act) {
 #pragma unroll
-  for (int t = 0; t < CW; ++t)
+    for (int t = 0; t < CW; ++t)
 #pragma unroll
-    for (int m = 0; m < DT; ++m) {
-      if (!act) {
-        S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else if constexpr (COMBA) {
+      for (int m = 0; m < DT; ++m) S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if constexpr (COMBA) {
+#pragma unroll
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int m = 0; m < DT; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[t][m][r] = *s_at(t, m, r);
-      } else {
-        S[t][m] = *reinterpret_cast<const f32x4*>(s_at(t, m, 0));
-      }
-    }
+  } else if (keep) {
+    // a slot that is only read: plain cache policy (verify windows of 4
+    // tokens 4% faster than with non-temporal loads), as buffer loads so
+    // that the compiler cannot merge them with the other branch's loads of
+    // the same addresses and drop the non-temporal hint
+    const __amdgpu_buffer_rsrc_t srs = store_rsrc(Sp, static_cast<uint32_t>(BV) * DK * sizeof(float));
+#pragma unroll
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int m = 0; m < DT; ++m)
+        S[t][m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                srs, static_cast<int>((s_at(t, m, 0) - Sp) * sizeof(float)), 0, 0));
+  } else {
+    // written back at the end: non-temporal (committed windows of 4-8
+    // tokens 5% faster)
+#pragma unroll
+    for (int t = 0; t < CW; ++t)
+#pragma unroll
+      for (int m = 0; m < DT; ++m) S[t][m] = load_stream(s_at(t, m, 0));
+  }
 
   // lane parts of the transposing reads
   const int tr_row = kg * 4 + (l16 >> 2), tr_col = 4 * (l16 & 3);
