@@ -1982,7 +1982,11 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
   bf16* Ph = reinterpret_cast<bf16*>(ws + L.ph);
   bf16* Pl = reinterpret_cast<bf16*>(ws + L.pl);
   float* fac = reinterpret_cast<float*>(ws + L.fac);
-  const size_t maxc = static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
+  // chunks of the batch: at most T_tot/chunk + N_s (the layout's bound);
+  // exactly N_s ceil(T/chunk) in a fixed-length batch, whose WY launch then
+  // has no waves without a chunk
+  const size_t maxc = fixb ? static_cast<size_t>(N_s) * static_cast<size_t>((fixb->T + chunk - 1) / chunk)
+                           : static_cast<size_t>(T_tot / chunk) + static_cast<size_t>(N_s);
   const size_t wy_blocks = maxc * static_cast<size_t>(Hv);
   const int per_seq = Hv * (Dv / (16 * NW * CW));  // chunk-loop workgroups per sequence, unsplit
   // when CUs would sit idle, the longest sequences run as two half-width
