@@ -113,6 +113,10 @@ CASES = [
     ([90, 33, 1], 1, 2, 160, 128, 64, "bf16"),     # Dk = 160: runs 32-token chunks
     ([64, 41], 2, 2, 192, 96, 32, "bf16"),
     ([77, 12], 1, 3, 224, 128, 64, "bf16"),
+    # value heads per key head: 8, and 1
+    ([66, 130], 1, 8, 128, 128, 64, "bf16"),
+    ([129, 63], 4, 4, 128, 128, 64, "bf16"),
+    ([20, 5, 64], 3, 6, 64, 64, 8, "f32"),         # fp32, chunk 8, three key heads
 ]
 
 
