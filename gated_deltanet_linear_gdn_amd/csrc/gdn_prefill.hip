@@ -1574,11 +1574,14 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       for (int m = 0; m < DT; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[t][m][r] = *s_at(t, m, r);
-  } else if (keep) {
-    // a slot that is only read: plain cache policy (verify windows of 4
-    // tokens 4% faster than with non-temporal loads), as buffer loads so
-    // that the compiler cannot merge them with the other branch's loads of
-    // the same addresses and drop the non-temporal hint
+  } else if (keep || !SINGLE) {
+    // plain cache policy, as buffer loads so that the compiler cannot merge
+    // them with the other branch's loads of the same addresses and drop the
+    // non-temporal hint: for a slot that is only read (verify windows of 4
+    // tokens 4% faster than with non-temporal loads), and in the
+    // double-buffered loop (one workgroup per CU; non-temporal loads made
+    // committed windows of 64 tokens 8% slower there and the varlen batch no
+    // faster)
     const __amdgpu_buffer_rsrc_t srs = store_rsrc(Sp, static_cast<uint32_t>(BV) * DK * sizeof(float));
 #pragma unroll
     for (int t = 0; t < CW; ++t)
@@ -1587,8 +1590,8 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         S[t][m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 srs, static_cast<int>((s_at(t, m, 0) - Sp) * sizeof(float)), 0, 0));
   } else {
-    // written back at the end: non-temporal (committed windows of 4-8
-    // tokens 5% faster)
+    // the single-set loop (three workgroups per CU) on a slot it writes
+    // back: non-temporal (committed windows of 4-8 tokens 5% faster)
 #pragma unroll
     for (int t = 0; t < CW; ++t)
 #pragma unroll
