@@ -134,10 +134,6 @@ template <> struct Frag<bf16> {
     }
     return s;
   }
-  static __device__ __forceinline__ void load8_raw(const bf16* p, uint32_t (&out)[4]) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-  }
 };
 
 template <> struct Frag<float> {
@@ -851,12 +847,9 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
                :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
 }
 
-// Buffer store of one bf16 (dropped at or past `bytes`).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void* base, uint32_t bytes) {
+// Buffer resource for stores (and loads) dropped at or past `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, float x) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), rsrc, voff, 0, 0);
 }
 
 // A tile of ROWS rows; row r is ITEMS 16-byte items at byte offset
@@ -1582,7 +1575,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     // double-buffered loop (one workgroup per CU; non-temporal loads made
     // committed windows of 64 tokens 8% slower there and the varlen batch no
     // faster)
-    const __amdgpu_buffer_rsrc_t srs = store_rsrc(Sp, static_cast<uint32_t>(BV) * DK * sizeof(float));
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(Sp, static_cast<uint32_t>(BV) * DK * sizeof(float));
 #pragma unroll
     for (int t = 0; t < CW; ++t)
 #pragma unroll
@@ -1701,7 +1694,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
         for (int j = 0; j < Tiles_::Qcopy::PER; ++j) cPr.issue_one(rp, sPr, w, j);
       }
       if (ci > 0) {
-        const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci - 1), vy_bytes(ci - 1));
+        const __amdgpu_buffer_rsrc_t yr = buf_rsrc(y + vy_off(ci - 1), vy_bytes(ci - 1));
 #pragma unroll
         for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
       }
@@ -1768,7 +1761,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
     const i32x4 rv = v_rsrc(ci + 1);
     i32x4 rp;
     if constexpr (COMBA) rp = kq_rsrc(pr, ci + 1);
-    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(ci > 0 ? ci - 1 : 0), ci > 0 ? vy_bytes(ci - 1) : 0u);
+    const __amdgpu_buffer_rsrc_t yr = buf_rsrc(y + vy_off(ci > 0 ? ci - 1 : 0), ci > 0 ? vy_bytes(ci - 1) : 0u);
 
     // ---- B: Delta = T R (blocks above the diagonal skipped)
     bf16x8v Rh[CW][CKB], Rl[CW][CKB];
@@ -1881,7 +1874,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prefill_stream_kernel(
       z_load(nch - 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    const __amdgpu_buffer_rsrc_t yr = store_rsrc(y + vy_off(nch - 1), vy_bytes(nch - 1));
+    const __amdgpu_buffer_rsrc_t yr = buf_rsrc(y + vy_off(nch - 1), vy_bytes(nch - 1));
 #pragma unroll
     for (int it = 0; it < NYS; ++it) store_y_one(yr, it);
   }
