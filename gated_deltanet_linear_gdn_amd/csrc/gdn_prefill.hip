@@ -42,6 +42,7 @@
 //     fp32 activations: gdn_prefill_kernel (section 3), register fragments
 //     from global memory, hi/lo on both sides of every product.
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -1912,13 +1913,16 @@ struct Layout {
 // Compute units of the current device (cached per device; 256 if the query
 // fails): the chunk map's test for "every sequence split still fits".
 inline int cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];  // 0: not looked up yet (calls may come from several threads)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
