@@ -381,6 +381,29 @@ def bench_layer(steps, warmup, device):
                                                        workspace=ws), steps, warmup)
     fused_sec = _timed(lambda i: gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y,
                                                        workspace=ws, z=z, gamma=gam), steps, warmup)
+    # the whole layer prefill from the raw channels: gdn_conv_prefill (conv
+    # inside the WY pass) against the separate calls it replaces
+    A_log = _dev(inp["A_log"], torch.float32, device)
+    dtb = _dev(inp["dt_bias"], torch.float32, device)
+    wsc = torch.empty(gdn.gdn_conv_prefill_workspace(T, len(lengths), Hk, Hv, Dk, Dv, C),
+                      dtype=torch.uint8, device=device)
+
+    def conv_prefill(z_=None, g_=None):
+        gdn.gdn_conv_prefill(qkv, w, hist, a, b, A_log, dtb, pool, ci, cu, Hk, Hv, Dk, Dv, chunk=C, y=y,
+                             workspace=wsc, z=z_, gamma=g_)
+
+    def separate(gated):
+        gdn.gdn_conv_silu(qkv, w, hist, ci, cu, Hk, Hv, Dk, Dv, q, k, v)
+        if gated:
+            gdn.gdn_prefill_gates(a, b, A_log, dtb, g, beta)
+            gdn.gdn_chunk_prefill(q, k, v, g, beta, pool, ci, cu, chunk=C, y=y, workspace=ws, z=z, gamma=gam)
+        else:
+            gdn.gdn_chunk_prefill_raw(q, k, v, a, b, A_log, dtb, pool, ci, cu, chunk=C, y=y, workspace=ws)
+
+    cp_sec = _timed(lambda i: conv_prefill(), steps, warmup)
+    cp_gated_sec = _timed(lambda i: conv_prefill(z, gam), steps, warmup)
+    sep_sec = _timed(lambda i: separate(False), steps, warmup)
+    sep_gated_sec = _timed(lambda i: separate(True), steps, warmup)
     # decode step of the conv: one token for each of 256 sequences
     B = synth.DECODE_B256["B"]
     qkv_d = _dev(synth.layer_inputs(rng, B, Hk, Hv, Dk, Dv, 1)["qkv"], bf, device)
@@ -397,7 +420,8 @@ def bench_layer(steps, warmup, device):
     norm_bytes = 3 * T * Hv * Dv * 2 + Dv * 4
     return dict(T=T, conv_sec=conv_sec, conv_bytes=conv_bytes, convd_sec=convd_sec,
                 convd_bytes=convd_bytes, norm_sec=norm_sec, norm_bytes=norm_bytes,
-                plain_sec=plain_sec, fused_sec=fused_sec)
+                plain_sec=plain_sec, fused_sec=fused_sec, cp_sec=cp_sec, cp_gated_sec=cp_gated_sec,
+                sep_sec=sep_sec, sep_gated_sec=sep_gated_sec)
 
 
 def bench_conv_decode(steps, warmup, device):
@@ -801,7 +825,18 @@ def main():
                        "norm_GBps": round(lay["norm_bytes"] / lay["norm_sec"] / 1e9, 1),
                        "prefill_us": round(lay["plain_sec"] * 1e6, 2),
                        "prefill_gated_fused_us": round(lay["fused_sec"] * 1e6, 2),
-                       "prefill_then_norm_us": round((lay["plain_sec"] + lay["norm_sec"]) * 1e6, 2)}
+                       "prefill_then_norm_us": round((lay["plain_sec"] + lay["norm_sec"]) * 1e6, 2),
+                       "conv_prefill": {
+                           "workload": "gdn_conv_prefill: conv + SiLU inside the WY pass, gates from raw a, b, "
+                                       "the chunked recurrence (and the gated norm) in one call, against "
+                                       "gdn_conv_silu + gdn_chunk_prefill_raw (and gdn_conv_silu + "
+                                       "gdn_prefill_gates + the gated gdn_chunk_prefill) timed as one step",
+                           "us_per_call": round(lay["cp_sec"] * 1e6, 2),
+                           "separate_us_per_call": round(lay["sep_sec"] * 1e6, 2),
+                           "gated_us_per_call": round(lay["cp_gated_sec"] * 1e6, 2),
+                           "separate_gated_us_per_call": round(lay["sep_gated_sec"] * 1e6, 2),
+                           "tokens_per_s": round(lay["T"] / lay["cp_sec"], 1),
+                           "gated_tokens_per_s": round(lay["T"] / lay["cp_gated_sec"], 1)}}
     if not args.no_cpu_baseline and only is None:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

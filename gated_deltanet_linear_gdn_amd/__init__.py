@@ -111,6 +111,10 @@ def load_library():
     lib.gdn_conv_decode_step.restype = _i
     lib.gdn_conv_decode_step.argtypes = [_vp] * 10 + [_i] * 5 + [_f, ctypes.c_uint, _i, _vp, ctypes.c_size_t, _vp]
     lib.gdn_stream_copy.restype = _i
+    lib.gdn_conv_prefill_workspace.argtypes = [_i64, _i, _i, _i, _i, _i, _i]
+    lib.gdn_conv_prefill_workspace.restype = ctypes.c_size_t
+    lib.gdn_conv_prefill.argtypes = ([_vp] * 8 + [_i64, _vp, _vp, _i, _i64] + [_i] * 5
+                                     + [_f, ctypes.c_uint, _vp, _vp, _f, _vp, _i, _vp, ctypes.c_size_t, _vp])
     lib.gdn_stream_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
     return lib
@@ -562,6 +566,60 @@ def gdn_conv_silu(qkv, conv_w, conv_state, cache_indices, cu_seqlens, Hk, Hv, Dk
           _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v),
           _act_of(qkv), _stream(dev))
     return q, k, v
+
+
+def gdn_conv_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk=64) -> int:
+    """Bytes of workspace ``gdn_conv_prefill`` needs (bf16 activations)."""
+    return int(load_library().gdn_conv_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk))
+
+
+def gdn_conv_prefill(qkv, conv_w, conv_state, a, b, A_log, dt_bias, state_pool, cache_indices, cu_seqlens,
+                     Hk, Hv, Dk, Dv, chunk=64, scale=None, l2norm=True, keep_state=False, z=None, gamma=None,
+                     eps=1e-6, y=None, workspace=None):
+    """The layer's prefill from its raw channels in one call (see
+    ``gdn_conv_prefill`` in include/gdn.h): conv + SiLU of qkv [T, C] bf16
+    with the history ``conv_state`` [pool, C, 3] f32 updated in place, gates
+    from a, b [T,Hv] bf16 and A_log, dt_bias [Hv] f32, the chunked
+    recurrence on ``state_pool`` [pool, Hv, Dv, Dk] f32, and the gated norm
+    when z [T,Hv,Dv] bf16 and gamma [Dv] f32 are given.  Returns y."""
+    T, C = qkv.shape
+    dev, act = qkv.device, qkv.dtype
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError(f"qkv has {C} channels, expected 2*Hk*Dk + Hv*Dv = {2 * Hk * Dk + Hv * Dv}")
+    P = state_pool.shape[0]
+    N_s = cache_indices.shape[0]
+    if y is None:
+        y = torch.empty((T, Hv, Dv), dtype=act, device=dev)
+    _check("qkv", qkv, (T, C), act, dev)
+    _check("conv_w", conv_w, (C, 4), torch.float32, dev)
+    _check("conv_state", conv_state, (P, C, 3), torch.float32, dev)
+    _check("a", a, (T, Hv), act, dev)
+    _check("b", b, (T, Hv), act, dev)
+    _check("A_log", A_log, (Hv,), torch.float32, dev)
+    _check("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check("state_pool", state_pool, (P, Hv, Dv, Dk), torch.float32, dev)
+    _check("cache_indices", cache_indices, (N_s,), torch.int64, dev)
+    _check("cu_seqlens", cu_seqlens, (N_s + 1,), torch.int64, dev)
+    _check("y", y, (T, Hv, Dv), act, dev)
+    if (z is None) != (gamma is None):
+        raise ValueError("z and gamma go together")
+    if z is not None:
+        _check("z", z, (T, Hv, Dv), act, dev)
+        _check("gamma", gamma, (Dv,), torch.float32, dev)
+    need = gdn_conv_prefill_workspace(T, N_s, Hk, Hv, Dk, Dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+    sc = 0.0 if scale is None else float(scale)
+    flags = (GDN_QK_L2NORM if l2norm else 0) | (GDN_KEEP_STATE if keep_state else 0)
+    zp = None if z is None else _ptr(z)
+    gp = None if gamma is None else _ptr(gamma)
+    _call("gdn_conv_prefill", dev, _ptr(qkv), _ptr(conv_w), _ptr(conv_state), _ptr(a), _ptr(b), _ptr(A_log),
+          _ptr(dt_bias), _ptr(state_pool), P, _ptr(cache_indices), _ptr(cu_seqlens), N_s, T, Hk, Hv, Dk, Dv,
+          int(chunk), sc, flags, zp, gp, float(eps), _ptr(y), _act_of(qkv), _ptr(workspace), workspace.numel(),
+          _stream(dev))
+    return y
 
 
 def gdn_gated_rmsnorm(o, z, gamma, eps=1e-6, y=None):

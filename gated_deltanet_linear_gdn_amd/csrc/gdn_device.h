@@ -38,6 +38,15 @@ __device__ __forceinline__ void gates_of(float xa, float A_log, float braw, floa
   beta = 1.0f / (1.0f + expf(-braw));
 }
 
+// sigmoid and SiLU on the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32; a few ulp), for the elementwise layer kernels, which are
+// otherwise bound by the instruction sequences of an exact exp and an IEEE
+// division.  Saturates correctly: a large -x gives exp = inf and a
+// reciprocal of 0.  The conv prologue of the prefill calls these wherever it
+// runs, so its outputs agree bit for bit.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_fast(float x) { return x * sigmoid_fast(x); }
+
 // ---------------------------------------------------- activation loads/stores
 
 template <typename T> struct Act;

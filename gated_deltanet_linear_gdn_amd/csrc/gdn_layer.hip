@@ -92,12 +92,6 @@ __device__ __forceinline__ float pick3(const float (&e)[3], int k) {
   return k == 0 ? e[0] : (k == 1 ? e[1] : e[2]);
 }
 
-// sigmoid and SiLU on the hardware exponential and reciprocal (v_exp_f32,
-// v_rcp_f32; a few ulp): the elementwise kernels are otherwise bound by the
-// instruction sequences of an exact exp and an IEEE division.  Saturates
-// correctly: a large -x gives exp = inf and a reciprocal of 0.
-__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
-__device__ __forceinline__ float silu(float x) { return x * sigmoid_fast(x); }
 
 // Sequence bounds clamped to [0, T): out-of-contract entries never index
 // outside the buffers.
@@ -193,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_silu_kernel(
         pre = fmaf(rr[j + 1].get(i), w4[i][1], pre);
         pre = fmaf(rr[j + 2].get(i), w4[i][2], pre);
         pre = fmaf(rr[j + 3].get(i), w4[i][3], pre);
-        out[i] = silu(pre);
+        out[i] = silu_fast(pre);
       }
       Vec8<T>::store(orow + static_cast<size_t>(ts + j) * ostride + oc, out);
     }
@@ -244,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_silu_kernel(
         pre = fmaf(win[1], w4[i][1], pre);
         pre = fmaf(win[2], w4[i][2], pre);
         pre = fmaf(rows[j + 3].get(i), w4[i][3], pre);
-        out[i] = silu(pre);
+        out[i] = silu_fast(pre);
       }
       Vec8<T>::store(orow + static_cast<size_t>(t) * ostride + oc, out);
       // the whole sequence lies in this tile: its new history, from here

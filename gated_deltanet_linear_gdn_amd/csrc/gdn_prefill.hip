@@ -196,13 +196,35 @@ template <> struct Raw<float> {
 // below compares against it); the order within a bit length is otherwise
 // arbitrary, and no result depends on it.
 
+// The layer prologue run inside the bf16 WY pass (gdn_conv_prefill): the raw
+// channels x [T, C] of every token (C = 2 Hk Dk + Hv Dv, laid out as q heads
+// | k heads | v heads), the conv weights W [C, 4] (tap 3 weighs the current
+// token), the rolling history hist [pool_size, C, 3] (oldest first), and the
+// convolved q, k [T, Hk, Dk] and v [T, Hv, Dv] that the rest of the WY pass
+// and the chunk loop read.  x == nullptr: no prologue.
+struct ConvIn {
+  const bf16* x;
+  const float* W;
+  float* hist;
+  const int64_t* ci;
+  int64_t pool_size;
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  bf16* trash;  // 16 bytes no one reads: the store of a row past the chunk
+  int Dv;
+  int keep;  // leave the history as it is (GDN_KEEP_STATE)
+};
+
 // Raw gate inputs of a prefill whose gates are formed inside the WY pass
-// (gdn_chunk_prefill_raw); a, b in the bf16 activation dtype.
+// (gdn_chunk_prefill_raw); a, b in the bf16 activation dtype; and the conv
+// prologue, when the pass runs it too.
 struct RawGates {
   const bf16* a;
   const bf16* b;
   const float* A_log;
   const float* dt_bias;
+  ConvIn cv;
 };
 
 __device__ __forceinline__ void seq_bounds(const int64_t* cu, int s, int64_t T_tot, int64_t& b0,
@@ -990,6 +1012,215 @@ __device__ __forceinline__ f32x4 mm3_la(s16x4 ah, s16x4 al, f32x4 b) {
 }
 
 // ----------------------------------------------------------------------------
+// The conv prologue of one chunk inside its WY wave (regolith `gdn.metal`,
+// header comment and the conv/SiLU block of its kernel): for every channel c
+// of key head hk's q and k heads and of the v heads of its group, and every
+// token t of the chunk,
+//   pre = x[t-3] W[c][0] + x[t-2] W[c][1] + x[t-1] W[c][2] + x[t] W[c][3],
+//   out = pre sigmoid(pre),
+// with inputs before the sequence's first token taken from the slot's
+// history -- the formula, operation order and SiLU of gdn_conv_silu, so the
+// outputs are the same bits.  Work items are (group of 8 channels, run of 16
+// rows) dealt over the lanes, consecutive lanes on consecutive channels (one
+// 16-byte load or store per lane and row).  The item loop is software
+// pipelined: the next item's window rows, first eight rows and weights are
+// loaded while the current item's first half computes, its last eight rows
+// while the second half computes, so the wave's loads stay in flight through
+// its arithmetic (the kernel holds two waves per SIMD, too few to hide a
+// load's latency otherwise).  The wave of a sequence's first chunk is the
+// only one that reads the slot's history for these channels; after those
+// reads it writes the new history (the newest three of history and inputs),
+// so no later kernel is needed for it.
+struct ConvItem {
+  int ch;       // first channel of the group in the raw row
+  int ostride;  // elements per output row
+  int r0;       // first row of the run in the chunk
+  bf16* out;    // the group's output column
+};
+
+template <int DK>
+__device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, int64_t len, int64_t t0, int n,
+                                           int Hk, int Hv, int hk, int HG) {
+  constexpr int NGQ = DK / 8;                 // 8-channel groups of one q (or k) head
+  const int NG = 2 * NGQ + HG * cv.Dv / 8;    // groups of the key head's channels
+  const int total = NG * ((n + 15) >> 4);
+  const int C = 2 * Hk * DK + Hv * cv.Dv;
+  const bool first = t0 == b0;
+  const int64_t slot = cv.ci[s];
+  const bool slot_ok = first && slot >= 0 && slot < cv.pool_size;
+
+  auto describe = [&](int it) __attribute__((always_inline)) {
+    ConvItem d;
+    const int sg = it / NG, gi = it - sg * NG;
+    d.r0 = sg * 16;
+    if (gi < NGQ) {
+      d.ch = hk * DK + gi * 8;
+      d.out = cv.q + hk * DK + gi * 8;
+      d.ostride = Hk * DK;
+    } else if (gi < 2 * NGQ) {
+      d.ch = (Hk + hk) * DK + (gi - NGQ) * 8;
+      d.out = cv.k + hk * DK + (gi - NGQ) * 8;
+      d.ostride = Hk * DK;
+    } else {
+      const int vc = hk * HG * cv.Dv + (gi - 2 * NGQ) * 8;
+      d.ch = 2 * Hk * DK + vc;
+      d.out = cv.v + vc;
+      d.ostride = Hv * cv.Dv;
+    }
+    return d;
+  };
+  auto row = [&](int64_t p, int ch) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(cv.x + static_cast<size_t>(p) * C + ch);
+  };
+  // eight rows of the run from row r (clamped to the chunk's last token)
+  auto load8 = [&](const ConvItem& d, int r, uint4 (&X)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) X[j] = row(t0 + min(d.r0 + r + j, n - 1), d.ch);
+  };
+  // the three window rows before the run.  Only a sequence's first run has
+  // rows before the sequence (all three, as a chunk holds at least 8 rows);
+  // its loads are clamped to a row of the sequence and replaced below, so
+  // that no select waits for them here.
+  auto load_win = [&](const ConvItem& d, uint4 (&Wr)[3]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int64_t p = t0 + d.r0 - 3 + m;
+      Wr[m] = row(p > b0 ? p : b0, d.ch);
+    }
+  };
+  auto load_w = [&](const ConvItem& d, f32x4 (&w)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const f32x4*>(cv.W + static_cast<size_t>(d.ch + i) * 4);
+  };
+  auto unpack = [](const uint4& x, float (&f)[8]) __attribute__((always_inline)) {
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  };
+  // rows r .. r+7 of the run from X, the window rolling along
+  auto compute8 = [&](const ConvItem& d, int r, const uint4 (&X)[8], const f32x4 (&w)[8], float (&win)[3][8])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float cur[8];
+      unpack(X[j], cur);
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float y2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c8 = 2 * i + e;
+          float pre = win[0][c8] * w[c8][0];
+          pre = fmaf(win[1][c8], w[c8][1], pre);
+          pre = fmaf(win[2][c8], w[c8][2], pre);
+          pre = fmaf(cur[c8], w[c8][3], pre);
+          y2[e] = silu_fast(pre);
+        }
+        o[i] = pk(y2[0], y2[1]);  // both to bf16 (nearest even) in one conversion
+      }
+      // rows past the chunk (computed from repeated inputs) go to the trash
+      // slot: a select, not a branch, whose join would make the compiler
+      // wait for every load in flight
+      const int rr = d.r0 + r + j;
+      bf16* dst = rr < n ? d.out + static_cast<size_t>(t0 + rr) * d.ostride : cv.trash;
+      *reinterpret_cast<uint4*>(dst) = uint4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        win[0][i] = win[1][i];
+        win[1][i] = win[2][i];
+        win[2][i] = cur[i];
+      }
+    }
+  };
+
+  // HIST: a sequence's first chunk (history reads and the new history).
+  // The loop is built twice so that the other chunks carry no history loads:
+  // under a lane-dependent branch those would make the compiler wait for
+  // every load in flight (the next item's rows too) where the branches join.
+  auto items = [&](auto hist_tag) __attribute__((always_inline)) {
+  constexpr bool HIST = decltype(hist_tag)::value;
+  int it = threadIdx.x;
+  ConvItem cur{};
+  uint4 A[8], B[8], Wr[3];
+  f32x4 w[8];
+  if (it < total) {
+    cur = describe(it);
+    load_win(cur, Wr);
+    load8(cur, 0, A);
+    load_w(cur, w);
+    load8(cur, 8, B);
+  }
+  for (; it < total; it += 64) {
+    const bool more = it + 64 < total;
+    const ConvItem nxt = more ? describe(it + 64) : cur;
+    // the window of this run: inputs, or (a sequence's first rows) history
+    float win[3][8];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) unpack(Wr[m], win[m]);
+    const bool hist_rows = HIST && cur.r0 == 0;  // t0 - 3 + m < b0 = t0 for every m
+    if (hist_rows) {
+      const float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3;
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) win[m][i] = slot_ok ? h[3 * i + m] : 0.f;
+    }
+    uint4 Wr2[3];
+    f32x4 w2[8];
+    compute8(cur, 0, A, w, win);
+    if (more) {
+      load_win(nxt, Wr2);
+      load8(nxt, 0, A);
+      load_w(nxt, w2);
+    }
+    compute8(cur, 8, B, w, win);
+    if (more) load8(nxt, 8, B);
+    // the slot's new history: inputs b0+len-3 .. b0+len-1, entries before
+    // the sequence from the old history (read above by this lane, and
+    // again here before the store)
+    if (hist_rows && slot_ok && !cv.keep) {
+      float nh[8][3];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const int64_t p = b0 + len - 3 + m;
+        float f[8];
+        if (p >= b0) {
+          unpack(row(p, cur.ch), f);
+        } else {
+          const float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3 + (p - b0 + 3);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = h[3 * i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) nh[i][m] = f[i];
+      }
+      float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3;
+#pragma unroll
+      for (int q4 = 0; q4 < 6; ++q4)
+        *reinterpret_cast<f32x4*>(h + 4 * q4) =
+            f32x4{nh[(4 * q4) / 3][(4 * q4) % 3], nh[(4 * q4 + 1) / 3][(4 * q4 + 1) % 3],
+                  nh[(4 * q4 + 2) / 3][(4 * q4 + 2) % 3], nh[(4 * q4 + 3) / 3][(4 * q4 + 3) % 3]};
+    }
+    if (more) {
+      cur = nxt;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) Wr[m] = Wr2[m];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = w2[i];
+    }
+  }
+  };
+  if (first)
+    items(std::true_type{});
+  else
+    items(std::false_type{});
+}
+
+// ----------------------------------------------------------------------------
 // 4. bf16 WY pass: one independent wave per (chunk, key head).
 //
 // The wave holds every K and Q fragment of the chunk in registers (rows past
@@ -1027,7 +1258,12 @@ __device__ __forceinline__ float ld_beta(const bf16* b, size_t i) { return bf16_
 // RAW: the gates come from the raw inputs a, b [T, Hv] (bf16), A_log and
 // dt_bias [Hv] (gates_of), formed where the gate scan needs them, instead
 // of from g and beta.
-template <int DK, int CT, bool COMBA = false, typename BT = float, bool RAW = false>
+//
+// CONV (with RAW): the wave first runs the conv prologue of its chunk's
+// channels (conv_chunk), writing the q, k and v the chunk loop reads, and
+// then takes its K and Q fragments from those rows (written by this wave,
+// so a workgroup barrier orders them).
+template <int DK, int CT, bool COMBA = false, typename BT = float, bool RAW = false, bool CONV = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gdn_wy_wave_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ pr,
     const float* __restrict__ g, const BT* __restrict__ beta, const int64_t* __restrict__ cu,
@@ -1036,6 +1272,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
     bf16* __restrict__ Tl, bf16* __restrict__ Ph, float* __restrict__ fac, RawGates rg, int own_map,
     int* __restrict__ map_out, int wg_per_seq, int num_cu, int allow_split, FixedBatch fb) {
   static_assert(!RAW || !COMBA, "raw gates: GDN only");
+  static_assert(!CONV || RAW, "the conv prologue comes with raw gates");
   constexpr int MT = CT / 16, KB = DK / 32;
   constexpr int NPAIR = MT * (MT + 1) / 2, FSTR = 3 * CT + 4;
   __shared__ __attribute__((aligned(16))) float sG[CT], sRK[CT], sRQ[CT], sB[CT];
@@ -1110,6 +1347,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
   const bool ok = lane < n;
   const size_t tg = static_cast<size_t>(t0 + min(lane, n - 1)) * Hv + hk * HG;  // gates of token `lane`
+  if constexpr (CONV) {
+    conv_chunk<DK>(rg.cv, lo, b0, len, t0, n, Hk, Hv, hk, HG);
+    __syncthreads();  // the convolved rows, stored by other lanes, before the fragment loads below
+  }
+  // where the fragments come from: the inputs, or the rows just convolved
+  const bf16* const qsrc = CONV ? rg.cv.q : q;
+  const bf16* const ksrc = CONV ? rg.cv.k : k;
 
   // gates of the first value head, then the K fragments: lane (l16, kg)
   // holds row I*16 + l16, elements kb*32 + kg*8 .. +7 (the same order on
@@ -1135,7 +1379,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   for (int I = 0; I < MT; ++I)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-      kf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(k + row_off(I) + kb * 32));
+      kf[I][kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(ksrc + row_off(I) + kb * 32));
   // row sums of squares: 8 elements per lane and k-block, then over kg
   auto sumsq = [&](const bf16x8v (&f)[KB]) __attribute__((always_inline)) {
     float a = 0.f;
@@ -1161,7 +1405,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gd
   auto load_qp = [&](int I) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      qn[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(q + row_off(I) + kb * 32));
+      qn[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(qsrc + row_off(I) + kb * 32));
       if constexpr (COMBA)
         pn[kb] = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const uint4*>(pr + row_off(I) + kb * 32));
     }
@@ -2005,7 +2249,13 @@ int launch_all(const void* q, const void* k, const void* v, const float* g, cons
     const FixedBatch fb = fixb ? *fixb : FixedBatch{0, nullptr, nullptr};
     const int64_t* wy_cu = fixb ? nullptr : cu;  // not read in a fixed-length batch
     const dim3 wy_grid(static_cast<unsigned>(maxc * static_cast<size_t>(Hk) + own));
-    if (raw)  // the gates formed inside the WY pass
+    if (raw && raw->cv.x)  // the conv prologue and the gates inside the WY pass (q, k: its outputs)
+      hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, false, float, true, true>), wy_grid, dim3(64), 0, stream,
+                         static_cast<const bf16*>(nullptr), static_cast<const bf16*>(nullptr),
+                         static_cast<const bf16*>(nullptr), static_cast<const float*>(nullptr),
+                         static_cast<const float*>(nullptr), wy_cu, scs, N_s, T_tot, Hk, Hv, chunk, scale, l2norm, Th,
+                         Tl, Ph, fac, *raw, own, scs, per_seq, cu_count(), split ? 1 : 0, fb);
+    else if (raw)  // the gates formed inside the WY pass
       hipLaunchKernelGGL((gdn_wy_wave_kernel<DK, CT, false, float, true>), wy_grid, dim3(64), 0, stream,
                          static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(nullptr),
                          static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), wy_cu, scs, N_s,
@@ -2396,6 +2646,93 @@ extern "C" int gdn_chunk_prefill_gated(const void* q, const void* k, const void*
   const Epilogue epi{z, gamma, eps};
   return chunk_prefill(q, k, v, g, beta, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot, Hk,
                        Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, workspace_bytes, &epi, stream);
+}
+
+// ------------------------------------------- prefill with the conv prologue
+//
+// gdn_conv_prefill: the layer's prefill from its raw channels.  The WY pass
+// runs the conv prologue of its chunk (conv_chunk) and the gates from the raw
+// inputs; the convolved q, k, v go to the workspace's tail, which the chunk
+// loop reads; the gated norm, when z is given, as gdn_chunk_prefill_gated.
+
+namespace gdn {
+namespace {
+
+struct ConvLayout {
+  size_t base, q, k, v, trash, total;
+};
+
+inline ConvLayout conv_layout(size_t base, int64_t T_tot, int Hk, int Hv, int Dk, int Dv) {
+  ConvLayout c;
+  c.base = base;
+  c.q = base;
+  c.k = c.q + up(static_cast<size_t>(T_tot) * Hk * Dk * sizeof(bf16));
+  c.v = c.k + up(static_cast<size_t>(T_tot) * Hk * Dk * sizeof(bf16));
+  c.trash = c.v + up(static_cast<size_t>(T_tot) * Hv * Dv * sizeof(bf16));
+  c.total = c.trash + kAlign;
+  return c;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" size_t gdn_conv_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv, int Dk, int Dv, int chunk) {
+  const size_t base = gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, GDN_BF16);
+  if (base == 0 || Dv <= 0) return 0;
+  return gdn::conv_layout(base, T_tot, Hk, Hv, Dk, Dv).total;
+}
+
+extern "C" int gdn_conv_prefill(const void* qkv, const float* conv_w, float* conv_state, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias, float* state_pool,
+                                int64_t pool_size, const int64_t* cache_indices, const int64_t* cu_seqlens,
+                                int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv, int chunk, float scale,
+                                unsigned flags, const void* z, const float* gamma, float eps, void* y,
+                                gdn_dtype act, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace gdn;
+  if (N_s < 0 || T_tot < 0 || pool_size < 0 || Hk <= 0 || Hv <= 0 || Dk <= 0 || Dv <= 0 || Hv % Hk != 0)
+    return GDN_ERR_SHAPE;
+  if (!is_act(act)) return GDN_ERR_DTYPE;
+  if (act != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (z && !(eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if (z && !pow2_head(Dv)) return GDN_ERR_UNSUPPORTED;
+  const size_t base = gdn_chunk_prefill_workspace(T_tot, N_s, Hk, Hv, Dk, Dv, chunk, act);
+  if (base == 0) return GDN_ERR_UNSUPPORTED;
+  const ConvLayout cl = conv_layout(base, T_tot, Hk, Hv, Dk, Dv);
+  if (N_s == 0) return GDN_OK;
+  if (!workspace) return GDN_ERR_NULL;
+  if (workspace_bytes < cl.total) return GDN_ERR_WORKSPACE;
+  const size_t C = 2 * static_cast<size_t>(Hk) * Dk + static_cast<size_t>(Hv) * Dv;
+  const size_t x_bytes = static_cast<size_t>(T_tot) * C * sizeof(bf16);
+  const size_t w_bytes = C * 4 * sizeof(float);
+  const size_t h_bytes = static_cast<size_t>(pool_size) * C * 3 * sizeof(float);
+  const size_t y_bytes = static_cast<size_t>(T_tot) * Hv * Dv * sizeof(bf16);
+  const size_t p_bytes = static_cast<size_t>(pool_size) * Hv * Dv * Dk * sizeof(float);
+  if (T_tot > 0) {
+    if (!qkv || !conv_w || !conv_state || (z && !gamma)) return GDN_ERR_NULL;
+    if (!aligned16(qkv) || !aligned16(conv_w) || !aligned16(conv_state) || (z && (!aligned16(z) || !aligned16(gamma))))
+      return GDN_ERR_ALIGN;
+    const size_t ab_bytes = static_cast<size_t>(T_tot) * Hv * sizeof(bf16);
+    const size_t hv_bytes = static_cast<size_t>(Hv) * sizeof(float);
+    const Span in[] = {{qkv, x_bytes}, {conv_w, w_bytes}, {z, z ? y_bytes : 0}, {a, ab_bytes},
+                       {b, ab_bytes}, {A_log, hv_bytes}, {dt_bias, hv_bytes}};
+    const Span out[] = {{conv_state, h_bytes}, {y, y_bytes}, {state_pool, p_bytes}, {workspace, cl.total}};
+    if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
+    if (overlaps(conv_state, h_bytes, y, y_bytes) || overlaps(conv_state, h_bytes, state_pool, p_bytes) ||
+        overlaps(conv_state, h_bytes, workspace, cl.total))
+      return GDN_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  bf16* cq = reinterpret_cast<bf16*>(ws + cl.q);
+  bf16* ck = reinterpret_cast<bf16*>(ws + cl.k);
+  bf16* cv = reinterpret_cast<bf16*>(ws + cl.v);
+  RawGates rg{static_cast<const bf16*>(a), static_cast<const bf16*>(b), A_log, dt_bias,
+              ConvIn{static_cast<const bf16*>(qkv), conv_w, conv_state, cache_indices, pool_size, cq, ck, cv,
+                     reinterpret_cast<bf16*>(ws + cl.trash), Dv, (flags & GDN_KEEP_STATE) ? 1 : 0}};
+  const Epilogue epi{z, gamma, eps};
+  // the prefill's own checks (the convolved rows lie past its workspace span)
+  return chunk_prefill(cq, ck, cv, nullptr, nullptr, state_pool, pool_size, cache_indices, cu_seqlens, N_s, T_tot,
+                       Hk, Hv, Dk, Dv, chunk, scale, flags, y, act, workspace, base, z ? &epi : nullptr, stream,
+                       false, 0, false, &rg);
 }
 
 extern "C" int gdn_validate_varlen(const int64_t* cu_seqlens, const int64_t* cache_indices, int N_s,

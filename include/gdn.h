@@ -476,6 +476,61 @@ int gdn_conv_decode_step(const float* state_in, float* state_out,
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_conv_prefill_workspace - bytes of device workspace gdn_conv_prefill
+ * needs (bf16 activations): gdn_chunk_prefill_workspace() plus the convolved
+ * q, k [T_tot, Hk, Dk] and v [T_tot, Hv, Dv] in bf16, each rounded up to 256
+ * bytes, plus 256 bytes.  0 for invalid arguments.
+ */
+size_t gdn_conv_prefill_workspace(int64_t T_tot, int N_s, int Hk, int Hv,
+                                  int Dk, int Dv, int chunk);
+
+/*
+ * gdn_conv_prefill - the layer's prefill from its raw channels: the conv
+ * prologue of gdn_conv_silu, the gates of gdn_prefill_gates, the recurrence
+ * of gdn_chunk_prefill and, when z is given, the gated norm of
+ * gdn_chunk_prefill_gated, in one call.  Source: regolith `gdn.metal`,
+ * header comment (conv, SiLU, norms and gates ahead of the recurrence, the
+ * gated norm after it) and the pymllm `gdn_extend_chunkwise` parameter list
+ * (raw gates, varlen batch, state pool).  The conv runs inside the prefill's
+ * WY pass, one chunk of one key head per wave (its q and k heads and the v
+ * heads of its group); the convolved q, k, v are written once, to the
+ * workspace, for the chunk loop.  Every result equals the separate calls
+ * (gdn_conv_silu, then gdn_chunk_prefill_raw, or gdn_chunk_prefill_gated
+ * with the gates of gdn_prefill_gates) bit for bit.
+ * qkv          [T_tot, C] bf16, C = 2*Hk*Dk + Hv*Dv channels per token laid
+ *              out as [q heads | k heads | v heads], read.
+ * conv_w       [C, 4] float32 (tap 3 weighs the current token), read.
+ * conv_state   [pool_size, C, 3] float32, the history (oldest first) per
+ *              state slot: read, then updated in place to the newest three of
+ *              (history, the sequence's inputs); left as it is with
+ *              GDN_KEEP_STATE.  Only the slots of non-empty sequences are
+ *              accessed.
+ * a, b         [T_tot, Hv] bf16.   A_log, dt_bias [Hv] float32.
+ * z, gamma     NULL: y is the recurrence's output.  Else z [T_tot, Hv, Dv]
+ *              bf16 and gamma [Dv] float32, eps >= 0, Dv in {32, 64, 128,
+ *              256}: y is the gated norm of it.
+ * Every other argument as for gdn_chunk_prefill (flags GDN_QK_L2NORM and/or
+ * GDN_KEEP_STATE, which then also keeps conv_state); act must be GDN_BF16
+ * (GDN_ERR_UNSUPPORTED otherwise).  workspace: at least
+ * gdn_conv_prefill_workspace() bytes, 16-byte aligned, scratch.
+ * Requirements: those of gdn_chunk_prefill; qkv, conv_w, conv_state, z and
+ * gamma 16-byte aligned (GDN_ERR_ALIGN); conv_state overlapping none of y,
+ * state_pool and the workspace, and no input (qkv, conv_w, z, a, b, A_log,
+ * dt_bias) overlapping an output (GDN_ERR_ALIAS).  N_s == 0 is a no-op.
+ * On an in-kernel failure the referenced state slots and histories are
+ * unspecified (both are updated in place).
+ */
+int gdn_conv_prefill(const void* qkv, const float* conv_w, float* conv_state,
+                     const void* a, const void* b, const float* A_log,
+                     const float* dt_bias, float* state_pool, int64_t pool_size,
+                     const int64_t* cache_indices, const int64_t* cu_seqlens,
+                     int N_s, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
+                     int chunk, float scale, unsigned flags, const void* z,
+                     const float* gamma, float eps, void* y, gdn_dtype act,
+                     void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
  * gdn_chunk_prefill_noalloc - gdn_chunk_prefill without a caller workspace,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  The

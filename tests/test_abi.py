@@ -413,3 +413,44 @@ def test_conv_decode_validation(lib):
     assert conv_decode(lib, y=A + 2 * BIG) == ALIAS       # y over the raw channels
     assert conv_decode(lib, hist=A + BIG + 128) == ALIAS  # history inside the new state
     assert conv_decode(lib, ws=A + 4 * BIG + 64) == ALIAS # workspace over the history
+
+
+def conv_prefill(lib, x=A, w=A + BIG, hist=A + 2 * BIG, a=A + 3 * BIG, b=A + 4 * BIG, A_log=A + 5 * BIG,
+                 dtb=A + 6 * BIG, pool=A + 7 * BIG, P=4, ci=A + 8 * BIG, cu=A + 9 * BIG, N_s=2, T=100, Hk=2,
+                 Hv=4, Dk=128, Dv=128, chunk=64, flags=1, z=0, gamma=0, eps=1e-6, y=A + 10 * BIG, act=1,
+                 ws=A + 11 * BIG, ws_bytes=1 << 30):
+    return lib.gdn_conv_prefill(_p(x), _p(w), _p(hist), _p(a), _p(b), _p(A_log), _p(dtb), _p(pool), P, _p(ci),
+                                _p(cu), N_s, T, Hk, Hv, Dk, Dv, chunk, 0.0, flags, _p(z), _p(gamma), eps, _p(y),
+                                act, _p(ws), ws_bytes, None)
+
+
+def test_conv_prefill_validation(lib):
+    f = lib.gdn_conv_prefill_workspace
+    base = lib.gdn_chunk_prefill_workspace(100, 2, 2, 4, 128, 128, 64, 1)
+    # the prefill's workspace, then the convolved q, k, v (bf16), each 256-byte aligned
+    assert f(100, 2, 2, 4, 128, 128, 64) == base + 2 * 51200 + 102400 + 256
+    assert f(100, 2, 2, 4, 128, 128, 48) == 0
+    assert f(-1, 2, 2, 4, 128, 128, 64) == 0
+    assert conv_prefill(lib, N_s=-1) == SHAPE
+    assert conv_prefill(lib, Hk=3) == SHAPE
+    assert conv_prefill(lib, act=7) == DTYPE
+    assert conv_prefill(lib, act=0) == UNSUP                     # bf16 activations only
+    assert conv_prefill(lib, Dk=80) == UNSUP
+    assert conv_prefill(lib, chunk=48) == UNSUP
+    assert conv_prefill(lib, flags=4) == UNSUP
+    assert conv_prefill(lib, z=A + 12 * BIG, gamma=A + 13 * BIG, Dv=96) == UNSUP   # the norm: Dv a power of two
+    assert conv_prefill(lib, z=A + 12 * BIG, gamma=A + 13 * BIG, eps=-1.0) == SHAPE
+    assert conv_prefill(lib, N_s=0, x=0, ws=0) == OK             # nothing to do
+    assert conv_prefill(lib, x=0) == NULL
+    assert conv_prefill(lib, hist=0) == NULL
+    assert conv_prefill(lib, a=0) == NULL
+    assert conv_prefill(lib, ws=0) == NULL
+    assert conv_prefill(lib, z=A + 12 * BIG) == NULL              # z without gamma
+    assert conv_prefill(lib, x=A + 8) == ALIGN
+    assert conv_prefill(lib, w=A + BIG + 4) == ALIGN
+    assert conv_prefill(lib, hist=A + 2 * BIG + 8) == ALIGN
+    assert conv_prefill(lib, ws_bytes=base) == WORKSPACE        # no room for the convolved rows
+    assert conv_prefill(lib, y=A + 64) == ALIAS                  # y over the raw channels
+    assert conv_prefill(lib, hist=A + 7 * BIG + 256) == ALIAS    # history inside the pool
+    assert conv_prefill(lib, a=A + 2 * BIG + 64) == ALIAS        # a raw gate under the history
+    assert conv_prefill(lib, w=A + 11 * BIG + base + 512) == ALIAS   # weights under the convolved rows
