@@ -552,9 +552,11 @@ def cpu_baseline(budget_s=8.0):
     beside the GPU figures of the same run: the B=256 decode step (the
     headline, GB/s over the same state bytes), the Comba step at B=128
     H=32 K=V=128 (GB/s over the KBench byte count) and the varlen prefill
-    (tokens/s over the same 8 sequences x 48 heads).  Independent (sequence,
-    head) units are split statically over N threads; each unit runs
-    sequentially.  N-thread and 1-thread times are both reported."""
+    (tokens/s over the same 8 sequences x 48 heads), the conv prologue over
+    that batch's 10,240 channels and the Comba prefill over the same lengths
+    (H=32).  Independent (sequence, head) units (channel blocks for the conv)
+    are split statically over N threads; each unit runs sequentially.
+    N-thread and 1-thread times are both reported."""
     import oracle
     from gated_deltanet_linear_gdn_amd import synth
     try:
@@ -640,12 +642,50 @@ def cpu_baseline(budget_s=8.0):
                                     "Hk=16 Hv=48 Dk=Dv=128", tokens=T, s_per_call=round(el, 3),
                            s_per_call_1thread=round(one, 3), tokens_per_s=round(T / el, 1),
                            tokens_per_s_1thread=round(T / one, 1))
+
+    # the layer prologue over the same batch: conv + SiLU of the 10,240 raw
+    # channels, independent channel blocks split over the threads
+    lay = synth.layer_inputs(rng, T, Hk, Hv, Dk, Dv, P)
+    Cch = lay["qkv"].shape[1]
+    blk = Cch // 16
+
+    def conv(j):
+        cs = slice(j * blk, (j + 1) * blk)
+        oracle.conv_silu(lay["qkv"][:, cs], lay["conv_w"][cs], lay["conv_state"][:, cs], inp["cache_indices"], cu)
+
+    el = _run_units(conv, list(range(16)), threads)
+    one = _run_units(conv, [0], 1) * 16
+    legs["conv"] = dict(workload="gdn_conv_silu (4-tap conv + SiLU, 10,240 channels, history per slot) over the "
+                                 "same 8 sequences", tokens=T, s_per_call=round(el, 3), s_per_call_1thread=round(one, 3),
+                        tokens_per_s=round(T / el, 1), tokens_per_s_1thread=round(T / one, 1))
+
+    # Comba prefill: the step over every token of the same 8 sequences, per
+    # (sequence, head) unit
+    H, K, V = 32, 128, 128
+    cin = synth.comba_prefill_inputs(rng, lengths, H, K, V, pool_size=P)
+    ccu = cin["cu_seqlens"]
+    cpool = np.zeros((P, H, K, V))
+
+    def cpre(u):
+        s, h = u
+        idx, hs = slice(int(ccu[s]), int(ccu[s + 1])), slice(h, h + 1)
+        slot = int(cin["cache_indices"][s])
+        oracle.comba_prefill(*(cin[n][idx, hs] for n in ("q", "k", "v", "p", "beta", "g")), cpool[slot:slot + 1, hs],
+                             [0], [0, int(ccu[s + 1] - ccu[s])])
+
+    # this oracle steps token by token from Python (one C call per token),
+    # so threads serialise on the interpreter: one thread over a sample of
+    # two heads of every sequence, scaled to the 32 heads
+    one = _run_units(cpre, [(s, h) for s in range(len(lengths)) for h in range(2)], 1) * (H / 2)
+    legs["comba_prefill"] = dict(workload="comba_chunk_prefill (token by token): the same 8 sequences, H=32 K=V=128",
+                                 tokens=T, sample="heads 0 and 1 of every sequence on 1 thread, scaled by 16",
+                                 s_per_call_1thread=round(one, 3), tokens_per_s_1thread=round(T / one, 1))
     d = legs["decode"]
     return dict(value=d["GBps"], unit="GB/s", cores=threads, kind="oracle", cpu=_cpu_model(),
                 sample=(f"{d['steps']} fp64 oracle decode steps of the whole B=256 Hk=16 Hv=48 Dk=Dv=128 batch "
                         f"on {threads} threads ({d['s_per_step']} s per step; 1 thread: "
-                        f"{d['s_per_step_1thread']} s per step from an eighth of the batch); Comba and "
-                        f"prefill legs below"),
+                        f"{d['s_per_step_1thread']} s per step from an eighth of the batch); Comba step, "
+                        f"prefill, conv prologue and Comba prefill legs below"),
                 legs=legs)
 
 
