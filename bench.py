@@ -44,11 +44,11 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 # read for a 2 GiB device copy), valid for the kernel built from these
 # sources only: after any change to them the figure is reported as null.
 DECODE_TRAFFIC = {
-    "bytes": 1659868912,
+    "bytes": 1659868570,
     "sources_sha256": {
         "gated_deltanet_linear_gdn_amd/csrc/gdn_decode.hip": "7736da6fa0045db52269febacb2aa07065fe5f09942bb1ce6155a50d9f207ccd",
         "gated_deltanet_linear_gdn_amd/csrc/gdn_decode_core.h": "a33da64879537627d6874f25c8cfee8a280d617ad4b467cc24edbd3161cb705b",
-        "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "0964ecae6a55ff6358f52d3a8eaa6ef06cca3141143eba2963554d8d93db62f6",
+        "gated_deltanet_linear_gdn_amd/csrc/gdn_device.h": "01aacca146e67000b45bb4777947468b8e851857e2a3f9cd7869ecc457f9b6e7",
     },
 }
 
