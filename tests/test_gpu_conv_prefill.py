@@ -96,6 +96,9 @@ CASES = [
     ([257, 90], 2, 2, 96, 32, 32, False),                # key heads of 96
     ([100, 33], 1, 2, 256, 128, 64, True),               # Dk 256: 32-token chunks
     ([700, 1300, 2], 16, 48, 128, 128, 64, True),        # the layer's 10,240 channels
+    ([37, 1, 0, 90, 3] * 14, 2, 16, 64, 32, 32, False),  # 70 sequences: the chunk map as its own kernel
+    ([150, 66], 2, 2, 128, 128, 64, True),               # one value head per key head
+    ([97, 12], 1, 8, 128, 64, 16, False),                # eight value heads per key head
 ]
 
 
