@@ -715,6 +715,7 @@ def main():
     if only and not only <= set(LEGS):
         sys.exit(f"--only: unknown legs {sorted(only - set(LEGS))}; known: {', '.join(LEGS)}")
     dec_ip = bench_decode(max(10, args.steps // 2), args.warmup, device, inplace=True) if want("inplace") else None
+    dec64 = bench_decode(max(10, args.steps // 2), args.warmup, device, B=64) if want("inplace") else None
     com = bench_comba(args.steps, args.warmup, device) if want("comba") else None
     com_shapes = {}
     if want("comba"):
@@ -766,6 +767,12 @@ def main():
     }
     if want("inplace"):
         out["decode_inplace_GBps"] = round(dec_ip["state_bytes"] / dec_ip["sec"] / 1e9, 2)
+        out["decode_b64"] = {"workload": "gdn_decode_step, decode batch B=64 Hk=16 Hv=48 Dk=Dv=128 bf16, fp32 state "
+                                         "(192 MiB per copy, functional ping-pong: 384 MiB, above the 256 MB MALL, "
+                                         "which still holds part of it between steps)",
+                             "us_per_step": round(dec64["sec"] * 1e6, 2),
+                             "GBps": round(dec64["state_bytes"] / dec64["sec"] / 1e9, 2),
+                             "frac_of_hbm_peak": round(dec64["state_bytes"] / dec64["sec"] / 1e9 / HBM_PEAK_GBPS, 4)}
     if want("copy"):
         out["torch_copy_GBps"] = round(copy_gbps, 1)
     if want("copy"):
