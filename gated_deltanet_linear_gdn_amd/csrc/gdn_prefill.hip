@@ -2718,7 +2718,8 @@ extern "C" int gdn_conv_prefill(const void* qkv, const float* conv_w, float* con
     const Span out[] = {{conv_state, h_bytes}, {y, y_bytes}, {state_pool, p_bytes}, {workspace, cl.total}};
     if (inputs_overlap_outputs(in, out)) return GDN_ERR_ALIAS;
     if (overlaps(conv_state, h_bytes, y, y_bytes) || overlaps(conv_state, h_bytes, state_pool, p_bytes) ||
-        overlaps(conv_state, h_bytes, workspace, cl.total))
+        overlaps(conv_state, h_bytes, workspace, cl.total) || overlaps(y, y_bytes, workspace, cl.total) ||
+        overlaps(state_pool, p_bytes, workspace, cl.total))
       return GDN_ERR_ALIAS;
   }
   char* ws = static_cast<char*>(workspace);

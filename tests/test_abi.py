@@ -454,3 +454,5 @@ def test_conv_prefill_validation(lib):
     assert conv_prefill(lib, hist=A + 7 * BIG + 256) == ALIAS    # history inside the pool
     assert conv_prefill(lib, a=A + 2 * BIG + 64) == ALIAS        # a raw gate under the history
     assert conv_prefill(lib, w=A + 11 * BIG + base + 512) == ALIAS   # weights under the convolved rows
+    ws_total = f(100, 2, 2, 4, 128, 128, 64)
+    assert conv_prefill(lib, y=A + 11 * BIG + ws_total - 256) == ALIAS  # y over the workspace's last bytes
