@@ -102,6 +102,37 @@ def test_comba_batch_b128():
         check_bf16_out(to_np(o)[sample], o_ref, f"o at step {step}")
 
 
+def test_comba_batch_b128_sampled_through_1000_steps():
+    """The benchmark's Comba launch configuration for its 1,000 timed steps:
+    B=128, H=32, K=V=128, 16 token sets used cyclically, ping-pong between
+    two states.  The oracle follows 8 sampled sequences (256 (b, h) slices)
+    through every step; state and o are checked every 250 steps."""
+    c = synth.COMBA_B128
+    rng = np.random.default_rng(8)
+    B, H, K, V = c["B"], c["H"], c["K"], c["V"]
+    W = _warm(rng, 16, H, K, V)
+    S = np.tile(W, (B // 16, 1, 1, 1))
+    sample = np.array([0, 3, 31, 64, 77, 100, 126, 127])
+    S_ref = S[sample].astype(np.float64)
+    bufs = [to_dev(S, torch.float32, DEV), torch.empty((B, H, K, V), dtype=torch.float32, device=DEV)]
+    del S
+    toks = [synth.comba_token(rng, B, H, K, V) for _ in range(16)]
+    dtoks = [_dev_tok(t, "bf16") for t in toks]
+    subs = [{n: a[sample] for n, a in t.items()} for t in toks]
+    o = torch.empty((B, H, V), dtype=torch.bfloat16, device=DEV)
+    idx = torch.from_numpy(sample).to(DEV)
+    for step in range(1000):
+        t = dtoks[step % 16]
+        gdn.comba_decode_step(bufs[step % 2], bufs[(step + 1) % 2], t["q"], t["k"], t["v"], t["p"], t["beta"],
+                              t["g"], o=o)
+        S_ref, o_ref = oracle_comba_batched(S_ref, subs[step % 16])
+        if (step + 1) % 250 == 0:
+            torch.cuda.synchronize()
+            print(f"comba b128 long run: step {step + 1}", flush=True)
+            assert maxrel(to_np(bufs[(step + 1) % 2][idx]), S_ref) <= 1e-5, step
+            check_bf16_out(to_np(o)[sample], o_ref, f"o at step {step + 1}")
+
+
 @pytest.mark.parametrize("shape", synth.COMBA_MEASURE_SHAPES)
 def test_comba_measure_shapes_sampled(shape):
     """The KBench measure shapes the bench times (K = 64 among them), from

@@ -181,6 +181,37 @@ def test_decode_batch_b256():
         _check_y(to_np(y)[sample], y_ref, "bf16")
 
 
+def test_decode_batch_b256_sampled_through_1000_steps():
+    """The benchmark's launch configuration for its 1,000 timed steps: B=256,
+    16 token sets used cyclically, functional ping-pong.  The oracle follows
+    8 sampled sequences (384 (b, hv) slices) through every step; their state
+    and y are checked every 250 steps, so error that builds up over the run
+    would show."""
+    c = synth.DECODE_B256
+    rng = np.random.default_rng(7)
+    B, Hk, Hv, Dk, Dv = c["B"], c["Hk"], c["Hv"], c["Dk"], c["Dv"]
+    W = _warm_state(rng, 16, Hk, Hv, Dk, Dv)
+    S = np.tile(W, (B // 16, 1, 1, 1))
+    sample = np.array([0, 5, 64, 100, 129, 190, 222, 255])
+    S_ref = S[sample].astype(np.float64)
+    bufs = [to_dev(S, torch.float32, DEV), torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=DEV)]
+    del S
+    toks = [synth.decode_token(rng, B, Hk, Hv, Dk, Dv) for _ in range(16)]
+    dtoks = [_dev_token(t, "bf16") for t in toks]
+    subs = [{n: a[sample] for n, a in t.items()} for t in toks]
+    y = torch.empty((B, Hv, Dv), dtype=torch.bfloat16, device=DEV)
+    idx = torch.from_numpy(sample).to(DEV)
+    for step in range(1000):
+        t = dtoks[step % 16]
+        gdn.gdn_decode_step(bufs[step % 2], bufs[(step + 1) % 2], t["q"], t["k"], t["v"], t["g"], t["beta"], y)
+        S_ref, y_ref = oracle_decode_batched(S_ref, subs[step % 16])
+        if (step + 1) % 250 == 0:
+            torch.cuda.synchronize()
+            print(f"b256 long run: step {step + 1}", flush=True)
+            assert maxrel(to_np(bufs[(step + 1) % 2][idx]), S_ref) <= 1e-5, step
+            _check_y(to_np(y)[sample], y_ref, "bf16")
+
+
 def test_batch_beyond_one_launch_grid():
     """65,538 sequences: more than one launch's grid holds (65,535 sequences),
     so the batch runs in two slices.  The oracle follows the sequences on both
