@@ -1020,14 +1020,16 @@ __device__ __forceinline__ f32x4 mm3_la(s16x4 ah, s16x4 al, f32x4 b) {
 //   out = pre sigmoid(pre),
 // with inputs before the sequence's first token taken from the slot's
 // history -- the formula, operation order and SiLU of gdn_conv_silu, so the
-// outputs are the same bits.  Work items are (group of 8 channels, run of 16
-// rows) dealt over the lanes, consecutive lanes on consecutive channels (one
-// 16-byte load or store per lane and row).  The item loop is software
-// pipelined: the next item's window rows, first eight rows and weights are
-// loaded while the current item's first half computes, its last eight rows
-// while the second half computes, so the wave's loads stay in flight through
-// its arithmetic (the kernel holds two waves per SIMD, too few to hide a
-// load's latency otherwise).  The wave of a sequence's first chunk is the
+// outputs are the same bits.  Channels go in groups of 8 (one 16-byte load
+// or store per lane and row), consecutive lanes on consecutive groups.  With
+// 64 groups or more, lane l first takes group l through all of the chunk's
+// rows (the window rolls on, the weights load once); the remaining groups
+// (all of them below 64) go as (group, run of 16 rows) items dealt over the
+// lanes.  Both loops are software pipelined: the next run's rows (and an
+// item's window rows and weights) load while the current run computes, so
+// the wave's loads stay in flight through its arithmetic (the kernel holds
+// two waves per SIMD, too few to hide a load's latency otherwise).  The
+// wave of a sequence's first chunk is the
 // only one that reads the slot's history for these channels; after those
 // reads it writes the new history (the newest three of history and inputs),
 // so no later kernel is needed for it.
@@ -1043,16 +1045,14 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
                                            int Hk, int Hv, int hk, int HG) {
   constexpr int NGQ = DK / 8;                 // 8-channel groups of one q (or k) head
   const int NG = 2 * NGQ + HG * cv.Dv / 8;    // groups of the key head's channels
-  const int total = NG * ((n + 15) >> 4);
   const int C = 2 * Hk * DK + Hv * cv.Dv;
   const bool first = t0 == b0;
   const int64_t slot = cv.ci[s];
   const bool slot_ok = first && slot >= 0 && slot < cv.pool_size;
 
-  auto describe = [&](int it) __attribute__((always_inline)) {
+  auto describe = [&](int gi, int r0) __attribute__((always_inline)) {
     ConvItem d;
-    const int sg = it / NG, gi = it - sg * NG;
-    d.r0 = sg * 16;
+    d.r0 = r0;
     if (gi < NGQ) {
       d.ch = hk * DK + gi * 8;
       d.out = cv.q + hk * DK + gi * 8;
@@ -1141,6 +1141,90 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
   // The loop is built twice so that the other chunks carry no history loads:
   // under a lane-dependent branch those would make the compiler wait for
   // every load in flight (the next item's rows too) where the branches join.
+  // the slot's new history for channel group ch: inputs b0+len-3 ..
+  // b0+len-1, entries before the sequence from the old history (read
+  // before by this lane, and again here before the store)
+  auto new_history = [&](int ch) __attribute__((always_inline)) {
+    float nh[8][3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int64_t p = b0 + len - 3 + m;
+      float f[8];
+      if (p >= b0) {
+        unpack(row(p, ch), f);
+      } else {
+        const float* h = cv.hist + (static_cast<size_t>(slot) * C + ch) * 3 + (p - b0 + 3);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = h[3 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nh[i][m] = f[i];
+    }
+    float* h = cv.hist + (static_cast<size_t>(slot) * C + ch) * 3;
+#pragma unroll
+    for (int q4 = 0; q4 < 6; ++q4)
+      *reinterpret_cast<f32x4*>(h + 4 * q4) =
+          f32x4{nh[(4 * q4) / 3][(4 * q4) % 3], nh[(4 * q4 + 1) / 3][(4 * q4 + 1) % 3],
+                nh[(4 * q4 + 2) / 3][(4 * q4 + 2) % 3], nh[(4 * q4 + 3) / 3][(4 * q4 + 3) % 3]};
+  };
+  // the window of a sequence's first run: the slot's history (zeros for a
+  // slot out of range)
+  auto history_window = [&](int ch, float (&win)[3][8]) __attribute__((always_inline)) {
+    const float* h = cv.hist + (static_cast<size_t>(slot) * C + ch) * 3;
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) win[m][i] = slot_ok ? h[3 * i + m] : 0.f;
+  };
+
+  // Groups 0..63 when the key head has at least 64: lane = group, all of
+  // the chunk's rows in order, the window rolling from run to run and the
+  // weights loaded once; the next run's eight-row halves load while the
+  // current ones compute.
+  const int g_roll = NG >= 64 ? 64 : 0;
+  auto rolling = [&](auto hist_tag) __attribute__((always_inline)) {
+    constexpr bool HIST = decltype(hist_tag)::value;
+    ConvItem d = describe(threadIdx.x, 0);
+    uint4 A[8], B[8], Wr[3];
+    f32x4 w[8];
+    if constexpr (!HIST) load_win(d, Wr);
+    load8(d, 0, A);
+    load_w(d, w);
+    load8(d, 8, B);
+    float win[3][8];
+    if constexpr (HIST) {
+      history_window(d.ch, win);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 3; ++m) unpack(Wr[m], win[m]);
+    }
+    for (int r0 = 0; r0 < n; r0 += 16) {
+      d.r0 = r0;
+      const bool more = r0 + 16 < n;
+      compute8(d, 0, A, w, win);
+      if (more) {
+        ConvItem nx = d;
+        nx.r0 = r0 + 16;
+        load8(nx, 0, A);
+      }
+      compute8(d, 8, B, w, win);
+      if (more) {
+        ConvItem nx = d;
+        nx.r0 = r0 + 16;
+        load8(nx, 8, B);
+      }
+    }
+    if (HIST && slot_ok && !cv.keep) new_history(d.ch);
+  };
+
+  // The other groups (all of them below 64) as (group, run of 16 rows)
+  // items dealt over the lanes, pipelined one item ahead.
+  const int NGr = NG - g_roll;
+  const int total = NGr * ((n + 15) >> 4);
+  auto item_of = [&](int it) __attribute__((always_inline)) {
+    const int sg = it / NGr;
+    return describe(g_roll + (it - sg * NGr), sg * 16);
+  };
   auto items = [&](auto hist_tag) __attribute__((always_inline)) {
   constexpr bool HIST = decltype(hist_tag)::value;
   int it = threadIdx.x;
@@ -1148,7 +1232,7 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
   uint4 A[8], B[8], Wr[3];
   f32x4 w[8];
   if (it < total) {
-    cur = describe(it);
+    cur = item_of(it);
     load_win(cur, Wr);
     load8(cur, 0, A);
     load_w(cur, w);
@@ -1156,19 +1240,13 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
   }
   for (; it < total; it += 64) {
     const bool more = it + 64 < total;
-    const ConvItem nxt = more ? describe(it + 64) : cur;
+    const ConvItem nxt = more ? item_of(it + 64) : cur;
     // the window of this run: inputs, or (a sequence's first rows) history
     float win[3][8];
 #pragma unroll
     for (int m = 0; m < 3; ++m) unpack(Wr[m], win[m]);
     const bool hist_rows = HIST && cur.r0 == 0;  // t0 - 3 + m < b0 = t0 for every m
-    if (hist_rows) {
-      const float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3;
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) win[m][i] = slot_ok ? h[3 * i + m] : 0.f;
-    }
+    if (hist_rows) history_window(cur.ch, win);
     uint4 Wr2[3];
     f32x4 w2[8];
     compute8(cur, 0, A, w, win);
@@ -1179,32 +1257,7 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
     }
     compute8(cur, 8, B, w, win);
     if (more) load8(nxt, 8, B);
-    // the slot's new history: inputs b0+len-3 .. b0+len-1, entries before
-    // the sequence from the old history (read above by this lane, and
-    // again here before the store)
-    if (hist_rows && slot_ok && !cv.keep) {
-      float nh[8][3];
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int64_t p = b0 + len - 3 + m;
-        float f[8];
-        if (p >= b0) {
-          unpack(row(p, cur.ch), f);
-        } else {
-          const float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3 + (p - b0 + 3);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = h[3 * i];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) nh[i][m] = f[i];
-      }
-      float* h = cv.hist + (static_cast<size_t>(slot) * C + cur.ch) * 3;
-#pragma unroll
-      for (int q4 = 0; q4 < 6; ++q4)
-        *reinterpret_cast<f32x4*>(h + 4 * q4) =
-            f32x4{nh[(4 * q4) / 3][(4 * q4) % 3], nh[(4 * q4 + 1) / 3][(4 * q4 + 1) % 3],
-                  nh[(4 * q4 + 2) / 3][(4 * q4 + 2) % 3], nh[(4 * q4 + 3) / 3][(4 * q4 + 3) % 3]};
-    }
+    if (hist_rows && slot_ok && !cv.keep) new_history(cur.ch);
     if (more) {
       cur = nxt;
 #pragma unroll
@@ -1214,10 +1267,13 @@ __device__ __forceinline__ void conv_chunk(const ConvIn& cv, int s, int64_t b0, 
     }
   }
   };
-  if (first)
+  if (first) {
+    if (g_roll) rolling(std::true_type{});
     items(std::true_type{});
-  else
+  } else {
+    if (g_roll) rolling(std::false_type{});
     items(std::false_type{});
+  }
 }
 
 // ----------------------------------------------------------------------------
