@@ -1028,11 +1028,10 @@ __device__ __forceinline__ f32x4 mm3_la(s16x4 ah, s16x4 al, f32x4 b) {
 // lanes.  Both loops are software pipelined: the next run's rows (and an
 // item's window rows and weights) load while the current run computes, so
 // the wave's loads stay in flight through its arithmetic (the kernel holds
-// two waves per SIMD, too few to hide a load's latency otherwise).  The
-// wave of a sequence's first chunk is the
-// only one that reads the slot's history for these channels; after those
-// reads it writes the new history (the newest three of history and inputs),
-// so no later kernel is needed for it.
+// two waves per SIMD, too few to hide a load's latency otherwise).  The wave
+// of a sequence's first chunk is the only one that reads the slot's history
+// for these channels; after those reads it writes the new history (the
+// newest three of history and inputs), so no later kernel is needed for it.
 struct ConvItem {
   int ch;       // first channel of the group in the raw row
   int ostride;  // elements per output row
