@@ -181,3 +181,41 @@ def test_conv_prefill_all_empty_is_a_no_op():
     assert y.shape[0] == 0
     assert torch.equal(pool, d["pool"])
     assert torch.equal(hist, d["hist"])
+
+
+def test_conv_prefill_varlen_workload():
+    """The bench's layer workload: 8 sequences of U[512, 4096] tokens,
+    Hk=16, Hv=48, Dk=Dv=128 (10,240 raw channels), bf16, chunk 64, pool 16,
+    with the gated norm.  Every output, slot and history entry equals the
+    separate calls bit for bit; the history equals the oracle's; the oracle
+    chain checks 2 sequences on key head 11 (value heads 33..35)."""
+    c = synth.PREFILL_VARLEN
+    rng = np.random.default_rng(0)
+    Hk, Hv, Dk, Dv, P = c["Hk"], c["Hv"], c["Dk"], c["Dv"], c["pool"]
+    lengths = synth.seq_lengths(rng, c["n_seq"], c["len_lo"], c["len_hi"])
+    inp, lay, pool0 = _case(rng, lengths, Hk, Hv, Dk, Dv, P)
+    d = _dev_inputs(inp, lay, pool0)
+    y2, pool2, hist2 = _fused(d, Hk, Hv, Dk, Dv, c["chunk"], True)
+    y1, pool1, hist1 = _separate(d, Hk, Hv, Dk, Dv, c["chunk"], True)
+    assert torch.equal(y2, y1)
+    assert torch.equal(pool2, pool1)
+    assert torch.equal(hist2, hist1)
+    ci, cu = inp["cache_indices"], inp["cu_seqlens"]
+    out, h_ref = oracle.conv_silu(lay["qkv"], lay["conv_w"], lay["conv_state"], ci, cu)
+    np.testing.assert_array_equal(to_np(hist2).astype(np.float32), h_ref.astype(np.float32))
+    out = synth.round_bf16(out).astype(np.float64)
+    g, beta = oracle.gates(inp["a"], inp["b"], inp["A_log"], inp["dt_bias"])
+    nq, hk, hs = Hk * Dk, 11, np.arange(33, 36)
+    yv = to_np(y2)
+    for s in (int(np.argmax(lengths)), 5):
+        idx = np.arange(cu[s], cu[s + 1])
+        slot = int(ci[s])
+        o = out[idx]
+        q = o[:, hk * Dk:(hk + 1) * Dk][:, None]
+        k = o[:, nq + hk * Dk:nq + (hk + 1) * Dk][:, None]
+        v = o[:, 2 * nq:].reshape(len(idx), Hv, Dv)[:, hs]
+        P_ref, y_ref = oracle.gdn_prefill(q, k, v, g[idx][:, hs], beta[idx][:, hs], pool0[[slot]][:, hs], [0],
+                                          [0, len(idx)])
+        y_ref = oracle.gated_rmsnorm(y_ref, lay["z"][idx][:, hs], lay["gamma"])
+        assert maxrel(to_np(pool2[slot][hs]), P_ref[0]) <= 1e-3, s
+        check_bf16_out(yv[idx][:, hs], y_ref, f"y of sequence {s}, key head {hk}")
