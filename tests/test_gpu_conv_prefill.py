@@ -99,6 +99,7 @@ CASES = [
     ([37, 1, 0, 90, 3] * 14, 2, 16, 64, 32, 32, False),  # 70 sequences: the chunk map as its own kernel
     ([150, 66], 2, 2, 128, 128, 64, True),               # one value head per key head
     ([97, 12], 1, 8, 128, 64, 16, False),                # eight value heads per key head
+    ([77, 20, 1], 1, 2, 128, 128, 64, False),            # exactly 64 channel groups per key head
 ]
 
 
