@@ -1,8 +1,10 @@
 """GPU parity of comba_decode_step and gdn_prefill_gates against the oracle.
 
 Comba: state max relative error <= 1e-5 and, as the KBench spec grades it,
-relative Frobenius <= 2e-2 on both state_new and o (bf16 o).  Gates: fp32
-transcendentals, max relative error <= 2e-6 on g and beta.
+relative Frobenius <= 2e-2 on both state_new and o; bf16 o also element by
+element (tests.helpers.check_bf16_out: max |error| <= 1e-2 of the largest
+value, per row <= 2e-2 of the row's largest).  Gates: fp32 transcendentals,
+max relative error <= 2e-6 on g and beta.
 """
 import numpy as np
 import pytest

@@ -1,8 +1,10 @@
 """GPU parity of comba_chunk_prefill (the chunkwise Comba forward) against
 the fp64 token-by-token oracle, through the C ABI.
 
-Tolerances: pool state max relative error <= 1e-3; o (bf16) relative
-Frobenius <= 2e-2; slots no sequence names bit-exact.
+Tolerances: pool state max relative error <= 1e-3; o (bf16) element by
+element (tests.helpers.check_bf16_out: relative Frobenius <= 2e-2, max
+|error| <= 1e-2 of the largest value, per row <= 2e-2 of the row's largest);
+slots no sequence names bit-exact.
 """
 import numpy as np
 import pytest

@@ -1,8 +1,10 @@
 """GPU parity of gdn_prefill_gates + gdn_chunk_prefill against the fp64
 token-by-token oracle, and bit-exact handling of cu_seqlens/cache_indices.
 
-Tolerances: pool state max relative error <= 1e-3; y relative Frobenius
-<= 2e-2 when bf16, max relative <= 1e-3 when fp32; index handling bit-exact.
+Tolerances: pool state max relative error <= 1e-3; y max relative <= 1e-3
+when fp32, and when bf16 element by element (tests.helpers.check_bf16_out:
+relative Frobenius <= 2e-2, max |error| <= 1e-2 of the largest value, every
+row's max |error| <= 2e-2 of that row's largest); index handling bit-exact.
 """
 import numpy as np
 import pytest
